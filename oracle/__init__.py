@@ -1,0 +1,185 @@
+"""fp64 CPU oracle of the batched draft-verification sampler (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY.  This package is imported by ``tests/``, by the
+smoke check in ``__graft_entry__`` and by the CPU-baseline leg of
+``bench.py``; the product path (``draft_verification_row_amd``) never imports
+it, and it never imports the product path.  The arithmetic lives in
+``spec_oracle.c`` (plain C, fp64, libm ``exp``/``log``, OpenMP over requests);
+see that file's header for the rules and the pages each follows.
+
+Near-tie tolerances:
+  EPS_ACCEPT  |u - r| (exact) or |p - tau| (relaxed) below this flags the test.
+  EPS_SAMPLE  u closer than this to a boundary of the fp64 CDF flags the
+              terminal sample.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["build", "load", "OracleResult", "greedy", "exact", "relaxed", "tree", "row_stats",
+           "set_threads", "max_threads", "EPS_ACCEPT", "EPS_SAMPLE"]
+
+EPS_ACCEPT = 1e-6
+EPS_SAMPLE = 1e-9
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spec_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc -O2 (no fast-math) and OpenMP."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        Dd = ctypes.c_double
+        lib.oracle_set_threads.argtypes = [I]
+        lib.oracle_max_threads.restype = I
+        lib.oracle_row_stats.argtypes = [P, I, ctypes.c_long, I, P, P, P]
+        lib.oracle_greedy.argtypes = [P, I, P, I, I, I, P, P, P, P, P, P]
+        lib.oracle_exact.argtypes = [P, P, I, P, P, I, I, I, Dd, Dd, P, P, P, P, P, P, P]
+        lib.oracle_relaxed.argtypes = [P, I, P, P, I, I, I, Dd, I, Dd, Dd, P, P, P, P, P, P, P]
+        lib.oracle_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, P, P]
+        _lib = lib
+    return _lib
+
+
+def set_threads(n: int) -> None:
+    load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(load().oracle_max_threads())
+
+
+@dataclass
+class OracleResult:
+    tokens: np.ndarray          # int32 [B][L], -1 padded
+    accept_len: np.ndarray      # int32 [B]
+    target_logprob: np.ndarray  # float64 [B][L]
+    behavior_logprob: np.ndarray
+    status: np.ndarray          # int32 [B]
+    flag: np.ndarray            # int32 [B], first near-tie position or -1
+    decisions: np.ndarray       # int32 [B]
+    path: Optional[np.ndarray] = None  # tree only: node ids [B][N]
+
+
+def _dt(dtype: str) -> int:
+    return BF16 if dtype == "bf16" else F32
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _logits(a, dtype):
+    return _c(a, np.uint16 if dtype == "bf16" else np.float32)
+
+
+def row_stats(x: np.ndarray, dtype: str):
+    """(M, g, S) per row of a [..., V] logit array."""
+    x = _logits(x, dtype)
+    V = x.shape[-1]
+    rows = x.size // V
+    M = np.empty(rows, np.float64)
+    g = np.empty(rows, np.int64)
+    S = np.empty(rows, np.float64)
+    load().oracle_row_stats(_ptr(x), _dt(dtype), rows, V, _ptr(M), _ptr(g), _ptr(S))
+    shp = x.shape[:-1]
+    return M.reshape(shp), g.reshape(shp), S.reshape(shp)
+
+
+def _outs(B, L):
+    return (np.empty((B, L), np.int32), np.empty(B, np.int32), np.empty((B, L), np.float64),
+            np.empty((B, L), np.float64), np.empty(B, np.int32), np.full(B, -1, np.int32),
+            np.empty(B, np.int32))
+
+
+def greedy(target, tokens, dtype: str) -> OracleResult:
+    T = _logits(target, dtype)
+    x = _c(tokens, np.int32)
+    B, L, V = T.shape
+    K = L - 1
+    assert x.shape == (B, K)
+    tok, ln, tlp, blp, st, fl, dec = _outs(B, L)
+    load().oracle_greedy(_ptr(T), _dt(dtype), _ptr(x), B, K, V, _ptr(tok), _ptr(ln), _ptr(tlp),
+                         _ptr(blp), _ptr(st), _ptr(dec))
+    return OracleResult(tok, ln, tlp, blp, st, fl, dec)
+
+
+def exact(target, draft, tokens, uniforms, dtype: str, eps_accept: float = EPS_ACCEPT,
+          eps_sample: float = EPS_SAMPLE) -> OracleResult:
+    T = _logits(target, dtype)
+    Dr = _logits(draft, dtype)
+    x = _c(tokens, np.int32)
+    u = _c(uniforms, np.float32)
+    B, L, V = T.shape
+    K = L - 1
+    assert Dr.shape == (B, K, V) and x.shape == (B, K) and u.shape == (B, L)
+    tok, ln, tlp, blp, st, fl, dec = _outs(B, L)
+    load().oracle_exact(_ptr(T), _ptr(Dr), _dt(dtype), _ptr(x), _ptr(u), B, K, V,
+                        float(eps_accept), float(eps_sample), _ptr(tok), _ptr(ln), _ptr(tlp),
+                        _ptr(blp), _ptr(st), _ptr(fl), _ptr(dec))
+    return OracleResult(tok, ln, tlp, blp, st, fl, dec)
+
+
+def relaxed(target, tokens, uniforms, dtype: str, tau: float, top_k: int,
+            eps_accept: float = EPS_ACCEPT, eps_sample: float = EPS_SAMPLE) -> OracleResult:
+    T = _logits(target, dtype)
+    x = _c(tokens, np.int32)
+    u = _c(uniforms, np.float32)
+    B, L, V = T.shape
+    K = L - 1
+    assert x.shape == (B, K) and u.shape == (B, L)
+    tok, ln, tlp, blp, st, fl, dec = _outs(B, L)
+    load().oracle_relaxed(_ptr(T), _dt(dtype), _ptr(x), _ptr(u), B, K, V, float(tau), int(top_k),
+                          float(eps_accept), float(eps_sample), _ptr(tok), _ptr(ln), _ptr(tlp),
+                          _ptr(blp), _ptr(st), _ptr(fl), _ptr(dec))
+    return OracleResult(tok, ln, tlp, blp, st, fl, dec)
+
+
+def tree(target, node_tok, parents, dtype: str, num_nodes=None) -> OracleResult:
+    T = _logits(target, dtype)
+    B, N, V = T.shape
+    nt = _c(node_tok, np.int32)
+    par = _c(parents, np.int32)
+    assert nt.shape == (B, N) and par.shape == (B, N)
+    nn = None if num_nodes is None else _c(num_nodes, np.int32)
+    path = np.empty((B, N), np.int32)
+    tok = np.empty((B, N), np.int32)
+    ln = np.empty(B, np.int32)
+    tlp = np.empty((B, N), np.float64)
+    blp = np.empty((B, N), np.float64)
+    st = np.empty(B, np.int32)
+    load().oracle_tree(_ptr(T), _dt(dtype), _ptr(nt), _ptr(par),
+                       None if nn is None else _ptr(nn), B, N, V, _ptr(path), _ptr(tok), _ptr(ln),
+                       _ptr(tlp), _ptr(blp), _ptr(st))
+    return OracleResult(tok, ln, tlp, blp, st, np.full(B, -1, np.int32),
+                        ln.copy(), path=path)
