@@ -1,0 +1,179 @@
+/*
+ * spec_verify.h -- C ABI of the batched draft-verification sampler (gfx950).
+ *
+ * One call verifies a batch of B speculative-decoding requests.  For each
+ * request the target model has scored the K drafted positions plus one bonus
+ * position in a single verify pass, giving K+1 logit rows over a vocabulary
+ * of V tokens (mini-sglang PR #134, "Modifications": verify_drafts takes the
+ * draft tokens and the target's K+1 verify-pass logits; spec-decode README,
+ * "How it works": the target scores all k+1 positions in one forward pass).
+ * The call turns them into an accepted prefix, one bonus or residual token,
+ * and per-token target and behaviour log-probs (nanospec README, acceptance
+ * rules: every emitted token carries log pi and log mu).
+ *
+ * Memory and layout
+ *   Every pointer is a DEVICE pointer unless stated otherwise.  Logits are
+ *   row-major and contiguous: request b, row r starts at element
+ *   (b * rows + r) * V.  dtype is SPEC_BF16 (16-bit brain float, read as the
+ *   top half of an fp32) or SPEC_F32.  Rows whose start is 16-byte aligned
+ *   (pointer % 16 == 0 and V * element size % 16 == 0) take the vector fast
+ *   path; any other V is handled element by element.  Logit rows must hold
+ *   at least one finite value; -inf entries are allowed and have probability
+ *   zero; NaN and +inf give unspecified tokens (never out-of-bounds access).
+ *   Softmax is taken at temperature 1; callers pre-scale for other
+ *   temperatures.
+ *
+ * Outputs (caller-owned, device)
+ *   out_tokens[b][i]            emitted tokens, i <= out_accept_len[b];
+ *                               later entries are set to -1
+ *   out_accept_len[b]           number of accepted drafts (0..K); the
+ *                               request emits out_accept_len[b] + 1 tokens
+ *   out_target_logprob[b][i]    log p_i(token i) under the target softmax
+ *   out_behavior_logprob[b][i]  log mu(token i), the probability that this
+ *                               sampler emitted it given the drafted token
+ *                               (nanospec README, acceptance rules); both
+ *                               log-prob arrays may be NULL (then not
+ *                               written); later entries are set to 0
+ *   out_status[b]               0, or 1 when the request's device data was
+ *                               malformed (a consulted draft token outside
+ *                               [0,V), or a tree parent outside [-1, i)):
+ *                               the offending draft counts as rejected and
+ *                               the offending tree node as unmatched.
+ *
+ * Randomness is supplied by the caller (spec-decode README, "Use it": the
+ * generator takes an rng), as uniforms[b][K+1] in [0,1): uniforms[b][j]
+ * drives the acceptance test of draft j, uniforms[b][K] drives the terminal
+ * sample.  Identical inputs give bitwise-identical outputs.
+ *
+ * Workspace
+ *   Each call needs a device workspace of at least
+ *   spec_verify_workspace_bytes(B, rows_per_request, V) bytes, 256-byte
+ *   aligned, ZERO-FILLED BEFORE ITS FIRST USE.  Every completed call leaves
+ *   it zero-filled again, so it can be reused by later calls on the same
+ *   stream.  Calls that run concurrently (different streams) need different
+ *   workspaces.  The library allocates nothing and keeps no state.
+ *
+ * Streams and errors
+ *   stream is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *   their kernels and return without synchronising.  Argument errors are
+ *   detected on the host before anything is enqueued and return SPEC_EINVAL,
+ *   SPEC_EDTYPE or SPEC_EWORKSPACE; a failed launch returns SPEC_EHIP.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_EINVAL = 1,     /* bad size, null required pointer, bad tau/top_k */
+    SPEC_EDTYPE = 2,     /* dtype is neither SPEC_F32 nor SPEC_BF16 */
+    SPEC_EWORKSPACE = 3, /* workspace null, misaligned or too small */
+    SPEC_EHIP = 4        /* the HIP runtime refused a launch */
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Largest K (drafts per request) and N (tree nodes per request). */
+#define SPEC_MAX_K 63
+#define SPEC_MAX_NODES 64
+
+/*
+ * Host-only query.  rows_per_request is the number of logit rows one request
+ * streams: K+1 for greedy and relaxed, 2K+1 for exact (target K+1 plus
+ * draft K), N for tree.  Returns 0 for invalid sizes.
+ */
+size_t spec_verify_workspace_bytes(int B, int rows_per_request, int V);
+
+/* Host-only: static description of a status code. */
+const char *spec_status_string(int status);
+
+/*
+ * Greedy chain verification (mini-sglang PR #134, "Modifications",
+ * verify_drafts): draft j is accepted while it equals the argmax of target
+ * row j (lowest index among equal maxima); the first unmatched row (row K if
+ * all match) contributes its argmax as the bonus token.  Behaviour log-probs
+ * are 0 (the rule is deterministic).
+ *
+ *   target_logits  [B][K+1][V]   dtype
+ *   draft_tokens   [B][K]        int32
+ *   outputs        tokens/log-probs [B][K+1], accept_len/status [B]
+ * Log-probs cost one exp per logit; pass NULL for both to skip them.
+ */
+spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
+                               const int32_t *draft_tokens, int B, int K, int V,
+                               int32_t *out_tokens, int32_t *out_accept_len,
+                               float *out_target_logprob, float *out_behavior_logprob,
+                               int32_t *out_status, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * Exact (lossless) speculative sampling (spec-decode README, "How it works"
+ * and "Provably exact"): with p = softmax(target row j), q = softmax(draft
+ * row j), draft x_j is accepted iff uniforms[b][j] < p(x_j)/q(x_j), in order;
+ * at the first rejection n the sampler emits y ~ normalize(relu(p_n - q_n))
+ * and stops; if all K are accepted it emits y ~ p_K.  y is the inverse CDF of
+ * that distribution in ascending token order at uniforms[b][K].  Behaviour
+ * log-probs: min(0, log p - log q) for accepted drafts, log(1 - r_n) +
+ * log w(y) - log Z for a residual sample, log p_K(y) for the bonus.
+ *
+ *   target_logits  [B][K+1][V], draft_logits [B][K][V], same dtype
+ *   draft_tokens   [B][K] int32, uniforms [B][K+1] float
+ */
+spec_status spec_verify_exact(const void *target_logits, const void *draft_logits,
+                              spec_dtype dtype, const int32_t *draft_tokens, const float *uniforms,
+                              int B, int K, int V, int32_t *out_tokens, int32_t *out_accept_len,
+                              float *out_target_logprob, float *out_behavior_logprob,
+                              int32_t *out_status, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * Relaxed acceptance (nanospec README, acceptance rules): draft x_j is
+ * accepted iff p_j(x_j) >= tau or x_j is in the target's top-k, where top-k
+ * membership is rank based: #{t : l_t > l_{x_j}} < top_k (tied tokens share
+ * a rank).  The rule is deterministic, so accepted drafts carry behaviour
+ * log-prob 0.  After the first rejection n (or n = K) the sampler emits
+ * y ~ p_n by inverse CDF at uniforms[b][K], with behaviour log-prob log p_n(y).
+ * Only uniforms[b][K] is read.  tau must not be NaN; top_k >= 0.
+ */
+spec_status spec_verify_relaxed(const void *target_logits, spec_dtype dtype,
+                                const int32_t *draft_tokens, const float *uniforms, int B, int K,
+                                int V, float tau, int top_k, int32_t *out_tokens,
+                                int32_t *out_accept_len, float *out_target_logprob,
+                                float *out_behavior_logprob, int32_t *out_status, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy tree verification (nanospec README: EAGLE-style chain/tree
+ * speculation whose output is identical to plain greedy decoding).  Node 0
+ * is the root (the last committed token; its token is not verified); node
+ * i >= 1 carries node_tokens[b][i] and has parent parents[b][i] < i.  Row i
+ * of the logits scores the token that follows node i.  A node is accepted
+ * when its token equals the argmax of its parent's row and its parent is
+ * accepted.  The deepest accepted node e (lowest index among equal depths)
+ * defines the emitted path; the argmax of row e is the bonus token.
+ *
+ *   target_logits   [B][N][V]
+ *   node_tokens     [B][N] int32, parents [B][N] int32 (parents[b][0] ignored)
+ *   num_nodes       [B] int32 valid nodes per request (1..N), or NULL for N
+ *   out_path_nodes  [B][N] accepted node ids root-first (root excluded), -1 pad
+ *   out_tokens, out_target_logprob, out_behavior_logprob [B][N]
+ */
+spec_status spec_verify_tree(const void *target_logits, spec_dtype dtype,
+                             const int32_t *node_tokens, const int32_t *parents,
+                             const int32_t *num_nodes, int B, int N, int V,
+                             int32_t *out_path_nodes, int32_t *out_tokens, int32_t *out_accept_len,
+                             float *out_target_logprob, float *out_behavior_logprob,
+                             int32_t *out_status, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,116 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and
+rejects bad arguments before anything is enqueued.  No kernel is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import draft_verification_row_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP = range(5)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed",
+                          "spec_verify_tree", "spec_verify_workspace_bytes", "spec_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.spec_status_string(code)
+    assert b"unknown" in lib.spec_status_string(99)
+
+
+def test_workspace_query(lib):
+    q = lib.spec_verify_workspace_bytes
+    assert q(0, 6, 100) == 0 and q(1, 0, 100) == 0 and q(1, 6, 0) == 0 and q(1, 128, 10) == 0
+    assert q(65537, 6, 100) == 0
+    a, b, c = q(8, 6, 128256), q(32, 11, 128256), q(32, 11, 151936)
+    assert 0 < a < b < c
+    assert a % 256 == 0
+    assert a >= 65536 * 16  # fixed control area
+
+
+ws_buf = (ctypes.c_uint8 * 64)()  # host memory: only its address is inspected
+
+
+def _greedy(lib, **over):
+    args = dict(T=ctypes.c_void_p(4096), dt=1, x=ctypes.c_void_p(4096), B=2, K=3, V=100,
+                tok=ctypes.c_void_p(4096), ln=ctypes.c_void_p(4096), tlp=None, blp=None,
+                st=ctypes.c_void_p(4096), ws=ctypes.c_void_p(1 << 20), wsb=0, stream=None)
+    args.update(over)
+    return lib.spec_verify_greedy(*args.values())
+
+
+def test_greedy_argument_errors(lib):
+    assert _greedy(lib, dt=2) == SPEC_EDTYPE
+    assert _greedy(lib, B=0) == SPEC_EINVAL
+    assert _greedy(lib, K=0) == SPEC_EINVAL
+    assert _greedy(lib, K=64) == SPEC_EINVAL
+    assert _greedy(lib, V=0) == SPEC_EINVAL
+    assert _greedy(lib, T=None) == SPEC_EINVAL
+    assert _greedy(lib, x=None) == SPEC_EINVAL
+    assert _greedy(lib, st=None) == SPEC_EINVAL
+    assert _greedy(lib, ws=None) == SPEC_EWORKSPACE
+    assert _greedy(lib, ws=ctypes.c_void_p((1 << 20) + 8)) == SPEC_EWORKSPACE  # misaligned
+    assert _greedy(lib, wsb=1024) == SPEC_EWORKSPACE                           # too small
+
+
+def test_exact_relaxed_tree_argument_errors(lib):
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    need = lib.spec_verify_workspace_bytes(2, 7, 100)
+    # exact: missing draft logits, missing uniforms
+    assert lib.spec_verify_exact(p, None, 1, p, p, 2, 3, 100, p, p, None, None, p, ws, need,
+                                 None) == SPEC_EINVAL
+    assert lib.spec_verify_exact(p, p, 1, p, None, 2, 3, 100, p, p, None, None, p, ws, need,
+                                 None) == SPEC_EINVAL
+    assert lib.spec_verify_exact(p, p, 9, p, p, 2, 3, 100, p, p, None, None, p, ws, need,
+                                 None) == SPEC_EDTYPE
+    # relaxed: NaN tau, negative top_k
+    assert lib.spec_verify_relaxed(p, 1, p, p, 2, 3, 100, ctypes.c_float(float("nan")), 4, p, p,
+                                   None, None, p, ws, need, None) == SPEC_EINVAL
+    assert lib.spec_verify_relaxed(p, 1, p, p, 2, 3, 100, ctypes.c_float(0.1), -1, p, p, None,
+                                   None, p, ws, need, None) == SPEC_EINVAL
+    # tree: N out of range, missing parents
+    assert lib.spec_verify_tree(p, 1, p, p, None, 2, 65, 100, p, p, p, None, None, p, ws, need,
+                                None) == SPEC_EINVAL
+    assert lib.spec_verify_tree(p, 1, p, None, None, 2, 8, 100, p, p, p, None, None, p, ws, need,
+                                None) == SPEC_EINVAL
+    assert lib.spec_verify_tree(p, 1, p, p, None, 2, 8, 100, p, p, p, None, None, p, ws, 16,
+                                None) == SPEC_EWORKSPACE
+
+
+def test_binding_rejects_host_tensors():
+    T = torch.zeros((2, 4, 50), dtype=torch.bfloat16)
+    x = torch.zeros((2, 3), dtype=torch.int32)
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_greedy(T, x)
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_exact(T, T[:, :3], x, torch.zeros((2, 4)))
+
+
+def test_header_has_no_torch_or_hip_types():
+    src = open(HEADER).read()
+    assert "torch" not in src.lower().replace("torch tensors", "")
+    assert "#include <hip" not in src

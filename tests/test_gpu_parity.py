@@ -1,0 +1,307 @@
+"""Parity of the HIP library (through the C ABI) with the fp64 oracle.
+
+Every test here runs on an MI355X.  Inputs come from the seeded generators in
+``synth``; expected values come only from ``oracle``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_verification_row_amd as sv
+import oracle
+import synth
+from parity import Tally, compare_chain, compare_tree, dev, dev_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def _exact(ci, **kw):
+    T = dev_logits(ci.target, ci.dtype)
+    D = dev_logits(ci.draft, ci.dtype)
+    r = sv.spec_verify_exact(T, D, dev(ci.tokens), dev(ci.uniforms), **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _greedy(ci, **kw):
+    r = sv.spec_verify_greedy(dev_logits(ci.target, ci.dtype), dev(ci.tokens), **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _relaxed(ci, **kw):
+    r = sv.spec_verify_relaxed(dev_logits(ci.target, ci.dtype), dev(ci.tokens), dev(ci.uniforms),
+                               ci.tau, ci.top_k, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _tree(ti, **kw):
+    r = sv.spec_verify_tree(dev_logits(ti.target, ti.dtype), dev(ti.node_tok), dev(ti.parents),
+                            dev(ti.num_nodes), **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+# ------------------------------------------------------------------ greedy
+@pytest.mark.parametrize("rnd", range(6))
+def test_greedy_c2_full_size(rnd):
+    """B=8, K=5, V=128256 bf16; the accepted length equals the construction."""
+    ci = synth.c2(rnd=rnd)
+    print(f"greedy c2 round {rnd}", flush=True)
+    o = oracle.greedy(ci.target, ci.tokens, "bf16")
+    np.testing.assert_array_equal(o.accept_len, ci.expected_accept_len)
+    compare_chain(_greedy(ci), o, what=f"c2 r{rnd}")
+    r = _greedy(ci, logprobs=False)
+    assert r.target_logprob is None
+    compare_chain(r, o, logprobs=False, what=f"c2 r{rnd} no-logprob")
+
+
+def test_greedy_c3_shape():
+    ci = synth.c3()
+    o = oracle.greedy(ci.target, ci.tokens, "bf16")
+    compare_chain(_greedy(ci), o, what="c3-shape greedy")
+
+
+@pytest.mark.parametrize("K", [1, 2, 5, 8, 63])
+def test_greedy_scenarios(K):
+    """all-correct + bonus, all-reject and every interior partial accept."""
+    rng = np.random.default_rng(200 + K)
+    V = 3001
+    B = K + 1
+    t = synth.bf16_rne(3.0 * rng.standard_normal((B, K + 1, V), dtype=np.float32))
+    g = np.argmax(synth.bf16_to_f32(t), -1)
+    x = g[:, :K].copy()
+    for n in range(K):  # request n rejects at position n; request K accepts all
+        x[n, n] = (g[n, n] + 1 + rng.integers(0, V - 1)) % V
+        while synth.bf16_to_f32(t[n, n])[x[n, n]] == synth.bf16_to_f32(t[n, n]).max():
+            x[n, n] = (x[n, n] + 1) % V
+    ci = synth.ChainInputs("scen", "bf16", B, K, V, t, None, x.astype(np.int32),
+                           np.zeros((B, K + 1), np.float32))
+    o = oracle.greedy(ci.target, ci.tokens, "bf16")
+    np.testing.assert_array_equal(o.accept_len, np.arange(K + 1))
+    compare_chain(_greedy(ci), o, what=f"scenarios K={K}")
+
+
+# ------------------------------------------------------------------- exact
+def test_exact_c1_batched():
+    """1000 rounds of B=1, K=4, V=32 fp32, run as one B=1000 call."""
+    ci = synth.c1()
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32")
+    t = compare_chain(_exact(ci), o, what="c1 batched")
+    assert t.within_budget(), t
+    og = oracle.greedy(ci.target, ci.tokens, "f32")
+    compare_chain(_greedy(ci), og, what="c1 greedy")
+
+
+def test_exact_c1_single_requests():
+    """The same rounds as individual B=1 calls (first 100)."""
+    ci = synth.c1()
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32")
+    tot = Tally()
+    for r in range(100):
+        sub = synth.ChainInputs("c1", "f32", 1, 4, 32, ci.target[r:r + 1], ci.draft[r:r + 1],
+                                ci.tokens[r:r + 1], ci.uniforms[r:r + 1])
+        osub = oracle.OracleResult(*(getattr(o, f)[r:r + 1] for f in
+                                     ("tokens", "accept_len", "target_logprob",
+                                      "behavior_logprob", "status", "flag", "decisions")))
+        tot.add(compare_chain(_exact(sub), osub, what=f"c1 round {r}"))
+    assert tot.within_budget(), tot
+
+
+@pytest.mark.parametrize("rnd", range(4))
+def test_exact_c3_full_size(rnd):
+    """B=32, K=5, V=128256 bf16 -- the benchmarked configuration."""
+    print(f"exact c3 round {rnd}", flush=True)
+    ci = synth.c3(rnd=rnd)
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")
+    t = compare_chain(_exact(ci), o, what=f"c3 r{rnd}")
+    assert t.within_budget(), t
+
+
+def test_exact_c5_full_size():
+    print("exact c5", flush=True)
+    ci = synth.c5()
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")
+    t = compare_chain(_exact(ci), o, what="c5 exact")
+    assert t.within_budget(), t
+
+
+# ----------------------------------------------------------------- relaxed
+def test_relaxed_c5_full_size():
+    print("relaxed c5", flush=True)
+    ci = synth.c5()
+    o = oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", ci.tau, ci.top_k)
+    t = compare_chain(_relaxed(ci), o, what="c5 relaxed")
+    assert t.within_budget(), t
+
+
+@pytest.mark.parametrize("tau,k", [(2.0, 0), (-1.0, 0), (2.0, 1), (0.05, 2), (0.5, 10)])
+def test_relaxed_special_cases(tau, k):
+    ci = synth.chain_inputs(16, 6, 20000, "bf16", seed=61, useed=62, d_noise=0.3)
+    ci.tau, ci.top_k = tau, k
+    o = oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", tau, k)
+    compare_chain(_relaxed(ci), o, what=f"relaxed tau={tau} k={k}")
+
+
+# -------------------------------------------------------------------- tree
+@pytest.mark.parametrize("rnd", range(3))
+def test_tree_c4_full_size(rnd):
+    print(f"tree c4 round {rnd}", flush=True)
+    ti = synth.c4(rnd=rnd)
+    o = oracle.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes)
+    for b in range(ti.B):
+        assert list(o.path[b, : o.accept_len[b]]) == ti.expected_path[b]
+    compare_tree(_tree(ti), o, what=f"c4 r{rnd}")
+    r = _tree(ti, logprobs=False)
+    compare_tree(r, o, logprobs=False, what=f"c4 r{rnd} no-logprob")
+
+
+def test_tree_chain_equals_greedy_on_gpu():
+    ci = synth.chain_inputs(8, 7, 5003, "bf16", seed=71, useed=72, with_draft=False)
+    g = np.argmax(synth.bf16_to_f32(ci.target), -1)
+    x = g[:, :7].copy()
+    x[np.random.default_rng(73).random(x.shape) < 0.3] = 11
+    ci.tokens = x.astype(np.int32)
+    N = 8
+    ti = synth.TreeInputs("chain", "bf16", 8, N, 5003, ci.target,
+                          np.concatenate([np.zeros((8, 1), np.int32), ci.tokens], 1),
+                          np.tile(np.arange(-1, N - 1, dtype=np.int32), (8, 1)),
+                          np.full(8, N, np.int32))
+    rt = _tree(ti)
+    rg = _greedy(ci)
+    ln = rg.accept_len.cpu().numpy()
+    np.testing.assert_array_equal(rt.accept_len.cpu().numpy(), ln)
+    tt, gt = rt.tokens.cpu().numpy(), rg.tokens.cpu().numpy()
+    for b in range(8):
+        np.testing.assert_array_equal(tt[b, : ln[b] + 1], gt[b, : ln[b] + 1])
+
+
+def test_tree_partial_node_counts_and_bad_parents():
+    ti = synth.tree_inputs(B=6, V=3001, seed=75)
+    ti.num_nodes = np.array([61, 1, 2, 30, 60, 17], np.int32)
+    ti.parents = ti.parents.copy()
+    ti.parents[3, 5] = 40     # not < 5: malformed
+    ti.node_tok = ti.node_tok.copy()
+    ti.node_tok[4, 7] = 10 ** 6  # out of vocabulary: malformed
+    o = oracle.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes)
+    assert o.status[3] == 1 and o.status[4] == 1
+    compare_tree(_tree(ti), o, what="tree edge")
+
+
+# ------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("B,K,V,dtype", [
+    (3, 1, 1, "bf16"), (3, 2, 2, "f32"), (5, 3, 7, "bf16"), (4, 4, 1000, "f32"),
+    (2, 5, 8191, "bf16"), (2, 5, 8193, "bf16"), (3, 3, 16385, "f32"), (2, 63, 300, "bf16"),
+    (40, 2, 2051, "bf16"), (1, 5, 128257, "bf16"),
+])
+def test_exact_greedy_relaxed_ragged_shapes(B, K, V, dtype):
+    """Sizes spanning several chunks with a ragged tail, odd V (element path),
+    V = 1, and the largest K."""
+    print(f"ragged B={B} K={K} V={V} {dtype}", flush=True)
+    ci = synth.chain_inputs(B, K, V, dtype, seed=1000 + V, useed=2000 + K)
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, dtype)
+    compare_chain(_exact(ci), o, what=f"exact {B},{K},{V}")
+    og = oracle.greedy(ci.target, ci.tokens, dtype)
+    compare_chain(_greedy(ci), og, what=f"greedy {B},{K},{V}")
+    orl = oracle.relaxed(ci.target, ci.tokens, ci.uniforms, dtype, 0.1, 4)
+    ci.tau, ci.top_k = 0.1, 4
+    compare_chain(_relaxed(ci), orl, what=f"relaxed {B},{K},{V}")
+
+
+def test_misaligned_rows_take_element_path():
+    """A view starting one element into an allocation is not 16-byte aligned."""
+    ci = synth.chain_inputs(3, 4, 4096, "bf16", seed=81, useed=82)
+    big = np.zeros(ci.target.size + 1, np.uint16)
+    big[1:] = ci.target.ravel()
+    T = dev_logits(big, "bf16")[1:].view(ci.target.shape)
+    bigd = np.zeros(ci.draft.size + 1, np.uint16)
+    bigd[1:] = ci.draft.ravel()
+    D = dev_logits(bigd, "bf16")[1:].view(ci.draft.shape)
+    assert T.data_ptr() % 16 != 0
+    r = sv.spec_verify_exact(T, D, dev(ci.tokens), dev(ci.uniforms))
+    torch.cuda.synchronize()
+    compare_chain(r, oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
+                  what="misaligned")
+
+
+def test_out_of_range_draft_tokens_set_status():
+    ci = synth.chain_inputs(6, 4, 5000, "bf16", seed=83, useed=84)
+    ci.tokens = ci.tokens.copy()
+    ci.tokens[0, 0] = -1
+    ci.tokens[1, 2] = 5000
+    ci.tokens[2, 3] = 2 ** 30
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")
+    r = _exact(ci)
+    compare_chain(r, o, what="oor exact")
+    assert r.status.cpu().numpy()[0] == 1
+    og = oracle.greedy(ci.target, ci.tokens, "bf16")
+    compare_chain(_greedy(ci), og, what="oor greedy")
+
+
+def test_masked_vocabulary_minus_inf():
+    """-inf logits have probability zero and are never emitted."""
+    ci = synth.chain_inputs(8, 3, 4000, "f32", seed=85, useed=86)
+    t = ci.target.copy()
+    d = ci.draft.copy()
+    t[:, :, 1000:2000] = -np.inf
+    d[:, :, 1500:2500] = -np.inf
+    ci.target, ci.draft = t, d
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32")
+    r = _exact(ci)
+    compare_chain(r, o, what="masked")
+    toks = r.tokens.cpu().numpy()
+    assert not ((toks >= 1000) & (toks < 2000)).any()
+
+
+def test_bitwise_determinism():
+    ci = synth.chain_inputs(16, 5, 50000, "bf16", seed=87, useed=88)
+    a = _exact(ci)
+    b = _exact(ci)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_workspace_reuse_across_shapes():
+    """The workspace is left zeroed: calls of different shapes can share it."""
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(64, 17, 151936), dtype=torch.uint8,
+                     device="cuda")
+    for (B, K, V) in [(4, 3, 5000), (32, 5, 20000), (2, 8, 3000), (32, 5, 20000)]:
+        ci = synth.chain_inputs(B, K, V, "bf16", seed=B * 7 + K, useed=V)
+        T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
+        r = sv.spec_verify_exact(T, D, dev(ci.tokens), dev(ci.uniforms), workspace=ws)
+        g = sv.spec_verify_greedy(T, dev(ci.tokens), workspace=ws)
+        torch.cuda.synchronize()
+        compare_chain(r, oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
+                      what=f"reuse exact {B},{K},{V}")
+        compare_chain(g, oracle.greedy(ci.target, ci.tokens, "bf16"), what=f"reuse greedy {B}")
+    assert int(ws[: 16 * 64].count_nonzero()) == 0
+
+
+# --------------------------------------------------------- statistical pin
+def test_first_token_histogram_matches_target():
+    """Fixed logits at V=32 and many uniforms: the law of the first emitted
+    token equals p_0 (spec-decode README, "Provably exact": empirical output
+    frequencies match target-only sampling).  This pins the GPU path without
+    the oracle."""
+    rng = np.random.default_rng(91)
+    V, K, n = 32, 2, 400000
+    t = (2.0 * rng.standard_normal((K + 1, V))).astype(np.float32)
+    d = (t[:K] + 0.7 * rng.standard_normal((K, V))).astype(np.float32)
+    q0 = np.exp(d[0].astype(np.float64) - d[0].max()); q0 /= q0.sum()
+    p0 = np.exp(t[0].astype(np.float64) - t[0].max()); p0 /= p0.sum()
+    x = np.stack([rng.choice(V, size=n, p=q0)] +
+                 [rng.integers(0, V, size=n) for _ in range(K - 1)], 1).astype(np.int32)
+    u = rng.random((n, K + 1), dtype=np.float32)
+    m = 50000  # requests per call (the library takes at most 65536)
+    T = torch.from_numpy(np.broadcast_to(t, (m, K + 1, V)).copy()).cuda()
+    D = torch.from_numpy(np.broadcast_to(d, (m, K, V)).copy()).cuda()
+    obs = np.zeros(V, np.int64)
+    for s in range(0, n, m):
+        r = sv.spec_verify_exact(T, D, dev(x[s:s + m]), dev(u[s:s + m]))
+        torch.cuda.synchronize()
+        obs += np.bincount(r.tokens[:, 0].cpu().numpy(), minlength=V)
+    exp = p0 * n
+    chi2 = ((obs - exp) ** 2 / exp).sum()
+    # chi-square with 31 degrees of freedom: P(chi2 > 70) < 1e-4
+    assert chi2 < 70, chi2
