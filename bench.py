@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched draft-verification sampler on one MI355X.
+
+Workload (one step = one exact verification call over one batch):
+    B=32 requests, K=5 drafts, V=128256, bf16 logits; target 3*N(0,1), draft
+    = target + 0.5*N(0,1), drafts sampled from the draft softmax, seeded fp32
+    uniforms.  Inputs are resident in HBM before timing starts.
+
+The timed loop rotates through enough distinct copies of the inputs that
+their total size is at least twice the 256 MB last-level cache (MALL), so
+logits are streamed from HBM, not from that cache.  The K timed calls are
+captured into one HIP graph and replayed once between two events (launches
+then cost no host time); the same loop run eagerly is reported alongside.
+
+The streaming kernel's duration is measured with HIP events that the library
+records around it (spec_verify_profile_next_call) over K further calls; its
+algorithmic bytes (every logit once, plus tokens, uniforms and outputs)
+divided by that duration give the roofline figure.  The fp64 CPU oracle is
+timed on a bounded sample of the same workload on the host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain 1 GiB device copy, for counters
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 1024 * 1024
+METRIC = "verify rounds/s + achieved HBM GB/s (% of peak), B=32 K=5 V=128256 bf16"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-graph", action="store_true", help="time the eager loop only")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls used for event timing."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.lib.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    t0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps,
+                      "ms_per_copy": ms, "gbs_read_plus_write": 2 * n / ms / 1e6}))
+
+
+class Case:
+    """Resident input sets and prebuilt C-call arguments for one entry point."""
+
+    def __init__(self, lib, mode, ci, sets, torch, dev):
+        import draft_verification_row_amd as sv
+        from numpy import int16
+        self.lib, self.mode, self.ci, self.sets = lib, mode, ci, sets
+        B, K, V = ci.B, ci.K, ci.V
+        T0 = torch.from_numpy(ci.target.view(int16)).view(torch.bfloat16).to(dev)
+        D0 = (torch.from_numpy(ci.draft.view(int16)).view(torch.bfloat16).to(dev)
+              if mode == "exact" else None)
+        x0 = torch.from_numpy(ci.tokens).to(dev)
+        u0 = torch.from_numpy(ci.uniforms).to(dev)
+        rows = 2 * K + 1 if mode == "exact" else K + 1
+        self.ws = torch.zeros(sv.spec_verify_workspace_bytes(B, rows, V), dtype=torch.uint8,
+                              device=dev)
+        self.inputs, self.outputs = [], []
+        for s in range(sets):
+            T = T0.clone()
+            D = D0.clone() if D0 is not None else None
+            self.inputs.append((T, D, x0.clone(), u0.clone()))
+            out = dict(tok=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                       ln=torch.empty(B, dtype=torch.int32, device=dev),
+                       st=torch.empty(B, dtype=torch.int32, device=dev))
+            if mode == "exact":
+                out["tlp"] = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
+                out["blp"] = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
+            self.outputs.append(out)
+        del T0, D0
+        self.torch = torch
+
+    def args(self, s, stream):
+        B, K, V = self.ci.B, self.ci.K, self.ci.V
+        T, D, x, u = self.inputs[s]
+        o = self.outputs[s]
+        P = ctypes.c_void_p
+        ws = self.ws
+        if self.mode == "exact":
+            return (P(T.data_ptr()), P(D.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K,
+                    V, P(o["tok"].data_ptr()), P(o["ln"].data_ptr()), P(o["tlp"].data_ptr()),
+                    P(o["blp"].data_ptr()), P(o["st"].data_ptr()), P(ws.data_ptr()), ws.numel(),
+                    P(stream))
+        return (P(T.data_ptr()), 1, P(x.data_ptr()), B, K, V, P(o["tok"].data_ptr()),
+                P(o["ln"].data_ptr()), None, None, P(o["st"].data_ptr()), P(ws.data_ptr()),
+                ws.numel(), P(stream))
+
+    def fn(self):
+        return self.lib.spec_verify_exact if self.mode == "exact" else self.lib.spec_verify_greedy
+
+    def run(self, n, start=0, stream=None):
+        torch = self.torch
+        st = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        f = self.fn()
+        argv = [self.args(s, st) for s in range(self.sets)]
+        for i in range(start, start + n):
+            rc = f(*argv[i % self.sets])
+            if rc != 0:
+                raise RuntimeError(f"{self.mode} call failed with status {rc}")
+
+    def snapshot(self):
+        return [{k: v.clone() for k, v in o.items()} for o in self.outputs]
+
+
+def time_case(case, steps, warmup, hip, use_graph):
+    import torch
+    case.run(warmup)
+    torch.cuda.synchronize()
+    res = {}
+    # eager loop
+    a, b = hip.event(), hip.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(a, ctypes.c_void_p(stream))
+    case.run(steps, stream=stream)
+    hip.lib.hipEventRecord(b, ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    res["eager_ms_per_step"] = hip.elapsed_ms(a, b) / steps
+    eager_out = case.snapshot()
+    # graph replay of exactly `steps` calls
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            case.run(steps, stream=torch.cuda.current_stream().cuda_stream)
+        g.replay()  # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        res["graph_ms_per_step"] = t0.elapsed_time(t1) / steps
+        # the timed replays must reproduce the eager results bit for bit
+        for o1, o2 in zip(eager_out, case.snapshot()):
+            for k in o1:
+                if not torch.equal(o1[k], o2[k]):
+                    raise RuntimeError(f"graph replay output {k} differs from the eager call")
+        del g
+    # streaming-kernel durations through the library's event hook
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    f = case.fn()
+    argv = [case.args(s, stream) for s in range(case.sets)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        case.lib.spec_verify_profile_next_call(evs[i][0], evs[i][1])
+        assert f(*argv[i % case.sets]) == 0
+    torch.cuda.synchronize()
+    ks = [hip.elapsed_ms(x, y) for x, y in evs]
+    res["kernel_ms_mean"] = sum(ks) / len(ks)
+    res["kernel_ms_min"] = min(ks)
+    for x, y in evs:
+        hip.destroy(x)
+        hip.destroy(y)
+    hip.destroy(a)
+    hip.destroy(b)
+    return res
+
+
+def cpu_baseline(ci, seconds):
+    import oracle
+    oracle.load()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "rounds/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{n} exact verification calls of the benchmark batch (B=32, K=5, "
+                      f"V=128256 bf16) on the same inputs, {el:.1f} s, fp64 C oracle, "
+                      f"OpenMP over requests"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(requests shard across GPUs with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+
+    import draft_verification_row_amd as sv
+    import synth
+
+    lib = sv.load_library()
+    lib.spec_verify_profile_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.spec_verify_profile_next_call.restype = None
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    ci = synth.c3()
+    bytes_exact = ci.algorithmic_bytes_exact
+    bytes_greedy = ci.algorithmic_bytes_greedy
+    sets_exact = math.ceil(2 * MALL_BYTES / bytes_exact)
+    sets_greedy = math.ceil(2 * MALL_BYTES / bytes_greedy)
+    use_graph = not args.no_graph
+
+    ex = Case(lib, "exact", ci, sets_exact, torch, dev)
+    r_ex = time_case(ex, args.steps, args.warmup, hip, use_graph)
+    del ex
+    gr = Case(lib, "greedy", ci, sets_greedy, torch, dev)
+    r_gr = time_case(gr, args.steps, args.warmup, hip, use_graph)
+    del gr
+    torch.cuda.synchronize()
+
+    ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
+    value = 1000.0 / ms
+    k_ms = r_ex["kernel_ms_mean"]
+    achieved = bytes_exact / (k_ms * 1e-3) / 1e9
+    g_ms = r_gr["graph_ms_per_step"] if use_graph else r_gr["eager_ms_per_step"]
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "exact verification (min(1,p/q) + residual), B=32 K=5 V=128256 "
+                               "bf16, target 3*N(0,1), draft target+0.5*N(0,1)",
+                   "B": ci.B, "K": ci.K, "V": ci.V, "input_sets": sets_exact,
+                   "launch": "hip graph replay of the timed calls" if use_graph else "eager"},
+        "hbm_gbs_call": bytes_exact / (ms * 1e-3) / 1e9,
+        "hbm_frac_call": bytes_exact / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_pass1<bf16, exact> (streams every logit once)",
+                     "kernel_us_mean": k_ms * 1e3, "kernel_us_min": r_ex["kernel_ms_min"] * 1e3,
+                     "algorithmic_bytes_per_launch": bytes_exact},
+        "eager": {"rounds_per_s": 1000.0 / r_ex["eager_ms_per_step"],
+                  "ms_per_step": r_ex["eager_ms_per_step"]},
+        "greedy_c3_shape": {
+            "rounds_per_s": 1000.0 / g_ms, "ms_per_step": g_ms,
+            "hbm_gbs_call": bytes_greedy / (g_ms * 1e-3) / 1e9,
+            "kernel_us_mean": r_gr["kernel_ms_mean"] * 1e3,
+            "kernel_gbs": bytes_greedy / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9,
+            "kernel_frac": bytes_greedy / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "eager_rounds_per_s": 1000.0 / r_gr["eager_ms_per_step"],
+            "algorithmic_bytes": bytes_greedy, "input_sets": sets_greedy},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(ci, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,9 +23,10 @@
 //           per vector, fp64 across vectors), and the rank count
 //           #{t : l_t > l_x}.  Waves reduce with cross-lane shuffles, the
 //           four waves combine through LDS in a fixed order, and the chunk
-//           partial goes to the workspace.  An atomic ticket per request
-//           elects the last workgroup of the request, which combines the
-//           chunk partials of every row (fixed order, fp64), evaluates the
+//           partial is published to the workspace.  An atomic ticket per
+//           request elects the last workgroup of the request, which gathers
+//           the chunk partials of every row and combines them (fixed order,
+//           fp64), evaluates the
 //           acceptance tests of all K drafts at once (one lane per draft,
 //           fp64), finds the first rejection with a wave ballot, and writes
 //           the accepted prefix.  Greedy and tree calls finish here.
@@ -43,6 +44,18 @@
 // Every reduction runs in a fixed order, so results are bitwise
 // reproducible.  No float atomics are used; atomics only elect the last
 // workgroup.
+//
+// Cross-workgroup hand-off.  The workgroups of one request run on all eight
+// XCDs, whose L2 caches are not coherent with each other.  A release/acquire
+// fence at device scope would make every workgroup write back and invalidate
+// its whole L2, which stalls the streaming kernel.  Instead each partial is
+// published as 64-bit words that carry a tag in their upper half
+// (payload | kTag << 32), written and read with relaxed device-scope atomics,
+// which the hardware keeps coherent across XCDs without cache maintenance.
+// Each word validates itself, so no ordering between words is needed: the
+// elected workgroup reads every word, re-reads (with a bounded wait) any
+// whose tag has not arrived yet, and writes zeros back, so the workspace is
+// all zeros between calls.
 #include <hip/hip_runtime.h>
 
 #include <limits.h>
@@ -56,24 +69,25 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kP1Vecs = 4;  // 16-byte vectors per thread per pass-1 chunk
-constexpr int kP2Vecs = 1;  // 16-byte vectors per thread per pass-2 chunk
+constexpr int kP1Vecs = 8;  // 16-byte vectors per thread per pass-1 chunk
+constexpr int kP2Vecs = 2;  // 16-byte vectors per thread per pass-2 chunk
 constexpr int kMaxRows = 2 * SPEC_MAX_K + 1;
-constexpr int kMaxB = 65536;
-constexpr size_t kCtrlBytes = (size_t)kMaxB * 16;  // 4 int32 per request, zero at rest
+constexpr int kMaxB = SPEC_MAX_B;
+// Per-request tickets, one 128-byte line each: atomics on a line shared by
+// several requests serialize behind each other.  Zero at rest.
+constexpr int kCtrlStride = 32;  // int32 per request
+constexpr size_t kCtrlBytes = (size_t)kMaxB * kCtrlStride * 4;
+constexpr int kMaxC2 = 256;  // pass-2 chunks per row at SPEC_MAX_V (bf16 and fp32)
+static_assert(SPEC_MAX_V <= kMaxC2 * kThreads * kP2Vecs * 4, "pass-2 chunk table too small");
+static_assert(kMaxC2 <= 256, "one pass-2 chunk per thread in the terminal scan");
+constexpr uint32_t kTag = 0x5ec0fa11u;
+constexpr int kMaxSpins = 1 << 20;  // bounded wait for a published word (~60 ms)
 
 enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3 };
 
-// Chunk partial of pass 1: max, lowest index of the max, rank count and
-// sum exp(l - m) over the chunk.
-struct alignas(8) Part1 {
-    float m;
-    int idx;
-    int cnt;
-    int pad;
-    double s;
-};
-
+// Chunk partial of pass 1 (five tagged words): max, lowest index of the
+// max, rank count, and the two halves of sum exp(l - m) (fp64).
+constexpr int kP1Words = 5;
 // What pass 2 needs to draw the terminal token of one request.
 struct alignas(8) Desc {
     int n;         // accepted drafts; the terminal token goes to position n
@@ -86,11 +100,10 @@ struct alignas(8) Desc {
     double lx, dx;      // target/draft logits at the rejected draft
 };
 
-// Chunk partial of pass 2 (fp64): sum of a = exp(l - Mt) and b = exp(d - Md)
-// over the chunk, and over its tokens with p > q.
-struct alignas(8) Part2 {
-    double sa, sb, pa, pb;
-};
+// Chunk partial of pass 2 (eight tagged words = four fp64 sums): sum of
+// a = exp(l - Mt) and b = exp(d - Md) over the chunk, and over its tokens
+// with p > q.
+constexpr int kP2Words = 8;
 
 struct Layout {
     size_t desc, p1, p2, total;
@@ -102,12 +115,26 @@ __host__ __device__ inline Layout make_layout(int B, int R, int C1, int C2) {
     Layout L;
     L.desc = kCtrlBytes;
     L.p1 = align_up(L.desc + (size_t)B * sizeof(Desc), 256);
-    L.p2 = align_up(L.p1 + (size_t)B * R * C1 * sizeof(Part1), 256);
-    L.total = align_up(L.p2 + (size_t)B * C2 * sizeof(Part2), 256);
+    L.p2 = align_up(L.p1 + (size_t)B * R * C1 * kP1Words * 8, 256);
+    L.total = align_up(L.p2 + (size_t)B * C2 * kP2Words * 8, 256);
     return L;
 }
 
 // --------------------------------------------------------------- element IO
+// Rows are read with buffer loads: the resource descriptor carries the row's
+// size, so the hardware returns zeros past its end and no bounds branch sits
+// between the loads; every thread issues all of its loads before it waits.
+// Row sizes on the 16-byte path are multiples of 16 bytes, so a vector is
+// either wholly inside the row or wholly past it.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer, 32-bit data format
+
+template <typename T>
+__device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const T* row, int V) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(row), (short)0, V * (int)sizeof(T),
+                                             kRsrcWord3);
+}
+
 template <typename T>
 struct Elem;
 
@@ -117,16 +144,19 @@ struct Elem<uint16_t> {  // bf16 bit patterns
     __device__ static inline float at(const uint16_t* p, size_t i) {
         return __uint_as_float((uint32_t)p[i] << 16);
     }
-    __device__ static inline void vload(const uint16_t* p, size_t i, float* v) {
-        const uint4 q = *reinterpret_cast<const uint4*>(p + i);
-        v[0] = __uint_as_float(q.x << 16);
-        v[1] = __uint_as_float(q.x & 0xffff0000u);
-        v[2] = __uint_as_float(q.y << 16);
-        v[3] = __uint_as_float(q.y & 0xffff0000u);
-        v[4] = __uint_as_float(q.z << 16);
-        v[5] = __uint_as_float(q.z & 0xffff0000u);
-        v[6] = __uint_as_float(q.w << 16);
-        v[7] = __uint_as_float(q.w & 0xffff0000u);
+    template <int AUX = 0>
+    __device__ static inline u32x4 vraw(__amdgpu_buffer_rsrc_t r, int e) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, e * 2, 0, AUX);
+    }
+    __device__ static inline float sraw(__amdgpu_buffer_rsrc_t r, int e) {
+        return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, e * 2, 0, 0) << 16);
+    }
+    __device__ static inline void unpack(const u32x4 q, float* v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(q[j] << 16);
+            v[2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
+        }
     }
 };
 
@@ -134,49 +164,99 @@ template <>
 struct Elem<float> {
     static constexpr int kVec = 4;
     __device__ static inline float at(const float* p, size_t i) { return p[i]; }
-    __device__ static inline void vload(const float* p, size_t i, float* v) {
-        const float4 q = *reinterpret_cast<const float4*>(p + i);
-        v[0] = q.x;
-        v[1] = q.y;
-        v[2] = q.z;
-        v[3] = q.w;
+    template <int AUX = 0>
+    __device__ static inline u32x4 vraw(__amdgpu_buffer_rsrc_t r, int e) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, AUX);
+    }
+    __device__ static inline float sraw(__amdgpu_buffer_rsrc_t r, int e) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, e * 4, 0, 0));
+    }
+    __device__ static inline void unpack(const u32x4 q, float* v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(q[j]);
     }
 };
 
-// Loads vector k of this thread's share of [c0, c1): elements
-// c0 + (k * kThreads + tid) * VEC + [0, VEC).  Out-of-range lanes read -inf.
-template <typename T>
-__device__ inline void load_vec(const T* row, long c0, long c1, int k, bool fast, float* v) {
+// Loads this thread's NV vectors of the chunk [c0, c1): vector k holds
+// elements c0 + (k * kThreads + tid) * VEC + [0, VEC).  Elements at or past
+// c1 read as -inf.  `vec` selects the 16-byte path (row start and size
+// 16-byte aligned); otherwise each element is loaded on its own.  AUX is the
+// cache-policy field of the vector loads (kStream: read once, do not keep).
+constexpr int kStream = 2;
+template <typename T, int NV, int AUX = 0>
+__device__ inline void load_chunk(__amdgpu_buffer_rsrc_t r, int c0, int c1, bool vec,
+                                  float (&v)[NV][Elem<T>::kVec]) {
     constexpr int VEC = Elem<T>::kVec;
-    const long e0 = c0 + ((long)k * kThreads + threadIdx.x) * VEC;
-    if (fast && e0 + VEC <= c1) {
-        Elem<T>::vload(row, (size_t)e0, v);
+    const int t0 = c0 + (int)threadIdx.x * VEC;
+    if (vec) {
+        u32x4 q[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) q[k] = Elem<T>::template vraw<AUX>(r, t0 + k * kThreads * VEC);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) Elem<T>::unpack(q[k], v[k]);
     } else {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i)
-            v[i] = (e0 + i < c1) ? Elem<T>::at(row, (size_t)(e0 + i)) : -INFINITY;
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) v[k][i] = Elem<T>::sraw(r, t0 + k * kThreads * VEC + i);
     }
+    if (c1 - c0 < NV * kThreads * VEC) {  // partial chunk (uniform per workgroup)
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                if (t0 + k * kThreads * VEC + i >= c1) v[k][i] = -INFINITY;
+    }
+}
+
+// Loads NV vectors of consecutive tokens [e0, e0 + NV*VEC) (one thread's
+// contiguous run); tokens at or past V read as -inf.
+template <typename T, int NV>
+__device__ inline void load_run(__amdgpu_buffer_rsrc_t r, int e0, int V, bool vec,
+                                float (&v)[NV * Elem<T>::kVec]) {
+    constexpr int VEC = Elem<T>::kVec;
+    if (vec) {
+        u32x4 q[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) q[k] = Elem<T>::vraw(r, e0 + k * VEC);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) Elem<T>::unpack(q[k], v + k * VEC);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV * VEC; ++i) v[i] = Elem<T>::sraw(r, e0 + i);
+    }
+#pragma unroll
+    for (int i = 0; i < NV * VEC; ++i)
+        if (e0 + i >= V) v[i] = -INFINITY;
 }
 
 // ------------------------------------------------------------ fp64 exp(x<=0)
 // Cody-Waite reduction x = k ln2/64 + r, |r| <= ln2/128, then a degree-4
 // Taylor polynomial (truncation error r^5/120 < 4e-14 relative) and
-// 2^(k/64) = 2^(k>>6) * tab[k & 63].
+// 2^(k/64) = 2^(k>>6) * tab[k & 63].  Branch-free and built from full-rate
+// fp64 fma/add/mul and integer ops only: adding 1.5*2^52 leaves round(y) in
+// the low word of the double, and 2^(k>>6) is applied by adding (k>>6) to the
+// exponent field of tab[k & 63] (results stay normal for x > -700).  x <= -700
+// (and -inf) gives exactly 0.
 constexpr double kInvLn2x64 = 92.332482616893656877;   // 64 / ln 2
 constexpr double kLn2o64Hi = 0.010830424726009368896;  // ln2/64 rounded to 24 bits
 constexpr double kLn2o64Lo = -2.9760223436840126e-11;  // ln2/64 - hi
+constexpr double kRoundMagic = 6755399441055744.0;     // 1.5 * 2^52
 
 __device__ inline double exp_nonpos(double x, const double* tab) {
-    if (!(x > -700.0)) return 0.0;
-    const double kd = __builtin_rint(x * kInvLn2x64);
-    const int k = (int)kd;
-    double r = fma(-kd, kLn2o64Hi, x);
+    const double xc = fmax(x, -700.0);
+    const double t = fma(xc, kInvLn2x64, kRoundMagic);
+    const int k = (int)(uint32_t)__double_as_longlong(t);  // round(xc * 64/ln2)
+    const double kd = t - kRoundMagic;
+    double r = fma(-kd, kLn2o64Hi, xc);
     r = fma(-kd, kLn2o64Lo, r);
     double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
     p = fma(p, r, 0.5);
     p = fma(p, r, 1.0);
     p = fma(p, r, 1.0);
-    return ldexp(tab[k & 63] * p, k >> 6);
+    const long long tb = __double_as_longlong(tab[k & 63]) + ((long long)(k >> 6) << 52);
+    const double e = __longlong_as_double(tb) * p;
+    return (x > -700.0) ? e : 0.0;
 }
 
 __device__ inline void fill_exp_table(double* tab) {
@@ -184,8 +264,67 @@ __device__ inline void fill_exp_table(double* tab) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.69314718055994530942;
 
 // ------------------------------------------------------------ wave helpers
+// Cross-lane steps use DPP (operands moved between lanes inside the VALU),
+// not LDS permutes: reductions and scans are fixed sequences of lane moves,
+// so every result is bit-reproducible.  Rows are 16 lanes, banks 4 lanes.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within a row
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr3 = 0x113, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142;  // lane 15 of each row -> next row
+constexpr int kDppBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+// Lanes that are masked off, or whose source lane does not exist, receive
+// `old`.
+template <int CTRL, int RM = 0xF, int BM = 0xF>
+__device__ inline int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, RM, BM, false);
+}
+template <int CTRL, int RM = 0xF, int BM = 0xF>
+__device__ inline float dpp_f(float old, float v) {
+    return __int_as_float(dpp_i<CTRL, RM, BM>(__float_as_int(old), __float_as_int(v)));
+}
+template <int CTRL, int RM = 0xF, int BM = 0xF>
+__device__ inline double dpp_d(double old, double v) {
+    const long long o = __double_as_longlong(old), u = __double_as_longlong(v);
+    const int lo = dpp_i<CTRL, RM, BM>((int)o, (int)u);
+    const int hi = dpp_i<CTRL, RM, BM>((int)(o >> 32), (int)(u >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+__device__ inline double readlane_d(double v, int l) {
+    const long long u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)u, l);
+    const int hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Wave total in every lane: butterfly within rows, then rows 1 and 3 pick up
+// rows 0 and 2, then row 3 picks up rows 0-1; lane 63 holds the total.
+__device__ inline double wave_sum(double v) {
+    v += dpp_d<kDppXor1>(0.0, v);
+    v += dpp_d<kDppXor2>(0.0, v);
+    v += dpp_d<kDppHalfMirror>(0.0, v);
+    v += dpp_d<kDppMirror>(0.0, v);
+    v += dpp_d<kDppBcast15, 0xA>(0.0, v);
+    v += dpp_d<kDppBcast31, 0xC>(0.0, v);
+    return readlane_d(v, 63);
+}
+
+__device__ inline int wave_sum_i(int v) {
+    v += dpp_i<kDppXor1>(0, v);
+    v += dpp_i<kDppXor2>(0, v);
+    v += dpp_i<kDppHalfMirror>(0, v);
+    v += dpp_i<kDppMirror>(0, v);
+    v += dpp_i<kDppBcast15, 0xA>(0, v);
+    v += dpp_i<kDppBcast31, 0xC>(0, v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ inline void argmax_combine(float& m, int& idx, float om, int oi) {
     if (om > m || (om == m && oi < idx)) {
         m = om;
@@ -193,16 +332,120 @@ __device__ inline void argmax_combine(float& m, int& idx, float om, int oi) {
     }
 }
 
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+template <int CTRL, int RM = 0xF>
+__device__ inline void argmax_step(float& m, int& idx) {
+    const float om = dpp_f<CTRL, RM>(m, m);  // masked-off lanes combine with themselves
+    const int oi = dpp_i<CTRL, RM>(idx, idx);
+    argmax_combine(m, idx, om, oi);
 }
 
-__device__ inline int wave_sum_i(int v) {
+// Wave max with the lowest index among equal maxima, in every lane.
+__device__ inline void wave_argmax(float& m, int& idx) {
+    argmax_step<kDppXor1>(m, idx);
+    argmax_step<kDppXor2>(m, idx);
+    argmax_step<kDppHalfMirror>(m, idx);
+    argmax_step<kDppMirror>(m, idx);
+    argmax_step<kDppBcast15, 0xA>(m, idx);
+    argmax_step<kDppBcast31, 0xC>(m, idx);
+    m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+    idx = __builtin_amdgcn_readlane(idx, 63);
+}
+
+template <int CTRL, int RM = 0xF>
+__device__ inline float max_step(float m) {
+    return fmaxf(m, dpp_f<CTRL, RM>(m, m));
+}
+
+__device__ inline float wave_max(float m) {
+    m = max_step<kDppXor1>(m);
+    m = max_step<kDppXor2>(m);
+    m = max_step<kDppHalfMirror>(m);
+    m = max_step<kDppMirror>(m);
+    m = max_step<kDppBcast15, 0xA>(m);
+    m = max_step<kDppBcast31, 0xC>(m);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+}
+
+// Inclusive prefix sum over the 64 lanes (in lane order).
+__device__ inline double wave_incl_scan(double v) {
+    double s = v + dpp_d<kDppShr1>(0.0, v);
+    s += dpp_d<kDppShr2>(0.0, v);
+    s += dpp_d<kDppShr3>(0.0, v);
+    s += dpp_d<kDppShr4, 0xF, 0xE>(0.0, s);
+    s += dpp_d<kDppShr8, 0xF, 0xC>(0.0, s);
+    s += dpp_d<kDppBcast15, 0xA>(0.0, s);
+    s += dpp_d<kDppBcast31, 0xC>(0.0, s);
+    return s;
+}
+
+// Smallest / largest int over the wave, in every lane.
+__device__ inline int wave_min_i(int v) {
+    v = min(v, dpp_i<kDppXor1>(v, v));
+    v = min(v, dpp_i<kDppXor2>(v, v));
+    v = min(v, dpp_i<kDppHalfMirror>(v, v));
+    v = min(v, dpp_i<kDppMirror>(v, v));
+    v = min(v, dpp_i<kDppBcast15, 0xA>(v, v));
+    v = min(v, dpp_i<kDppBcast31, 0xC>(v, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ inline int wave_max_i(int v) {
+    v = max(v, dpp_i<kDppXor1>(v, v));
+    v = max(v, dpp_i<kDppXor2>(v, v));
+    v = max(v, dpp_i<kDppHalfMirror>(v, v));
+    v = max(v, dpp_i<kDppMirror>(v, v));
+    v = max(v, dpp_i<kDppBcast15, 0xA>(v, v));
+    v = max(v, dpp_i<kDppBcast31, 0xC>(v, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// ------------------------------------------------- tagged-word hand-off
+__device__ inline void put_word(uint64_t* p, uint32_t v) {
+    __hip_atomic_store(p, ((uint64_t)kTag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void put_double(uint64_t* p, double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    put_word(p, (uint32_t)u);
+    put_word(p + 1, (uint32_t)(u >> 32));
+}
+
+// Reads n tagged words into out[], waiting (bounded) for any not yet
+// published, then returns them to zero.  Returns false on timeout.
+template <int N>
+__device__ inline bool take_words(uint64_t* p, uint32_t* out) {
+    uint64_t w[N];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    for (int i = 0; i < N; ++i) w[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        int spins = 0;
+        while ((uint32_t)(w[i] >> 32) != kTag) {
+            if (++spins > kMaxSpins) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            w[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        out[i] = (uint32_t)w[i];
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) __hip_atomic_store(p + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return ok;
+}
+
+__device__ inline double join_double(uint32_t lo, uint32_t hi) {
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ inline int ticket_add(int* t) {
+    return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void ticket_reset(int* t) {
+    __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------- args
@@ -230,9 +473,11 @@ struct Args {
     unsigned char* ws;
 };
 
-__device__ inline int* ticket1(const Args& a, int b) { return reinterpret_cast<int*>(a.ws) + 4 * b; }
+__device__ inline int* ticket1(const Args& a, int b) {
+    return reinterpret_cast<int*>(a.ws) + kCtrlStride * b;
+}
 __device__ inline int* ticket2(const Args& a, int b) {
-    return reinterpret_cast<int*>(a.ws) + 4 * b + 1;
+    return reinterpret_cast<int*>(a.ws) + kCtrlStride * b + 1;
 }
 
 // -------------------------------------------------------------------- pass 1
@@ -244,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void k_pass1(const Args a) {
     constexpr bool COUNT = (MODE == kRelaxed);
 
     const Layout lay = make_layout(a.B, a.R, a.C1, a.C2);
-    Part1* part = reinterpret_cast<Part1*>(a.ws + lay.p1);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(a.ws + lay.p1);
     Desc* desc = reinterpret_cast<Desc*>(a.ws + lay.desc);
 
     const int bid = blockIdx.x;
@@ -280,18 +525,19 @@ __global__ __launch_bounds__(kThreads) void k_pass1(const Args a) {
     __shared__ int s_last;
 
     if (active) {
-        const long c0 = (long)c * CH;
-        const long c1 = min(c0 + (long)CH, (long)a.V);
+        const int c0 = c * CH;
+        const int c1 = min(c0 + CH, a.V);
         float v[kP1Vecs][VEC];
-#pragma unroll
-        for (int k = 0; k < kP1Vecs; ++k) load_vec<T>(row, c0, c1, k, fast, v[k]);
+        // greedy and tree never revisit a row: stream it past the caches
+        load_chunk<T, kP1Vecs, (MODE == kGreedy || MODE == kTree) ? kStream : 0>(row_rsrc(row, a.V), c0, c1,
+                                                                                fast, v);
 
         float m = -INFINITY;
         int idx = INT_MAX;
         int cnt = 0;
 #pragma unroll
         for (int k = 0; k < kP1Vecs; ++k) {
-            const int base = (int)(c0 + ((long)k * kThreads + threadIdx.x) * VEC);
+            const int base = c0 + (k * kThreads + (int)threadIdx.x) * VEC;
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
                 if (ARGMAX) {
@@ -305,120 +551,184 @@ __global__ __launch_bounds__(kThreads) void k_pass1(const Args a) {
                 if (COUNT) cnt += (v[k][i] > thr) ? 1 : 0;
             }
         }
-        // wave max (and lowest-index argmax)
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float om = __shfl_xor(m, off);
-            if (ARGMAX) {
-                const int oi = __shfl_xor(idx, off);
-                argmax_combine(m, idx, om, oi);
-            } else {
-                m = fmaxf(m, om);
-            }
+        // workgroup max (and lowest-index argmax): waves, then LDS
+        if (ARGMAX)
+            wave_argmax(m, idx);
+        else
+            m = wave_max(m);
+        if (lane == 0) {
+            s_m[wave] = m;
+            s_i[wave] = idx;
         }
+        __syncthreads();
+        float M = s_m[0];
+        int I = s_i[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) argmax_combine(M, I, s_m[w], s_i[w]);
+        // sum exp(l - M) against the workgroup max: no rescaling afterwards
         double s = 0.0;
-        if (SUM && m > -INFINITY) {
+        if (SUM && M > -INFINITY) {
+            // exp(l - M) = 2^(l*L - ML) * 2^(ML - M*L): one fma per element;
+            // the rounding of ML = fl(M*L) is undone once per workgroup.
+            const float ML = M * kLog2e;
 #pragma unroll
             for (int k = 0; k < kP1Vecs; ++k) {
                 float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < VEC; ++i)
-                    acc += __builtin_amdgcn_exp2f((v[k][i] - m) * kLog2e);
+                for (int i = 0; i < VEC; ++i) acc += __builtin_amdgcn_exp2f(fmaf(v[k][i], kLog2e, -ML));
                 s += (double)acc;
             }
             s = wave_sum(s);
         }
         if (COUNT) cnt = wave_sum_i(cnt);
         if (lane == 0) {
-            s_m[wave] = m;
-            s_i[wave] = idx;
             s_c[wave] = cnt;
             s_s[wave] = s;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
-            float M = s_m[0];
-            int I = s_i[0];
-            for (int w = 1; w < kWaves; ++w) argmax_combine(M, I, s_m[w], s_i[w]);
             double S = 0.0;
             int C = 0;
+#pragma unroll
             for (int w = 0; w < kWaves; ++w) {
-                if (SUM && s_m[w] > -INFINITY) S += s_s[w] * exp((double)s_m[w] - (double)M);
+                S += s_s[w];
                 C += s_c[w];
             }
-            Part1 p;
-            p.m = M;
-            p.idx = I;
-            p.cnt = C;
-            p.pad = 0;
-            p.s = S;
-            part[bid] = p;
+            if (SUM && M > -INFINITY) {
+                const float ML = M * kLog2e;
+                const double delta = (double)ML - (double)M * (double)kLog2e;  // |delta| < 2^-20
+                S *= fma(delta, kLn2, 1.0);
+            }
+            uint64_t* w = slots + (size_t)bid * kP1Words;
+            put_word(w, __float_as_uint(M));
+            put_word(w + 1, (uint32_t)I);
+            put_word(w + 2, (uint32_t)C);
+            put_double(w + 3, S);
         }
     }
 
     // elect the last workgroup of this request
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const int prev = atomicAdd(ticket1(a, b), 1);
-        s_last = (prev == a.R * a.C1 - 1);
-    }
+    if (threadIdx.x == 0) s_last = (ticket_add(ticket1(a, b)) == a.R * a.C1 - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
 
     // ---- per-request decision (last workgroup only)
     __shared__ float r_M[kMaxRows];
     __shared__ int r_g[kMaxRows];
     __shared__ int r_c[kMaxRows];
+    __shared__ double r_S[kMaxRows];
     __shared__ double r_lnS[kMaxRows];
-
-    const int rows_used = (MODE == kTree) ? nb : a.R;
-    for (int r = threadIdx.x; r < rows_used; r += kThreads) {
-        const Part1* pr = part + (size_t)(b * a.R + r) * a.C1;
-        float M = -INFINITY;
-        int g = INT_MAX;
-        int C = 0;
-        for (int cc = 0; cc < a.C1; ++cc) {
-            const Part1 p = pr[cc];
-            argmax_combine(M, g, p.m, p.idx);
-            C += p.cnt;
-        }
-        double S = 0.0;
-        if (SUM && M > -INFINITY)
-            for (int cc = 0; cc < a.C1; ++cc) {
-                const Part1 p = pr[cc];
-                if (p.m > -INFINITY) S += p.s * exp((double)p.m - (double)M);
-            }
-        r_M[r] = M;
-        r_g[r] = g;
-        r_c[r] = C;
-        r_lnS[r] = log(S);
-    }
-    __syncthreads();
+    __shared__ float q_m[kThreads];
+    __shared__ int q_i[kThreads];
+    __shared__ int q_c[kThreads];
+    __shared__ double q_s[kThreads];
+    __shared__ float b_M[kMaxRows];
+    __shared__ int s_bad_ws;
 
     const T* Tp = reinterpret_cast<const T*>(a.T);
     const T* Dp = reinterpret_cast<const T*>(a.D);
     const int K = a.K;
     const int L = a.L;
+    // Chain modes: wave 0, lane j < K fetches draft j and the logits at it
+    // now, so that these loads overlap the gather of the partials.
+    int x = -1;
+    bool bad = false;
+    float lxf = -INFINITY, dxf = -INFINITY;
+    if (MODE != kTree && wave == 0 && lane < K) {
+        x = a.tok[b * K + lane];
+        bad = (unsigned)x >= (unsigned)a.V;
+        if (!bad && MODE != kGreedy) {
+            lxf = Elem<T>::at(Tp, (size_t)(b * a.rows_t + lane) * a.V + x);
+            if (MODE == kExact) dxf = Elem<T>::at(Dp, (size_t)(b * K + lane) * a.V + x);
+        }
+    }
+
+    const int rows_used = (MODE == kTree) ? nb : a.R;
+    for (int r = threadIdx.x; r < rows_used; r += kThreads) {
+        r_M[r] = -INFINITY;
+        r_g[r] = INT_MAX;
+        r_c[r] = 0;
+        r_S[r] = 0.0;
+    }
+    if (threadIdx.x == 0) s_bad_ws = 0;
+    __syncthreads();
+    // Gather the chunk partials one slot per thread, kThreads slots at a
+    // time.  Per batch: row max / argmax / count by one thread per row, then
+    // each slot rescales its own sum to the batch row max (one exp per slot,
+    // in parallel), then each row adds its slots in ascending chunk order and
+    // merges the batch into its running total.
+    const int nslots = rows_used * a.C1;
+    uint64_t* req_slots = slots + (size_t)b * a.R * a.C1 * kP1Words;
+    for (int base = 0; base < nslots; base += kThreads) {
+        const int si = base + (int)threadIdx.x;
+        if (si < nslots) {
+            uint32_t w[kP1Words];
+            if (!take_words<kP1Words>(req_slots + (size_t)si * kP1Words, w)) s_bad_ws = 1;
+            q_m[threadIdx.x] = __uint_as_float(w[0]);
+            q_i[threadIdx.x] = (int)w[1];
+            q_c[threadIdx.x] = (int)w[2];
+            q_s[threadIdx.x] = join_double(w[3], w[4]);
+        }
+        __syncthreads();
+        const int bend = min(base + kThreads, nslots);
+        const int r_lo = base / a.C1, r_hi = (bend - 1) / a.C1;  // rows touched by this batch
+        for (int r = r_lo + (int)threadIdx.x; r <= r_hi; r += kThreads) {
+            const int lo = max(base, r * a.C1), hi = min(bend, (r + 1) * a.C1);
+            float M = -INFINITY;
+            int g = INT_MAX, C = 0;
+            for (int q = lo; q < hi; ++q) {
+                argmax_combine(M, g, q_m[q - base], q_i[q - base]);
+                C += q_c[q - base];
+            }
+            b_M[r] = M;
+            float RM = r_M[r];
+            int rg = r_g[r];
+            argmax_combine(RM, rg, M, g);
+            r_g[r] = rg;
+            r_c[r] += C;
+        }
+        __syncthreads();
+        if (SUM) {
+            if (si < bend) {
+                const float m = q_m[threadIdx.x];
+                const float M = b_M[si / a.C1];
+                q_s[threadIdx.x] = (m > -INFINITY) ? q_s[threadIdx.x] * exp((double)m - (double)M) : 0.0;
+            }
+            __syncthreads();
+            for (int r = r_lo + (int)threadIdx.x; r <= r_hi; r += kThreads) {
+                const int lo = max(base, r * a.C1), hi = min(bend, (r + 1) * a.C1);
+                double S = 0.0;
+                for (int q = lo; q < hi; ++q) S += q_s[q - base];
+                const float M = b_M[r], RM = r_M[r];
+                if (M > RM) {
+                    r_S[r] = (RM > -INFINITY ? r_S[r] * exp((double)RM - (double)M) : 0.0) + S;
+                    r_M[r] = M;
+                } else if (M > -INFINITY) {
+                    r_S[r] += S * exp((double)M - (double)RM);
+                }
+            }
+        } else {
+            for (int r = r_lo + (int)threadIdx.x; r <= r_hi; r += kThreads) r_M[r] = fmaxf(r_M[r], b_M[r]);
+        }
+        __syncthreads();
+    }
+    for (int r = threadIdx.x; r < rows_used; r += kThreads) r_lnS[r] = log(r_S[r]);
+    __syncthreads();
 
     if (MODE == kGreedy || MODE == kExact || MODE == kRelaxed) {
         if (wave == 0) {
             const int j = lane;
-            bool acc = false, bad = false;
-            int x = -1;
-            double lp = 0.0, lq = 0.0, lx = -INFINITY, dx = -INFINITY;
+            bool acc = false;
+            double lp = 0.0, lq = 0.0;
+            const double lx = lxf, dx = dxf;
             if (j < K) {
-                x = a.tok[b * K + j];
-                bad = (unsigned)x >= (unsigned)a.V;
                 if (!bad) {
                     if (MODE == kGreedy) {
                         acc = (x == r_g[j]);
                         lp = -r_lnS[j];
                     } else {
-                        lx = Elem<T>::at(Tp, (size_t)(b * a.rows_t + j) * a.V + x);
                         lp = (lx - (double)r_M[j]) - r_lnS[j];
                         if (MODE == kExact) {
-                            dx = Elem<T>::at(Dp, (size_t)(b * K + j) * a.V + x);
                             lq = (dx - (double)r_M[a.rows_t + j]) - r_lnS[a.rows_t + j];
                             double r;
                             if (lp == -INFINITY)
@@ -449,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void k_pass1(const Args a) {
                 if (oblp) oblp[j] = 0.f;
             } else if (j == n) {
                 a.out_len[b] = n;
-                a.out_status[b] = (n < K && bad) ? 1 : 0;
+                a.out_status[b] = s_bad_ws ? 2 : ((n < K && bad) ? 1 : 0);
                 if (MODE == kGreedy) {
                     otok[n] = r_g[n];
                     if (otlp) otlp[n] = (float)(-r_lnS[n]);
@@ -529,19 +839,68 @@ __global__ __launch_bounds__(kThreads) void k_pass1(const Args a) {
         }
         if (threadIdx.x == 0) {
             a.out_len[b] = d;
-            a.out_status[b] = t_bad;
+            a.out_status[b] = s_bad_ws ? 2 : t_bad;
         }
     }
-    if (threadIdx.x == 0) *ticket1(a, b) = 0;
+    if (threadIdx.x == 0) ticket_reset(ticket1(a, b));
 }
 
 // -------------------------------------------------------------------- pass 2
+// Block-wide sums and scans in a fixed order (deterministic).
+__device__ inline double block_sum(double v, double* scratch) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double t = 0.0;
+    for (int w = 0; w < kWaves; ++w) t += scratch[w];
+    return t;
+}
+
+// Scan of v over threads in thread order.  Returns the inclusive prefix;
+// *excl receives the previous thread's inclusive prefix (0 for thread 0), so
+// the intervals [excl, incl) of consecutive threads tile [0, total) exactly.
+__device__ inline double block_scan(double v, double* scratch, double* all, double* excl) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_incl_scan(v);
+    __syncthreads();
+    if (lane == 63) scratch[wave] = v;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) v += scratch[w];
+    all[threadIdx.x] = v;
+    __syncthreads();
+    *excl = threadIdx.x ? all[threadIdx.x - 1] : 0.0;
+    return v;
+}
+
+// Block-wide int max / min (every thread gets the result).
+__device__ inline int block_max_i(int v, int* scratch) {
+    v = wave_max_i(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = scratch[0];
+    for (int w = 1; w < kWaves; ++w) r = max(r, scratch[w]);
+    return r;
+}
+
+__device__ inline int block_min_i(int v, int* scratch) {
+    v = wave_min_i(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = scratch[0];
+    for (int w = 1; w < kWaves; ++w) r = min(r, scratch[w]);
+    return r;
+}
+
 template <typename T, bool EXACT>
 __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
     constexpr int VEC = Elem<T>::kVec;
-    constexpr int CH = kThreads * kP2Vecs * VEC;
+    constexpr int PER = kP2Vecs * VEC;  // tokens per thread
+    constexpr int CH = kThreads * PER;
     const Layout lay = make_layout(a.B, a.R, a.C1, a.C2);
-    Part2* part = reinterpret_cast<Part2*>(a.ws + lay.p2);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(a.ws + lay.p2);
     const Desc* descs = reinterpret_cast<const Desc*>(a.ws + lay.desc);
 
     const int b = blockIdx.x / a.C2;
@@ -551,182 +910,158 @@ __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
 
     __shared__ double tab[64];
     __shared__ double red[kWaves][4];
+    __shared__ double scr[kWaves];
+    __shared__ double scan_all[kThreads];
+    __shared__ int iscr[kWaves];
     __shared__ int s_last;
     fill_exp_table(tab);
-    __syncthreads();
 
     const Desc d = descs[b];
     const bool residual = EXACT && d.residual;
     const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)d.row_t * a.V;
-    const T* drow = reinterpret_cast<const T*>(a.D) + (size_t)d.row_d * a.V;
+    const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)d.row_d * a.V : trow;
     const double Mt = d.Mt, Md = d.Md;
     const double cls = d.lnSt - d.lnSd;  // p > q  <=>  (l - Mt) - (d - Md) > lnSt - lnSd
+    const __amdgpu_buffer_rsrc_t rt = row_rsrc(trow, a.V);
+    const __amdgpu_buffer_rsrc_t rd = row_rsrc(drow, a.V);
+    __syncthreads();
 
-    const long c0 = (long)c * CH;
-    const long c1 = min(c0 + (long)CH, (long)a.V);
-    double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0;
+    // ---- sweep: fp64 sums over this chunk (coalesced, interleaved layout)
+    {
+        const int c0 = c * CH;
+        const int c1 = min(c0 + CH, a.V);
+        float vt[kP2Vecs][VEC], vd[kP2Vecs][VEC];
+        // both rows are always loaded (rd aliases the target row when no
+        // draft row is needed) so that all loads issue before any wait
+        load_chunk<T, kP2Vecs>(rt, c0, c1, a.vec_t, vt);
+        load_chunk<T, kP2Vecs>(rd, c0, c1, residual ? a.vec_d : a.vec_t, vd);
+        double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0;
 #pragma unroll
-    for (int k = 0; k < kP2Vecs; ++k) {
-        float vt[VEC], vd[VEC];
-        load_vec<T>(trow, c0, c1, k, a.vec_t, vt);
-        if (residual) load_vec<T>(drow, c0, c1, k, a.vec_d, vd);
+        for (int k = 0; k < kP2Vecs; ++k)
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            const double xa = (double)vt[i] - Mt;
-            const double ea = exp_nonpos(xa, tab);
-            sa += ea;
-            if (residual) {
-                const double xb = (double)vd[i] - Md;
-                const double eb = exp_nonpos(xb, tab);
-                sb += eb;
-                if (xa - xb > cls) {
-                    pa += ea;
-                    pb += eb;
+            for (int i = 0; i < VEC; ++i) {
+                const double xa = (double)vt[k][i] - Mt;
+                const double ea = exp_nonpos(xa, tab);
+                sa += ea;
+                if (residual) {
+                    const double xb = (double)vd[k][i] - Md;
+                    const double eb = exp_nonpos(xb, tab);
+                    sb += eb;
+                    if (xa - xb > cls) {
+                        pa += ea;
+                        pb += eb;
+                    }
                 }
             }
+        sa = wave_sum(sa);
+        if (residual) {
+            sb = wave_sum(sb);
+            pa = wave_sum(pa);
+            pb = wave_sum(pb);
         }
-    }
-    sa = wave_sum(sa);
-    if (residual) {
-        sb = wave_sum(sb);
-        pa = wave_sum(pa);
-        pb = wave_sum(pb);
-    }
-    if (lane == 0) {
-        red[wave][0] = sa;
-        red[wave][1] = sb;
-        red[wave][2] = pa;
-        red[wave][3] = pb;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        Part2 p = {0.0, 0.0, 0.0, 0.0};
-        for (int w = 0; w < kWaves; ++w) {
-            p.sa += red[w][0];
-            p.sb += red[w][1];
-            p.pa += red[w][2];
-            p.pb += red[w][3];
+        if (lane == 0) {
+            red[wave][0] = sa;
+            red[wave][1] = sb;
+            red[wave][2] = pa;
+            red[wave][3] = pb;
         }
-        part[(size_t)b * a.C2 + c] = p;
-        __threadfence();
-        const int prev = atomicAdd(ticket2(a, b), 1);
-        s_last = (prev == a.C2 - 1);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t[4] = {0.0, 0.0, 0.0, 0.0};
+            for (int w = 0; w < kWaves; ++w)
+                for (int i = 0; i < 4; ++i) t[i] += red[w][i];
+            uint64_t* w = slots + ((size_t)b * a.C2 + c) * kP2Words;
+            for (int i = 0; i < 4; ++i) put_double(w + 2 * i, t[i]);
+            s_last = (ticket_add(ticket2(a, b)) == a.C2 - 1);
+        }
+        __syncthreads();
+        if (!s_last) return;
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
 
     // ---- terminal sample (last workgroup of the request)
-    __shared__ double s_S, s_Sq, s_Z, s_base, s_target;
-    __shared__ int s_cstar, s_res;
+    // Chunk partials, one chunk per thread (a.C2 <= kThreads).
+    __shared__ int s_bad_ws;
+    __shared__ double s_base, s_Z;
     __shared__ int s_y, s_ylast, s_yany;
-    const Part2* pr = part + (size_t)b * a.C2;
-    if (threadIdx.x == 0) {
-        double S = 0.0, Sq = 0.0;
-        for (int cc = 0; cc < a.C2; ++cc) {
-            S += pr[cc].sa;
-            Sq += pr[cc].sb;
-        }
-        bool res = residual;
-        double Z = 0.0;
-        if (res) {
-            for (int cc = 0; cc < a.C2; ++cc) Z += pr[cc].pa / S - pr[cc].pb / Sq;
-            if (!(Z > 0.0)) res = false;
-        }
-        if (!res) Z = S;
-        const double target = (double)a.u[b * (a.K + 1) + a.K] * Z;
-        double cum = 0.0, base_last = 0.0;
-        int cstar = -1, clast = 0;
-        for (int cc = 0; cc < a.C2; ++cc) {
-            const double W = res ? (pr[cc].pa / S - pr[cc].pb / Sq) : pr[cc].sa;
-            if (!(W > 0.0)) continue;
-            if (cum + W > target) {
-                cstar = cc;
-                break;
-            }
-            clast = cc;
-            base_last = cum;
-            cum += W;
-        }
-        if (cstar < 0) {  // rounding: fall back to the last chunk with mass
-            cstar = clast;
-            cum = base_last;
-        }
-        s_S = S;
-        s_Sq = Sq;
-        s_Z = Z;
-        s_res = res;
-        s_base = cum;
-        s_target = target;
-        s_cstar = cstar;
-        s_y = INT_MAX;
-        s_ylast = -1;
-        s_yany = -1;
-    }
+    if (threadIdx.x == 0) s_bad_ws = 0;
     __syncthreads();
-    const bool res = s_res;
-    const double S = s_S, Sq = s_Sq;
-    const double target = s_target;
+    double csa = 0.0, csb = 0.0, cpa = 0.0, cpb = 0.0;
+    if ((int)threadIdx.x < a.C2) {
+        uint32_t w[kP2Words];
+        if (!take_words<kP2Words>(slots + ((size_t)b * a.C2 + threadIdx.x) * kP2Words, w)) s_bad_ws = 1;
+        csa = join_double(w[0], w[1]);
+        csb = join_double(w[2], w[3]);
+        cpa = join_double(w[4], w[5]);
+        cpb = join_double(w[6], w[7]);
+    }
+    const double S = block_sum(csa, scr);
+    const double Sq = residual ? block_sum(csb, scr) : 0.0;
+    const double iS = 1.0 / S, iSq = residual ? 1.0 / Sq : 0.0;
+    // residual mass of this chunk (clamped: tokens classified with the pass-1
+    // normalizers can leave a rounding-size negative); fall back to p when
+    // relu(p - q) has no mass
+    double W = residual ? fmax(cpa * iS - cpb * iSq, 0.0) : csa;
+    const double Zr = residual ? block_sum(W, scr) : 0.0;
+    const bool res = residual && (Zr > 0.0);
+    if (residual && !res) W = csa;
+    const double Z = res ? Zr : S;
+    const double target = (double)a.u[b * (a.K + 1) + a.K] * Z;
+    double excl;
+    const double incl = block_scan(W, scr, scan_all, &excl);
+    // the unique chunk whose interval [excl, incl) holds target; if rounding
+    // pushed target past the last boundary, the last chunk with mass
+    const bool mine = (int)threadIdx.x < a.C2 && W > 0.0 && excl <= target && target < incl;
+    int cstar = block_max_i(mine ? (int)threadIdx.x : -1, iscr);
+    if (cstar < 0) cstar = block_max_i(((int)threadIdx.x < a.C2 && W > 0.0) ? (int)threadIdx.x : -1, iscr);
+    cstar = max(cstar, 0);
+    if ((int)threadIdx.x == cstar) s_base = excl;
+    if (threadIdx.x == 0) s_Z = Z;
+    __syncthreads();
+
+    // ---- rescan chunk cstar; thread t owns tokens [e0 + t*PER, +PER)
     {
-        const long e0c = (long)s_cstar * CH;
-        const long e1c = min(e0c + (long)CH, (long)a.V);
-        double w[kP2Vecs * VEC];
+        const int e0 = cstar * CH + (int)threadIdx.x * PER;
+        float lt_[PER], ld_[PER];
+        load_run<T, kP2Vecs>(rt, e0, a.V, a.vec_t, lt_);
+        load_run<T, kP2Vecs>(rd, e0, a.V, residual ? a.vec_d : a.vec_t, ld_);
+        double w[PER];
         double tsum = 0.0;
         int lastpos = -1, anypos = -1;
 #pragma unroll
-        for (int k = 0; k < kP2Vecs; ++k) {
-            float vt[VEC], vd[VEC];
-            load_vec<T>(trow, e0c, e1c, k, a.vec_t, vt);
-            if (res) load_vec<T>(drow, e0c, e1c, k, a.vec_d, vd);
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                const double xa = (double)vt[i] - Mt;
-                const double ea = exp_nonpos(xa, tab);
-                double wi;
-                if (res) {
-                    const double xb = (double)vd[i] - Md;
-                    const double eb = exp_nonpos(xb, tab);
-                    wi = (xa - xb > cls) ? fmax(ea / S - eb / Sq, 0.0) : 0.0;
-                } else {
-                    wi = ea;
-                }
-                w[k * VEC + i] = wi;
-                tsum += wi;
-                const int pos = (int)(e0c + ((long)k * kThreads + threadIdx.x) * VEC + i);
-                if (wi > 0.0) lastpos = pos;
-                if (ea > 0.0) anypos = pos;
+        for (int i = 0; i < PER; ++i) {
+            const int e = e0 + i;
+            const double xa = (double)lt_[i] - Mt;
+            const double ea = exp_nonpos(xa, tab);
+            double wi = ea;
+            if (res) {
+                const double xb = (double)ld_[i] - Md;
+                const double eb = exp_nonpos(xb, tab);
+                wi = (xa - xb > cls) ? fmax(ea * iS - eb * iSq, 0.0) : 0.0;
             }
+            w[i] = wi;
+            tsum += wi;
+            if (wi > 0.0) lastpos = e;
+            if (ea > 0.0) anypos = e;
         }
-        // exclusive scan of per-thread sums in thread order.  With
-        // kP2Vecs == 1 each thread owns one contiguous run of VEC tokens, so
-        // thread order is token order.
-        static_assert(kP2Vecs == 1, "in-chunk scan assumes one vector per thread");
-        double incl = tsum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        __shared__ double wtot[kWaves];
-        if (lane == 63) wtot[wave] = incl;
-        __syncthreads();
-        double excl = s_base + (incl - tsum);
-        for (int ww = 0; ww < wave; ++ww) excl += wtot[ww];
-        double cum = excl;
+        double texcl;
+        block_scan(tsum, scr, scan_all, &texcl);
+        double cum = s_base + texcl;
         int cand = INT_MAX;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            if (w[i] > 0.0) {
+        for (int i = 0; i < PER; ++i) {
+            if (w[i] > 0.0 && cand == INT_MAX) {
                 cum += w[i];
-                if (cum > target) {
-                    cand = (int)(e0c + (long)threadIdx.x * VEC + i);
-                    break;
-                }
+                if (cum > target) cand = e0 + i;
             }
         }
-        if (cand != INT_MAX) atomicMin(&s_y, cand);
-        if (lastpos >= 0) atomicMax(&s_ylast, lastpos);
-        if (anypos >= 0) atomicMax(&s_yany, anypos);
+        const int ycross = block_min_i(cand, iscr);
+        const int ylast = block_max_i(lastpos, iscr);
+        const int yany = block_max_i(anypos, iscr);
+        if (threadIdx.x == 0) {
+            s_y = ycross;
+            s_ylast = ylast;
+            s_yany = yany;
+        }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -745,14 +1080,15 @@ __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
         if (res) {
             const double lnSq = log(Sq);
             const double dy = (double)Elem<T>::at(drow, (size_t)y);
-            const double wy = exp_nonpos(ly - Mt, tab) / S - exp_nonpos(dy - Md, tab) / Sq;
+            const double wy = exp_nonpos(ly - Mt, tab) * iS - exp_nonpos(dy - Md, tab) * iSq;
             const double lp = (d.lx - Mt) - lnS, lq = (d.dx - Md) - lnSq;
             const double rn = (lp == -INFINITY) ? 0.0 : exp(lp - lq);
             blp = log1p(-rn) + log(wy) - log(s_Z);
         }
         if (a.out_tlp) a.out_tlp[(size_t)b * L + n] = (float)tlp;
         if (a.out_blp) a.out_blp[(size_t)b * L + n] = (float)blp;
-        *ticket2(a, b) = 0;
+        if (s_bad_ws) a.out_status[b] = 2;
+        ticket_reset(ticket2(a, b));
     }
 }
 
@@ -773,14 +1109,24 @@ spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt)
     return bytes >= L.total ? SPEC_OK : SPEC_EWORKSPACE;
 }
 
+// One-shot profiling hook: events to record around the streaming (pass-1)
+// kernel of the next call made from this thread.
+thread_local hipEvent_t g_prof_before = nullptr;
+thread_local hipEvent_t g_prof_after = nullptr;
+
 template <int MODE, bool SUM>
 spec_status launch_p1(const Args& a, spec_dtype dt, hipStream_t st) {
     const int grid = a.B * a.R * a.C1;
+    hipEvent_t before = g_prof_before, after = g_prof_after;
+    g_prof_before = g_prof_after = nullptr;
+    if (before && hipEventRecord(before, st) != hipSuccess) return SPEC_EHIP;
     if (dt == SPEC_BF16)
         hipLaunchKernelGGL((k_pass1<uint16_t, MODE, SUM>), dim3(grid), dim3(kThreads), 0, st, a);
     else
         hipLaunchKernelGGL((k_pass1<float, MODE, SUM>), dim3(grid), dim3(kThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    if (after && hipEventRecord(after, st) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
 }
 
 template <bool EXACT>
@@ -796,7 +1142,7 @@ spec_status launch_p2(const Args& a, spec_dtype dt, hipStream_t st) {
 bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
 
 bool sizes_ok(int B, int K, int V, long rows_per_req) {
-    if (B < 1 || B > kMaxB || K < 1 || V < 1) return false;
+    if (B < 1 || B > kMaxB || K < 1 || V < 1 || V > SPEC_MAX_V) return false;
     // every element offset of one tensor must fit comfortably in 64 bits and
     // block counts in 31 bits
     const long long grid = (long long)B * rows_per_req * ((V + 1023) / 1024);
@@ -809,10 +1155,17 @@ bool sizes_ok(int B, int K, int V, long rows_per_req) {
 extern "C" {
 
 size_t spec_verify_workspace_bytes(int B, int rows_per_request, int V) {
-    if (B < 1 || B > kMaxB || rows_per_request < 1 || rows_per_request > kMaxRows || V < 1) return 0;
+    if (B < 1 || B > kMaxB || rows_per_request < 1 || rows_per_request > kMaxRows || V < 1 ||
+        V > SPEC_MAX_V)
+        return 0;
     // fp32 uses the smaller chunks, so its layout bounds both dtypes
     const Layout L = make_layout(B, rows_per_request, c1_of(SPEC_F32, V), c2_of(SPEC_F32, V));
     return L.total;
+}
+
+void spec_verify_profile_next_call(void* before_event, void* after_event) {
+    g_prof_before = static_cast<hipEvent_t>(before_event);
+    g_prof_after = static_cast<hipEvent_t>(after_event);
 }
 
 const char* spec_status_string(int s) {

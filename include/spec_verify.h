@@ -38,7 +38,10 @@
  *                               malformed (a consulted draft token outside
  *                               [0,V), or a tree parent outside [-1, i)):
  *                               the offending draft counts as rejected and
- *                               the offending tree node as unmatched.
+ *                               the offending tree node as unmatched; 2 when
+ *                               the workspace was not all zeros at the start
+ *                               of the call (the request's outputs are then
+ *                               unspecified, but every kernel still ends).
  *
  * Randomness is supplied by the caller (spec-decode README, "Use it": the
  * generator takes an rng), as uniforms[b][K+1] in [0,1): uniforms[b][j]
@@ -49,9 +52,10 @@
  *   Each call needs a device workspace of at least
  *   spec_verify_workspace_bytes(B, rows_per_request, V) bytes, 256-byte
  *   aligned, ZERO-FILLED BEFORE ITS FIRST USE.  Every completed call leaves
- *   it zero-filled again, so it can be reused by later calls on the same
- *   stream.  Calls that run concurrently (different streams) need different
- *   workspaces.  The library allocates nothing and keeps no state.
+ *   it zero-filled again, so it can be reused by later calls of any shape
+ *   on the same stream.  Calls that run concurrently (different streams) need different
+ *   workspaces.  The library allocates nothing and keeps no state besides the
+ *   one-shot, per-thread profiling hook (spec_verify_profile_next_call).
  *
  * Streams and errors
  *   stream is a hipStream_t (NULL = the default stream).  Calls enqueue
@@ -79,9 +83,12 @@ typedef enum {
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 
-/* Largest K (drafts per request) and N (tree nodes per request). */
+/* Largest K (drafts per request), N (tree nodes per request), V (vocabulary)
+ * and B (requests per call). */
 #define SPEC_MAX_K 63
 #define SPEC_MAX_NODES 64
+#define SPEC_MAX_V 262144
+#define SPEC_MAX_B 65536
 
 /*
  * Host-only query.  rows_per_request is the number of logit rows one request
@@ -92,6 +99,17 @@ size_t spec_verify_workspace_bytes(int B, int rows_per_request, int V);
 
 /* Host-only: static description of a status code. */
 const char *spec_status_string(int status);
+
+/*
+ * Host-only profiling hook (for benchmarks).  before_event and after_event are
+ * hipEvent_t handles created by the caller.  The next spec_verify_* call made
+ * from the calling thread records before_event on its stream immediately
+ * before its streaming kernel (the one that reads every logit once) and
+ * after_event immediately after it, so that hipEventElapsedTime gives that
+ * kernel's duration.  The hook applies to one call and is then cleared;
+ * passing NULLs clears it.
+ */
+void spec_verify_profile_next_call(void *before_event, void *after_event);
 
 /*
  * Greedy chain verification (mini-sglang PR #134, "Modifications",
