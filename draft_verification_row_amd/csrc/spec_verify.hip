@@ -69,35 +69,33 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kP1Vecs = 8;  // 16-byte vectors per thread per pass-1 chunk
+constexpr int kTileVecs = 2;  // 16-byte vectors per thread per streaming tile
+constexpr int kWgPerCu = 8;   // streaming workgroups per compute unit
+constexpr int kMaxGrid = 8192;
 constexpr int kP2Vecs = 2;  // 16-byte vectors per thread per pass-2 chunk
 constexpr int kMaxRows = 2 * SPEC_MAX_K + 1;
 constexpr int kMaxB = SPEC_MAX_B;
-// Per-request tickets, one 128-byte line each: atomics on a line shared by
-// several requests serialize behind each other.  Zero at rest.
+// Per-request tickets of pass 2, one 128-byte line each: atomics on a line
+// shared by several requests serialize behind each other.  Zero at rest.
 constexpr int kCtrlStride = 32;  // int32 per request
 constexpr size_t kCtrlBytes = (size_t)kMaxB * kCtrlStride * 4;
 constexpr int kMaxC2 = 256;  // pass-2 chunks per row at SPEC_MAX_V (bf16 and fp32)
 static_assert(SPEC_MAX_V <= kMaxC2 * kThreads * kP2Vecs * 4, "pass-2 chunk table too small");
-static_assert(kMaxC2 <= 256, "one pass-2 chunk per thread in the terminal scan");
+static_assert(kMaxC2 <= kThreads, "one pass-2 chunk per thread in the terminal scan");
 constexpr uint32_t kTag = 0x5ec0fa11u;
 constexpr int kMaxSpins = 1 << 20;  // bounded wait for a published word (~60 ms)
 
 enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3 };
 
-// Chunk partial of pass 1 (five tagged words): max, lowest index of the
-// max, rank count, and the two halves of sum exp(l - m) (fp64).
-constexpr int kP1Words = 5;
-// What pass 2 needs to draw the terminal token of one request.
-struct alignas(8) Desc {
-    int n;         // accepted drafts; the terminal token goes to position n
-    int residual;  // 1: sample normalize(relu(p_n - q_n)); 0: sample p_n
-    int row_t;     // absolute target row
-    int row_d;     // absolute draft row (residual only)
-    float Mt, Md;  // row maxima (exact)
-    int pad0, pad1;
-    double lnSt, lnSd;  // pass-1 log normalizers (fp32 exps, ~1e-7 relative)
-    double lx, dx;      // target/draft logits at the rejected draft
+// Statistics of one row segment, written by the streaming kernel and read by
+// the next kernel on the stream (the launch boundary makes them visible):
+// max, lowest index of the max, rank count, sum exp(l - max).
+struct alignas(8) Seg {
+    float m;
+    int idx;
+    int cnt;
+    int pad;
+    double s;
 };
 
 // Chunk partial of pass 2 (eight tagged words = four fp64 sums): sum of
@@ -106,16 +104,16 @@ struct alignas(8) Desc {
 constexpr int kP2Words = 8;
 
 struct Layout {
-    size_t desc, p1, p2, total;
+    size_t seg, p2, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ inline Layout make_layout(int B, int R, int C1, int C2) {
+__host__ __device__ inline Layout make_layout(int B, int R, int C2) {
     Layout L;
-    L.desc = kCtrlBytes;
-    L.p1 = align_up(L.desc + (size_t)B * sizeof(Desc), 256);
-    L.p2 = align_up(L.p1 + (size_t)B * R * C1 * kP1Words * 8, 256);
+    // one segment record per (streaming workgroup, row it touches): ids w + row
+    L.seg = kCtrlBytes;
+    L.p2 = align_up(L.seg + ((size_t)kMaxGrid + (size_t)B * R) * sizeof(Seg), 256);
     L.total = align_up(L.p2 + (size_t)B * C2 * kP2Words * 8, 256);
     return L;
 }
@@ -127,6 +125,7 @@ __host__ __device__ inline Layout make_layout(int B, int R, int C1, int C2) {
 // Row sizes on the 16-byte path are multiples of 16 bytes, so a vector is
 // either wholly inside the row or wholly past it.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;  // in global memory
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer, 32-bit data format
 
 template <typename T>
@@ -151,6 +150,16 @@ struct Elem<uint16_t> {  // bf16 bit patterns
     __device__ static inline float sraw(__amdgpu_buffer_rsrc_t r, int e) {
         return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, e * 2, 0, 0) << 16);
     }
+    // VEC elements from e on (indices clamped to V-1), one load each, packed
+    // like a 16-byte vector load
+    __device__ static inline u32x4 gather_clamped(const uint16_t* pp, int e, int V) {
+        const __attribute__((address_space(1))) uint16_t* p = (const __attribute__((address_space(1))) uint16_t*)pp;
+        u32x4 q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            q[j] = (uint32_t)p[min(e + 2 * j, V - 1)] | ((uint32_t)p[min(e + 2 * j + 1, V - 1)] << 16);
+        return q;
+    }
     __device__ static inline void unpack(const u32x4 q, float* v) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -170,6 +179,13 @@ struct Elem<float> {
     }
     __device__ static inline float sraw(__amdgpu_buffer_rsrc_t r, int e) {
         return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, e * 4, 0, 0));
+    }
+    __device__ static inline u32x4 gather_clamped(const float* pp, int e, int V) {
+        const __attribute__((address_space(1))) float* p = (const __attribute__((address_space(1))) float*)pp;
+        u32x4 q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = __float_as_uint(p[min(e + j, V - 1)]);
+        return q;
     }
     __device__ static inline void unpack(const u32x4 q, float* v) {
 #pragma unroll
@@ -459,7 +475,9 @@ struct Args {
     int B, K, V;
     int rows_t;  // target rows per request: K+1, or N for a tree
     int R;       // rows streamed per request
-    int C1, C2;  // chunks per row in pass 1 / pass 2
+    int tpr;     // streaming tiles per row
+    int G;       // streaming workgroups
+    int C2;      // pass-2 chunks per row
     int vec_t, vec_d;
     float tau;
     int top_k;
@@ -473,376 +491,501 @@ struct Args {
     unsigned char* ws;
 };
 
-__device__ inline int* ticket1(const Args& a, int b) {
+__device__ inline int* ticket2(const Args& a, int b) {
     return reinterpret_cast<int*>(a.ws) + kCtrlStride * b;
 }
-__device__ inline int* ticket2(const Args& a, int b) {
-    return reinterpret_cast<int*>(a.ws) + kCtrlStride * b + 1;
+
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The streaming split: all tiles of the call (row-major: global row g of the
+// call, then tile c of the row) are cut into G contiguous, equal ranges.
+__host__ __device__ inline int split_lo(long long total, int G, int w) { return (int)(total * w / G); }
+// workgroup whose range holds tile t
+__host__ __device__ inline int split_owner(long long total, int G, long long t) {
+    return (int)(((t + 1) * G - 1) / total);
 }
 
-// -------------------------------------------------------------------- pass 1
-template <typename T, int MODE, bool SUM>
-__global__ __launch_bounds__(kThreads) void k_pass1(const Args a) {
+template <typename T>
+__device__ inline const T* uniform_ptr(const T* p) {
+    const uint64_t u = (uint64_t)p;
+    const uint32_t lo = (uint32_t)uniform((int)(uint32_t)u), hi = (uint32_t)uniform((int)(uint32_t)(u >> 32));
+    return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Logit row g of the call (request g / R, row g % R of that request).  The
+// result is wave-uniform, so loads use a scalar base and 32-bit offsets.
+template <typename T, int MODE>
+__device__ inline const T* call_row(const Args& a, int g, int& vec, int& active) {
+    const int b = g / a.R, rr = g - (g / a.R) * a.R;
+    active = 1;
+    if (MODE == kTree && a.num_nodes) active = uniform(rr < min(max(a.num_nodes[b], 1), a.rows_t));
+    if (MODE == kExact && rr >= a.rows_t) {
+        vec = a.vec_d;
+        return uniform_ptr(reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + (rr - a.rows_t)) * a.V);
+    }
+    vec = a.vec_t;
+    return uniform_ptr(reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + rr) * a.V);
+}
+
+// Issues this thread's loads of tile c of a row: vector k covers tokens
+// c*TILE + (k*kThreads + tid)*VEC + [0, VEC).  Indices are clamped into the
+// row and the caller masks tokens past V, so no load leaves the row.
+template <typename T, bool NT, bool VECP>
+__device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[kTileVecs]) {
     constexpr int VEC = Elem<T>::kVec;
-    constexpr int CH = kThreads * kP1Vecs * VEC;
+    constexpr int TILE = kThreads * kTileVecs * VEC;
+    const int t0 = c * TILE + (int)threadIdx.x * VEC;
+    if (VECP) {  // V is a multiple of VEC and every row is 16-byte aligned
+#pragma unroll
+        for (int k = 0; k < kTileVecs; ++k) {
+            // global address space: global loads wait on vmcnt only, so the
+            // look-ahead loads stay in flight while this tile is reduced
+            const gu32x4* p = (const gu32x4*)(row + min(t0 + k * kThreads * VEC, V - VEC));
+            q[k] = NT ? __builtin_nontemporal_load(p) : *p;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kTileVecs; ++k) q[k] = Elem<T>::gather_clamped(row, t0 + k * kThreads * VEC, V);
+    }
+}
+
+// ----------------------------------------------------------- streaming pass
+// Every logit row is read once.  Workgroup w walks tiles [lo(w), lo(w+1))
+// with one tile of look-ahead and keeps per-thread running statistics; at
+// the end of each row segment it reduces them over the workgroup and writes
+// one Seg record, id w + row.  Per element: widen, max (and argmax), and for
+// the normalizer one fma, one exp2 and one add.
+// VECP: every row of the call takes the 16-byte path (chosen on the host).
+template <typename T, int MODE, bool SUM, bool VECP>
+__global__ __launch_bounds__(kThreads, kWgPerCu) void k_stream(const Args a) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int TILE = kThreads * kTileVecs * VEC;
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
+    constexpr bool NT = ARGMAX;  // greedy and tree never revisit a row
 
-    const Layout lay = make_layout(a.B, a.R, a.C1, a.C2);
-    uint64_t* slots = reinterpret_cast<uint64_t*>(a.ws + lay.p1);
-    Desc* desc = reinterpret_cast<Desc*>(a.ws + lay.desc);
-
-    const int bid = blockIdx.x;
-    const int c = bid % a.C1;
-    const int rr = (bid / a.C1) % a.R;
-    const int b = bid / (a.C1 * a.R);
+    Seg* segs = reinterpret_cast<Seg*>(a.ws + make_layout(a.B, a.R, a.C2).seg);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-
-    int nb = a.rows_t;
-    if (MODE == kTree && a.num_nodes) nb = min(max(a.num_nodes[b], 1), a.rows_t);
-
-    const T* row;
-    bool fast;
-    if (MODE == kExact && rr >= a.rows_t) {
-        row = reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + (rr - a.rows_t)) * a.V;
-        fast = a.vec_d;
-    } else {
-        row = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + rr) * a.V;
-        fast = a.vec_t;
-    }
-    const bool active = (MODE != kTree) || rr < nb;
-    float thr = INFINITY;
-    if (COUNT && rr < a.K) {
-        const int x = a.tok[b * a.K + rr];
-        if ((unsigned)x < (unsigned)a.V) thr = Elem<T>::at(row, (size_t)x);
-    }
-
+    __shared__ double tab[64];
     __shared__ float s_m[kWaves];
     __shared__ int s_i[kWaves];
     __shared__ int s_c[kWaves];
     __shared__ double s_s[kWaves];
-    __shared__ int s_last;
+    if (SUM) fill_exp_table(tab);
+    __syncthreads();
 
-    if (active) {
-        const int c0 = c * CH;
-        const int c1 = min(c0 + CH, a.V);
-        float v[kP1Vecs][VEC];
-        // greedy and tree never revisit a row: stream it past the caches
-        load_chunk<T, kP1Vecs, (MODE == kGreedy || MODE == kTree) ? kStream : 0>(row_rsrc(row, a.V), c0, c1,
-                                                                                fast, v);
+    const long long total = (long long)a.B * a.R * a.tpr;
+    const int w = blockIdx.x;
+    const int t_lo = split_lo(total, gridDim.x, w), t_hi = split_lo(total, gridDim.x, w + 1);
+    if (t_lo >= t_hi) return;
+    int g = uniform(t_lo / a.tpr);
+    int c = uniform(t_lo - g * a.tpr);
+    int vec, act, nvec, nact;
+    const T* row = call_row<T, MODE>(a, g, vec, act);
+    const T* nrow = row;
+    u32x4 qn[kTileVecs];
+    if (act) load_tile<T, NT, VECP>(row, a.V, c, qn);
 
-        float m = -INFINITY;
-        int idx = INT_MAX;
-        int cnt = 0;
+    auto rank_threshold = [&](int gg, const T* rp) -> float {
+        const int b = gg / a.R, rr = gg - (gg / a.R) * a.R;
+        if (!COUNT || rr >= a.K) return INFINITY;
+        const int x = a.tok[b * a.K + rr];
+        return ((unsigned)x < (unsigned)a.V) ? Elem<T>::at(rp, (size_t)x) : INFINITY;
+    };
+    float thr = COUNT ? rank_threshold(g, row) : INFINITY;
+
+    float m = -INFINITY, mL = -INFINITY;
+    int idx = INT_MAX, cnt = 0;
+    double s = 0.0;
+    for (int t = t_lo; t < t_hi; ++t) {
+        u32x4 q[kTileVecs];
 #pragma unroll
-        for (int k = 0; k < kP1Vecs; ++k) {
-            const int base = c0 + (k * kThreads + (int)threadIdx.x) * VEC;
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                if (ARGMAX) {
-                    if (v[k][i] > m) {
-                        m = v[k][i];
-                        idx = base + i;
-                    }
-                } else {
-                    m = fmaxf(m, v[k][i]);
-                }
-                if (COUNT) cnt += (v[k][i] > thr) ? 1 : 0;
+        for (int k = 0; k < kTileVecs; ++k) q[k] = qn[k];
+        const bool row_end = (c + 1 == a.tpr);
+        nvec = vec;
+        nact = act;
+        if (t + 1 < t_hi) {  // look ahead one tile
+            if (row_end) {
+                nrow = call_row<T, MODE>(a, g + 1, nvec, nact);
+                if (nact) load_tile<T, NT, VECP>(nrow, a.V, 0, qn);
+            } else if (act) {
+                load_tile<T, NT, VECP>(row, a.V, c + 1, qn);
             }
         }
-        // workgroup max (and lowest-index argmax): waves, then LDS
-        if (ARGMAX)
-            wave_argmax(m, idx);
-        else
-            m = wave_max(m);
-        if (lane == 0) {
-            s_m[wave] = m;
-            s_i[wave] = idx;
-        }
-        __syncthreads();
-        float M = s_m[0];
-        int I = s_i[0];
+        if (act) {
+            const int t0 = c * TILE + (int)threadIdx.x * VEC;
+            float v[kTileVecs][VEC];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) argmax_combine(M, I, s_m[w], s_i[w]);
-        // sum exp(l - M) against the workgroup max: no rescaling afterwards
-        double s = 0.0;
-        if (SUM && M > -INFINITY) {
-            // exp(l - M) = 2^(l*L - ML) * 2^(ML - M*L): one fma per element;
-            // the rounding of ML = fl(M*L) is undone once per workgroup.
-            const float ML = M * kLog2e;
+            for (int k = 0; k < kTileVecs; ++k) Elem<T>::unpack(q[k], v[k]);
+            if (row_end && a.V % TILE != 0) {  // ragged last tile: clamped lanes
 #pragma unroll
-            for (int k = 0; k < kP1Vecs; ++k) {
+                for (int k = 0; k < kTileVecs; ++k)
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i)
+                        if (t0 + k * kThreads * VEC + i >= a.V) v[k][i] = -INFINITY;
+            }
+            float tm = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kTileVecs; ++k) {
+                const int base = t0 + k * kThreads * VEC;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    if (ARGMAX) {
+                        if (v[k][i] > m) {
+                            m = v[k][i];
+                            idx = base + i;
+                        }
+                    } else {
+                        tm = fmaxf(tm, v[k][i]);
+                    }
+                    if (COUNT) cnt += (v[k][i] > thr) ? 1 : 0;
+                }
+            }
+            if (!ARGMAX) m = fmaxf(m, tm);
+            if (SUM && m > -INFINITY) {
+                // Running sum of 2^(l*L - mL) against a reference mL = fl(m*L)
+                // that only moves up (the sum is rescaled when it does).
+                const float nL = m * kLog2e;
+                if (nL > mL) {
+                    s *= (double)__builtin_amdgcn_exp2f(mL - nL);
+                    mL = nL;
+                }
                 float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) acc += __builtin_amdgcn_exp2f(fmaf(v[k][i], kLog2e, -ML));
+                for (int k = 0; k < kTileVecs; ++k)
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc += __builtin_amdgcn_exp2f(fmaf(v[k][i], kLog2e, -mL));
                 s += (double)acc;
             }
-            s = wave_sum(s);
         }
-        if (COUNT) cnt = wave_sum_i(cnt);
-        if (lane == 0) {
-            s_c[wave] = cnt;
-            s_s[wave] = s;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            double S = 0.0;
-            int C = 0;
+        if (row_end || t + 1 == t_hi) {
+            // ---- end of a row segment: reduce over the workgroup, write it
+            if (act) {
+                float M = m;
+                int I = idx;
+                if (ARGMAX)
+                    wave_argmax(M, I);
+                else
+                    M = wave_max(M);
+                if (lane == 0) {
+                    s_m[wave] = M;
+                    s_i[wave] = I;
+                }
+                __syncthreads();
+                M = s_m[0];
+                I = s_i[0];
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                S += s_s[w];
-                C += s_c[w];
+                for (int ww = 1; ww < kWaves; ++ww) argmax_combine(M, I, s_m[ww], s_i[ww]);
+                double st = 0.0;
+                if (SUM && M > -INFINITY && m > -INFINITY)  // times 2^(mL - M*L), in fp64
+                    st = s * exp_nonpos(((double)mL - (double)M * (double)kLog2e) * kLn2, tab);
+                if (SUM) st = wave_sum(st);
+                const int ct = COUNT ? wave_sum_i(cnt) : 0;
+                if (lane == 0) {
+                    s_s[wave] = st;
+                    s_c[wave] = ct;
+                }
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    Seg sg;
+                    sg.m = M;
+                    sg.idx = I;
+                    sg.cnt = 0;
+                    sg.pad = 0;
+                    sg.s = 0.0;
+#pragma unroll
+                    for (int ww = 0; ww < kWaves; ++ww) {
+                        sg.s += s_s[ww];
+                        sg.cnt += s_c[ww];
+                    }
+                    segs[(size_t)w + g] = sg;
+                }
+                __syncthreads();  // s_* are reused by the next segment
             }
-            if (SUM && M > -INFINITY) {
-                const float ML = M * kLog2e;
-                const double delta = (double)ML - (double)M * (double)kLog2e;  // |delta| < 2^-20
-                S *= fma(delta, kLn2, 1.0);
-            }
-            uint64_t* w = slots + (size_t)bid * kP1Words;
-            put_word(w, __float_as_uint(M));
-            put_word(w + 1, (uint32_t)I);
-            put_word(w + 2, (uint32_t)C);
-            put_double(w + 3, S);
+            m = -INFINITY;
+            mL = -INFINITY;
+            idx = INT_MAX;
+            cnt = 0;
+            s = 0.0;
+        }
+        if (row_end) {
+            ++g;
+            c = 0;
+            row = nrow;
+            vec = nvec;
+            act = nact;
+            if (COUNT && t + 1 < t_hi) thr = rank_threshold(g, row);
+        } else {
+            ++c;
         }
     }
+}
 
-    // elect the last workgroup of this request
-    if (threadIdx.x == 0) s_last = (ticket_add(ticket1(a, b)) == a.R * a.C1 - 1);
-    __syncthreads();
-    if (!s_last) return;
+// ------------------------------------------------------- row statistics
+// Combines the Seg records of rows [0, rows) of request b into row max M,
+// argmax g (lowest index), rank count c and log normalizer lnS, in LDS.
+// Segments are gathered one per thread (kThreads per batch); each row then
+// folds its segments in ascending order.  Deterministic.
+struct RowStats {
+    float M[kMaxRows];
+    int g[kMaxRows];
+    int c[kMaxRows];
+    double lnS[kMaxRows];
+    // scratch
+    double S[kMaxRows];
+    float bM[kMaxRows];
+    int off[kMaxRows + 1];
+    int w0[kMaxRows];
+    float qm[kThreads];
+    int qi[kThreads];
+    int qc[kThreads];
+    double qs[kThreads];
+};
 
-    // ---- per-request decision (last workgroup only)
-    __shared__ float r_M[kMaxRows];
-    __shared__ int r_g[kMaxRows];
-    __shared__ int r_c[kMaxRows];
-    __shared__ double r_S[kMaxRows];
-    __shared__ double r_lnS[kMaxRows];
-    __shared__ float q_m[kThreads];
-    __shared__ int q_i[kThreads];
-    __shared__ int q_c[kThreads];
-    __shared__ double q_s[kThreads];
-    __shared__ float b_M[kMaxRows];
-    __shared__ int s_bad_ws;
-
-    const T* Tp = reinterpret_cast<const T*>(a.T);
-    const T* Dp = reinterpret_cast<const T*>(a.D);
-    const int K = a.K;
-    const int L = a.L;
-    // Chain modes: wave 0, lane j < K fetches draft j and the logits at it
-    // now, so that these loads overlap the gather of the partials.
-    int x = -1;
-    bool bad = false;
-    float lxf = -INFINITY, dxf = -INFINITY;
-    if (MODE != kTree && wave == 0 && lane < K) {
-        x = a.tok[b * K + lane];
-        bad = (unsigned)x >= (unsigned)a.V;
-        if (!bad && MODE != kGreedy) {
-            lxf = Elem<T>::at(Tp, (size_t)(b * a.rows_t + lane) * a.V + x);
-            if (MODE == kExact) dxf = Elem<T>::at(Dp, (size_t)(b * K + lane) * a.V + x);
-        }
+template <bool SUM>
+__device__ void gather_rows(const Args& a, int b, int rows, RowStats& rs) {
+    const Seg* segs = reinterpret_cast<const Seg*>(a.ws + make_layout(a.B, a.R, a.C2).seg);
+    const long long total = (long long)a.B * a.R * a.tpr;
+    for (int r = threadIdx.x; r < rows; r += kThreads) {
+        const long long rg = (long long)b * a.R + r;
+        const int w0 = split_owner(total, a.G, rg * a.tpr), w1 = split_owner(total, a.G, (rg + 1) * a.tpr - 1);
+        rs.w0[r] = w0;
+        rs.off[r + 1] = w1 - w0 + 1;
+        rs.M[r] = -INFINITY;
+        rs.g[r] = INT_MAX;
+        rs.c[r] = 0;
+        rs.S[r] = 0.0;
     }
-
-    const int rows_used = (MODE == kTree) ? nb : a.R;
-    for (int r = threadIdx.x; r < rows_used; r += kThreads) {
-        r_M[r] = -INFINITY;
-        r_g[r] = INT_MAX;
-        r_c[r] = 0;
-        r_S[r] = 0.0;
-    }
-    if (threadIdx.x == 0) s_bad_ws = 0;
     __syncthreads();
-    // Gather the chunk partials one slot per thread, kThreads slots at a
-    // time.  Per batch: row max / argmax / count by one thread per row, then
-    // each slot rescales its own sum to the batch row max (one exp per slot,
-    // in parallel), then each row adds its slots in ascending chunk order and
-    // merges the batch into its running total.
-    const int nslots = rows_used * a.C1;
-    uint64_t* req_slots = slots + (size_t)b * a.R * a.C1 * kP1Words;
+    if (threadIdx.x == 0) {
+        rs.off[0] = 0;
+        for (int r = 0; r < rows; ++r) rs.off[r + 1] += rs.off[r];
+    }
+    __syncthreads();
+    const int nslots = rs.off[rows];
     for (int base = 0; base < nslots; base += kThreads) {
         const int si = base + (int)threadIdx.x;
+        int sr = 0;
         if (si < nslots) {
-            uint32_t w[kP1Words];
-            if (!take_words<kP1Words>(req_slots + (size_t)si * kP1Words, w)) s_bad_ws = 1;
-            q_m[threadIdx.x] = __uint_as_float(w[0]);
-            q_i[threadIdx.x] = (int)w[1];
-            q_c[threadIdx.x] = (int)w[2];
-            q_s[threadIdx.x] = join_double(w[3], w[4]);
+            while (rs.off[sr + 1] <= si) ++sr;
+            const Seg sg = segs[(size_t)rs.w0[sr] + (si - rs.off[sr]) + (size_t)b * a.R + sr];
+            rs.qm[threadIdx.x] = sg.m;
+            rs.qi[threadIdx.x] = sg.idx;
+            rs.qc[threadIdx.x] = sg.cnt;
+            rs.qs[threadIdx.x] = sg.s;
         }
         __syncthreads();
         const int bend = min(base + kThreads, nslots);
-        const int r_lo = base / a.C1, r_hi = (bend - 1) / a.C1;  // rows touched by this batch
-        for (int r = r_lo + (int)threadIdx.x; r <= r_hi; r += kThreads) {
-            const int lo = max(base, r * a.C1), hi = min(bend, (r + 1) * a.C1);
+        for (int r = threadIdx.x; r < rows; r += kThreads) {
+            const int lo = max(base, rs.off[r]), hi = min(bend, rs.off[r + 1]);
+            if (lo >= hi) continue;
             float M = -INFINITY;
             int g = INT_MAX, C = 0;
             for (int q = lo; q < hi; ++q) {
-                argmax_combine(M, g, q_m[q - base], q_i[q - base]);
-                C += q_c[q - base];
+                argmax_combine(M, g, rs.qm[q - base], rs.qi[q - base]);
+                C += rs.qc[q - base];
             }
-            b_M[r] = M;
-            float RM = r_M[r];
-            int rg = r_g[r];
-            argmax_combine(RM, rg, M, g);
-            r_g[r] = rg;
-            r_c[r] += C;
+            rs.bM[r] = M;
+            float RM = rs.M[r];
+            int RG = rs.g[r];
+            argmax_combine(RM, RG, M, g);
+            rs.g[r] = RG;
+            rs.c[r] += C;
+            if (!SUM) rs.M[r] = RM;
         }
         __syncthreads();
         if (SUM) {
-            if (si < bend) {
-                const float m = q_m[threadIdx.x];
-                const float M = b_M[si / a.C1];
-                q_s[threadIdx.x] = (m > -INFINITY) ? q_s[threadIdx.x] * exp((double)m - (double)M) : 0.0;
+            if (si < bend) {  // rescale this segment's sum to its batch row max
+                const float mq = rs.qm[threadIdx.x];
+                rs.qs[threadIdx.x] = (mq > -INFINITY) ? rs.qs[threadIdx.x] * exp((double)mq - (double)rs.bM[sr]) : 0.0;
             }
             __syncthreads();
-            for (int r = r_lo + (int)threadIdx.x; r <= r_hi; r += kThreads) {
-                const int lo = max(base, r * a.C1), hi = min(bend, (r + 1) * a.C1);
+            for (int r = threadIdx.x; r < rows; r += kThreads) {
+                const int lo = max(base, rs.off[r]), hi = min(bend, rs.off[r + 1]);
+                if (lo >= hi) continue;
                 double S = 0.0;
-                for (int q = lo; q < hi; ++q) S += q_s[q - base];
-                const float M = b_M[r], RM = r_M[r];
+                for (int q = lo; q < hi; ++q) S += rs.qs[q - base];
+                const float M = rs.bM[r], RM = rs.M[r];
                 if (M > RM) {
-                    r_S[r] = (RM > -INFINITY ? r_S[r] * exp((double)RM - (double)M) : 0.0) + S;
-                    r_M[r] = M;
+                    rs.S[r] = (RM > -INFINITY ? rs.S[r] * exp((double)RM - (double)M) : 0.0) + S;
+                    rs.M[r] = M;
                 } else if (M > -INFINITY) {
-                    r_S[r] += S * exp((double)M - (double)RM);
+                    rs.S[r] += S * exp((double)M - (double)RM);
                 }
             }
-        } else {
-            for (int r = r_lo + (int)threadIdx.x; r <= r_hi; r += kThreads) r_M[r] = fmaxf(r_M[r], b_M[r]);
+            __syncthreads();
         }
-        __syncthreads();
     }
-    for (int r = threadIdx.x; r < rows_used; r += kThreads) r_lnS[r] = log(r_S[r]);
+    for (int r = threadIdx.x; r < rows; r += kThreads) rs.lnS[r] = log(rs.S[r]);
     __syncthreads();
+}
 
-    if (MODE == kGreedy || MODE == kExact || MODE == kRelaxed) {
-        if (wave == 0) {
-            const int j = lane;
-            bool acc = false;
-            double lp = 0.0, lq = 0.0;
-            const double lx = lxf, dx = dxf;
-            if (j < K) {
-                if (!bad) {
-                    if (MODE == kGreedy) {
-                        acc = (x == r_g[j]);
-                        lp = -r_lnS[j];
+// ------------------------------------------------------ chain decision
+// Lane j < K of wave 0 evaluates the test of draft j; a ballot finds the
+// first rejection n (lane K never accepts, so n <= K).  Results go to LDS.
+struct ChainDecision {
+    int n, bad_n;
+    int x[64];
+    double lp[64], lq[64], lx[64], dx[64];
+};
+
+template <typename T, int MODE>
+__device__ void chain_decide(const Args& a, int b, const RowStats& rs, ChainDecision& cd) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+        const int j = lane, K = a.K;
+        bool acc = false, bad = false;
+        int x = -1;
+        double lp = 0.0, lq = 0.0, lx = -INFINITY, dx = -INFINITY;
+        if (j < K) {
+            x = a.tok[b * K + j];
+            bad = (unsigned)x >= (unsigned)a.V;
+            if (!bad) {
+                if (MODE == kGreedy) {
+                    acc = (x == rs.g[j]);
+                    lp = -rs.lnS[j];  // the accepted token is the row max
+                } else {
+                    const T* Tp = reinterpret_cast<const T*>(a.T);
+                    lx = Elem<T>::at(Tp, (size_t)(b * a.rows_t + j) * a.V + x);
+                    lp = (lx - (double)rs.M[j]) - rs.lnS[j];
+                    if (MODE == kExact) {
+                        const T* Dp = reinterpret_cast<const T*>(a.D);
+                        dx = Elem<T>::at(Dp, (size_t)(b * K + j) * a.V + x);
+                        lq = (dx - (double)rs.M[a.rows_t + j]) - rs.lnS[a.rows_t + j];
+                        double r;
+                        if (lp == -INFINITY)
+                            r = 0.0;
+                        else if (lq == -INFINITY)
+                            r = INFINITY;
+                        else
+                            r = exp(lp - lq);
+                        acc = (double)a.u[b * (K + 1) + j] < r;
                     } else {
-                        lp = (lx - (double)r_M[j]) - r_lnS[j];
-                        if (MODE == kExact) {
-                            lq = (dx - (double)r_M[a.rows_t + j]) - r_lnS[a.rows_t + j];
-                            double r;
-                            if (lp == -INFINITY)
-                                r = 0.0;
-                            else if (lq == -INFINITY)
-                                r = INFINITY;
-                            else
-                                r = exp(lp - lq);
-                            acc = (double)a.u[b * (K + 1) + j] < r;
-                        } else {
-                            acc = (r_c[j] < a.top_k) || (exp(lp) >= (double)a.tau);
-                        }
+                        acc = (rs.c[j] < a.top_k) || (exp(lp) >= (double)a.tau);
                     }
                 }
             }
-            const unsigned long long mask = __ballot(acc);
-            const int n = __builtin_ctzll(~mask);  // lane K never accepts, so n <= K
-            int32_t* otok = a.out_tok + (size_t)b * L;
-            float* otlp = a.out_tlp ? a.out_tlp + (size_t)b * L : nullptr;
-            float* oblp = a.out_blp ? a.out_blp + (size_t)b * L : nullptr;
-            if (j < n) {
-                otok[j] = x;
-                if (otlp) otlp[j] = (float)lp;
-                if (oblp) oblp[j] = (MODE == kExact) ? (float)fmin(0.0, lp - lq) : 0.f;
-            } else if (j > n && j < L) {
-                otok[j] = -1;
-                if (otlp) otlp[j] = 0.f;
-                if (oblp) oblp[j] = 0.f;
-            } else if (j == n) {
-                a.out_len[b] = n;
-                a.out_status[b] = s_bad_ws ? 2 : ((n < K && bad) ? 1 : 0);
-                if (MODE == kGreedy) {
-                    otok[n] = r_g[n];
-                    if (otlp) otlp[n] = (float)(-r_lnS[n]);
-                    if (oblp) oblp[n] = 0.f;
-                } else {
-                    Desc d;
-                    d.n = n;
-                    d.residual = (MODE == kExact && n < K) ? 1 : 0;
-                    d.row_t = b * a.rows_t + n;
-                    d.row_d = b * K + n;
-                    d.Mt = r_M[n];
-                    d.lnSt = r_lnS[n];
-                    d.Md = d.residual ? r_M[a.rows_t + n] : 0.f;
-                    d.lnSd = d.residual ? r_lnS[a.rows_t + n] : 0.0;
-                    d.lx = lx;
-                    d.dx = dx;
-                    d.pad0 = d.pad1 = 0;
-                    desc[b] = d;
-                }
-            }
         }
-    } else {  // tree
-        __shared__ int t_par[SPEC_MAX_NODES];
-        __shared__ int t_match[SPEC_MAX_NODES];
-        __shared__ int t_path[SPEC_MAX_NODES];
-        __shared__ int t_d, t_e, t_bad;
-        const int N = a.rows_t;
-        if (wave == 0) {
-            const int i = lane;
-            bool bad = false;
-            if (i >= 1 && i < nb) {
-                const int p = a.parents[b * N + i];
-                const int t = a.tok[b * N + i];
-                bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.V);
-                t_par[i] = bad ? -1 : p;
-                t_match[i] = bad ? 0 : (t == r_g[p]);
-            }
-            const unsigned long long bm = __ballot(bad);
-            if (lane == 0) t_bad = bm != 0ull;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            // accepted iff matched and parent accepted; parents precede children
-            unsigned long long accm = 1ull;  // bit i: node i accepted
-            int depth[SPEC_MAX_NODES];
-            depth[0] = 0;
-            int e = 0;
-            for (int i = 1; i < nb; ++i) {
-                const int p = t_par[i];
-                depth[i] = 0;
-                if (p >= 0 && t_match[i] && ((accm >> p) & 1ull)) {
-                    accm |= 1ull << i;
-                    depth[i] = depth[p] + 1;
-                    if (depth[i] > depth[e]) e = i;
-                }
-            }
-            const int d = depth[e];
-            for (int v = e, k = d - 1; k >= 0; --k, v = t_par[v]) t_path[k] = v;
-            t_d = d;
-            t_e = e;
-        }
-        __syncthreads();
-        const int d = t_d, e = t_e;
-        for (int k = threadIdx.x; k < N; k += kThreads) {
-            int32_t* otok = a.out_tok + (size_t)b * N;
-            if (k < d) {
-                const int v = t_path[k];
-                a.out_path[(size_t)b * N + k] = v;
-                otok[k] = a.tok[b * N + v];
-                if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (float)(-r_lnS[t_par[v]]);
-            } else {
-                a.out_path[(size_t)b * N + k] = -1;
-                otok[k] = (k == d) ? r_g[e] : -1;
-                if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (k == d) ? (float)(-r_lnS[e]) : 0.f;
-            }
-            if (a.out_blp) a.out_blp[(size_t)b * N + k] = 0.f;
-        }
-        if (threadIdx.x == 0) {
-            a.out_len[b] = d;
-            a.out_status[b] = s_bad_ws ? 2 : t_bad;
+        const unsigned long long mask = __ballot(acc);
+        const int n = __builtin_ctzll(~mask);
+        cd.x[j] = x;
+        cd.lp[j] = lp;
+        cd.lq[j] = lq;
+        cd.lx[j] = lx;
+        cd.dx[j] = dx;
+        if (j == n) {
+            cd.n = n;
+            cd.bad_n = (n < K && bad) ? 1 : 0;
         }
     }
-    if (threadIdx.x == 0) ticket_reset(ticket1(a, b));
+    __syncthreads();
+}
+
+// Writes positions j < n (accepted drafts) and n < j < L (padding) of the
+// chain outputs, plus accept_len and status.  Position n is the caller's.
+template <int MODE>
+__device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
+    const int n = cd.n, L = a.L;
+    int32_t* otok = a.out_tok + (size_t)b * L;
+    float* otlp = a.out_tlp ? a.out_tlp + (size_t)b * L : nullptr;
+    float* oblp = a.out_blp ? a.out_blp + (size_t)b * L : nullptr;
+    for (int j = threadIdx.x; j < L; j += kThreads) {
+        if (j < n) {
+            otok[j] = cd.x[j];
+            if (otlp) otlp[j] = (float)cd.lp[j];
+            if (oblp) oblp[j] = (MODE == kExact) ? (float)fmin(0.0, cd.lp[j] - cd.lq[j]) : 0.f;
+        } else if (j > n) {
+            otok[j] = -1;
+            if (otlp) otlp[j] = 0.f;
+            if (oblp) oblp[j] = 0.f;
+        }
+    }
+    if (threadIdx.x == 0) {
+        a.out_len[b] = n;
+        a.out_status[b] = cd.bad_n;
+    }
+}
+
+// -------------------------------------------------- greedy and tree: decide
+template <typename T, int MODE, bool SUM>
+__global__ __launch_bounds__(kThreads) void k_decide(const Args a) {
+    const int b = blockIdx.x;
+    __shared__ RowStats rs;
+    const int nb = (MODE == kTree && a.num_nodes) ? min(max(a.num_nodes[b], 1), a.rows_t) : a.rows_t;
+    gather_rows<SUM>(a, b, MODE == kTree ? nb : a.R, rs);
+    if (MODE == kGreedy) {
+        __shared__ ChainDecision cd;
+        chain_decide<T, kGreedy>(a, b, rs, cd);
+        write_prefix<kGreedy>(a, b, cd);
+        if (threadIdx.x == 0) {
+            const int n = cd.n;
+            a.out_tok[(size_t)b * a.L + n] = rs.g[n];
+            if (a.out_tlp) a.out_tlp[(size_t)b * a.L + n] = (float)(-rs.lnS[n]);
+            if (a.out_blp) a.out_blp[(size_t)b * a.L + n] = 0.f;
+        }
+        return;
+    }
+    // tree: a node is accepted iff its token is its parent's argmax and its
+    // parent is accepted; parents precede children
+    __shared__ int t_par[SPEC_MAX_NODES];
+    __shared__ int t_match[SPEC_MAX_NODES];
+    __shared__ int t_path[SPEC_MAX_NODES];
+    __shared__ int t_d, t_e, t_bad;
+    const int N = a.rows_t;
+    if (threadIdx.x < 64) {
+        const int i = threadIdx.x;
+        bool bad = false;
+        if (i >= 1 && i < nb) {
+            const int p = a.parents[b * N + i];
+            const int t = a.tok[b * N + i];
+            bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.V);
+            t_par[i] = bad ? -1 : p;
+            t_match[i] = bad ? 0 : (t == rs.g[p]);
+        }
+        const unsigned long long bm = __ballot(bad);
+        if (i == 0) t_bad = bm != 0ull;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long accm = 1ull;  // bit i: node i accepted
+        int depth[SPEC_MAX_NODES];
+        depth[0] = 0;
+        int e = 0;
+        for (int i = 1; i < nb; ++i) {
+            const int p = t_par[i];
+            depth[i] = 0;
+            if (p >= 0 && t_match[i] && ((accm >> p) & 1ull)) {
+                accm |= 1ull << i;
+                depth[i] = depth[p] + 1;
+                if (depth[i] > depth[e]) e = i;
+            }
+        }
+        const int d = depth[e];
+        for (int v = e, k = d - 1; k >= 0; --k, v = t_par[v]) t_path[k] = v;
+        t_d = d;
+        t_e = e;
+    }
+    __syncthreads();
+    const int d = t_d, e = t_e;
+    for (int k = threadIdx.x; k < N; k += kThreads) {
+        int32_t* otok = a.out_tok + (size_t)b * N;
+        if (k < d) {
+            const int v = t_path[k];
+            a.out_path[(size_t)b * N + k] = v;
+            otok[k] = a.tok[b * N + v];
+            if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (float)(-rs.lnS[t_par[v]]);
+        } else {
+            a.out_path[(size_t)b * N + k] = -1;
+            otok[k] = (k == d) ? rs.g[e] : -1;
+            if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (k == d) ? (float)(-rs.lnS[e]) : 0.f;
+        }
+        if (a.out_blp) a.out_blp[(size_t)b * N + k] = 0.f;
+    }
+    if (threadIdx.x == 0) {
+        a.out_len[b] = d;
+        a.out_status[b] = t_bad;
+    }
 }
 
 // -------------------------------------------------------------------- pass 2
@@ -899,9 +1042,7 @@ __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int PER = kP2Vecs * VEC;  // tokens per thread
     constexpr int CH = kThreads * PER;
-    const Layout lay = make_layout(a.B, a.R, a.C1, a.C2);
-    uint64_t* slots = reinterpret_cast<uint64_t*>(a.ws + lay.p2);
-    const Desc* descs = reinterpret_cast<const Desc*>(a.ws + lay.desc);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(a.ws + make_layout(a.B, a.R, a.C2).p2);
 
     const int b = blockIdx.x / a.C2;
     const int c = blockIdx.x % a.C2;
@@ -916,12 +1057,21 @@ __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
     __shared__ int s_last;
     fill_exp_table(tab);
 
-    const Desc d = descs[b];
-    const bool residual = EXACT && d.residual;
-    const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)d.row_t * a.V;
-    const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)d.row_d * a.V : trow;
-    const double Mt = d.Mt, Md = d.Md;
-    const double cls = d.lnSt - d.lnSd;  // p > q  <=>  (l - Mt) - (d - Md) > lnSt - lnSd
+    // Every workgroup of the request derives the same decision from the
+    // streamed row statistics (deterministic), then works on the row(s) the
+    // terminal token is drawn from: target row n, and draft row n for a
+    // residual.
+    __shared__ RowStats rs;
+    __shared__ ChainDecision cd;
+    gather_rows<true>(a, b, a.R, rs);
+    chain_decide<T, EXACT ? kExact : kRelaxed>(a, b, rs, cd);
+    const int n = cd.n;
+    const bool residual = EXACT && n < a.K;
+    const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
+    const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
+    const double Mt = rs.M[n], Md = residual ? (double)rs.M[a.rows_t + n] : 0.0;
+    // p > q  <=>  (l - Mt) - (d - Md) > lnSt - lnSd (streamed normalizers)
+    const double cls = residual ? rs.lnS[n] - rs.lnS[a.rows_t + n] : 0.0;
     const __amdgpu_buffer_rsrc_t rt = row_rsrc(trow, a.V);
     const __amdgpu_buffer_rsrc_t rd = row_rsrc(drow, a.V);
     __syncthreads();
@@ -1070,7 +1220,6 @@ __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
         // a valid index.
         int y = (s_y != INT_MAX) ? s_y : (s_ylast >= 0 ? s_ylast : s_yany);
         if (y < 0 || y >= a.V) y = 0;
-        const int n = d.n;
         const int L = a.L;
         a.out_tok[(size_t)b * L + n] = y;
         const double lnS = log(S);
@@ -1081,22 +1230,23 @@ __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
             const double lnSq = log(Sq);
             const double dy = (double)Elem<T>::at(drow, (size_t)y);
             const double wy = exp_nonpos(ly - Mt, tab) * iS - exp_nonpos(dy - Md, tab) * iSq;
-            const double lp = (d.lx - Mt) - lnS, lq = (d.dx - Md) - lnSq;
+            const double lp = (cd.lx[n] - Mt) - lnS, lq = (cd.dx[n] - Md) - lnSq;
             const double rn = (lp == -INFINITY) ? 0.0 : exp(lp - lq);
             blp = log1p(-rn) + log(wy) - log(s_Z);
         }
         if (a.out_tlp) a.out_tlp[(size_t)b * L + n] = (float)tlp;
         if (a.out_blp) a.out_blp[(size_t)b * L + n] = (float)blp;
-        if (s_bad_ws) a.out_status[b] = 2;
         ticket_reset(ticket2(a, b));
     }
+    write_prefix<EXACT ? kExact : kRelaxed>(a, b, cd);
+    if (threadIdx.x == 0 && s_bad_ws) a.out_status[b] = 2;
 }
 
 // ------------------------------------------------------------------- host
 inline int vec_elems(spec_dtype dt) { return dt == SPEC_BF16 ? 8 : 4; }
 inline int esize(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
 inline int chunks(int V, int ch) { return (V + ch - 1) / ch; }
-inline int c1_of(spec_dtype dt, int V) { return chunks(V, kThreads * kP1Vecs * vec_elems(dt)); }
+inline int tpr_of(spec_dtype dt, int V) { return chunks(V, kThreads * kTileVecs * vec_elems(dt)); }
 inline int c2_of(spec_dtype dt, int V) { return chunks(V, kThreads * kP2Vecs * vec_elems(dt)); }
 
 inline bool vec_ok(const void* p, spec_dtype dt, int V) {
@@ -1105,7 +1255,7 @@ inline bool vec_ok(const void* p, spec_dtype dt, int V) {
 
 spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt) {
     if (!ws || ((uintptr_t)ws % 256) != 0) return SPEC_EWORKSPACE;
-    const Layout L = make_layout(B, R, c1_of(dt, V), c2_of(dt, V));
+    const Layout L = make_layout(B, R, c2_of(dt, V));
     return bytes >= L.total ? SPEC_OK : SPEC_EWORKSPACE;
 }
 
@@ -1114,28 +1264,55 @@ spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt)
 thread_local hipEvent_t g_prof_before = nullptr;
 thread_local hipEvent_t g_prof_after = nullptr;
 
+// Streaming grid: kWgPerCu workgroups per compute unit of the current
+// device, never more workgroups than tiles.
+int stream_grid(long long tiles) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    long long g = (long long)cus * kWgPerCu;
+    if (g > kMaxGrid) g = kMaxGrid;
+    if (g > tiles) g = tiles;
+    return (int)g;
+}
+
+// Streaming kernel, then the per-request kernel (decision, or decision and
+// terminal sample).
 template <int MODE, bool SUM>
-spec_status launch_p1(const Args& a, spec_dtype dt, hipStream_t st) {
-    const int grid = a.B * a.R * a.C1;
+spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
+    a.tpr = tpr_of(dt, a.V);
+    a.G = stream_grid((long long)a.B * a.R * a.tpr);
     hipEvent_t before = g_prof_before, after = g_prof_after;
     g_prof_before = g_prof_after = nullptr;
     if (before && hipEventRecord(before, st) != hipSuccess) return SPEC_EHIP;
-    if (dt == SPEC_BF16)
-        hipLaunchKernelGGL((k_pass1<uint16_t, MODE, SUM>), dim3(grid), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_pass1<float, MODE, SUM>), dim3(grid), dim3(kThreads), 0, st, a);
+    const bool vecp = a.vec_t && (MODE != kExact || a.vec_d);
+    if (dt == SPEC_BF16) {
+        if (vecp)
+            hipLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true>), dim3(a.G), dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false>), dim3(a.G), dim3(kThreads), 0, st, a);
+    } else {
+        if (vecp)
+            hipLaunchKernelGGL((k_stream<float, MODE, SUM, true>), dim3(a.G), dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_stream<float, MODE, SUM, false>), dim3(a.G), dim3(kThreads), 0, st, a);
+    }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (after && hipEventRecord(after, st) != hipSuccess) return SPEC_EHIP;
-    return SPEC_OK;
-}
-
-template <bool EXACT>
-spec_status launch_p2(const Args& a, spec_dtype dt, hipStream_t st) {
-    const int grid = a.B * a.C2;
-    if (dt == SPEC_BF16)
-        hipLaunchKernelGGL((k_pass2<uint16_t, EXACT>), dim3(grid), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_pass2<float, EXACT>), dim3(grid), dim3(kThreads), 0, st, a);
+    if (MODE == kGreedy || MODE == kTree) {
+        if (dt == SPEC_BF16)
+            hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM>), dim3(a.B), dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_decide<float, MODE, SUM>), dim3(a.B), dim3(kThreads), 0, st, a);
+    } else {
+        constexpr bool EXACT = (MODE == kExact);
+        const int grid = a.B * a.C2;
+        if (dt == SPEC_BF16)
+            hipLaunchKernelGGL((k_pass2<uint16_t, EXACT>), dim3(grid), dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_pass2<float, EXACT>), dim3(grid), dim3(kThreads), 0, st, a);
+    }
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
@@ -1159,7 +1336,7 @@ size_t spec_verify_workspace_bytes(int B, int rows_per_request, int V) {
         V > SPEC_MAX_V)
         return 0;
     // fp32 uses the smaller chunks, so its layout bounds both dtypes
-    const Layout L = make_layout(B, rows_per_request, c1_of(SPEC_F32, V), c2_of(SPEC_F32, V));
+    const Layout L = make_layout(B, rows_per_request, c2_of(SPEC_F32, V));
     return L.total;
 }
 
@@ -1199,7 +1376,6 @@ spec_status spec_verify_greedy(const void* target_logits, spec_dtype dtype,
     a.V = V;
     a.rows_t = K + 1;
     a.R = K + 1;
-    a.C1 = c1_of(dtype, V);
     a.C2 = c2_of(dtype, V);
     a.vec_t = vec_ok(target_logits, dtype, V);
     a.out_tok = out_tokens;
@@ -1210,8 +1386,8 @@ spec_status spec_verify_greedy(const void* target_logits, spec_dtype dtype,
     a.L = K + 1;
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (out_target_logprob) return launch_p1<kGreedy, true>(a, dtype, st);
-    return launch_p1<kGreedy, false>(a, dtype, st);
+    if (out_target_logprob) return launch<kGreedy, true>(a, dtype, st);
+    return launch<kGreedy, false>(a, dtype, st);
 }
 
 spec_status spec_verify_exact(const void* target_logits, const void* draft_logits,
@@ -1237,7 +1413,6 @@ spec_status spec_verify_exact(const void* target_logits, const void* draft_logit
     a.V = V;
     a.rows_t = K + 1;
     a.R = 2 * K + 1;
-    a.C1 = c1_of(dtype, V);
     a.C2 = c2_of(dtype, V);
     a.vec_t = vec_ok(target_logits, dtype, V);
     a.vec_d = vec_ok(draft_logits, dtype, V);
@@ -1249,9 +1424,7 @@ spec_status spec_verify_exact(const void* target_logits, const void* draft_logit
     a.L = K + 1;
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    spec_status s = launch_p1<kExact, true>(a, dtype, st);
-    if (s != SPEC_OK) return s;
-    return launch_p2<true>(a, dtype, st);
+    return launch<kExact, true>(a, dtype, st);
 }
 
 spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
@@ -1277,7 +1450,6 @@ spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
     a.V = V;
     a.rows_t = K + 1;
     a.R = K + 1;
-    a.C1 = c1_of(dtype, V);
     a.C2 = c2_of(dtype, V);
     a.vec_t = vec_ok(target_logits, dtype, V);
     a.tau = tau;
@@ -1290,9 +1462,7 @@ spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
     a.L = K + 1;
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    spec_status s = launch_p1<kRelaxed, true>(a, dtype, st);
-    if (s != SPEC_OK) return s;
-    return launch_p2<false>(a, dtype, st);
+    return launch<kRelaxed, true>(a, dtype, st);
 }
 
 spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
@@ -1319,7 +1489,6 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
     a.V = V;
     a.rows_t = N;
     a.R = N;
-    a.C1 = c1_of(dtype, V);
     a.C2 = c2_of(dtype, V);
     a.vec_t = vec_ok(target_logits, dtype, V);
     a.out_tok = out_tokens;
@@ -1331,8 +1500,8 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
     a.L = N;
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (out_target_logprob) return launch_p1<kTree, true>(a, dtype, st);
-    return launch_p1<kTree, false>(a, dtype, st);
+    if (out_target_logprob) return launch<kTree, true>(a, dtype, st);
+    return launch<kTree, false>(a, dtype, st);
 }
 
 }  // extern "C"
