@@ -36,6 +36,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_verify.hip")
+
+# HBM traffic of one exact-mode streaming-kernel dispatch on this workload,
+# from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch,
+# averaged over dispatches), scaled by what the same counters read for a
+# plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
+# Reported only while the kernel source is the one the counters were taken
+# on.
+TRAFFIC = None
+
 MALL_BYTES = 256 * 1024 * 1024
 METRIC = "verify rounds/s + achieved HBM GB/s (% of peak), B=32 K=5 V=128256 bf16"
 
@@ -199,24 +209,42 @@ def time_case(case, steps, warmup, hip, use_graph):
                 if not torch.equal(o1[k], o2[k]):
                     raise RuntimeError(f"graph replay output {k} differs from the eager call")
         del g
-    # streaming-kernel durations through the library's event hook
-    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    # per-kernel durations through the library's event hook: the streaming
+    # kernel, and the rest of the call
+    evs = [(hip.event(), hip.event(), hip.event()) for _ in range(steps)]
     f = case.fn()
     argv = [case.args(s, stream) for s in range(case.sets)]
     torch.cuda.synchronize()
     for i in range(steps):
-        case.lib.spec_verify_profile_next_call(evs[i][0], evs[i][1])
+        case.lib.spec_verify_profile_next_call(*evs[i])
         assert f(*argv[i % case.sets]) == 0
     torch.cuda.synchronize()
-    ks = [hip.elapsed_ms(x, y) for x, y in evs]
+    ks = [hip.elapsed_ms(x, y) for x, y, _ in evs]
+    rest = [hip.elapsed_ms(y, z) for _, y, z in evs]
     res["kernel_ms_mean"] = sum(ks) / len(ks)
     res["kernel_ms_min"] = min(ks)
-    for x, y in evs:
-        hip.destroy(x)
-        hip.destroy(y)
+    res["rest_ms_mean"] = sum(rest) / len(rest)
+    for e in evs:
+        for x in e:
+            hip.destroy(x)
     hip.destroy(a)
     hip.destroy(b)
     return res
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_bytes():
+    """HBM bytes per streaming-kernel dispatch from the recorded counters, or
+    None when none are recorded for the current kernel source."""
+    if not TRAFFIC or TRAFFIC["source_sha256"] != kernel_source_sha256():
+        return None
+    return int(TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] * 1024 +
+               TRAFFIC["write_kib"] * TRAFFIC["write_scale"] * 1024)
 
 
 def cpu_baseline(ci, seconds):
@@ -252,7 +280,7 @@ def main():
     import synth
 
     lib = sv.load_library()
-    lib.spec_verify_profile_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.spec_verify_profile_next_call.argtypes = [ctypes.c_void_p] * 3
     lib.spec_verify_profile_next_call.restype = None
     dev = torch.device("cuda:0")
     hip = Hip()
@@ -274,7 +302,9 @@ def main():
     ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
     value = 1000.0 / ms
     k_ms = r_ex["kernel_ms_mean"]
-    achieved = bytes_exact / (k_ms * 1e-3) / 1e9
+    # the streaming kernel reads every logit once: its algorithmic bytes
+    stream_bytes = ci.target.nbytes + ci.draft.nbytes
+    achieved = stream_bytes / (k_ms * 1e-3) / 1e9
     g_ms = r_gr["graph_ms_per_step"] if use_graph else r_gr["eager_ms_per_step"]
     out = {
         "metric": METRIC,
@@ -296,18 +326,20 @@ def main():
         "hbm_gbs_call": bytes_exact / (ms * 1e-3) / 1e9,
         "hbm_frac_call": bytes_exact / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "k_pass1<bf16, exact> (streams every logit once)",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(),
+                     "kernel": "k_stream<bf16, exact> (reads every logit once)",
                      "kernel_us_mean": k_ms * 1e3, "kernel_us_min": r_ex["kernel_ms_min"] * 1e3,
-                     "algorithmic_bytes_per_launch": bytes_exact},
+                     "algorithmic_bytes_per_launch": stream_bytes,
+                     "rest_of_call_us_mean": r_ex["rest_ms_mean"] * 1e3},
         "eager": {"rounds_per_s": 1000.0 / r_ex["eager_ms_per_step"],
                   "ms_per_step": r_ex["eager_ms_per_step"]},
         "greedy_c3_shape": {
             "rounds_per_s": 1000.0 / g_ms, "ms_per_step": g_ms,
             "hbm_gbs_call": bytes_greedy / (g_ms * 1e-3) / 1e9,
             "kernel_us_mean": r_gr["kernel_ms_mean"] * 1e3,
-            "kernel_gbs": bytes_greedy / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9,
-            "kernel_frac": bytes_greedy / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_gbs": ci.target.nbytes / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9,
+            "kernel_frac": ci.target.nbytes / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "rest_of_call_us_mean": r_gr["rest_ms_mean"] * 1e3,
             "eager_rounds_per_s": 1000.0 / r_gr["eager_ms_per_step"],
             "algorithmic_bytes": bytes_greedy, "input_sets": sets_greedy},
         "cpu_baseline": None,

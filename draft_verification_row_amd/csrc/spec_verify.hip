@@ -14,48 +14,52 @@
 //   * greedy tree verification of an EAGLE-style draft tree (nanospec
 //     README, intro and benchmark section).
 //
-// How it is computed here (no kernel design comes from the pages):
+// How it is computed here (no kernel design comes from the pages): two
+// kernels per call on the caller's stream.
 //
-//   pass 1  one workgroup per (request, row, vocabulary chunk).  Each thread
-//           streams kP1Vecs 16-byte vectors of its chunk, widens bf16 to
-//           fp32 exactly and keeps the row statistics the rule needs:
-//           max and lowest-index argmax, sum exp(l - m) (v_exp_f32, fp32
-//           per vector, fp64 across vectors), and the rank count
-//           #{t : l_t > l_x}.  Waves reduce with cross-lane shuffles, the
-//           four waves combine through LDS in a fixed order, and the chunk
-//           partial is published to the workspace.  An atomic ticket per
-//           request elects the last workgroup of the request, which gathers
-//           the chunk partials of every row and combines them (fixed order,
-//           fp64), evaluates the
-//           acceptance tests of all K drafts at once (one lane per draft,
-//           fp64), finds the first rejection with a wave ballot, and writes
-//           the accepted prefix.  Greedy and tree calls finish here.
+//   k_stream  one workgroup per (logit row, 16 KB tile).  Each thread issues
+//             its four 16-byte loads at once; the workgroup reduces the tile
+//             max (with the lowest index among equal maxima for the greedy
+//             rules, and the rank count #{t : l_t > l_x} for the relaxed
+//             rule) and, where a normalizer is needed, the sum of
+//             exp(l - tile max): v_exp_f32 per logit, fp32 within a vector,
+//             fp64 beyond.  One 16-byte record per tile goes to the
+//             workspace.  This kernel reads every logit once and carries all
+//             of the call's HBM traffic.
 //
-//   pass 2  (exact and relaxed) one workgroup per (request, chunk) sweeps
-//           the row(s) the terminal token is drawn from, in fp64 with an
-//           explicit Cody-Waite exp: exact normalizers sum_t exp(l_t - M)
-//           for the target (and draft) row and, for a residual, the chunk
-//           sums of exp(l - M) and exp(d - M_q) over the tokens with p > q.
-//           The last workgroup of the request turns these into chunk masses
-//           of relu(p - q) (or of p), picks the chunk holding u_K * Z by a
-//           sequential prefix, rescans that one chunk with a block
-//           exclusive scan and writes the token and its log-probs.
+//   k_decide  (greedy, tree) one workgroup per request.  A wave folds the
+//             tile records of a row, one record per lane: max and argmax by
+//             cross-lane steps, the tile sums rescaled to the row max in
+//             fp64.  Wave 0 then runs the acceptance tests (one lane per
+//             draft or tree node) and writes the outputs.
+//
+//   k_pass2   (exact, relaxed) one workgroup per (request, 4096-token
+//             chunk).  Every workgroup of a request folds the records and
+//             takes the decision itself (same data, same order, same result),
+//             then sweeps its chunk of the row(s) the terminal token is drawn
+//             from, in fp64 with an explicit Cody-Waite exp: sums of
+//             exp(l - Mt) and exp(d - Md) over the chunk and over its tokens
+//             with p > q.  One workgroup per request, elected by an atomic
+//             ticket, turns the chunk sums into chunk masses of relu(p - q)
+//             (or of p), finds the chunk holding u_K * Z with a one-wave scan,
+//             rescans that chunk with a block scan and writes the terminal
+//             token, the log-probs and the accepted prefix.
 //
 // Every reduction runs in a fixed order, so results are bitwise
-// reproducible.  No float atomics are used; atomics only elect the last
-// workgroup.
+// reproducible.  No float atomics are used.
 //
-// Cross-workgroup hand-off.  The workgroups of one request run on all eight
-// XCDs, whose L2 caches are not coherent with each other.  A release/acquire
-// fence at device scope would make every workgroup write back and invalidate
-// its whole L2, which stalls the streaming kernel.  Instead each partial is
-// published as 64-bit words that carry a tag in their upper half
-// (payload | kTag << 32), written and read with relaxed device-scope atomics,
-// which the hardware keeps coherent across XCDs without cache maintenance.
-// Each word validates itself, so no ordering between words is needed: the
-// elected workgroup reads every word, re-reads (with a bounded wait) any
-// whose tag has not arrived yet, and writes zeros back, so the workspace is
-// all zeros between calls.
+// Cross-workgroup hand-off inside k_pass2.  The workgroups of one request run
+// on all eight XCDs, whose L2 caches are not coherent with each other.  A
+// release/acquire fence at device scope would make every workgroup write back
+// and invalidate its whole L2.  Instead each chunk sum is published as 64-bit
+// words that carry a tag in their upper half (payload | kTag << 32), written
+// and read with relaxed device-scope atomics, which the hardware keeps
+// coherent across XCDs without cache maintenance.  Each word validates
+// itself, so no ordering between words is needed: the elected workgroup reads
+// every word, re-reads (with a bounded wait) any whose tag has not arrived
+// yet, and writes zeros back, so those words are zero between calls.  The
+// tile records of k_stream need no such care: the kernel boundary makes them
+// visible to the next kernel.
 #include <hip/hip_runtime.h>
 
 #include <limits.h>
@@ -69,34 +73,41 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTileVecs = 2;  // 16-byte vectors per thread per streaming tile
-constexpr int kWgPerCu = 8;   // streaming workgroups per compute unit
-constexpr int kMaxGrid = 8192;
-constexpr int kP2Vecs = 2;  // 16-byte vectors per thread per pass-2 chunk
+constexpr int kTileBytes = 16384;                        // streaming tile
+constexpr int kTileVecs = kTileBytes / (kThreads * 16);  // 16-byte loads per thread
+constexpr int kStreamWavesPerSimd = 8;                   // k_stream occupancy target
+constexpr int kChunk = 4096;                             // pass-2 tokens per workgroup
+constexpr int kPass2WavesPerSimd = 4;                    // k_pass2 occupancy target
+constexpr int kRun = kChunk / kThreads;                  // pass-2 tokens per thread
 constexpr int kMaxRows = 2 * SPEC_MAX_K + 1;
 constexpr int kMaxB = SPEC_MAX_B;
 // Per-request tickets of pass 2, one 128-byte line each: atomics on a line
-// shared by several requests serialize behind each other.  Zero at rest.
+// shared by several requests serialize behind each other.  The region has a
+// fixed size, so no other data of any call shape ever lands on a ticket.
 constexpr int kCtrlStride = 32;  // int32 per request
 constexpr size_t kCtrlBytes = (size_t)kMaxB * kCtrlStride * 4;
-constexpr int kMaxC2 = 256;  // pass-2 chunks per row at SPEC_MAX_V (bf16 and fp32)
-static_assert(SPEC_MAX_V <= kMaxC2 * kThreads * kP2Vecs * 4, "pass-2 chunk table too small");
-static_assert(kMaxC2 <= kThreads, "one pass-2 chunk per thread in the terminal scan");
+// Tiles per row at SPEC_MAX_V (fp32 has the most): one record per lane.
+constexpr int kMaxTiles = (SPEC_MAX_V * 4 + kTileBytes - 1) / kTileBytes;
+static_assert(kMaxTiles <= 64, "a row's tile records must fit one wave");
+constexpr int kMaxC2 = (SPEC_MAX_V + kChunk - 1) / kChunk;
+static_assert(kMaxC2 <= 64, "a row's pass-2 chunks must fit one wave");
 constexpr uint32_t kTag = 0x5ec0fa11u;
 constexpr int kMaxSpins = 1 << 20;  // bounded wait for a published word (~60 ms)
 
 enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3 };
 
-// Statistics of one row segment, written by the streaming kernel and read by
-// the next kernel on the stream (the launch boundary makes them visible):
-// max, lowest index of the max, rank count, sum exp(l - max).
-struct alignas(8) Seg {
+// Statistics of one tile: max m, then the lowest index of the max (greedy,
+// tree) or the rank count (relaxed), and s = sum over the tile of
+// 2^(l*log2e - fl(m*log2e)), i.e. sum exp(l - m) up to the rounding of the
+// reference.  Neither 64-bit half of a record can equal a tagged word (the
+// int is below 2^18 or INT_MAX; s is at most 8192), so records left in the
+// workspace never pass for published pass-2 words.
+struct alignas(16) Seg {
     float m;
-    int idx;
-    int cnt;
-    int pad;
+    int ic;
     double s;
 };
+static_assert(sizeof(Seg) == 16, "one 16-byte load per record");
 
 // Chunk partial of pass 2 (eight tagged words = four fp64 sums): sum of
 // a = exp(l - Mt) and b = exp(d - Md) over the chunk, and over its tokens
@@ -109,11 +120,11 @@ struct Layout {
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ inline Layout make_layout(int B, int R, int C2) {
+// [tickets: fixed kCtrlBytes][tile records B*R*tpr][pass-2 words B*C2*8]
+inline Layout make_layout(int B, int R, int tpr, int C2) {
     Layout L;
-    // one segment record per (streaming workgroup, row it touches): ids w + row
     L.seg = kCtrlBytes;
-    L.p2 = align_up(L.seg + ((size_t)kMaxGrid + (size_t)B * R) * sizeof(Seg), 256);
+    L.p2 = align_up(L.seg + (size_t)B * R * tpr * sizeof(Seg), 256);
     L.total = align_up(L.p2 + (size_t)B * C2 * kP2Words * 8, 256);
     return L;
 }
@@ -147,8 +158,18 @@ struct Elem<uint16_t> {  // bf16 bit patterns
     __device__ static inline u32x4 vraw(__amdgpu_buffer_rsrc_t r, int e) {
         return __builtin_amdgcn_raw_buffer_load_b128(r, e * 2, 0, AUX);
     }
-    __device__ static inline float sraw(__amdgpu_buffer_rsrc_t r, int e) {
-        return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, e * 2, 0, 0) << 16);
+    // VEC elements from e on, one buffer load each, packed like a vector
+    __device__ static inline u32x4 sgather(__amdgpu_buffer_rsrc_t r, int e) {
+        u32x4 q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            q[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (e + 2 * j) * 2, 0, 0) |
+                   ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (e + 2 * j + 1) * 2, 0, 0) << 16);
+        return q;
+    }
+    // element j of a packed vector
+    __device__ static inline float get(const u32x4& q, int j) {
+        return __uint_as_float((j & 1) ? (q[j >> 1] & 0xffff0000u) : (q[j >> 1] << 16));
     }
     // VEC elements from e on (indices clamped to V-1), one load each, packed
     // like a 16-byte vector load
@@ -167,6 +188,15 @@ struct Elem<uint16_t> {  // bf16 bit patterns
             v[2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
         }
     }
+    // Sets the elements e + i >= V of a packed vector to -inf (bits 0xff80).
+    __device__ static inline void mask_tail(u32x4& q, int e, int V) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = (e + 2 * j < V) ? (q[j] & 0xffffu) : 0xff80u;
+            const uint32_t hi = (e + 2 * j + 1 < V) ? (q[j] & 0xffff0000u) : 0xff800000u;
+            q[j] = lo | hi;
+        }
+    }
 };
 
 template <>
@@ -177,9 +207,13 @@ struct Elem<float> {
     __device__ static inline u32x4 vraw(__amdgpu_buffer_rsrc_t r, int e) {
         return __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, AUX);
     }
-    __device__ static inline float sraw(__amdgpu_buffer_rsrc_t r, int e) {
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, e * 4, 0, 0));
+    __device__ static inline u32x4 sgather(__amdgpu_buffer_rsrc_t r, int e) {
+        u32x4 q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = __builtin_amdgcn_raw_buffer_load_b32(r, (e + j) * 4, 0, 0);
+        return q;
     }
+    __device__ static inline float get(const u32x4& q, int j) { return __uint_as_float(q[j]); }
     __device__ static inline u32x4 gather_clamped(const float* pp, int e, int V) {
         const __attribute__((address_space(1))) float* p = (const __attribute__((address_space(1))) float*)pp;
         u32x4 q;
@@ -191,59 +225,40 @@ struct Elem<float> {
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(q[j]);
     }
+    __device__ static inline void mask_tail(u32x4& q, int e, int V) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e + j >= V) q[j] = 0xff800000u;
+    }
 };
 
-// Loads this thread's NV vectors of the chunk [c0, c1): vector k holds
-// elements c0 + (k * kThreads + tid) * VEC + [0, VEC).  Elements at or past
-// c1 read as -inf.  `vec` selects the 16-byte path (row start and size
-// 16-byte aligned); otherwise each element is loaded on its own.  AUX is the
-// cache-policy field of the vector loads (kStream: read once, do not keep).
-constexpr int kStream = 2;
-template <typename T, int NV, int AUX = 0>
-__device__ inline void load_chunk(__amdgpu_buffer_rsrc_t r, int c0, int c1, bool vec,
-                                  float (&v)[NV][Elem<T>::kVec]) {
+// Loads this thread's NV packed vectors of the chunk [c0, c1): vector k
+// holds elements c0 + (k * kThreads + tid) * VEC + [0, VEC).  Elements at or
+// past c1 read as -inf.  `vec` selects the 16-byte path (row start and size
+// 16-byte aligned); otherwise each element is loaded on its own.  Values stay
+// packed (bf16: two per register) until they are used.
+template <typename T, int NV>
+__device__ inline void load_chunk(__amdgpu_buffer_rsrc_t r, int c0, int c1, bool vec, u32x4 (&q)[NV]) {
     constexpr int VEC = Elem<T>::kVec;
     const int t0 = c0 + (int)threadIdx.x * VEC;
-    if (vec) {
-        u32x4 q[NV];
 #pragma unroll
-        for (int k = 0; k < NV; ++k) q[k] = Elem<T>::template vraw<AUX>(r, t0 + k * kThreads * VEC);
-#pragma unroll
-        for (int k = 0; k < NV; ++k) Elem<T>::unpack(q[k], v[k]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < NV; ++k)
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) v[k][i] = Elem<T>::sraw(r, t0 + k * kThreads * VEC + i);
-    }
+    for (int k = 0; k < NV; ++k)
+        q[k] = vec ? Elem<T>::vraw(r, t0 + k * kThreads * VEC) : Elem<T>::sgather(r, t0 + k * kThreads * VEC);
     if (c1 - c0 < NV * kThreads * VEC) {  // partial chunk (uniform per workgroup)
 #pragma unroll
-        for (int k = 0; k < NV; ++k)
-#pragma unroll
-            for (int i = 0; i < VEC; ++i)
-                if (t0 + k * kThreads * VEC + i >= c1) v[k][i] = -INFINITY;
+        for (int k = 0; k < NV; ++k) Elem<T>::mask_tail(q[k], t0 + k * kThreads * VEC, c1);
     }
 }
 
-// Loads NV vectors of consecutive tokens [e0, e0 + NV*VEC) (one thread's
-// contiguous run); tokens at or past V read as -inf.
+// Loads NV packed vectors of consecutive tokens [e0, e0 + NV*VEC) (one
+// thread's contiguous run); tokens at or past V read as -inf.
 template <typename T, int NV>
-__device__ inline void load_run(__amdgpu_buffer_rsrc_t r, int e0, int V, bool vec,
-                                float (&v)[NV * Elem<T>::kVec]) {
+__device__ inline void load_run(__amdgpu_buffer_rsrc_t r, int e0, int V, bool vec, u32x4 (&q)[NV]) {
     constexpr int VEC = Elem<T>::kVec;
-    if (vec) {
-        u32x4 q[NV];
 #pragma unroll
-        for (int k = 0; k < NV; ++k) q[k] = Elem<T>::vraw(r, e0 + k * VEC);
+    for (int k = 0; k < NV; ++k) q[k] = vec ? Elem<T>::vraw(r, e0 + k * VEC) : Elem<T>::sgather(r, e0 + k * VEC);
 #pragma unroll
-        for (int k = 0; k < NV; ++k) Elem<T>::unpack(q[k], v + k * VEC);
-    } else {
-#pragma unroll
-        for (int i = 0; i < NV * VEC; ++i) v[i] = Elem<T>::sraw(r, e0 + i);
-    }
-#pragma unroll
-    for (int i = 0; i < NV * VEC; ++i)
-        if (e0 + i >= V) v[i] = -INFINITY;
+    for (int k = 0; k < NV; ++k) Elem<T>::mask_tail(q[k], e0 + k * VEC, V);
 }
 
 // ------------------------------------------------------------ fp64 exp(x<=0)
@@ -456,12 +471,12 @@ __device__ inline double join_double(uint32_t lo, uint32_t hi) {
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-__device__ inline int ticket_add(int* t) {
-    return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ inline unsigned ticket_add(int* t) {
+    return (unsigned)__hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ inline void ticket_reset(int* t) {
-    __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ inline void ticket_sub(int* t, int v) {
+    __hip_atomic_fetch_add(t, -v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------- args
@@ -476,7 +491,6 @@ struct Args {
     int rows_t;  // target rows per request: K+1, or N for a tree
     int R;       // rows streamed per request
     int tpr;     // streaming tiles per row
-    int G;       // streaming workgroups
     int C2;      // pass-2 chunks per row
     int vec_t, vec_d;
     float tau;
@@ -489,21 +503,12 @@ struct Args {
     int32_t* out_path;
     int L;  // output row length: K+1, or N for a tree
     unsigned char* ws;
+    Seg* segs;        // [B][R][tpr]
+    uint64_t* p2;     // [B][C2][kP2Words]
+    int* tickets;     // [B][kCtrlStride]
 };
 
-__device__ inline int* ticket2(const Args& a, int b) {
-    return reinterpret_cast<int*>(a.ws) + kCtrlStride * b;
-}
-
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// The streaming split: all tiles of the call (row-major: global row g of the
-// call, then tile c of the row) are cut into G contiguous, equal ranges.
-__host__ __device__ inline int split_lo(long long total, int G, int w) { return (int)(total * w / G); }
-// workgroup whose range holds tile t
-__host__ __device__ inline int split_owner(long long total, int G, long long t) {
-    return (int)(((t + 1) * G - 1) / total);
-}
 
 template <typename T>
 __device__ inline const T* uniform_ptr(const T* p) {
@@ -538,8 +543,7 @@ __device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[kTileVec
     if (VECP) {  // V is a multiple of VEC and every row is 16-byte aligned
 #pragma unroll
         for (int k = 0; k < kTileVecs; ++k) {
-            // global address space: global loads wait on vmcnt only, so the
-            // look-ahead loads stay in flight while this tile is reduced
+            // global (not flat) address space: these loads wait on vmcnt only
             const gu32x4* p = (const gu32x4*)(row + min(t0 + k * kThreads * VEC, V - VEC));
             q[k] = NT ? __builtin_nontemporal_load(p) : *p;
         }
@@ -550,336 +554,277 @@ __device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[kTileVec
 }
 
 // ----------------------------------------------------------- streaming pass
-// Every logit row is read once.  Workgroup w walks tiles [lo(w), lo(w+1))
-// with one tile of look-ahead and keeps per-thread running statistics; at
-// the end of each row segment it reduces them over the workgroup and writes
-// one Seg record, id w + row.  Per element: widen, max (and argmax), and for
-// the normalizer one fma, one exp2 and one add.
+// Every logit row is read once, one tile per workgroup.  Per element: widen,
+// max (or argmax, or rank compare), and for the normalizer one fma, one exp2
+// and one add against the tile max, which the workgroup agrees on first.
 // VECP: every row of the call takes the 16-byte path (chosen on the host).
 template <typename T, int MODE, bool SUM, bool VECP>
-__global__ __launch_bounds__(kThreads, kWgPerCu) void k_stream(const Args a) {
+__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const Args a) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int TILE = kThreads * kTileVecs * VEC;
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
     constexpr bool NT = ARGMAX;  // greedy and tree never revisit a row
 
-    Seg* segs = reinterpret_cast<Seg*>(a.ws + make_layout(a.B, a.R, a.C2).seg);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    __shared__ double tab[64];
     __shared__ float s_m[kWaves];
     __shared__ int s_i[kWaves];
-    __shared__ int s_c[kWaves];
     __shared__ double s_s[kWaves];
-    if (SUM) fill_exp_table(tab);
-    __syncthreads();
 
-    const long long total = (long long)a.B * a.R * a.tpr;
-    const int w = blockIdx.x;
-    const int t_lo = split_lo(total, gridDim.x, w), t_hi = split_lo(total, gridDim.x, w + 1);
-    if (t_lo >= t_hi) return;
-    int g = uniform(t_lo / a.tpr);
-    int c = uniform(t_lo - g * a.tpr);
-    int vec, act, nvec, nact;
+    const int g = uniform((int)(blockIdx.x / (unsigned)a.tpr));
+    const int c = (int)blockIdx.x - g * a.tpr;
+    int vec, act;
     const T* row = call_row<T, MODE>(a, g, vec, act);
-    const T* nrow = row;
-    u32x4 qn[kTileVecs];
-    if (act) load_tile<T, NT, VECP>(row, a.V, c, qn);
-
-    auto rank_threshold = [&](int gg, const T* rp) -> float {
-        const int b = gg / a.R, rr = gg - (gg / a.R) * a.R;
-        if (!COUNT || rr >= a.K) return INFINITY;
-        const int x = a.tok[b * a.K + rr];
-        return ((unsigned)x < (unsigned)a.V) ? Elem<T>::at(rp, (size_t)x) : INFINITY;
-    };
-    float thr = COUNT ? rank_threshold(g, row) : INFINITY;
-
-    float m = -INFINITY, mL = -INFINITY;
-    int idx = INT_MAX, cnt = 0;
-    double s = 0.0;
-    for (int t = t_lo; t < t_hi; ++t) {
-        u32x4 q[kTileVecs];
-#pragma unroll
-        for (int k = 0; k < kTileVecs; ++k) q[k] = qn[k];
-        const bool row_end = (c + 1 == a.tpr);
-        nvec = vec;
-        nact = act;
-        if (t + 1 < t_hi) {  // look ahead one tile
-            if (row_end) {
-                nrow = call_row<T, MODE>(a, g + 1, nvec, nact);
-                if (nact) load_tile<T, NT, VECP>(nrow, a.V, 0, qn);
-            } else if (act) {
-                load_tile<T, NT, VECP>(row, a.V, c + 1, qn);
-            }
+    if (!act) return;  // tree node past num_nodes: never read
+    u32x4 q[kTileVecs];
+    load_tile<T, NT, VECP>(row, a.V, c, q);
+    float thr = INFINITY;  // relaxed: count the tokens strictly above l_x
+    if (COUNT) {
+        const int b = g / a.R, rr = g - b * a.R;
+        if (rr < a.K) {
+            const int x = a.tok[b * a.K + rr];
+            if ((unsigned)x < (unsigned)a.V) thr = Elem<T>::at(row, (size_t)x);
         }
-        if (act) {
-            const int t0 = c * TILE + (int)threadIdx.x * VEC;
-            float v[kTileVecs][VEC];
+    }
+
+    const int t0 = c * TILE + (int)threadIdx.x * VEC;
+    if (c == a.tpr - 1 && a.V % TILE != 0) {  // ragged last tile: clamped lanes
 #pragma unroll
-            for (int k = 0; k < kTileVecs; ++k) Elem<T>::unpack(q[k], v[k]);
-            if (row_end && a.V % TILE != 0) {  // ragged last tile: clamped lanes
+        for (int k = 0; k < kTileVecs; ++k) Elem<T>::mask_tail(q[k], t0 + k * kThreads * VEC, a.V);
+    }
+    // Values are unpacked from the packed vectors where they are used, so
+    // only the 16-byte vectors stay live between the two phases.
+    float m = -INFINITY;
+    int slot = 0, cnt = 0;  // slot k*VEC + i: first maximum of this thread
 #pragma unroll
-                for (int k = 0; k < kTileVecs; ++k)
+    for (int k = 0; k < kTileVecs; ++k) {
+        float v[VEC];
+        Elem<T>::unpack(q[k], v);
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i)
-                        if (t0 + k * kThreads * VEC + i >= a.V) v[k][i] = -INFINITY;
+        for (int i = 0; i < VEC; ++i) {
+            if (ARGMAX) {
+                if (v[i] > m) {  // ascending token order: keeps the first maximum
+                    m = v[i];
+                    slot = k * VEC + i;
+                }
+            } else {
+                m = fmaxf(m, v[i]);
             }
-            float tm = -INFINITY;
+            if (COUNT) cnt += (v[i] > thr) ? 1 : 0;
+        }
+    }
+    int idx = (m > -INFINITY) ? t0 + (slot / VEC) * (kThreads * VEC) + slot % VEC : INT_MAX;
+    if (ARGMAX)
+        wave_argmax(m, idx);
+    else
+        m = wave_max(m);
+    if (COUNT) cnt = wave_sum_i(cnt);
+    if (lane == 0) {
+        s_m[wave] = m;
+        s_i[wave] = ARGMAX ? idx : cnt;
+    }
+    __syncthreads();
+    float M = s_m[0];
+    int I = s_i[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        if (ARGMAX) {
+            argmax_combine(M, I, s_m[w], s_i[w]);
+        } else {
+            M = fmaxf(M, s_m[w]);
+            I += s_i[w];
+        }
+    }
+    double s = 0.0;
+    if (SUM) {
+        if (M > -INFINITY) {
+            // 2^(l*L - mL) with the reference mL = fl(M*L): every term <= 1
+            const float mL = M * kLog2e;
 #pragma unroll
             for (int k = 0; k < kTileVecs; ++k) {
-                const int base = t0 + k * kThreads * VEC;
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) {
-                    if (ARGMAX) {
-                        if (v[k][i] > m) {
-                            m = v[k][i];
-                            idx = base + i;
-                        }
-                    } else {
-                        tm = fmaxf(tm, v[k][i]);
-                    }
-                    if (COUNT) cnt += (v[k][i] > thr) ? 1 : 0;
-                }
-            }
-            if (!ARGMAX) m = fmaxf(m, tm);
-            if (SUM && m > -INFINITY) {
-                // Running sum of 2^(l*L - mL) against a reference mL = fl(m*L)
-                // that only moves up (the sum is rescaled when it does).
-                const float nL = m * kLog2e;
-                if (nL > mL) {
-                    s *= (double)__builtin_amdgcn_exp2f(mL - nL);
-                    mL = nL;
-                }
+                float v[VEC];
+                Elem<T>::unpack(q[k], v);
                 float acc = 0.f;
 #pragma unroll
-                for (int k = 0; k < kTileVecs; ++k)
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) acc += __builtin_amdgcn_exp2f(fmaf(v[k][i], kLog2e, -mL));
+                for (int i = 0; i < VEC; ++i) acc += __builtin_amdgcn_exp2f(fmaf(v[i], kLog2e, -mL));
                 s += (double)acc;
             }
         }
-        if (row_end || t + 1 == t_hi) {
-            // ---- end of a row segment: reduce over the workgroup, write it
-            if (act) {
-                float M = m;
-                int I = idx;
-                if (ARGMAX)
-                    wave_argmax(M, I);
-                else
-                    M = wave_max(M);
-                if (lane == 0) {
-                    s_m[wave] = M;
-                    s_i[wave] = I;
-                }
-                __syncthreads();
-                M = s_m[0];
-                I = s_i[0];
-#pragma unroll
-                for (int ww = 1; ww < kWaves; ++ww) argmax_combine(M, I, s_m[ww], s_i[ww]);
-                double st = 0.0;
-                if (SUM && M > -INFINITY && m > -INFINITY)  // times 2^(mL - M*L), in fp64
-                    st = s * exp_nonpos(((double)mL - (double)M * (double)kLog2e) * kLn2, tab);
-                if (SUM) st = wave_sum(st);
-                const int ct = COUNT ? wave_sum_i(cnt) : 0;
-                if (lane == 0) {
-                    s_s[wave] = st;
-                    s_c[wave] = ct;
-                }
-                __syncthreads();
-                if (threadIdx.x == 0) {
-                    Seg sg;
-                    sg.m = M;
-                    sg.idx = I;
-                    sg.cnt = 0;
-                    sg.pad = 0;
-                    sg.s = 0.0;
-#pragma unroll
-                    for (int ww = 0; ww < kWaves; ++ww) {
-                        sg.s += s_s[ww];
-                        sg.cnt += s_c[ww];
-                    }
-                    segs[(size_t)w + g] = sg;
-                }
-                __syncthreads();  // s_* are reused by the next segment
-            }
-            m = -INFINITY;
-            mL = -INFINITY;
-            idx = INT_MAX;
-            cnt = 0;
-            s = 0.0;
-        }
-        if (row_end) {
-            ++g;
-            c = 0;
-            row = nrow;
-            vec = nvec;
-            act = nact;
-            if (COUNT && t + 1 < t_hi) thr = rank_threshold(g, row);
-        } else {
-            ++c;
-        }
+        s = wave_sum(s);
+        if (lane == 0) s_s[wave] = s;
+        __syncthreads();
+        s = ((s_s[0] + s_s[1]) + s_s[2]) + s_s[3];
+    }
+    if (threadIdx.x == 0) {
+        Seg sg;
+        sg.m = M;
+        sg.ic = (ARGMAX || COUNT) ? I : 0;
+        sg.s = s;
+        a.segs[blockIdx.x] = sg;
     }
 }
 
 // ------------------------------------------------------- row statistics
-// Combines the Seg records of rows [0, rows) of request b into row max M,
-// argmax g (lowest index), rank count c and log normalizer lnS, in LDS.
-// Segments are gathered one per thread (kThreads per batch); each row then
-// folds its segments in ascending order.  Deterministic.
+// Row max M, argmax g (lowest index), rank count c and log normalizer
+// lnS = log sum exp(l - M) of the rows of one request, in LDS.
 struct RowStats {
     float M[kMaxRows];
     int g[kMaxRows];
     int c[kMaxRows];
     double lnS[kMaxRows];
-    // scratch
-    double S[kMaxRows];
-    float bM[kMaxRows];
-    int off[kMaxRows + 1];
-    int w0[kMaxRows];
-    float qm[kThreads];
-    int qi[kThreads];
-    int qc[kThreads];
-    double qs[kThreads];
 };
 
-template <bool SUM>
-__device__ void gather_rows(const Args& a, int b, int rows, RowStats& rs) {
-    const Seg* segs = reinterpret_cast<const Seg*>(a.ws + make_layout(a.B, a.R, a.C2).seg);
-    const long long total = (long long)a.B * a.R * a.tpr;
-    for (int r = threadIdx.x; r < rows; r += kThreads) {
-        const long long rg = (long long)b * a.R + r;
-        const int w0 = split_owner(total, a.G, rg * a.tpr), w1 = split_owner(total, a.G, (rg + 1) * a.tpr - 1);
-        rs.w0[r] = w0;
-        rs.off[r + 1] = w1 - w0 + 1;
-        rs.M[r] = -INFINITY;
-        rs.g[r] = INT_MAX;
-        rs.c[r] = 0;
-        rs.S[r] = 0.0;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        rs.off[0] = 0;
-        for (int r = 0; r < rows; ++r) rs.off[r + 1] += rs.off[r];
-    }
-    __syncthreads();
-    const int nslots = rs.off[rows];
-    for (int base = 0; base < nslots; base += kThreads) {
-        const int si = base + (int)threadIdx.x;
-        int sr = 0;
-        if (si < nslots) {
-            while (rs.off[sr + 1] <= si) ++sr;
-            const Seg sg = segs[(size_t)rs.w0[sr] + (si - rs.off[sr]) + (size_t)b * a.R + sr];
-            rs.qm[threadIdx.x] = sg.m;
-            rs.qi[threadIdx.x] = sg.idx;
-            rs.qc[threadIdx.x] = sg.cnt;
-            rs.qs[threadIdx.x] = sg.s;
-        }
-        __syncthreads();
-        const int bend = min(base + kThreads, nslots);
-        for (int r = threadIdx.x; r < rows; r += kThreads) {
-            const int lo = max(base, rs.off[r]), hi = min(bend, rs.off[r + 1]);
-            if (lo >= hi) continue;
-            float M = -INFINITY;
-            int g = INT_MAX, C = 0;
-            for (int q = lo; q < hi; ++q) {
-                argmax_combine(M, g, rs.qm[q - base], rs.qi[q - base]);
-                C += rs.qc[q - base];
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+// Folds the tile records of rows [0, nrows) of request b.  Wave w takes rows
+// w, w + 4, ... in batches of four, one tile record per lane; every batch's
+// loads are issued before any is used, and `hook` runs once after the first
+// batch is issued (the caller's dependent loads overlap the fold).  The
+// table of exp_nonpos must be ready.  Ends with a barrier.
+template <int MODE, bool SUM, typename Hook>
+__device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const double* tab, Hook hook) {
+    constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
+    constexpr bool COUNT = (MODE == kRelaxed);
+    constexpr int kBatch = 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    bool hooked = false;
+    for (int k0 = 0; k0 == 0 || wave + kWaves * k0 < nrows; k0 += kBatch) {
+        Seg sg[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int r = wave + kWaves * (k0 + j);
+            if (r < nrows && lane < a.tpr) {
+                sg[j] = a.segs[((size_t)b * a.R + r) * a.tpr + lane];
+            } else {
+                sg[j].m = -INFINITY;
+                sg[j].ic = ARGMAX ? INT_MAX : 0;
+                sg[j].s = 0.0;
             }
-            rs.bM[r] = M;
-            float RM = rs.M[r];
-            int RG = rs.g[r];
-            argmax_combine(RM, RG, M, g);
-            rs.g[r] = RG;
-            rs.c[r] += C;
-            if (!SUM) rs.M[r] = RM;
         }
-        __syncthreads();
-        if (SUM) {
-            if (si < bend) {  // rescale this segment's sum to its batch row max
-                const float mq = rs.qm[threadIdx.x];
-                rs.qs[threadIdx.x] = (mq > -INFINITY) ? rs.qs[threadIdx.x] * exp((double)mq - (double)rs.bM[sr]) : 0.0;
-            }
-            __syncthreads();
-            for (int r = threadIdx.x; r < rows; r += kThreads) {
-                const int lo = max(base, rs.off[r]), hi = min(bend, rs.off[r + 1]);
-                if (lo >= hi) continue;
-                double S = 0.0;
-                for (int q = lo; q < hi; ++q) S += rs.qs[q - base];
-                const float M = rs.bM[r], RM = rs.M[r];
-                if (M > RM) {
-                    rs.S[r] = (RM > -INFINITY ? rs.S[r] * exp((double)RM - (double)M) : 0.0) + S;
-                    rs.M[r] = M;
-                } else if (M > -INFINITY) {
-                    rs.S[r] += S * exp((double)M - (double)RM);
+        if (!hooked) {
+            hook();
+            hooked = true;
+        }
+        double Sl = 1.0;  // lane j: normalizer of batch row j
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int r = wave + kWaves * (k0 + j);
+            if (r >= nrows) break;
+            float M = sg[j].m;
+            int ic = sg[j].ic;
+            if (ARGMAX)
+                wave_argmax(M, ic);
+            else
+                M = wave_max(M);
+            if (COUNT) ic = wave_sum_i(ic);
+            if (SUM) {
+                // tile sum * 2^(fl(m*L) - M*L), exact reference difference in fp64
+                double t = 0.0;
+                if (sg[j].m > -INFINITY) {
+                    const float mL = sg[j].m * kLog2e;
+                    t = sg[j].s * exp_nonpos(((double)mL - (double)M * (double)kLog2e) * kLn2, tab);
                 }
+                const double S = wave_sum(t);
+                if (lane == j) Sl = S;
             }
-            __syncthreads();
+            if (lane == 0) {
+                rs.M[r] = M;
+                rs.g[r] = ARGMAX ? ic : 0;
+                rs.c[r] = COUNT ? ic : 0;
+            }
+        }
+        if (SUM) {
+            const double lS = log(Sl);  // one log for the whole batch
+            const int r = wave + kWaves * (k0 + lane);
+            if (lane < kBatch && r < nrows) rs.lnS[r] = lS;
         }
     }
-    for (int r = threadIdx.x; r < rows; r += kThreads) rs.lnS[r] = log(rs.S[r]);
     __syncthreads();
 }
 
 // ------------------------------------------------------ chain decision
-// Lane j < K of wave 0 evaluates the test of draft j; a ballot finds the
-// first rejection n (lane K never accepts, so n <= K).  Results go to LDS.
+// Per-draft inputs, held by lane j < K of wave 0.
+struct ChainVals {
+    int x;
+    bool bad;
+    float lx, dx, u;
+};
+
+// Draft token (and its uniform); issued before the row records are folded.
+template <int MODE>
+__device__ inline void chain_load_tokens(const Args& a, int b, ChainVals& cv) {
+    const int j = threadIdx.x;
+    cv.x = -1;
+    cv.bad = false;
+    cv.lx = cv.dx = -INFINITY;
+    cv.u = 0.f;
+    if (j < a.K) {
+        cv.x = a.tok[b * a.K + j];
+        if (MODE == kExact) cv.u = a.u[b * (a.K + 1) + j];
+    }
+}
+
+// Logits of the drafted token in target row j (and draft row j): depends on
+// the token load, so it runs as the fold's hook.
+template <typename T, int MODE>
+__device__ inline void chain_load_values(const Args& a, int b, ChainVals& cv) {
+    const int j = threadIdx.x;
+    if (j < a.K) {
+        cv.bad = (unsigned)cv.x >= (unsigned)a.V;
+        if (!cv.bad && MODE != kGreedy) {
+            cv.lx = Elem<T>::at(reinterpret_cast<const T*>(a.T), (size_t)(b * a.rows_t + j) * a.V + cv.x);
+            if (MODE == kExact)
+                cv.dx = Elem<T>::at(reinterpret_cast<const T*>(a.D), (size_t)(b * a.K + j) * a.V + cv.x);
+        }
+    }
+}
+
 struct ChainDecision {
     int n, bad_n;
     int x[64];
-    double lp[64], lq[64], lx[64], dx[64];
+    double lp[64], lq[64], r[64];
 };
 
-template <typename T, int MODE>
-__device__ void chain_decide(const Args& a, int b, const RowStats& rs, ChainDecision& cd) {
-    const int lane = threadIdx.x & 63;
-    if (threadIdx.x < 64) {
-        const int j = lane, K = a.K;
-        bool acc = false, bad = false;
-        int x = -1;
-        double lp = 0.0, lq = 0.0, lx = -INFINITY, dx = -INFINITY;
-        if (j < K) {
-            x = a.tok[b * K + j];
-            bad = (unsigned)x >= (unsigned)a.V;
-            if (!bad) {
-                if (MODE == kGreedy) {
-                    acc = (x == rs.g[j]);
-                    lp = -rs.lnS[j];  // the accepted token is the row max
-                } else {
-                    const T* Tp = reinterpret_cast<const T*>(a.T);
-                    lx = Elem<T>::at(Tp, (size_t)(b * a.rows_t + j) * a.V + x);
-                    lp = (lx - (double)rs.M[j]) - rs.lnS[j];
-                    if (MODE == kExact) {
-                        const T* Dp = reinterpret_cast<const T*>(a.D);
-                        dx = Elem<T>::at(Dp, (size_t)(b * K + j) * a.V + x);
-                        lq = (dx - (double)rs.M[a.rows_t + j]) - rs.lnS[a.rows_t + j];
-                        double r;
-                        if (lp == -INFINITY)
-                            r = 0.0;
-                        else if (lq == -INFINITY)
-                            r = INFINITY;
-                        else
-                            r = exp(lp - lq);
-                        acc = (double)a.u[b * (K + 1) + j] < r;
-                    } else {
-                        acc = (rs.c[j] < a.top_k) || (exp(lp) >= (double)a.tau);
-                    }
-                }
+// Wave 0: lane j < K evaluates the test of draft j in fp64; a ballot finds
+// the first rejection n (lane K never accepts, so n <= K).  Results go to LDS.
+template <int MODE>
+__device__ void chain_decide(const Args& a, const RowStats& rs, const ChainVals& cv, ChainDecision& cd) {
+    const int j = threadIdx.x, K = a.K;
+    bool acc = false;
+    double lp = 0.0, lq = 0.0, r = 0.0;  // a malformed token is rejected outright
+    if (j < K && !cv.bad) {
+        if (MODE == kGreedy) {
+            acc = (cv.x == rs.g[j]);
+            lp = -rs.lnS[j];  // the accepted token is the row max
+        } else {
+            lp = ((double)cv.lx - (double)rs.M[j]) - rs.lnS[j];
+            if (MODE == kExact) {
+                lq = ((double)cv.dx - (double)rs.M[a.rows_t + j]) - rs.lnS[a.rows_t + j];
+                if (lp == -INFINITY)
+                    r = 0.0;
+                else if (lq == -INFINITY)
+                    r = INFINITY;
+                else
+                    r = exp(lp - lq);
+                acc = (double)cv.u < r;
+            } else {
+                acc = (rs.c[j] < a.top_k) || (exp(lp) >= (double)a.tau);
             }
         }
-        const unsigned long long mask = __ballot(acc);
-        const int n = __builtin_ctzll(~mask);
-        cd.x[j] = x;
-        cd.lp[j] = lp;
-        cd.lq[j] = lq;
-        cd.lx[j] = lx;
-        cd.dx[j] = dx;
-        if (j == n) {
-            cd.n = n;
-            cd.bad_n = (n < K && bad) ? 1 : 0;
-        }
     }
-    __syncthreads();
+    const unsigned long long mask = __ballot(acc);
+    const int n = __builtin_ctzll(~mask);
+    cd.x[j] = cv.x;
+    cd.lp[j] = lp;
+    cd.lq[j] = lq;
+    cd.r[j] = r;
+    if (j == n) {
+        cd.n = n;
+        cd.bad_n = (n < K && cv.bad) ? 1 : 0;
+    }
 }
 
 // Writes positions j < n (accepted drafts) and n < j < L (padding) of the
@@ -911,12 +856,20 @@ __device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
 template <typename T, int MODE, bool SUM>
 __global__ __launch_bounds__(kThreads) void k_decide(const Args a) {
     const int b = blockIdx.x;
+    __shared__ double tab[64];
     __shared__ RowStats rs;
-    const int nb = (MODE == kTree && a.num_nodes) ? min(max(a.num_nodes[b], 1), a.rows_t) : a.rows_t;
-    gather_rows<SUM>(a, b, MODE == kTree ? nb : a.R, rs);
-    if (MODE == kGreedy) {
+    if (SUM) fill_exp_table(tab);
+    if constexpr (MODE == kGreedy) {
         __shared__ ChainDecision cd;
-        chain_decide<T, kGreedy>(a, b, rs, cd);
+        ChainVals cv;
+        if (threadIdx.x < 64) chain_load_tokens<kGreedy>(a, b, cv);
+        __syncthreads();
+        fold_rows<kGreedy, SUM>(a, b, a.R, rs, tab, NoHook());
+        if (threadIdx.x < 64) {
+            chain_load_values<T, kGreedy>(a, b, cv);
+            chain_decide<kGreedy>(a, rs, cv, cd);
+        }
+        __syncthreads();
         write_prefix<kGreedy>(a, b, cd);
         if (threadIdx.x == 0) {
             const int n = cd.n;
@@ -933,12 +886,18 @@ __global__ __launch_bounds__(kThreads) void k_decide(const Args a) {
     __shared__ int t_path[SPEC_MAX_NODES];
     __shared__ int t_d, t_e, t_bad;
     const int N = a.rows_t;
+    const int nb = a.num_nodes ? min(max(a.num_nodes[b], 1), N) : N;
+    int p = -1, t = -1;
+    if (threadIdx.x >= 1 && (int)threadIdx.x < nb) {  // issued before the fold
+        p = a.parents[b * N + threadIdx.x];
+        t = a.tok[b * N + threadIdx.x];
+    }
+    __syncthreads();
+    fold_rows<kTree, SUM>(a, b, nb, rs, tab, NoHook());
     if (threadIdx.x < 64) {
         const int i = threadIdx.x;
         bool bad = false;
         if (i >= 1 && i < nb) {
-            const int p = a.parents[b * N + i];
-            const int t = a.tok[b * N + i];
             bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.V);
             t_par[i] = bad ? -1 : p;
             t_match[i] = bad ? 0 : (t == rs.g[p]);
@@ -953,11 +912,11 @@ __global__ __launch_bounds__(kThreads) void k_decide(const Args a) {
         depth[0] = 0;
         int e = 0;
         for (int i = 1; i < nb; ++i) {
-            const int p = t_par[i];
+            const int pi = t_par[i];
             depth[i] = 0;
-            if (p >= 0 && t_match[i] && ((accm >> p) & 1ull)) {
+            if (pi >= 0 && t_match[i] && ((accm >> pi) & 1ull)) {
                 accm |= 1ull << i;
-                depth[i] = depth[p] + 1;
+                depth[i] = depth[pi] + 1;
                 if (depth[i] > depth[e]) e = i;
             }
         }
@@ -989,82 +948,35 @@ __global__ __launch_bounds__(kThreads) void k_decide(const Args a) {
 }
 
 // -------------------------------------------------------------------- pass 2
-// Block-wide sums and scans in a fixed order (deterministic).
-__device__ inline double block_sum(double v, double* scratch) {
-    v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double t = 0.0;
-    for (int w = 0; w < kWaves; ++w) t += scratch[w];
-    return t;
-}
-
-// Scan of v over threads in thread order.  Returns the inclusive prefix;
-// *excl receives the previous thread's inclusive prefix (0 for thread 0), so
-// the intervals [excl, incl) of consecutive threads tile [0, total) exactly.
-__device__ inline double block_scan(double v, double* scratch, double* all, double* excl) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_incl_scan(v);
-    __syncthreads();
-    if (lane == 63) scratch[wave] = v;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) v += scratch[w];
-    all[threadIdx.x] = v;
-    __syncthreads();
-    *excl = threadIdx.x ? all[threadIdx.x - 1] : 0.0;
-    return v;
-}
-
-// Block-wide int max / min (every thread gets the result).
-__device__ inline int block_max_i(int v, int* scratch) {
-    v = wave_max_i(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-    __syncthreads();
-    int r = scratch[0];
-    for (int w = 1; w < kWaves; ++w) r = max(r, scratch[w]);
-    return r;
-}
-
-__device__ inline int block_min_i(int v, int* scratch) {
-    v = wave_min_i(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-    __syncthreads();
-    int r = scratch[0];
-    for (int w = 1; w < kWaves; ++w) r = min(r, scratch[w]);
-    return r;
-}
-
 template <typename T, bool EXACT>
-__global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
+__global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_pass2(const Args a) {
+    constexpr int MODE = EXACT ? kExact : kRelaxed;
     constexpr int VEC = Elem<T>::kVec;
-    constexpr int PER = kP2Vecs * VEC;  // tokens per thread
-    constexpr int CH = kThreads * PER;
-    uint64_t* slots = reinterpret_cast<uint64_t*>(a.ws + make_layout(a.B, a.R, a.C2).p2);
+    constexpr int NV = kRun / VEC;  // 16-byte vectors per thread per chunk
 
     const int b = blockIdx.x / a.C2;
-    const int c = blockIdx.x % a.C2;
+    const int c = blockIdx.x - b * a.C2;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
     __shared__ double tab[64];
+    __shared__ RowStats rs;
+    __shared__ ChainDecision cd;
     __shared__ double red[kWaves][4];
-    __shared__ double scr[kWaves];
-    __shared__ double scan_all[kThreads];
-    __shared__ int iscr[kWaves];
     __shared__ int s_last;
     fill_exp_table(tab);
 
     // Every workgroup of the request derives the same decision from the
-    // streamed row statistics (deterministic), then works on the row(s) the
-    // terminal token is drawn from: target row n, and draft row n for a
-    // residual.
-    __shared__ RowStats rs;
-    __shared__ ChainDecision cd;
-    gather_rows<true>(a, b, a.R, rs);
-    chain_decide<T, EXACT ? kExact : kRelaxed>(a, b, rs, cd);
+    // tile records (deterministic), then works on the row(s) the terminal
+    // token is drawn from: target row n, and draft row n for a residual.
+    ChainVals cv;
+    if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
+    __syncthreads();
+    fold_rows<MODE, true>(a, b, a.R, rs, tab, [&]() {
+        if (threadIdx.x < 64) chain_load_values<T, MODE>(a, b, cv);
+    });
+    if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
+    __syncthreads();
     const int n = cd.n;
     const bool residual = EXACT && n < a.K;
     const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
@@ -1074,27 +986,27 @@ __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
     const double cls = residual ? rs.lnS[n] - rs.lnS[a.rows_t + n] : 0.0;
     const __amdgpu_buffer_rsrc_t rt = row_rsrc(trow, a.V);
     const __amdgpu_buffer_rsrc_t rd = row_rsrc(drow, a.V);
-    __syncthreads();
+    const bool vd = residual ? a.vec_d : a.vec_t;
 
     // ---- sweep: fp64 sums over this chunk (coalesced, interleaved layout)
     {
-        const int c0 = c * CH;
-        const int c1 = min(c0 + CH, a.V);
-        float vt[kP2Vecs][VEC], vd[kP2Vecs][VEC];
+        const int c0 = c * kChunk;
+        const int c1 = min(c0 + kChunk, a.V);
+        u32x4 qt[NV], qd[NV];
         // both rows are always loaded (rd aliases the target row when no
         // draft row is needed) so that all loads issue before any wait
-        load_chunk<T, kP2Vecs>(rt, c0, c1, a.vec_t, vt);
-        load_chunk<T, kP2Vecs>(rd, c0, c1, residual ? a.vec_d : a.vec_t, vd);
+        load_chunk<T, NV>(rt, c0, c1, a.vec_t, qt);
+        load_chunk<T, NV>(rd, c0, c1, vd, qd);
         double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0;
 #pragma unroll
-        for (int k = 0; k < kP2Vecs; ++k)
+        for (int k = 0; k < NV; ++k)
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
-                const double xa = (double)vt[k][i] - Mt;
+                const double xa = (double)Elem<T>::get(qt[k], i) - Mt;
                 const double ea = exp_nonpos(xa, tab);
                 sa += ea;
                 if (residual) {
-                    const double xb = (double)vd[k][i] - Md;
+                    const double xb = (double)Elem<T>::get(qd[k], i) - Md;
                     const double eb = exp_nonpos(xb, tab);
                     sb += eb;
                     if (xa - xb > cls) {
@@ -1120,134 +1032,202 @@ __global__ __launch_bounds__(kThreads) void k_pass2(const Args a) {
             double t[4] = {0.0, 0.0, 0.0, 0.0};
             for (int w = 0; w < kWaves; ++w)
                 for (int i = 0; i < 4; ++i) t[i] += red[w][i];
-            uint64_t* w = slots + ((size_t)b * a.C2 + c) * kP2Words;
+            uint64_t* w = a.p2 + ((size_t)b * a.C2 + c) * kP2Words;
             for (int i = 0; i < 4; ++i) put_double(w + 2 * i, t[i]);
-            s_last = (ticket_add(ticket2(a, b)) == a.C2 - 1);
+            // The arrival whose ticket is C2 - 1 (mod C2) is elected; it waits
+            // for any word not yet visible, so arrival order does not matter.
+            s_last = (ticket_add(a.tickets + (size_t)kCtrlStride * b) % (unsigned)a.C2 == (unsigned)a.C2 - 1);
         }
         __syncthreads();
         if (!s_last) return;
     }
 
-    // ---- terminal sample (last workgroup of the request)
-    // Chunk partials, one chunk per thread (a.C2 <= kThreads).
-    __shared__ int s_bad_ws;
-    __shared__ double s_base, s_Z;
-    __shared__ int s_y, s_ylast, s_yany;
-    if (threadIdx.x == 0) s_bad_ws = 0;
-    __syncthreads();
-    double csa = 0.0, csb = 0.0, cpa = 0.0, cpb = 0.0;
-    if ((int)threadIdx.x < a.C2) {
-        uint32_t w[kP2Words];
-        if (!take_words<kP2Words>(slots + ((size_t)b * a.C2 + threadIdx.x) * kP2Words, w)) s_bad_ws = 1;
-        csa = join_double(w[0], w[1]);
-        csb = join_double(w[2], w[3]);
-        cpa = join_double(w[4], w[5]);
-        cpb = join_double(w[6], w[7]);
+    // ---- terminal sample (elected workgroup of the request)
+    __shared__ int s_cstar, s_bad_ws, s_res;
+    __shared__ double s_base, s_target, s_iS, s_iSq, s_lnS, s_lnZ, s_l1r;
+    if (wave == 0) {
+        // lane l holds chunk l: sums, masses, scan and the chunk holding the
+        // target, all within the wave
+        double csa = 0.0, csb = 0.0, cpa = 0.0, cpb = 0.0;
+        bool ok = true;
+        if (lane < a.C2) {
+            uint32_t w[kP2Words];
+            ok = take_words<kP2Words>(a.p2 + ((size_t)b * a.C2 + lane) * kP2Words, w);
+            csa = join_double(w[0], w[1]);
+            csb = join_double(w[2], w[3]);
+            cpa = join_double(w[4], w[5]);
+            cpb = join_double(w[6], w[7]);
+        }
+        const bool bad = __ballot(!ok) != 0ull;
+        const double S = wave_sum(csa);
+        const double Sq = residual ? wave_sum(csb) : 1.0;
+        const double iS = 1.0 / S, iSq = 1.0 / Sq;
+        // residual mass of this chunk (clamped: tokens classified with the
+        // streamed normalizers can leave a rounding-size negative); fall back
+        // to p when relu(p - q) has no mass
+        double W = residual ? fmax(cpa * iS - cpb * iSq, 0.0) : csa;
+        const double Zr = residual ? wave_sum(W) : 0.0;
+        const bool res = residual && (Zr > 0.0);
+        if (residual && !res) W = csa;
+        const double Z = res ? Zr : S;
+        const double target = (double)a.u[b * (a.K + 1) + a.K] * Z;
+        const double incl = wave_incl_scan(W);
+        double excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = 0.0;  // [excl, incl) of consecutive chunks tile [0, Z)
+        const bool has = lane < a.C2 && W > 0.0;
+        const unsigned long long mine = __ballot(has && excl <= target && target < incl);
+        const unsigned long long hasm = __ballot(has);
+        // the unique chunk whose interval holds target; if rounding pushed
+        // target past the last boundary, the last chunk with mass
+        const int cstar = mine ? __builtin_ctzll(mine) : (hasm ? 63 - __builtin_clzll(hasm) : 0);
+        const double base = readlane_d(excl, cstar);
+        // logs in parallel lanes: lane 0 log S, lane 1 log Z
+        const double lg = log(lane == 0 ? S : Z);
+        const double l1r = res ? log1p(-cd.r[n]) : 0.0;
+        if (lane == 0) {
+            s_cstar = cstar;
+            s_base = base;
+            s_target = target;
+            s_iS = iS;
+            s_iSq = iSq;
+            s_res = res;
+            s_bad_ws = bad;
+            s_lnS = lg;
+            s_l1r = l1r;
+        }
+        if (lane == 1) s_lnZ = lg;
     }
-    const double S = block_sum(csa, scr);
-    const double Sq = residual ? block_sum(csb, scr) : 0.0;
-    const double iS = 1.0 / S, iSq = residual ? 1.0 / Sq : 0.0;
-    // residual mass of this chunk (clamped: tokens classified with the pass-1
-    // normalizers can leave a rounding-size negative); fall back to p when
-    // relu(p - q) has no mass
-    double W = residual ? fmax(cpa * iS - cpb * iSq, 0.0) : csa;
-    const double Zr = residual ? block_sum(W, scr) : 0.0;
-    const bool res = residual && (Zr > 0.0);
-    if (residual && !res) W = csa;
-    const double Z = res ? Zr : S;
-    const double target = (double)a.u[b * (a.K + 1) + a.K] * Z;
-    double excl;
-    const double incl = block_scan(W, scr, scan_all, &excl);
-    // the unique chunk whose interval [excl, incl) holds target; if rounding
-    // pushed target past the last boundary, the last chunk with mass
-    const bool mine = (int)threadIdx.x < a.C2 && W > 0.0 && excl <= target && target < incl;
-    int cstar = block_max_i(mine ? (int)threadIdx.x : -1, iscr);
-    if (cstar < 0) cstar = block_max_i(((int)threadIdx.x < a.C2 && W > 0.0) ? (int)threadIdx.x : -1, iscr);
-    cstar = max(cstar, 0);
-    if ((int)threadIdx.x == cstar) s_base = excl;
-    if (threadIdx.x == 0) s_Z = Z;
     __syncthreads();
 
-    // ---- rescan chunk cstar; thread t owns tokens [e0 + t*PER, +PER)
-    {
-        const int e0 = cstar * CH + (int)threadIdx.x * PER;
-        float lt_[PER], ld_[PER];
-        load_run<T, kP2Vecs>(rt, e0, a.V, a.vec_t, lt_);
-        load_run<T, kP2Vecs>(rd, e0, a.V, residual ? a.vec_d : a.vec_t, ld_);
-        double w[PER];
-        double tsum = 0.0;
-        int lastpos = -1, anypos = -1;
+    // ---- rescan chunk cstar; thread t owns tokens [e0 + t*kRun, +kRun)
+    const int cstar = s_cstar;
+    const bool res = s_res;
+    const double iS = s_iS, iSq = s_iSq, target = s_target;
+    const int e0 = cstar * kChunk + (int)threadIdx.x * kRun;
+    u32x4 qt[NV], qd[NV];
+    load_run<T, NV>(rt, e0, a.V, a.vec_t, qt);
+    load_run<T, NV>(rd, e0, a.V, vd, qd);
+    auto lt = [&](int i) { return Elem<T>::get(qt[i / VEC], i % VEC); };
+    auto ld = [&](int i) { return Elem<T>::get(qd[i / VEC], i % VEC); };
+    // residual term of a token with logits (l, d) (0 where p <= q)
+    auto term = [&](float l, float d, double& ea) -> double {
+        const double xa = (double)l - Mt;
+        ea = exp_nonpos(xa, tab);
+        if (!res) return ea;
+        const double xb = (double)d - Md;
+        const double eb = exp_nonpos(xb, tab);
+        return (xa - xb > cls) ? fmax(ea * iS - eb * iSq, 0.0) : 0.0;
+    };
+    double tsum = 0.0;
+    unsigned pos = 0u, fin = 0u;  // bit i: token i has mass / a finite logit
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = e0 + i;
-            const double xa = (double)lt_[i] - Mt;
-            const double ea = exp_nonpos(xa, tab);
-            double wi = ea;
-            if (res) {
-                const double xb = (double)ld_[i] - Md;
-                const double eb = exp_nonpos(xb, tab);
-                wi = (xa - xb > cls) ? fmax(ea * iS - eb * iSq, 0.0) : 0.0;
-            }
-            w[i] = wi;
-            tsum += wi;
-            if (wi > 0.0) lastpos = e;
-            if (ea > 0.0) anypos = e;
-        }
-        double texcl;
-        block_scan(tsum, scr, scan_all, &texcl);
-        double cum = s_base + texcl;
-        int cand = INT_MAX;
+    for (int i = 0; i < kRun; ++i) {
+        double ea;
+        const double wi = term(lt(i), ld(i), ea);
+        tsum += wi;
+        pos |= (wi > 0.0) ? (1u << i) : 0u;
+        fin |= (lt(i) > -INFINITY) ? (1u << i) : 0u;
+    }
+    const int firstpos = pos ? e0 + __builtin_ctz(pos) : INT_MAX;
+    const int lastpos = pos ? e0 + 31 - __builtin_clz(pos) : -1;
+    const int anypos = fin ? e0 + 31 - __builtin_clz(fin) : -1;
+    // block scan in thread order; the exclusive prefix of a thread is the
+    // previous thread's inclusive prefix, bit for bit
+    __shared__ double s_wtot[kWaves];
+    __shared__ int s_pick[kWaves][3];
+    const double wincl = wave_incl_scan(tsum);
+    if (lane == 63) s_wtot[wave] = wincl;
+    __syncthreads();
+    double off = 0.0;
+    for (int ww = 0; ww < wave; ++ww) off += s_wtot[ww];
+    const double tincl = wincl + off;
+    double texcl = __shfl_up(tincl, 1);
+    if (lane == 0) texcl = off;
+    // First crossing of the running sum past target.  A thread that starts
+    // past target crosses at its first token with mass; the others walk their
+    // tokens (terms recomputed, bit-identical).
+    double cum = s_base + texcl;
+    int cand = INT_MAX;
+    if (cum > target) {
+        cand = firstpos;
+    } else if (tsum > 0.0) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (w[i] > 0.0 && cand == INT_MAX) {
-                cum += w[i];
-                if (cum > target) cand = e0 + i;
+        for (int i = 0; i < kRun; ++i) {
+            if (cand == INT_MAX) {
+                // recomputed rather than kept from the first pass (the empty
+                // asm hides the equality, so the terms need no registers)
+                float l = lt(i), d = ld(i);
+                __asm__ volatile("" : "+v"(l), "+v"(d));
+                double ea;
+                const double wi = term(l, d, ea);
+                if (wi > 0.0) {
+                    cum += wi;
+                    if (cum > target) cand = e0 + i;
+                }
             }
         }
-        const int ycross = block_min_i(cand, iscr);
-        const int ylast = block_max_i(lastpos, iscr);
-        const int yany = block_max_i(anypos, iscr);
-        if (threadIdx.x == 0) {
-            s_y = ycross;
-            s_ylast = ylast;
-            s_yany = yany;
-        }
+    }
+    const int wc = wave_min_i(cand), wl = wave_max_i(lastpos), wa = wave_max_i(anypos);
+    if (lane == 0) {
+        s_pick[wave][0] = wc;
+        s_pick[wave][1] = wl;
+        s_pick[wave][2] = wa;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        // The crossing token; if rounding left none, the last token with mass
-        // in the chunk; if the chunk had none, its last finite token.  Always
-        // a valid index.
-        int y = (s_y != INT_MAX) ? s_y : (s_ylast >= 0 ? s_ylast : s_yany);
-        if (y < 0 || y >= a.V) y = 0;
+    int yc = INT_MAX, yl = -1, ya = -1;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+        yc = min(yc, s_pick[ww][0]);
+        yl = max(yl, s_pick[ww][1]);
+        ya = max(ya, s_pick[ww][2]);
+    }
+    // The crossing token; if rounding left none, the last token with mass in
+    // the chunk; if the chunk had none, its last finite token.  Always a valid
+    // index.
+    int y = (yc != INT_MAX) ? yc : (yl >= 0 ? yl : ya);
+    if (y < 0 || y >= a.V) y = 0;
+    const int rel = y - cstar * kChunk;
+    const int owner = (rel >= 0 && rel < kChunk) ? rel / kRun : 0;
+    if ((int)threadIdx.x == owner) {
+        float ly, dy;
+        if (rel >= 0 && rel < kChunk) {
+            ly = lt(0);
+            dy = ld(0);
+#pragma unroll
+            for (int i = 1; i < kRun; ++i)
+                if (e0 + i == y) {
+                    ly = lt(i);
+                    dy = ld(i);
+                }
+        } else {
+            ly = Elem<T>::at(trow, (size_t)y);
+            dy = Elem<T>::at(drow, (size_t)y);
+        }
+        // the emitted token's residual term, defined as in the scan
+        double wy = 0.0;
+        if (res) {
+            const double xa = (double)ly - Mt, xb = (double)dy - Md;
+            if (xa - xb > cls) wy = fmax(exp_nonpos(xa, tab) * iS - exp_nonpos(xb, tab) * iSq, 0.0);
+        }
         const int L = a.L;
         a.out_tok[(size_t)b * L + n] = y;
-        const double lnS = log(S);
-        const double ly = (double)Elem<T>::at(trow, (size_t)y);
-        const double tlp = (ly - Mt) - lnS;
-        double blp = tlp;
-        if (res) {
-            const double lnSq = log(Sq);
-            const double dy = (double)Elem<T>::at(drow, (size_t)y);
-            const double wy = exp_nonpos(ly - Mt, tab) * iS - exp_nonpos(dy - Md, tab) * iSq;
-            const double lp = (cd.lx[n] - Mt) - lnS, lq = (cd.dx[n] - Md) - lnSq;
-            const double rn = (lp == -INFINITY) ? 0.0 : exp(lp - lq);
-            blp = log1p(-rn) + log(wy) - log(s_Z);
-        }
+        const double tlp = ((double)ly - Mt) - s_lnS;
+        const double blp = res ? s_l1r + log(wy) - s_lnZ : tlp;
         if (a.out_tlp) a.out_tlp[(size_t)b * L + n] = (float)tlp;
         if (a.out_blp) a.out_blp[(size_t)b * L + n] = (float)blp;
-        ticket_reset(ticket2(a, b));
     }
-    write_prefix<EXACT ? kExact : kRelaxed>(a, b, cd);
-    if (threadIdx.x == 0 && s_bad_ws) a.out_status[b] = 2;
+    write_prefix<MODE>(a, b, cd);
+    if (threadIdx.x == 0) {
+        if (s_bad_ws) a.out_status[b] = 2;
+        ticket_sub(a.tickets + (size_t)kCtrlStride * b, a.C2);
+    }
 }
 
 // ------------------------------------------------------------------- host
-inline int vec_elems(spec_dtype dt) { return dt == SPEC_BF16 ? 8 : 4; }
 inline int esize(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
-inline int chunks(int V, int ch) { return (V + ch - 1) / ch; }
-inline int tpr_of(spec_dtype dt, int V) { return chunks(V, kThreads * kTileVecs * vec_elems(dt)); }
-inline int c2_of(spec_dtype dt, int V) { return chunks(V, kThreads * kP2Vecs * vec_elems(dt)); }
+inline int tile_elems(spec_dtype dt) { return kTileBytes / esize(dt); }
+inline int tpr_of(spec_dtype dt, int V) { return (V + tile_elems(dt) - 1) / tile_elems(dt); }
+inline int c2_of(spec_dtype, int V) { return (V + kChunk - 1) / kChunk; }
 
 inline bool vec_ok(const void* p, spec_dtype dt, int V) {
     return ((uintptr_t)p % 16 == 0) && (((size_t)V * esize(dt)) % 16 == 0);
@@ -1255,75 +1235,67 @@ inline bool vec_ok(const void* p, spec_dtype dt, int V) {
 
 spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt) {
     if (!ws || ((uintptr_t)ws % 256) != 0) return SPEC_EWORKSPACE;
-    const Layout L = make_layout(B, R, c2_of(dt, V));
+    const Layout L = make_layout(B, R, tpr_of(dt, V), c2_of(dt, V));
     return bytes >= L.total ? SPEC_OK : SPEC_EWORKSPACE;
 }
 
-// One-shot profiling hook: events to record around the streaming (pass-1)
-// kernel of the next call made from this thread.
-thread_local hipEvent_t g_prof_before = nullptr;
-thread_local hipEvent_t g_prof_after = nullptr;
-
-// Streaming grid: kWgPerCu workgroups per compute unit of the current
-// device, never more workgroups than tiles.
-int stream_grid(long long tiles) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        cus = 256;
-    long long g = (long long)cus * kWgPerCu;
-    if (g > kMaxGrid) g = kMaxGrid;
-    if (g > tiles) g = tiles;
-    return (int)g;
-}
+// One-shot profiling hook: events to record around the kernels of the next
+// call made from this thread.
+thread_local hipEvent_t g_prof[3] = {nullptr, nullptr, nullptr};
 
 // Streaming kernel, then the per-request kernel (decision, or decision and
 // terminal sample).
 template <int MODE, bool SUM>
 spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
     a.tpr = tpr_of(dt, a.V);
-    a.G = stream_grid((long long)a.B * a.R * a.tpr);
-    hipEvent_t before = g_prof_before, after = g_prof_after;
-    g_prof_before = g_prof_after = nullptr;
-    if (before && hipEventRecord(before, st) != hipSuccess) return SPEC_EHIP;
+    const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
+    a.tickets = reinterpret_cast<int*>(a.ws);
+    a.segs = reinterpret_cast<Seg*>(a.ws + lay.seg);
+    a.p2 = reinterpret_cast<uint64_t*>(a.ws + lay.p2);
+    hipEvent_t ev[3] = {g_prof[0], g_prof[1], g_prof[2]};
+    g_prof[0] = g_prof[1] = g_prof[2] = nullptr;
+    const unsigned grid = (unsigned)a.B * (unsigned)a.R * (unsigned)a.tpr;
+    if (ev[0] && hipEventRecord(ev[0], st) != hipSuccess) return SPEC_EHIP;
     const bool vecp = a.vec_t && (MODE != kExact || a.vec_d);
     if (dt == SPEC_BF16) {
         if (vecp)
-            hipLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true>), dim3(a.G), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true>), dim3(grid), dim3(kThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false>), dim3(a.G), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false>), dim3(grid), dim3(kThreads), 0, st, a);
     } else {
         if (vecp)
-            hipLaunchKernelGGL((k_stream<float, MODE, SUM, true>), dim3(a.G), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_stream<float, MODE, SUM, true>), dim3(grid), dim3(kThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((k_stream<float, MODE, SUM, false>), dim3(a.G), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_stream<float, MODE, SUM, false>), dim3(grid), dim3(kThreads), 0, st, a);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    if (after && hipEventRecord(after, st) != hipSuccess) return SPEC_EHIP;
-    if (MODE == kGreedy || MODE == kTree) {
+    if (ev[1] && hipEventRecord(ev[1], st) != hipSuccess) return SPEC_EHIP;
+    if constexpr (MODE == kGreedy || MODE == kTree) {
         if (dt == SPEC_BF16)
             hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM>), dim3(a.B), dim3(kThreads), 0, st, a);
         else
             hipLaunchKernelGGL((k_decide<float, MODE, SUM>), dim3(a.B), dim3(kThreads), 0, st, a);
     } else {
         constexpr bool EXACT = (MODE == kExact);
-        const int grid = a.B * a.C2;
+        const unsigned grid2 = (unsigned)a.B * (unsigned)a.C2;
         if (dt == SPEC_BF16)
-            hipLaunchKernelGGL((k_pass2<uint16_t, EXACT>), dim3(grid), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_pass2<uint16_t, EXACT>), dim3(grid2), dim3(kThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((k_pass2<float, EXACT>), dim3(grid), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_pass2<float, EXACT>), dim3(grid2), dim3(kThreads), 0, st, a);
     }
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
 }
 
 bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
 
 bool sizes_ok(int B, int K, int V, long rows_per_req) {
     if (B < 1 || B > kMaxB || K < 1 || V < 1 || V > SPEC_MAX_V) return false;
-    // every element offset of one tensor must fit comfortably in 64 bits and
-    // block counts in 31 bits
-    const long long grid = (long long)B * rows_per_req * ((V + 1023) / 1024);
-    return grid < (1ll << 31) && (long long)B * rows_per_req * V < (1ll << 40);
+    if (rows_per_req < 1 || rows_per_req > kMaxRows) return false;
+    // streaming grid (fp32 has the most tiles) and element offsets
+    const long long tiles = (V + 4095) / 4096;
+    return (long long)B * rows_per_req * tiles < (1ll << 31) && (long long)B * rows_per_req * V < (1ll << 40);
 }
 
 }  // namespace
@@ -1335,14 +1307,15 @@ size_t spec_verify_workspace_bytes(int B, int rows_per_request, int V) {
     if (B < 1 || B > kMaxB || rows_per_request < 1 || rows_per_request > kMaxRows || V < 1 ||
         V > SPEC_MAX_V)
         return 0;
-    // fp32 uses the smaller chunks, so its layout bounds both dtypes
-    const Layout L = make_layout(B, rows_per_request, c2_of(SPEC_F32, V));
+    // fp32 has the most tiles per row, so its layout bounds both dtypes
+    const Layout L = make_layout(B, rows_per_request, tpr_of(SPEC_F32, V), c2_of(SPEC_F32, V));
     return L.total;
 }
 
-void spec_verify_profile_next_call(void* before_event, void* after_event) {
-    g_prof_before = static_cast<hipEvent_t>(before_event);
-    g_prof_after = static_cast<hipEvent_t>(after_event);
+void spec_verify_profile_next_call(void* before_stream, void* after_stream, void* after_call) {
+    g_prof[0] = static_cast<hipEvent_t>(before_stream);
+    g_prof[1] = static_cast<hipEvent_t>(after_stream);
+    g_prof[2] = static_cast<hipEvent_t>(after_call);
 }
 
 const char* spec_status_string(int s) {

@@ -51,9 +51,12 @@
  * Workspace
  *   Each call needs a device workspace of at least
  *   spec_verify_workspace_bytes(B, rows_per_request, V) bytes, 256-byte
- *   aligned, ZERO-FILLED BEFORE ITS FIRST USE.  Every completed call leaves
- *   it zero-filled again, so it can be reused by later calls of any shape
- *   on the same stream.  Calls that run concurrently (different streams) need different
+ *   aligned, ZERO-FILLED BEFORE ITS FIRST USE.  A call uses part of it for
+ *   per-tile statistics (left behind as scratch) and part for counters and
+ *   hand-off words between workgroups, which every completed call returns to
+ *   zero; the scratch can never be mistaken for hand-off data, so the
+ *   workspace can be reused by later calls of any shape on the same stream
+ *   without clearing it again.  Calls that run concurrently (different streams) need different
  *   workspaces.  The library allocates nothing and keeps no state besides the
  *   one-shot, per-thread profiling hook (spec_verify_profile_next_call).
  *
@@ -101,15 +104,16 @@ size_t spec_verify_workspace_bytes(int B, int rows_per_request, int V);
 const char *spec_status_string(int status);
 
 /*
- * Host-only profiling hook (for benchmarks).  before_event and after_event are
- * hipEvent_t handles created by the caller.  The next spec_verify_* call made
- * from the calling thread records before_event on its stream immediately
- * before its streaming kernel (the one that reads every logit once) and
- * after_event immediately after it, so that hipEventElapsedTime gives that
- * kernel's duration.  The hook applies to one call and is then cleared;
- * passing NULLs clears it.
+ * Host-only profiling hook (for benchmarks).  The arguments are hipEvent_t
+ * handles created by the caller, or NULL.  The next spec_verify_* call made
+ * from the calling thread records before_stream on its stream immediately
+ * before its streaming kernel (the one that reads every logit once),
+ * after_stream immediately after that kernel, and after_call after the
+ * call's last kernel, so that hipEventElapsedTime gives the streaming
+ * kernel's duration and the rest of the call's.  The hook applies to one call
+ * and is then cleared; passing NULLs clears it.
  */
-void spec_verify_profile_next_call(void *before_event, void *after_event);
+void spec_verify_profile_next_call(void *before_stream, void *after_stream, void *after_call);
 
 /*
  * Greedy chain verification (mini-sglang PR #134, "Modifications",
