@@ -12,10 +12,10 @@ logits are streamed from HBM, not from that cache.  The K timed calls are
 captured into one HIP graph and replayed once between two events (launches
 then cost no host time); the same loop run eagerly is reported alongside.
 
-The streaming kernel's duration is measured with HIP events that the library
-records around it (spec_verify_profile_next_call) over K further calls; its
-algorithmic bytes (every logit once, plus tokens, uniforms and outputs)
-divided by that duration give the roofline figure.  The fp64 CPU oracle is
+The streaming kernel's duration is measured with HIP start/stop events that
+its dispatch timestamps itself (spec_verify_profile_next_call) over K further
+calls; its algorithmic bytes (every logit read once) divided by that duration
+give the roofline figure.  The fp64 CPU oracle is
 timed on a bounded sample of the same workload on the host's cores.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -210,7 +210,7 @@ def time_case(case, steps, warmup, hip, use_graph):
                     raise RuntimeError(f"graph replay output {k} differs from the eager call")
         del g
     # per-kernel durations through the library's event hook: the streaming
-    # kernel, and the rest of the call
+    # kernel's own start/stop timestamps, and the rest of the call
     evs = [(hip.event(), hip.event(), hip.event()) for _ in range(steps)]
     f = case.fn()
     argv = [case.args(s, stream) for s in range(case.sets)]

@@ -14,8 +14,8 @@
 //   * greedy tree verification of an EAGLE-style draft tree (nanospec
 //     README, intro and benchmark section).
 //
-// How it is computed here (no kernel design comes from the pages): two
-// kernels per call on the caller's stream.
+// How it is computed here (no kernel design comes from the pages): two or
+// three kernels per call on the caller's stream.
 //
 //   k_stream  one workgroup per (logit row, 16 KB tile).  Each thread issues
 //             its four 16-byte loads at once; the workgroup reduces the tile
@@ -33,33 +33,27 @@
 //             fp64.  Wave 0 then runs the acceptance tests (one lane per
 //             draft or tree node) and writes the outputs.
 //
-//   k_pass2   (exact, relaxed) one workgroup per (request, 4096-token
+//   k_sweep   (exact, relaxed) one workgroup per (request, 4096-token
 //             chunk).  Every workgroup of a request folds the records and
-//             takes the decision itself (same data, same order, same result),
-//             then sweeps its chunk of the row(s) the terminal token is drawn
-//             from, in fp64 with an explicit Cody-Waite exp: sums of
-//             exp(l - Mt) and exp(d - Md) over the chunk and over its tokens
-//             with p > q.  One workgroup per request, elected by an atomic
-//             ticket, turns the chunk sums into chunk masses of relu(p - q)
-//             (or of p), finds the chunk holding u_K * Z with a one-wave scan,
-//             rescans that chunk with a block scan and writes the terminal
-//             token, the log-probs and the accepted prefix.
+//             takes the decision itself (same data, same order, same result);
+//             chunk 0 writes the accepted prefix.  Each workgroup then sums its
+//             chunk of the row(s) the terminal token is drawn from, in fp64
+//             with an explicit Cody-Waite exp: exp(l - Mt) and exp(d - Md),
+//             over the chunk and over its tokens with p > q.
+//
+//   k_sample  (exact, relaxed) one workgroup per request.  Wave 0 turns the
+//             chunk sums into chunk masses of relu(p - q) (or of p), scans
+//             them and finds the chunk holding u_K * Z; the workgroup rescans
+//             that chunk with a block scan and writes the terminal token and
+//             its log-probs.
 //
 // Every reduction runs in a fixed order, so results are bitwise
-// reproducible.  No float atomics are used.
-//
-// Cross-workgroup hand-off inside k_pass2.  The workgroups of one request run
-// on all eight XCDs, whose L2 caches are not coherent with each other.  A
-// release/acquire fence at device scope would make every workgroup write back
-// and invalidate its whole L2.  Instead each chunk sum is published as 64-bit
-// words that carry a tag in their upper half (payload | kTag << 32), written
-// and read with relaxed device-scope atomics, which the hardware keeps
-// coherent across XCDs without cache maintenance.  Each word validates
-// itself, so no ordering between words is needed: the elected workgroup reads
-// every word, re-reads (with a bounded wait) any whose tag has not arrived
-// yet, and writes zeros back, so those words are zero between calls.  The
-// tile records of k_stream need no such care: the kernel boundary makes them
-// visible to the next kernel.
+// reproducible.  No atomics are used: data passes between workgroups only
+// across kernel boundaries, which make the previous kernel's writes visible
+// to the next one on every XCD (their L2 caches are not coherent with each
+// other, and a fence inside a kernel would write back and invalidate a whole
+// L2).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <limits.h>
@@ -79,29 +73,25 @@ constexpr int kStreamWavesPerSimd = 8;                   // k_stream occupancy t
 constexpr int kChunk = 4096;                             // pass-2 tokens per workgroup
 constexpr int kPass2WavesPerSimd = 4;                    // k_pass2 occupancy target
 constexpr int kRun = kChunk / kThreads;                  // pass-2 tokens per thread
+constexpr int kSampleThreads = 1024;                     // k_sample workgroup
+constexpr int kDecideThreads = 1024;                     // k_decide workgroup
+constexpr int kSampleRun = kChunk / kSampleThreads;      // k_sample tokens per thread
+constexpr int kSampleWaves = kSampleThreads / 64;
+static_assert(kSampleRun == 4, "k_sample loads four tokens per thread");
 constexpr int kMaxRows = 2 * SPEC_MAX_K + 1;
 constexpr int kMaxB = SPEC_MAX_B;
-// Per-request tickets of pass 2, one 128-byte line each: atomics on a line
-// shared by several requests serialize behind each other.  The region has a
-// fixed size, so no other data of any call shape ever lands on a ticket.
-constexpr int kCtrlStride = 32;  // int32 per request
-constexpr size_t kCtrlBytes = (size_t)kMaxB * kCtrlStride * 4;
 // Tiles per row at SPEC_MAX_V (fp32 has the most): one record per lane.
 constexpr int kMaxTiles = (SPEC_MAX_V * 4 + kTileBytes - 1) / kTileBytes;
 static_assert(kMaxTiles <= 64, "a row's tile records must fit one wave");
 constexpr int kMaxC2 = (SPEC_MAX_V + kChunk - 1) / kChunk;
 static_assert(kMaxC2 <= 64, "a row's pass-2 chunks must fit one wave");
-constexpr uint32_t kTag = 0x5ec0fa11u;
-constexpr int kMaxSpins = 1 << 20;  // bounded wait for a published word (~60 ms)
 
 enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3 };
 
 // Statistics of one tile: max m, then the lowest index of the max (greedy,
 // tree) or the rank count (relaxed), and s = sum over the tile of
 // 2^(l*log2e - fl(m*log2e)), i.e. sum exp(l - m) up to the rounding of the
-// reference.  Neither 64-bit half of a record can equal a tagged word (the
-// int is below 2^18 or INT_MAX; s is at most 8192), so records left in the
-// workspace never pass for published pass-2 words.
+// reference.
 struct alignas(16) Seg {
     float m;
     int ic;
@@ -109,23 +99,38 @@ struct alignas(16) Seg {
 };
 static_assert(sizeof(Seg) == 16, "one 16-byte load per record");
 
-// Chunk partial of pass 2 (eight tagged words = four fp64 sums): sum of
-// a = exp(l - Mt) and b = exp(d - Md) over the chunk, and over its tokens
-// with p > q.
-constexpr int kP2Words = 8;
+// What the decide kernel hands to the sweep and sampling kernels for one
+// request: the decision and the reference maxima of the terminal row(s).
+struct alignas(16) Decision {
+    int n;         // first rejection (K: all accepted)
+    int residual;  // exact rule and n < K: sample relu(p_n - q_n)
+    int pad0, pad1;
+    double Mt, Md;  // maxima of target row n and draft row n
+    double cls;     // p > q  <=>  (l - Mt) - (d - Md) > cls
+    double rn;      // p_n(x_n) / q_n(x_n) of the rejected draft
+};
+
+// Fp64 sums of one pass-2 chunk: exp(l - Mt) and exp(d - Md) over the chunk,
+// and over its tokens with p > q.
+struct alignas(16) ChunkSums {
+    double sa, sb, pa, pb;
+};
 
 struct Layout {
-    size_t seg, p2, total;
+    size_t seg, dec, sums, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// [tickets: fixed kCtrlBytes][tile records B*R*tpr][pass-2 words B*C2*8]
+// [tile records B*R*tpr][decisions B][chunk sums B*C2]; every region is
+// written before it is read within a call, so the workspace needs no
+// initialization and keeps nothing between calls.
 inline Layout make_layout(int B, int R, int tpr, int C2) {
     Layout L;
-    L.seg = kCtrlBytes;
-    L.p2 = align_up(L.seg + (size_t)B * R * tpr * sizeof(Seg), 256);
-    L.total = align_up(L.p2 + (size_t)B * C2 * kP2Words * 8, 256);
+    L.seg = 0;
+    L.dec = align_up(L.seg + (size_t)B * R * tpr * 16, 256);
+    L.sums = align_up(L.dec + (size_t)B * 64, 256);
+    L.total = align_up(L.sums + (size_t)B * C2 * 32, 256);
     return L;
 }
 
@@ -171,6 +176,27 @@ struct Elem<uint16_t> {  // bf16 bit patterns
     __device__ static inline float get(const u32x4& q, int j) {
         return __uint_as_float((j & 1) ? (q[j >> 1] & 0xffff0000u) : (q[j >> 1] << 16));
     }
+    // tokens e .. e+3 (e a multiple of 4), -inf at or past V
+    __device__ static inline void load4(__amdgpu_buffer_rsrc_t r, int e, int V, bool vec, float (&v)[4]) {
+        uint32_t w0, w1;
+        if (vec) {
+            const auto q = __builtin_amdgcn_raw_buffer_load_b64(r, e * 2, 0, 0);
+            w0 = q[0];
+            w1 = q[1];
+        } else {
+            w0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, e * 2, 0, 0) |
+                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, e * 2 + 2, 0, 0) << 16);
+            w1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, e * 2 + 4, 0, 0) |
+                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, e * 2 + 6, 0, 0) << 16);
+        }
+        v[0] = __uint_as_float(w0 << 16);
+        v[1] = __uint_as_float(w0 & 0xffff0000u);
+        v[2] = __uint_as_float(w1 << 16);
+        v[3] = __uint_as_float(w1 & 0xffff0000u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e + j >= V) v[j] = -INFINITY;
+    }
     // VEC elements from e on (indices clamped to V-1), one load each, packed
     // like a 16-byte vector load
     __device__ static inline u32x4 gather_clamped(const uint16_t* pp, int e, int V) {
@@ -214,6 +240,19 @@ struct Elem<float> {
         return q;
     }
     __device__ static inline float get(const u32x4& q, int j) { return __uint_as_float(q[j]); }
+    __device__ static inline void load4(__amdgpu_buffer_rsrc_t r, int e, int V, bool vec, float (&v)[4]) {
+        if (vec) {
+            const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(q[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (e + j) * 4, 0, 0));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e + j >= V) v[j] = -INFINITY;
+    }
     __device__ static inline u32x4 gather_clamped(const float* pp, int e, int V) {
         const __attribute__((address_space(1))) float* p = (const __attribute__((address_space(1))) float*)pp;
         u32x4 q;
@@ -262,36 +301,31 @@ __device__ inline void load_run(__amdgpu_buffer_rsrc_t r, int e0, int V, bool ve
 }
 
 // ------------------------------------------------------------ fp64 exp(x<=0)
-// Cody-Waite reduction x = k ln2/64 + r, |r| <= ln2/128, then a degree-4
-// Taylor polynomial (truncation error r^5/120 < 4e-14 relative) and
-// 2^(k/64) = 2^(k>>6) * tab[k & 63].  Branch-free and built from full-rate
-// fp64 fma/add/mul and integer ops only: adding 1.5*2^52 leaves round(y) in
-// the low word of the double, and 2^(k>>6) is applied by adding (k>>6) to the
-// exponent field of tab[k & 63] (results stay normal for x > -700).  x <= -700
-// (and -inf) gives exactly 0.
-constexpr double kInvLn2x64 = 92.332482616893656877;   // 64 / ln 2
-constexpr double kLn2o64Hi = 0.010830424726009368896;  // ln2/64 rounded to 24 bits
-constexpr double kLn2o64Lo = -2.9760223436840126e-11;  // ln2/64 - hi
-constexpr double kRoundMagic = 6755399441055744.0;     // 1.5 * 2^52
+// Reduction x = k ln2/256 + r with k = rint(x * 256/ln2) and |r| <= ln2/512,
+// a degree-3 Taylor polynomial (truncation error r^4/24 < 1.5e-13 relative)
+// and 2^(k/256) = 2^(k>>8) * tab[k & 255], the power of two applied by
+// v_ldexp.  r uses the double nearest ln2/256 in one fma: its error,
+// |k| * 2^-61, stays below 3e-15 relative for x >= -30 and below 2e-13 at the
+// clamp.  x is first clamped to -1000 (which also maps -inf to -1000), where
+// v_ldexp underflows to exactly 0.  Branch-free; every op is full rate.
+constexpr int kExpTab = 256;
+constexpr double kInvLn2x256 = 369.3299304675746;       // 256 / ln 2
+constexpr double kLn2o256 = 0.0027076061740622863;      // ln 2 / 256
 
 __device__ inline double exp_nonpos(double x, const double* tab) {
-    const double xc = fmax(x, -700.0);
-    const double t = fma(xc, kInvLn2x64, kRoundMagic);
-    const int k = (int)(uint32_t)__double_as_longlong(t);  // round(xc * 64/ln2)
-    const double kd = t - kRoundMagic;
-    double r = fma(-kd, kLn2o64Hi, xc);
-    r = fma(-kd, kLn2o64Lo, r);
-    double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
-    p = fma(p, r, 0.5);
+    const double xc = fmax(x, -1000.0);
+    const double kd = __builtin_rint(xc * kInvLn2x256);
+    const int k = (int)kd;
+    const double r = fma(-kd, kLn2o256, xc);
+    double p = fma(r, 1.0 / 6.0, 0.5);
     p = fma(p, r, 1.0);
     p = fma(p, r, 1.0);
-    const long long tb = __double_as_longlong(tab[k & 63]) + ((long long)(k >> 6) << 52);
-    const double e = __longlong_as_double(tb) * p;
-    return (x > -700.0) ? e : 0.0;
+    return ldexp(tab[k & (kExpTab - 1)] * p, k >> 8);
 }
 
+// tab[j] = 2^(j/256); needs kExpTab threads
 __device__ inline void fill_exp_table(double* tab) {
-    if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+    if (threadIdx.x < kExpTab) tab[threadIdx.x] = exp2((double)threadIdx.x / kExpTab);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -430,55 +464,6 @@ __device__ inline int wave_max_i(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// ------------------------------------------------- tagged-word hand-off
-__device__ inline void put_word(uint64_t* p, uint32_t v) {
-    __hip_atomic_store(p, ((uint64_t)kTag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline void put_double(uint64_t* p, double v) {
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    put_word(p, (uint32_t)u);
-    put_word(p + 1, (uint32_t)(u >> 32));
-}
-
-// Reads n tagged words into out[], waiting (bounded) for any not yet
-// published, then returns them to zero.  Returns false on timeout.
-template <int N>
-__device__ inline bool take_words(uint64_t* p, uint32_t* out) {
-    uint64_t w[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) w[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        int spins = 0;
-        while ((uint32_t)(w[i] >> 32) != kTag) {
-            if (++spins > kMaxSpins) {
-                ok = false;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-            w[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        out[i] = (uint32_t)w[i];
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) __hip_atomic_store(p + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return ok;
-}
-
-__device__ inline double join_double(uint32_t lo, uint32_t hi) {
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-__device__ inline unsigned ticket_add(int* t) {
-    return (unsigned)__hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline void ticket_sub(int* t, int v) {
-    __hip_atomic_fetch_add(t, -v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ------------------------------------------------------------------- args
 struct Args {
     const void* T;
@@ -504,8 +489,8 @@ struct Args {
     int L;  // output row length: K+1, or N for a tree
     unsigned char* ws;
     Seg* segs;        // [B][R][tpr]
-    uint64_t* p2;     // [B][C2][kP2Words]
-    int* tickets;     // [B][kCtrlStride]
+    Decision* dec;    // [B]
+    ChunkSums* sums;  // [B][C2]
 };
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -679,23 +664,23 @@ struct NoHook {
     __device__ void operator()() const {}
 };
 
-// Folds the tile records of rows [0, nrows) of request b.  Wave w takes rows
-// w, w + 4, ... in batches of four, one tile record per lane; every batch's
+// Folds the tile records of rows [0, nrows) of request b.  Wave w of NW takes
+// rows w, w + NW, ... in batches of four, one tile record per lane; every batch's
 // loads are issued before any is used, and `hook` runs once after the first
 // batch is issued (the caller's dependent loads overlap the fold).  The
 // table of exp_nonpos must be ready.  Ends with a barrier.
-template <int MODE, bool SUM, typename Hook>
+template <int MODE, bool SUM, int NW, typename Hook>
 __device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const double* tab, Hook hook) {
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
     constexpr int kBatch = 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     bool hooked = false;
-    for (int k0 = 0; k0 == 0 || wave + kWaves * k0 < nrows; k0 += kBatch) {
+    for (int k0 = 0; k0 == 0 || wave + NW * k0 < nrows; k0 += kBatch) {
         Seg sg[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int r = wave + kWaves * (k0 + j);
+            const int r = wave + NW * (k0 + j);
             if (r < nrows && lane < a.tpr) {
                 sg[j] = a.segs[((size_t)b * a.R + r) * a.tpr + lane];
             } else {
@@ -711,7 +696,7 @@ __device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const d
         double Sl = 1.0;  // lane j: normalizer of batch row j
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int r = wave + kWaves * (k0 + j);
+            const int r = wave + NW * (k0 + j);
             if (r >= nrows) break;
             float M = sg[j].m;
             int ic = sg[j].ic;
@@ -738,7 +723,7 @@ __device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const d
         }
         if (SUM) {
             const double lS = log(Sl);  // one log for the whole batch
-            const int r = wave + kWaves * (k0 + lane);
+            const int r = wave + NW * (k0 + lane);
             if (lane < kBatch && r < nrows) rs.lnS[r] = lS;
         }
     }
@@ -835,7 +820,7 @@ __device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
     int32_t* otok = a.out_tok + (size_t)b * L;
     float* otlp = a.out_tlp ? a.out_tlp + (size_t)b * L : nullptr;
     float* oblp = a.out_blp ? a.out_blp + (size_t)b * L : nullptr;
-    for (int j = threadIdx.x; j < L; j += kThreads) {
+    for (int j = threadIdx.x; j < L; j += blockDim.x) {
         if (j < n) {
             otok[j] = cd.x[j];
             if (otlp) otlp[j] = (float)cd.lp[j];
@@ -852,25 +837,27 @@ __device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
     }
 }
 
-// -------------------------------------------------- greedy and tree: decide
+// -------------------------------------------------------------- decide
+// Greedy and tree: one workgroup (kDecideThreads) per request folds the tile
+// records (one row per wave), takes the decision and writes the outputs.
 template <typename T, int MODE, bool SUM>
-__global__ __launch_bounds__(kThreads) void k_decide(const Args a) {
+__global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
+    constexpr int NW = kDecideThreads / 64;
     const int b = blockIdx.x;
-    __shared__ double tab[64];
+    __shared__ double tab[kExpTab];
     __shared__ RowStats rs;
     if (SUM) fill_exp_table(tab);
     if constexpr (MODE == kGreedy) {
         __shared__ ChainDecision cd;
         ChainVals cv;
-        if (threadIdx.x < 64) chain_load_tokens<kGreedy>(a, b, cv);
+        if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
         __syncthreads();
-        fold_rows<kGreedy, SUM>(a, b, a.R, rs, tab, NoHook());
-        if (threadIdx.x < 64) {
-            chain_load_values<T, kGreedy>(a, b, cv);
-            chain_decide<kGreedy>(a, rs, cv, cd);
-        }
+        fold_rows<MODE, SUM, NW>(a, b, a.R, rs, tab, [&]() {
+            if (threadIdx.x < 64) chain_load_values<T, MODE>(a, b, cv);
+        });
+        if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
         __syncthreads();
-        write_prefix<kGreedy>(a, b, cd);
+        write_prefix<MODE>(a, b, cd);
         if (threadIdx.x == 0) {
             const int n = cd.n;
             a.out_tok[(size_t)b * a.L + n] = rs.g[n];
@@ -878,78 +865,85 @@ __global__ __launch_bounds__(kThreads) void k_decide(const Args a) {
             if (a.out_blp) a.out_blp[(size_t)b * a.L + n] = 0.f;
         }
         return;
-    }
-    // tree: a node is accepted iff its token is its parent's argmax and its
-    // parent is accepted; parents precede children
-    __shared__ int t_par[SPEC_MAX_NODES];
-    __shared__ int t_match[SPEC_MAX_NODES];
-    __shared__ int t_path[SPEC_MAX_NODES];
-    __shared__ int t_d, t_e, t_bad;
-    const int N = a.rows_t;
-    const int nb = a.num_nodes ? min(max(a.num_nodes[b], 1), N) : N;
-    int p = -1, t = -1;
-    if (threadIdx.x >= 1 && (int)threadIdx.x < nb) {  // issued before the fold
-        p = a.parents[b * N + threadIdx.x];
-        t = a.tok[b * N + threadIdx.x];
-    }
-    __syncthreads();
-    fold_rows<kTree, SUM>(a, b, nb, rs, tab, NoHook());
-    if (threadIdx.x < 64) {
-        const int i = threadIdx.x;
-        bool bad = false;
-        if (i >= 1 && i < nb) {
-            bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.V);
-            t_par[i] = bad ? -1 : p;
-            t_match[i] = bad ? 0 : (t == rs.g[p]);
+    } else {
+        // tree: a node is accepted iff its token is its parent's argmax and
+        // its parent is accepted; parents precede children
+        __shared__ int t_par[SPEC_MAX_NODES];
+        __shared__ int t_match[SPEC_MAX_NODES];
+        __shared__ int t_path[SPEC_MAX_NODES];
+        __shared__ int t_d, t_e, t_bad;
+        const int N = a.rows_t;
+        const int nb = a.num_nodes ? min(max(a.num_nodes[b], 1), N) : N;
+        int p = -1, t = -1;
+        if (threadIdx.x >= 1 && (int)threadIdx.x < nb) {  // issued before the fold
+            p = a.parents[b * N + threadIdx.x];
+            t = a.tok[b * N + threadIdx.x];
         }
-        const unsigned long long bm = __ballot(bad);
-        if (i == 0) t_bad = bm != 0ull;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long accm = 1ull;  // bit i: node i accepted
-        int depth[SPEC_MAX_NODES];
-        depth[0] = 0;
-        int e = 0;
-        for (int i = 1; i < nb; ++i) {
-            const int pi = t_par[i];
-            depth[i] = 0;
-            if (pi >= 0 && t_match[i] && ((accm >> pi) & 1ull)) {
-                accm |= 1ull << i;
-                depth[i] = depth[pi] + 1;
-                if (depth[i] > depth[e]) e = i;
+        __syncthreads();
+        fold_rows<kTree, SUM, NW>(a, b, nb, rs, tab, NoHook());
+        if (threadIdx.x < 64) {
+            const int i = threadIdx.x;
+            bool bad = false;
+            if (i >= 1 && i < nb) {
+                bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.V);
+                t_par[i] = bad ? -1 : p;
+                t_match[i] = bad ? 0 : (t == rs.g[p]);
             }
+            const unsigned long long bm = __ballot(bad);
+            if (i == 0) t_bad = bm != 0ull;
         }
-        const int d = depth[e];
-        for (int v = e, k = d - 1; k >= 0; --k, v = t_par[v]) t_path[k] = v;
-        t_d = d;
-        t_e = e;
-    }
-    __syncthreads();
-    const int d = t_d, e = t_e;
-    for (int k = threadIdx.x; k < N; k += kThreads) {
-        int32_t* otok = a.out_tok + (size_t)b * N;
-        if (k < d) {
-            const int v = t_path[k];
-            a.out_path[(size_t)b * N + k] = v;
-            otok[k] = a.tok[b * N + v];
-            if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (float)(-rs.lnS[t_par[v]]);
-        } else {
-            a.out_path[(size_t)b * N + k] = -1;
-            otok[k] = (k == d) ? rs.g[e] : -1;
-            if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (k == d) ? (float)(-rs.lnS[e]) : 0.f;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long accm = 1ull;  // bit i: node i accepted
+            int depth[SPEC_MAX_NODES];
+            depth[0] = 0;
+            int e = 0;
+            for (int i = 1; i < nb; ++i) {
+                const int pi = t_par[i];
+                depth[i] = 0;
+                if (pi >= 0 && t_match[i] && ((accm >> pi) & 1ull)) {
+                    accm |= 1ull << i;
+                    depth[i] = depth[pi] + 1;
+                    if (depth[i] > depth[e]) e = i;
+                }
+            }
+            const int d = depth[e];
+            for (int v = e, k = d - 1; k >= 0; --k, v = t_par[v]) t_path[k] = v;
+            t_d = d;
+            t_e = e;
         }
-        if (a.out_blp) a.out_blp[(size_t)b * N + k] = 0.f;
-    }
-    if (threadIdx.x == 0) {
-        a.out_len[b] = d;
-        a.out_status[b] = t_bad;
+        __syncthreads();
+        const int d = t_d, e = t_e;
+        for (int k = threadIdx.x; k < N; k += kDecideThreads) {
+            int32_t* otok = a.out_tok + (size_t)b * N;
+            if (k < d) {
+                const int v = t_path[k];
+                a.out_path[(size_t)b * N + k] = v;
+                otok[k] = a.tok[b * N + v];
+                if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (float)(-rs.lnS[t_par[v]]);
+            } else {
+                a.out_path[(size_t)b * N + k] = -1;
+                otok[k] = (k == d) ? rs.g[e] : -1;
+                if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (k == d) ? (float)(-rs.lnS[e]) : 0.f;
+            }
+            if (a.out_blp) a.out_blp[(size_t)b * N + k] = 0.f;
+        }
+        if (threadIdx.x == 0) {
+            a.out_len[b] = d;
+            a.out_status[b] = t_bad;
+        }
     }
 }
 
 // -------------------------------------------------------------------- pass 2
+// Sweep: one workgroup per (request, 4096-token chunk).  Every workgroup of
+// the request folds the tile records and takes the decision itself (same
+// data, same order, same result), so no kernel boundary sits between the
+// decision and the sweep; chunk 0 also writes the accepted prefix and the
+// decision record.  Each workgroup then sums its chunk of the row(s) the
+// terminal token is drawn from, in fp64.
 template <typename T, bool EXACT>
-__global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_pass2(const Args a) {
+__global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Args a) {
     constexpr int MODE = EXACT ? kExact : kRelaxed;
     constexpr int VEC = Elem<T>::kVec;
     constexpr int NV = kRun / VEC;  // 16-byte vectors per thread per chunk
@@ -959,116 +953,134 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_pass2(const Ar
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
-    __shared__ double tab[64];
+    __shared__ double tab[kExpTab];
     __shared__ RowStats rs;
     __shared__ ChainDecision cd;
     __shared__ double red[kWaves][4];
-    __shared__ int s_last;
     fill_exp_table(tab);
-
-    // Every workgroup of the request derives the same decision from the
-    // tile records (deterministic), then works on the row(s) the terminal
-    // token is drawn from: target row n, and draft row n for a residual.
     ChainVals cv;
     if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
     __syncthreads();
-    fold_rows<MODE, true>(a, b, a.R, rs, tab, [&]() {
+    fold_rows<MODE, true, kWaves>(a, b, a.R, rs, tab, [&]() {
         if (threadIdx.x < 64) chain_load_values<T, MODE>(a, b, cv);
     });
     if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
     __syncthreads();
     const int n = cd.n;
     const bool residual = EXACT && n < a.K;
+    const double Mt = rs.M[n], Md = residual ? (double)rs.M[a.rows_t + n] : 0.0;
+    // p > q  <=>  (l - Mt) - (d - Md) > lnSt - lnSd, with the streamed
+    // normalizers
+    const double cls = residual ? rs.lnS[n] - rs.lnS[a.rows_t + n] : 0.0;
+    if (c == 0) {
+        write_prefix<MODE>(a, b, cd);
+        if (threadIdx.x == 0) {
+            Decision d;
+            d.n = n;
+            d.residual = residual;
+            d.pad0 = d.pad1 = 0;
+            d.Mt = Mt;
+            d.Md = Md;
+            d.cls = cls;
+            d.rn = cd.r[n < a.K ? n : 0];
+            a.dec[b] = d;
+        }
+    }
     const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
     const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
-    const double Mt = rs.M[n], Md = residual ? (double)rs.M[a.rows_t + n] : 0.0;
-    // p > q  <=>  (l - Mt) - (d - Md) > lnSt - lnSd (streamed normalizers)
-    const double cls = residual ? rs.lnS[n] - rs.lnS[a.rows_t + n] : 0.0;
     const __amdgpu_buffer_rsrc_t rt = row_rsrc(trow, a.V);
     const __amdgpu_buffer_rsrc_t rd = row_rsrc(drow, a.V);
-    const bool vd = residual ? a.vec_d : a.vec_t;
 
-    // ---- sweep: fp64 sums over this chunk (coalesced, interleaved layout)
-    {
-        const int c0 = c * kChunk;
-        const int c1 = min(c0 + kChunk, a.V);
-        u32x4 qt[NV], qd[NV];
-        // both rows are always loaded (rd aliases the target row when no
-        // draft row is needed) so that all loads issue before any wait
+    const int c0 = c * kChunk;
+    const int c1 = min(c0 + kChunk, a.V);
+    u32x4 qt[NV], qd[NV];
+    double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0;
+    if (residual) {  // uniform: one loop per case, no per-token branch
         load_chunk<T, NV>(rt, c0, c1, a.vec_t, qt);
-        load_chunk<T, NV>(rd, c0, c1, vd, qd);
-        double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0;
+        load_chunk<T, NV>(rd, c0, c1, a.vec_d, qd);
 #pragma unroll
         for (int k = 0; k < NV; ++k)
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
                 const double xa = (double)Elem<T>::get(qt[k], i) - Mt;
+                const double xb = (double)Elem<T>::get(qd[k], i) - Md;
                 const double ea = exp_nonpos(xa, tab);
+                const double eb = exp_nonpos(xb, tab);
                 sa += ea;
-                if (residual) {
-                    const double xb = (double)Elem<T>::get(qd[k], i) - Md;
-                    const double eb = exp_nonpos(xb, tab);
-                    sb += eb;
-                    if (xa - xb > cls) {
-                        pa += ea;
-                        pb += eb;
-                    }
-                }
+                sb += eb;
+                const double pq = (xa - xb > cls) ? 1.0 : 0.0;  // p > q
+                pa = fma(ea, pq, pa);
+                pb = fma(eb, pq, pb);
             }
-        sa = wave_sum(sa);
-        if (residual) {
-            sb = wave_sum(sb);
-            pa = wave_sum(pa);
-            pb = wave_sum(pb);
-        }
-        if (lane == 0) {
-            red[wave][0] = sa;
-            red[wave][1] = sb;
-            red[wave][2] = pa;
-            red[wave][3] = pb;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            double t[4] = {0.0, 0.0, 0.0, 0.0};
-            for (int w = 0; w < kWaves; ++w)
-                for (int i = 0; i < 4; ++i) t[i] += red[w][i];
-            uint64_t* w = a.p2 + ((size_t)b * a.C2 + c) * kP2Words;
-            for (int i = 0; i < 4; ++i) put_double(w + 2 * i, t[i]);
-            // The arrival whose ticket is C2 - 1 (mod C2) is elected; it waits
-            // for any word not yet visible, so arrival order does not matter.
-            s_last = (ticket_add(a.tickets + (size_t)kCtrlStride * b) % (unsigned)a.C2 == (unsigned)a.C2 - 1);
-        }
-        __syncthreads();
-        if (!s_last) return;
+    } else {
+        load_chunk<T, NV>(rt, c0, c1, a.vec_t, qt);
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) sa += exp_nonpos((double)Elem<T>::get(qt[k], i) - Mt, tab);
     }
-
-    // ---- terminal sample (elected workgroup of the request)
-    __shared__ int s_cstar, s_bad_ws, s_res;
-    __shared__ double s_base, s_target, s_iS, s_iSq, s_lnS, s_lnZ, s_l1r;
-    if (wave == 0) {
-        // lane l holds chunk l: sums, masses, scan and the chunk holding the
-        // target, all within the wave
-        double csa = 0.0, csb = 0.0, cpa = 0.0, cpb = 0.0;
-        bool ok = true;
-        if (lane < a.C2) {
-            uint32_t w[kP2Words];
-            ok = take_words<kP2Words>(a.p2 + ((size_t)b * a.C2 + lane) * kP2Words, w);
-            csa = join_double(w[0], w[1]);
-            csb = join_double(w[2], w[3]);
-            cpa = join_double(w[4], w[5]);
-            cpb = join_double(w[6], w[7]);
+    sa = wave_sum(sa);
+    if (residual) {
+        sb = wave_sum(sb);
+        pa = wave_sum(pa);
+        pb = wave_sum(pb);
+    }
+    if (lane == 0) {
+        red[wave][0] = sa;
+        red[wave][1] = sb;
+        red[wave][2] = pa;
+        red[wave][3] = pb;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ChunkSums cs = {0.0, 0.0, 0.0, 0.0};
+        for (int w = 0; w < kWaves; ++w) {
+            cs.sa += red[w][0];
+            cs.sb += red[w][1];
+            cs.pa += red[w][2];
+            cs.pb += red[w][3];
         }
-        const bool bad = __ballot(!ok) != 0ull;
-        const double S = wave_sum(csa);
-        const double Sq = residual ? wave_sum(csb) : 1.0;
+        a.sums[(size_t)b * a.C2 + c] = cs;
+    }
+}
+
+// Terminal sample: one workgroup per request (the kernel boundary makes the
+// chunk sums visible).  Wave 0 turns the chunk sums into chunk masses of
+// relu(p - q) (or of p), scans them and finds the chunk holding u_K * Z; the
+// workgroup (1024 threads, four consecutive tokens each) then rescans that
+// chunk with a block scan and writes the terminal token and its log-probs.
+template <typename T, bool EXACT>
+__global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int t = threadIdx.x;
+
+    __shared__ double tab[kExpTab];
+    __shared__ int s_cstar, s_res;
+    __shared__ double s_base, s_target, s_iS, s_iSq, s_lnS, s_lnZ, s_l1r;
+    __shared__ double s_wtot[kSampleWaves];
+    __shared__ int s_pick[kSampleWaves][3];
+    fill_exp_table(tab);
+
+    const Decision dc = a.dec[b];
+    const int n = dc.n;
+    const bool residual = EXACT && dc.residual;
+    const double Mt = dc.Mt, Md = dc.Md, cls = dc.cls;
+    if (wave == 0) {
+        // lane l holds chunk l
+        ChunkSums cs = {0.0, 0.0, 0.0, 0.0};
+        if (lane < a.C2) cs = a.sums[(size_t)b * a.C2 + lane];
+        const double S = wave_sum(cs.sa);
+        const double Sq = residual ? wave_sum(cs.sb) : 1.0;
         const double iS = 1.0 / S, iSq = 1.0 / Sq;
-        // residual mass of this chunk (clamped: tokens classified with the
+        // residual mass of the chunk (clamped: tokens classified with the
         // streamed normalizers can leave a rounding-size negative); fall back
         // to p when relu(p - q) has no mass
-        double W = residual ? fmax(cpa * iS - cpb * iSq, 0.0) : csa;
+        double W = residual ? fmax(cs.pa * iS - cs.pb * iSq, 0.0) : cs.sa;
         const double Zr = residual ? wave_sum(W) : 0.0;
         const bool res = residual && (Zr > 0.0);
-        if (residual && !res) W = csa;
+        if (residual && !res) W = cs.sa;
         const double Z = res ? Zr : S;
         const double target = (double)a.u[b * (a.K + 1) + a.K] * Z;
         const double incl = wave_incl_scan(W);
@@ -1081,9 +1093,9 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_pass2(const Ar
         // target past the last boundary, the last chunk with mass
         const int cstar = mine ? __builtin_ctzll(mine) : (hasm ? 63 - __builtin_clzll(hasm) : 0);
         const double base = readlane_d(excl, cstar);
-        // logs in parallel lanes: lane 0 log S, lane 1 log Z
-        const double lg = log(lane == 0 ? S : Z);
-        const double l1r = res ? log1p(-cd.r[n]) : 0.0;
+        const double lg = log(lane == 0 ? S : Z);  // lane 0: log S, lane 1: log Z
+        const double lgz = readlane_d(lg, 1);
+        const double l1r = res ? log1p(-dc.rn) : 0.0;
         if (lane == 0) {
             s_cstar = cstar;
             s_base = base;
@@ -1091,82 +1103,69 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_pass2(const Ar
             s_iS = iS;
             s_iSq = iSq;
             s_res = res;
-            s_bad_ws = bad;
             s_lnS = lg;
+            s_lnZ = lgz;
             s_l1r = l1r;
         }
-        if (lane == 1) s_lnZ = lg;
     }
     __syncthreads();
 
-    // ---- rescan chunk cstar; thread t owns tokens [e0 + t*kRun, +kRun)
     const int cstar = s_cstar;
     const bool res = s_res;
     const double iS = s_iS, iSq = s_iSq, target = s_target;
-    const int e0 = cstar * kChunk + (int)threadIdx.x * kRun;
-    u32x4 qt[NV], qd[NV];
-    load_run<T, NV>(rt, e0, a.V, a.vec_t, qt);
-    load_run<T, NV>(rd, e0, a.V, vd, qd);
-    auto lt = [&](int i) { return Elem<T>::get(qt[i / VEC], i % VEC); };
-    auto ld = [&](int i) { return Elem<T>::get(qd[i / VEC], i % VEC); };
-    // residual term of a token with logits (l, d) (0 where p <= q)
-    auto term = [&](float l, float d, double& ea) -> double {
-        const double xa = (double)l - Mt;
-        ea = exp_nonpos(xa, tab);
-        if (!res) return ea;
-        const double xb = (double)d - Md;
-        const double eb = exp_nonpos(xb, tab);
-        return (xa - xb > cls) ? fmax(ea * iS - eb * iSq, 0.0) : 0.0;
-    };
+    const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
+    const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
+    const int e0 = cstar * kChunk + t * kSampleRun;
+    float lt[kSampleRun], ld[kSampleRun];
+    Elem<T>::load4(row_rsrc(trow, a.V), e0, a.V, a.vec_t, lt);
+    Elem<T>::load4(row_rsrc(drow, a.V), e0, a.V, residual ? a.vec_d : a.vec_t, ld);
+    double w[kSampleRun];
     double tsum = 0.0;
     unsigned pos = 0u, fin = 0u;  // bit i: token i has mass / a finite logit
 #pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-        double ea;
-        const double wi = term(lt(i), ld(i), ea);
+    for (int i = 0; i < kSampleRun; ++i) {
+        const double xa = (double)lt[i] - Mt;
+        const double ea = exp_nonpos(xa, tab);
+        double wi = ea;
+        if (res) {
+            const double xb = (double)ld[i] - Md;
+            const double eb = exp_nonpos(xb, tab);
+            wi = (xa - xb > cls) ? fmax(ea * iS - eb * iSq, 0.0) : 0.0;
+        }
+        w[i] = wi;
         tsum += wi;
         pos |= (wi > 0.0) ? (1u << i) : 0u;
-        fin |= (lt(i) > -INFINITY) ? (1u << i) : 0u;
+        fin |= (lt[i] > -INFINITY) ? (1u << i) : 0u;
     }
-    const int firstpos = pos ? e0 + __builtin_ctz(pos) : INT_MAX;
-    const int lastpos = pos ? e0 + 31 - __builtin_clz(pos) : -1;
-    const int anypos = fin ? e0 + 31 - __builtin_clz(fin) : -1;
     // block scan in thread order; the exclusive prefix of a thread is the
     // previous thread's inclusive prefix, bit for bit
-    __shared__ double s_wtot[kWaves];
-    __shared__ int s_pick[kWaves][3];
     const double wincl = wave_incl_scan(tsum);
     if (lane == 63) s_wtot[wave] = wincl;
     __syncthreads();
+    // offset of this wave: the earlier waves' totals added in wave order (all
+    // read at once, then summed)
+    double tot[kSampleWaves];
+#pragma unroll
+    for (int ww = 0; ww < kSampleWaves; ++ww) tot[ww] = s_wtot[ww];
     double off = 0.0;
-    for (int ww = 0; ww < wave; ++ww) off += s_wtot[ww];
+#pragma unroll
+    for (int ww = 0; ww < kSampleWaves; ++ww)
+        if (ww < wave) off += tot[ww];
     const double tincl = wincl + off;
     double texcl = __shfl_up(tincl, 1);
     if (lane == 0) texcl = off;
-    // First crossing of the running sum past target.  A thread that starts
-    // past target crosses at its first token with mass; the others walk their
-    // tokens (terms recomputed, bit-identical).
+    // first crossing of the running sum past target in this thread's tokens
     double cum = s_base + texcl;
     int cand = INT_MAX;
-    if (cum > target) {
-        cand = firstpos;
-    } else if (tsum > 0.0) {
 #pragma unroll
-        for (int i = 0; i < kRun; ++i) {
-            if (cand == INT_MAX) {
-                // recomputed rather than kept from the first pass (the empty
-                // asm hides the equality, so the terms need no registers)
-                float l = lt(i), d = ld(i);
-                __asm__ volatile("" : "+v"(l), "+v"(d));
-                double ea;
-                const double wi = term(l, d, ea);
-                if (wi > 0.0) {
-                    cum += wi;
-                    if (cum > target) cand = e0 + i;
-                }
-            }
+    for (int i = 0; i < kSampleRun; ++i) {
+        if (w[i] > 0.0 && cand == INT_MAX) {
+            cum += w[i];
+            if (cum > target) cand = e0 + i;
         }
     }
+    const int lastpos = pos ? e0 + 31 - __builtin_clz(pos) : -1;
+    const int anypos = fin ? e0 + 31 - __builtin_clz(fin) : -1;
     const int wc = wave_min_i(cand), wl = wave_max_i(lastpos), wa = wave_max_i(anypos);
     if (lane == 0) {
         s_pick[wave][0] = wc;
@@ -1176,7 +1175,7 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_pass2(const Ar
     __syncthreads();
     int yc = INT_MAX, yl = -1, ya = -1;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < kSampleWaves; ++ww) {
         yc = min(yc, s_pick[ww][0]);
         yl = max(yl, s_pick[ww][1]);
         ya = max(ya, s_pick[ww][2]);
@@ -1187,27 +1186,23 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_pass2(const Ar
     int y = (yc != INT_MAX) ? yc : (yl >= 0 ? yl : ya);
     if (y < 0 || y >= a.V) y = 0;
     const int rel = y - cstar * kChunk;
-    const int owner = (rel >= 0 && rel < kChunk) ? rel / kRun : 0;
-    if ((int)threadIdx.x == owner) {
-        float ly, dy;
-        if (rel >= 0 && rel < kChunk) {
-            ly = lt(0);
-            dy = ld(0);
+    const bool inchunk = rel >= 0 && rel < kChunk;
+    if (t == (inchunk ? rel / kSampleRun : 0)) {
+        float ly = lt[0];
+        double wy = w[0];
+        if (inchunk) {
 #pragma unroll
-            for (int i = 1; i < kRun; ++i)
+            for (int i = 1; i < kSampleRun; ++i)
                 if (e0 + i == y) {
-                    ly = lt(i);
-                    dy = ld(i);
+                    ly = lt[i];
+                    wy = w[i];
                 }
         } else {
             ly = Elem<T>::at(trow, (size_t)y);
-            dy = Elem<T>::at(drow, (size_t)y);
-        }
-        // the emitted token's residual term, defined as in the scan
-        double wy = 0.0;
-        if (res) {
+            const float dy = Elem<T>::at(drow, (size_t)y);
             const double xa = (double)ly - Mt, xb = (double)dy - Md;
-            if (xa - xb > cls) wy = fmax(exp_nonpos(xa, tab) * iS - exp_nonpos(xb, tab) * iSq, 0.0);
+            wy = 0.0;
+            if (res && xa - xb > cls) wy = fmax(exp_nonpos(xa, tab) * iS - exp_nonpos(xb, tab) * iSq, 0.0);
         }
         const int L = a.L;
         a.out_tok[(size_t)b * L + n] = y;
@@ -1215,11 +1210,6 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_pass2(const Ar
         const double blp = res ? s_l1r + log(wy) - s_lnZ : tlp;
         if (a.out_tlp) a.out_tlp[(size_t)b * L + n] = (float)tlp;
         if (a.out_blp) a.out_blp[(size_t)b * L + n] = (float)blp;
-    }
-    write_prefix<MODE>(a, b, cd);
-    if (threadIdx.x == 0) {
-        if (s_bad_ws) a.out_status[b] = 2;
-        ticket_sub(a.tickets + (size_t)kCtrlStride * b, a.C2);
     }
 }
 
@@ -1239,49 +1229,54 @@ spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt)
     return bytes >= L.total ? SPEC_OK : SPEC_EWORKSPACE;
 }
 
-// One-shot profiling hook: events to record around the kernels of the next
-// call made from this thread.
+// One-shot profiling hook: events for the kernels of the next call made from
+// this thread.
 thread_local hipEvent_t g_prof[3] = {nullptr, nullptr, nullptr};
 
-// Streaming kernel, then the per-request kernel (decision, or decision and
-// terminal sample).
+// Streaming kernel, then the per-request kernels: decide (greedy, tree), or
+// sweep and sample (exact, relaxed).  With the profiling hook set, the
+// streaming kernel is launched with start/stop events that the dispatch
+// itself timestamps, so their interval is the kernel's own duration.
 template <int MODE, bool SUM>
 spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
     a.tpr = tpr_of(dt, a.V);
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
-    a.tickets = reinterpret_cast<int*>(a.ws);
     a.segs = reinterpret_cast<Seg*>(a.ws + lay.seg);
-    a.p2 = reinterpret_cast<uint64_t*>(a.ws + lay.p2);
+    a.dec = reinterpret_cast<Decision*>(a.ws + lay.dec);
+    a.sums = reinterpret_cast<ChunkSums*>(a.ws + lay.sums);
     hipEvent_t ev[3] = {g_prof[0], g_prof[1], g_prof[2]};
     g_prof[0] = g_prof[1] = g_prof[2] = nullptr;
-    const unsigned grid = (unsigned)a.B * (unsigned)a.R * (unsigned)a.tpr;
-    if (ev[0] && hipEventRecord(ev[0], st) != hipSuccess) return SPEC_EHIP;
+    const dim3 grid((unsigned)a.B * (unsigned)a.R * (unsigned)a.tpr), block(kThreads);
     const bool vecp = a.vec_t && (MODE != kExact || a.vec_d);
     if (dt == SPEC_BF16) {
         if (vecp)
-            hipLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true>), dim3(grid), dim3(kThreads), 0, st, a);
+            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
         else
-            hipLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false>), dim3(grid), dim3(kThreads), 0, st, a);
+            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
     } else {
         if (vecp)
-            hipLaunchKernelGGL((k_stream<float, MODE, SUM, true>), dim3(grid), dim3(kThreads), 0, st, a);
+            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
         else
-            hipLaunchKernelGGL((k_stream<float, MODE, SUM, false>), dim3(grid), dim3(kThreads), 0, st, a);
+            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    if (ev[1] && hipEventRecord(ev[1], st) != hipSuccess) return SPEC_EHIP;
     if constexpr (MODE == kGreedy || MODE == kTree) {
         if (dt == SPEC_BF16)
-            hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM>), dim3(a.B), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((k_decide<float, MODE, SUM>), dim3(a.B), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decide<float, MODE, SUM>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
     } else {
         constexpr bool EXACT = (MODE == kExact);
-        const unsigned grid2 = (unsigned)a.B * (unsigned)a.C2;
-        if (dt == SPEC_BF16)
-            hipLaunchKernelGGL((k_pass2<uint16_t, EXACT>), dim3(grid2), dim3(kThreads), 0, st, a);
-        else
-            hipLaunchKernelGGL((k_pass2<float, EXACT>), dim3(grid2), dim3(kThreads), 0, st, a);
+        const dim3 grid2((unsigned)a.B * (unsigned)a.C2);
+        if (dt == SPEC_BF16) {
+            hipLaunchKernelGGL((k_sweep<uint16_t, EXACT>), grid2, block, 0, st, a);
+            if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+            hipLaunchKernelGGL((k_sample<uint16_t, EXACT>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((k_sweep<float, EXACT>), grid2, block, 0, st, a);
+            if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+            hipLaunchKernelGGL((k_sample<float, EXACT>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
+        }
     }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;

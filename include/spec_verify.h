@@ -38,10 +38,7 @@
  *                               malformed (a consulted draft token outside
  *                               [0,V), or a tree parent outside [-1, i)):
  *                               the offending draft counts as rejected and
- *                               the offending tree node as unmatched; 2 when
- *                               the workspace was not all zeros at the start
- *                               of the call (the request's outputs are then
- *                               unspecified, but every kernel still ends).
+ *                               the offending tree node as unmatched.
  *
  * Randomness is supplied by the caller (spec-decode README, "Use it": the
  * generator takes an rng), as uniforms[b][K+1] in [0,1): uniforms[b][j]
@@ -51,14 +48,13 @@
  * Workspace
  *   Each call needs a device workspace of at least
  *   spec_verify_workspace_bytes(B, rows_per_request, V) bytes, 256-byte
- *   aligned, ZERO-FILLED BEFORE ITS FIRST USE.  A call uses part of it for
- *   per-tile statistics (left behind as scratch) and part for counters and
- *   hand-off words between workgroups, which every completed call returns to
- *   zero; the scratch can never be mistaken for hand-off data, so the
- *   workspace can be reused by later calls of any shape on the same stream
- *   without clearing it again.  Calls that run concurrently (different streams) need different
- *   workspaces.  The library allocates nothing and keeps no state besides the
- *   one-shot, per-thread profiling hook (spec_verify_profile_next_call).
+ *   aligned, for per-tile statistics and per-chunk sums passed between the
+ *   call's kernels.  It needs no initialization and carries nothing from one
+ *   call to the next, so one workspace serves calls of any shape in turn on
+ *   the same stream.  Calls that run concurrently (different streams) need
+ *   different workspaces.  The library allocates nothing and keeps no state
+ *   besides the one-shot, per-thread profiling hook
+ *   (spec_verify_profile_next_call).
  *
  * Streams and errors
  *   stream is a hipStream_t (NULL = the default stream).  Calls enqueue
@@ -105,13 +101,14 @@ const char *spec_status_string(int status);
 
 /*
  * Host-only profiling hook (for benchmarks).  The arguments are hipEvent_t
- * handles created by the caller, or NULL.  The next spec_verify_* call made
- * from the calling thread records before_stream on its stream immediately
- * before its streaming kernel (the one that reads every logit once),
- * after_stream immediately after that kernel, and after_call after the
- * call's last kernel, so that hipEventElapsedTime gives the streaming
- * kernel's duration and the rest of the call's.  The hook applies to one call
- * and is then cleared; passing NULLs clears it.
+ * handles created by the caller (with timing enabled), or NULL.  The next
+ * spec_verify_* call made from the calling thread launches its streaming
+ * kernel (the one that reads every logit once) with before_stream and
+ * after_stream as the dispatch's own start and stop events, so that
+ * hipEventElapsedTime(before_stream, after_stream) is that kernel's
+ * duration, and records after_call on its stream after the call's last
+ * kernel.  The hook applies to one call and is then cleared; passing NULLs
+ * clears it.
  */
 void spec_verify_profile_next_call(void *before_stream, void *after_stream, void *after_call);
 

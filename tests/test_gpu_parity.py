@@ -263,9 +263,11 @@ def test_bitwise_determinism():
 
 
 def test_workspace_reuse_across_shapes():
-    """The workspace is left zeroed: calls of different shapes can share it."""
-    ws = torch.zeros(sv.spec_verify_workspace_bytes(64, 17, 151936), dtype=torch.uint8,
-                     device="cuda")
+    """The workspace needs no initialization and keeps nothing between calls:
+    one buffer, filled with random bytes first, serves calls of several
+    shapes in turn."""
+    nb = sv.spec_verify_workspace_bytes(64, 17, 151936)
+    ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda")
     for (B, K, V) in [(4, 3, 5000), (32, 5, 20000), (2, 8, 3000), (32, 5, 20000)]:
         ci = synth.chain_inputs(B, K, V, "bf16", seed=B * 7 + K, useed=V)
         T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
@@ -275,7 +277,6 @@ def test_workspace_reuse_across_shapes():
         compare_chain(r, oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
                       what=f"reuse exact {B},{K},{V}")
         compare_chain(g, oracle.greedy(ci.target, ci.tokens, "bf16"), what=f"reuse greedy {B}")
-    assert int(ws[: 16 * 64].count_nonzero()) == 0
 
 
 # --------------------------------------------------------- statistical pin
