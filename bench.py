@@ -44,7 +44,8 @@ KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_veri
 # plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Reported only while the kernel source is the one the counters were taken
 # on.
-TRAFFIC = None
+TRAFFIC = {"source_sha256": "39e969ace72ce8997420ab309bda73c60a04275a71173eee15f0136b04b3ff78",
+           "fetch_kib": 44124.0, "write_kib": 176.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 MALL_BYTES = 256 * 1024 * 1024
 METRIC = "verify rounds/s + achieved HBM GB/s (% of peak), B=32 K=5 V=128256 bf16"

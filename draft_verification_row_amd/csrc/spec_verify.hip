@@ -549,7 +549,10 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     constexpr int TILE = kThreads * kTileVecs * VEC;
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
-    constexpr bool NT = ARGMAX;  // greedy and tree never revisit a row
+    // Non-temporal loads: the stream touches every line once.  (The one or
+    // two rows the terminal sample re-reads are a small share, and measured
+    // calls are faster this way.)
+    constexpr bool NT = true;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
