@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     __shared__ float s_m[kWaves];
-    __shared__ int s_i[kWaves];
+    __shared__ int s_i[kWaves], s_j[kWaves];
     __shared__ double s_s[kWaves];
 
     const int g = uniform((int)(blockIdx.x / (unsigned)a.tpr));
@@ -582,67 +582,66 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
         for (int k = 0; k < kTileVecs; ++k) Elem<T>::mask_tail(q[k], t0 + k * kThreads * VEC, a.V);
     }
     // Values are unpacked from the packed vectors where they are used, so
-    // only the 16-byte vectors stay live between the two phases.
+    // only the 16-byte vectors stay live between the phases.
     float m = -INFINITY;
-    int slot = 0, cnt = 0;  // slot k*VEC + i: first maximum of this thread
+    int cnt = 0;
 #pragma unroll
     for (int k = 0; k < kTileVecs; ++k) {
         float v[VEC];
         Elem<T>::unpack(q[k], v);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-            if (ARGMAX) {
-                if (v[i] > m) {  // ascending token order: keeps the first maximum
-                    m = v[i];
-                    slot = k * VEC + i;
-                }
-            } else {
-                m = fmaxf(m, v[i]);
-            }
+            m = fmaxf(m, v[i]);
             if (COUNT) cnt += (v[i] > thr) ? 1 : 0;
         }
     }
-    int idx = (m > -INFINITY) ? t0 + (slot / VEC) * (kThreads * VEC) + slot % VEC : INT_MAX;
-    if (ARGMAX)
-        wave_argmax(m, idx);
-    else
-        m = wave_max(m);
+    float M = wave_max(m);
     if (COUNT) cnt = wave_sum_i(cnt);
     if (lane == 0) {
-        s_m[wave] = m;
-        s_i[wave] = ARGMAX ? idx : cnt;
+        s_m[wave] = M;
+        s_i[wave] = cnt;
     }
     __syncthreads();
-    float M = s_m[0];
-    int I = s_i[0];
+    M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    int I = COUNT ? ((s_i[0] + s_i[1]) + s_i[2]) + s_i[3] : 0;
+    // Greedy rules: the lowest index holding the tile max.  Only threads whose
+    // own max is the tile max search their tokens (ascending, first hit), so
+    // the common path pays one max per token.
+    int idx = INT_MAX;
+    if (ARGMAX && m == M && M > -INFINITY) {
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-        if (ARGMAX) {
-            argmax_combine(M, I, s_m[w], s_i[w]);
-        } else {
-            M = fmaxf(M, s_m[w]);
-            I += s_i[w];
+        for (int k = kTileVecs - 1; k >= 0; --k) {
+            float v[VEC];
+            Elem<T>::unpack(q[k], v);
+#pragma unroll
+            for (int i = VEC - 1; i >= 0; --i)
+                if (v[i] == M) idx = t0 + k * kThreads * VEC + i;
         }
     }
     double s = 0.0;
-    if (SUM) {
-        if (M > -INFINITY) {
-            // 2^(l*L - mL) with the reference mL = fl(M*L): every term <= 1
-            const float mL = M * kLog2e;
+    if (SUM && M > -INFINITY) {
+        // 2^(l*L - mL) with the reference mL = fl(M*L): every term <= 1
+        const float mL = M * kLog2e;
 #pragma unroll
-            for (int k = 0; k < kTileVecs; ++k) {
-                float v[VEC];
-                Elem<T>::unpack(q[k], v);
-                float acc = 0.f;
+        for (int k = 0; k < kTileVecs; ++k) {
+            float v[VEC];
+            Elem<T>::unpack(q[k], v);
+            float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) acc += __builtin_amdgcn_exp2f(fmaf(v[i], kLog2e, -mL));
-                s += (double)acc;
-            }
+            for (int i = 0; i < VEC; ++i) acc += __builtin_amdgcn_exp2f(fmaf(v[i], kLog2e, -mL));
+            s += (double)acc;
         }
-        s = wave_sum(s);
-        if (lane == 0) s_s[wave] = s;
+    }
+    if (SUM || ARGMAX) {
+        if (SUM) s = wave_sum(s);
+        if (ARGMAX) idx = wave_min_i(idx);
+        if (lane == 0) {
+            s_s[wave] = s;
+            s_j[wave] = idx;
+        }
         __syncthreads();
         s = ((s_s[0] + s_s[1]) + s_s[2]) + s_s[3];
+        if (ARGMAX) I = min(min(s_j[0], s_j[1]), min(s_j[2], s_j[3]));
     }
     if (threadIdx.x == 0) {
         Seg sg;
