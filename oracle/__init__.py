@@ -22,7 +22,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["build", "load", "OracleResult", "greedy", "exact", "relaxed", "tree", "row_stats",
+__all__ = ["build", "load", "OracleResult", "OracleSample", "greedy", "exact", "relaxed", "tree",
+           "sample", "row_stats",
            "set_threads", "max_threads", "EPS_ACCEPT", "EPS_SAMPLE"]
 
 EPS_ACCEPT = 1e-6
@@ -62,6 +63,7 @@ def load():
         lib.oracle_greedy.argtypes = [P, I, P, I, I, I, P, P, P, P, P, P]
         lib.oracle_exact.argtypes = [P, P, I, P, P, I, I, I, Dd, Dd, P, P, P, P, P, P, P]
         lib.oracle_relaxed.argtypes = [P, I, P, P, I, I, I, Dd, I, Dd, Dd, P, P, P, P, P, P, P]
+        lib.oracle_sample.argtypes = [P, I, P, ctypes.c_long, I, Dd, P, P, P]
         lib.oracle_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, P, P]
         _lib = lib
     return _lib
@@ -163,6 +165,31 @@ def relaxed(target, tokens, uniforms, dtype: str, tau: float, top_k: int,
                           float(eps_accept), float(eps_sample), _ptr(tok), _ptr(ln), _ptr(tlp),
                           _ptr(blp), _ptr(st), _ptr(fl), _ptr(dec))
     return OracleResult(tok, ln, tlp, blp, st, fl, dec)
+
+
+@dataclass
+class OracleSample:
+    """One draw per logit row: token, its log-prob under the row's softmax, and
+    a near-boundary flag (u*Z within EPS_SAMPLE*Z of a CDF boundary)."""
+    tokens: np.ndarray
+    logq: np.ndarray
+    flag: np.ndarray
+
+
+def sample(logits, uniforms, dtype: str, eps_sample: float = EPS_SAMPLE) -> OracleSample:
+    """Draft sampler: y = inverse CDF of softmax(row) at the row's uniform.
+    logits [..., V]; uniforms with the leading shape of logits."""
+    X = _logits(logits, dtype)
+    lead, V = X.shape[:-1], X.shape[-1]
+    u = _c(uniforms, np.float32)
+    assert u.shape == lead
+    rows = int(np.prod(lead)) if lead else 1
+    tok = np.empty(lead, np.int32)
+    lq = np.empty(lead, np.float64)
+    fl = np.empty(lead, np.int32)
+    load().oracle_sample(_ptr(X), _dt(dtype), _ptr(u), rows, V, float(eps_sample), _ptr(tok),
+                         _ptr(lq), _ptr(fl))
+    return OracleSample(tok, lq, fl)
 
 
 def tree(target, node_tok, parents, dtype: str, num_nodes=None) -> OracleResult:

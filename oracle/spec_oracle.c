@@ -444,3 +444,33 @@ void oracle_tree(const void *T, int dt, const int32_t *node_tok, const int32_t *
         free(par);
     }
 }
+
+/* ----------------------------------------------------------- draft sampler
+ * Independent draws, one per logit row: y_r = inverse CDF of softmax(X_r) at
+ * u_r (ascending token order, smallest t whose inclusive prefix exceeds
+ * u_r * Z), and log q_r(y_r).  This is the draft model's proposal step that
+ * feeds the verifier (spec-decode README, "How it works": the draft samples
+ * its k tokens from q); the uniform per row and the inverse-CDF order are the
+ * same conventions as the terminal sample above.                           */
+void oracle_sample(const void *X, int dt, const float *u, long rows, int V, double eps_sample,
+                   int32_t *out_tok, double *out_logq, int32_t *out_flag)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (long r = 0; r < rows; ++r) {
+        row_stats sq;
+        stats(X, dt, (size_t)r, V, &sq);
+        double *w = (double *)malloc(sizeof(double) * (size_t)V);
+        double Z = 0.0;
+        for (int t = 0; t < V; ++t) {
+            w[t] = exp(ld(X, dt, (size_t)r * V + t) - sq.M);
+            Z += w[t];
+        }
+        double lo, hi, target = (double)u[r] * Z;
+        long y = inverse_cdf(w, V, target, &lo, &hi);
+        out_tok[r] = (int32_t)y;
+        out_logq[r] = logp(X, dt, (size_t)r, V, y, &sq);
+        out_flag[r] = sample_flag(target, lo, hi, Z, eps_sample);
+        free(w);
+    }
+}
+

@@ -47,6 +47,12 @@ void oracle_tree(const void *T, int dt, const int32_t *node_tok, const int32_t *
                  int32_t *out_path, int32_t *out_tok, int32_t *out_len, double *out_tlp,
                  double *out_blp, int32_t *out_status);
 
+/* X [rows][V]; u [rows]; out_tok, out_logq, out_flag [rows]: one inverse-CDF
+ * draw per row and its log-prob; flag 1 when u*Z lies within eps_sample*Z
+ * of a CDF boundary */
+void oracle_sample(const void *X, int dt, const float *u, long rows, int V, double eps_sample,
+                   int32_t *out_tok, double *out_logq, int32_t *out_flag);
+
 #ifdef __cplusplus
 }
 #endif

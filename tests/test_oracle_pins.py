@@ -480,3 +480,59 @@ def test_tree_bad_parent_sets_status(orc):
     r = orc.tree(T, node_tok, parents, "f32")
     assert r.status[0] == 1
     assert r.accept_len[0] == 2 and list(r.path[0, :2]) == [1, 3]
+
+
+# ------------------------------------------------------------ draft sampler
+# The proposal step before verification: one draw per draft row from
+# q = softmax(row) (spec-decode README, "How it works"), by inverse CDF at a
+# caller uniform.
+def test_sampler_matches_searchsorted(orc):
+    """A library routine on the fp64 softmax: searchsorted(cumsum(w), u*Z,
+    'right') is the smallest t whose inclusive prefix exceeds u*Z."""
+    rng = np.random.default_rng(71)
+    for dtype, V in (("f32", 97), ("bf16", 3000), ("f32", 1)):
+        x32 = (3.0 * rng.standard_normal((6, 4, V))).astype(np.float32)
+        x = synth.bf16_rne(x32) if dtype == "bf16" else x32
+        u = rng.random((6, 4), dtype=np.float32)
+        r = orc.sample(x, u, dtype)
+        xw = synth.widen(x, dtype)
+        for idx in np.ndindex(6, 4):
+            w = np.exp(xw[idx] - xw[idx].max())
+            c = np.cumsum(w)
+            want = min(int(np.searchsorted(c, float(u[idx]) * c[-1], side="right")), V - 1)
+            if not r.flag[idx]:
+                assert r.tokens[idx] == want, (dtype, idx)
+        np.testing.assert_allclose(r.logq, log_softmax64(xw)[np.arange(6)[:, None], np.arange(4)[None, :],
+                                                           r.tokens], rtol=0, atol=1e-12)
+
+
+def test_sampler_law_on_a_grid(orc):
+    """Brute force: over a midpoint grid of M uniforms the frequency of each
+    token is its probability to within 1/M (each CDF boundary moves at most
+    one grid point)."""
+    rng = np.random.default_rng(72)
+    M = 4000
+    for V in (2, 5, 8):
+        x = (2.0 * rng.standard_normal(V)).astype(np.float32)
+        u = ((np.arange(M) + 0.5) / M).astype(np.float32)
+        r = orc.sample(np.broadcast_to(x, (M, V)).copy(), u, "f32")
+        freq = np.bincount(r.tokens, minlength=V) / M
+        p = softmax64(x.astype(np.float64))
+        assert np.abs(freq - p).max() <= 1.0 / M + 1e-12, (V, freq, p)
+
+
+def test_sampler_special_cases(orc):
+    """A row with one finite logit always yields that token (log q = 0); a row
+    of equal logits yields floor(u*V) away from the multiples of 1/V."""
+    V = 16
+    x = np.full((5, V), -np.inf, np.float32)
+    x[np.arange(5), [0, 3, 7, 12, 15]] = np.array([1.5, -2.0, 0.0, 40.0, -7.25], np.float32)
+    u = np.array([0.0, 0.3, 0.5, 0.9, 0.999], np.float32)
+    r = orc.sample(x, u, "f32")
+    assert list(r.tokens) == [0, 3, 7, 12, 15]
+    assert np.all(r.logq == 0.0)
+    e = np.zeros((7, 10), np.float32)
+    u = np.array([0.01, 0.17, 0.35, 0.52, 0.66, 0.81, 0.97], np.float32)
+    r = orc.sample(e, u, "f32")
+    assert list(r.tokens) == [int(math.floor(float(v) * 10)) for v in u]
+    np.testing.assert_allclose(r.logq, -math.log(10.0), rtol=0, atol=1e-15)
