@@ -116,19 +116,30 @@ class Case:
         from numpy import int16
         self.lib, self.mode, self.ci, self.sets = lib, mode, ci, sets
         B, K, V = ci.B, ci.K, ci.V
-        T0 = torch.from_numpy(ci.target.view(int16)).view(torch.bfloat16).to(dev)
+        src = ci.draft if mode == "sample" else ci.target
+        T0 = torch.from_numpy(src.view(int16)).view(torch.bfloat16).to(dev)
         D0 = (torch.from_numpy(ci.draft.view(int16)).view(torch.bfloat16).to(dev)
               if mode == "exact" else None)
         x0 = torch.from_numpy(ci.tokens).to(dev)
         u0 = torch.from_numpy(ci.uniforms).to(dev)
-        rows = 2 * K + 1 if mode == "exact" else K + 1
-        self.ws = torch.zeros(sv.spec_verify_workspace_bytes(B, rows, V), dtype=torch.uint8,
-                              device=dev)
+        if mode == "sample":
+            u0 = torch.from_numpy(ci.uniforms[:, :K].copy()).to(dev)
+            nbytes = sv.spec_sample_workspace_bytes(B * K, V)
+        else:
+            rows = 2 * K + 1 if mode == "exact" else K + 1
+            nbytes = sv.spec_verify_workspace_bytes(B, rows, V)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         self.inputs, self.outputs = [], []
         for s in range(sets):
             T = T0.clone()
             D = D0.clone() if D0 is not None else None
             self.inputs.append((T, D, x0.clone(), u0.clone()))
+            if mode == "sample":
+                out = dict(tok=torch.empty((B, K), dtype=torch.int32, device=dev),
+                           lq=torch.empty((B, K), dtype=torch.float32, device=dev),
+                           st=torch.empty((B, K), dtype=torch.int32, device=dev))
+                self.outputs.append(out)
+                continue
             out = dict(tok=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
                        ln=torch.empty(B, dtype=torch.int32, device=dev),
                        st=torch.empty(B, dtype=torch.int32, device=dev))
@@ -145,6 +156,10 @@ class Case:
         o = self.outputs[s]
         P = ctypes.c_void_p
         ws = self.ws
+        if self.mode == "sample":
+            return (P(T.data_ptr()), 1, P(u.data_ptr()), B * K, V, P(o["tok"].data_ptr()),
+                    P(o["lq"].data_ptr()), P(o["st"].data_ptr()), P(ws.data_ptr()), ws.numel(),
+                    P(stream))
         if self.mode == "exact":
             return (P(T.data_ptr()), P(D.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K,
                     V, P(o["tok"].data_ptr()), P(o["ln"].data_ptr()), P(o["tlp"].data_ptr()),
@@ -155,7 +170,8 @@ class Case:
                 ws.numel(), P(stream))
 
     def fn(self):
-        return self.lib.spec_verify_exact if self.mode == "exact" else self.lib.spec_verify_greedy
+        return {"exact": self.lib.spec_verify_exact, "greedy": self.lib.spec_verify_greedy,
+                "sample": self.lib.spec_sample_drafts}[self.mode]
 
     def run(self, n, start=0, stream=None):
         torch = self.torch
@@ -282,6 +298,10 @@ def main():
 
     lib = sv.load_library()
     lib.spec_verify_profile_next_call.argtypes = [ctypes.c_void_p] * 3
+    lib.spec_sample_drafts.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
     lib.spec_verify_profile_next_call.restype = None
     dev = torch.device("cuda:0")
     hip = Hip()
@@ -298,6 +318,10 @@ def main():
     gr = Case(lib, "greedy", ci, sets_greedy, torch, dev)
     r_gr = time_case(gr, args.steps, args.warmup, hip, use_graph)
     del gr
+    sets_sample = math.ceil(2 * MALL_BYTES / ci.draft.nbytes)
+    sa = Case(lib, "sample", ci, sets_sample, torch, dev)
+    r_sa = time_case(sa, args.steps, args.warmup, hip, use_graph)
+    del sa
     torch.cuda.synchronize()
 
     ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
@@ -307,6 +331,7 @@ def main():
     stream_bytes = ci.target.nbytes + ci.draft.nbytes
     achieved = stream_bytes / (k_ms * 1e-3) / 1e9
     g_ms = r_gr["graph_ms_per_step"] if use_graph else r_gr["eager_ms_per_step"]
+    s_ms = r_sa["graph_ms_per_step"] if use_graph else r_sa["eager_ms_per_step"]
     out = {
         "metric": METRIC,
         "value": value,
@@ -343,6 +368,13 @@ def main():
             "rest_of_call_us_mean": r_gr["rest_ms_mean"] * 1e3,
             "eager_rounds_per_s": 1000.0 / r_gr["eager_ms_per_step"],
             "algorithmic_bytes": bytes_greedy, "input_sets": sets_greedy},
+        "draft_sampler_c3_draft_rows": {
+            "calls_per_s": 1000.0 / s_ms, "ms_per_call": s_ms, "rows": ci.B * ci.K,
+            "hbm_gbs_call": ci.draft.nbytes / (s_ms * 1e-3) / 1e9,
+            "kernel_us_mean": r_sa["kernel_ms_mean"] * 1e3,
+            "kernel_gbs": ci.draft.nbytes / (r_sa["kernel_ms_mean"] * 1e-3) / 1e9,
+            "rest_of_call_us_mean": r_sa["rest_ms_mean"] * 1e3,
+            "logit_bytes": ci.draft.nbytes, "input_sets": sets_sample},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -3,7 +3,7 @@
 A thin ctypes layer over ``libspecverify.so`` (the C ABI declared in
 ``include/spec_verify.h``).  It only marshals arguments: it checks that the
 torch tensors are on the GPU, contiguous and of the right dtype and shape,
-allocates the outputs and the zero-filled workspace with torch, and passes
+allocates the outputs and the workspace with torch, and passes
 raw device pointers and torch's current HIP stream to the library.  Every
 step of verification runs in the library's HIP kernels; there is no CPU
 path, and every entry point raises if the library is not built.
@@ -17,7 +17,8 @@ from typing import NamedTuple, Optional
 import torch
 
 __all__ = ["spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed", "spec_verify_tree",
-           "spec_verify_workspace_bytes", "VerifyResult", "TreeResult", "SpecVerifyError",
+           "spec_sample_drafts", "spec_verify_workspace_bytes", "spec_sample_workspace_bytes",
+           "VerifyResult", "TreeResult", "SampleResult", "SpecVerifyError",
            "library_path", "load_library", "SPEC_MAX_K", "SPEC_MAX_NODES"]
 
 SPEC_F32, SPEC_BF16 = 0, 1
@@ -55,7 +56,11 @@ def load_library():
     lib.spec_verify_exact.argtypes = [P, P, I, P, P, I, I, I, P, P, P, P, P, P, Z, P]
     lib.spec_verify_relaxed.argtypes = [P, I, P, P, I, I, I, F, I, P, P, P, P, P, P, Z, P]
     lib.spec_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, P, P, P, Z, P]
-    for fn in ("spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed", "spec_verify_tree"):
+    lib.spec_sample_workspace_bytes.argtypes = [I, I]
+    lib.spec_sample_workspace_bytes.restype = Z
+    lib.spec_sample_drafts.argtypes = [P, I, P, I, I, P, P, P, P, Z, P]
+    for fn in ("spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed", "spec_verify_tree",
+               "spec_sample_drafts"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -117,11 +122,9 @@ def spec_verify_workspace_bytes(B: int, rows_per_request: int, V: int) -> int:
 
 
 def _workspace(device: torch.device, nbytes: int, workspace: Optional[torch.Tensor]):
-    """Caller-provided workspace, or one cached per (device, stream).
-
-    A cached workspace is zero-filled once at allocation; the library leaves
-    it zeroed after every call on that stream.
-    """
+    """Caller-provided workspace, or one cached per (device, stream).  The
+    library needs no initialization of it and keeps nothing in it between
+    calls; calls on one stream may share it."""
     if workspace is not None:
         _check(workspace, "workspace", torch.uint8)
         return workspace
@@ -223,6 +226,40 @@ def spec_verify_relaxed(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
                                  _ptr(blp), _ptr(st), _ptr(ws), ws.numel(), _stream_ptr(dev))
     _raise(rc, "spec_verify_relaxed")
     return VerifyResult(tok, ln, tlp, blp, st)
+
+
+class SampleResult(NamedTuple):
+    tokens: torch.Tensor   # int32 [...]
+    logprob: torch.Tensor  # float32 [...], or None
+    status: torch.Tensor   # int32 [...]
+
+
+def spec_sample_workspace_bytes(rows: int, V: int) -> int:
+    return int(load_library().spec_sample_workspace_bytes(int(rows), int(V)))
+
+
+def spec_sample_drafts(logits: torch.Tensor, uniforms: torch.Tensor, *, logprobs: bool = True,
+                       workspace: Optional[torch.Tensor] = None) -> SampleResult:
+    """Draft-token sampler: one inverse-CDF draw per logit row.  logits
+    [..., V]; uniforms float32 with the leading shape of logits."""
+    lib = load_library()
+    X = _check(logits, "logits")
+    if X.dim() < 1:
+        raise SpecVerifyError("logits must have a vocabulary dimension")
+    lead, V = tuple(X.shape[:-1]), X.shape[-1]
+    rows = 1
+    for d in lead:
+        rows *= d
+    u = _check(uniforms, "uniforms", torch.float32, lead)
+    dev = X.device
+    ws = _workspace(dev, spec_sample_workspace_bytes(rows, V), workspace)
+    tok = torch.empty(lead, dtype=torch.int32, device=dev)
+    st = torch.empty(lead, dtype=torch.int32, device=dev)
+    lq = torch.empty(lead, dtype=torch.float32, device=dev) if logprobs else None
+    rc = lib.spec_sample_drafts(_ptr(X), _dtype_code(X), _ptr(u), rows, V, _ptr(tok), _ptr(lq),
+                                _ptr(st), _ptr(ws), ws.numel(), _stream_ptr(dev))
+    _raise(rc, "spec_sample_drafts")
+    return SampleResult(tok, lq, st)
 
 
 def spec_verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor,

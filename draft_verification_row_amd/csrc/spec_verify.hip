@@ -1287,6 +1287,13 @@ spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
 
 bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
 
+// The draft sampler runs the relaxed path with no drafts: each row is a
+// request whose only row is sampled at its uniform.  Its accept lengths (all
+// zero) go to the workspace after the layout.
+size_t sample_layout_bytes(int rows, int V, spec_dtype dt) {
+    return make_layout(rows, 1, tpr_of(dt, V), c2_of(dt, V)).total + align_up((size_t)rows * 4, 256);
+}
+
 bool sizes_ok(int B, int K, int V, long rows_per_req) {
     if (B < 1 || B > kMaxB || K < 1 || V < 1 || V > SPEC_MAX_V) return false;
     if (rows_per_req < 1 || rows_per_req > kMaxRows) return false;
@@ -1433,6 +1440,43 @@ spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return launch<kRelaxed, true>(a, dtype, st);
+}
+
+size_t spec_sample_workspace_bytes(int rows, int V) {
+    if (rows < 1 || rows > kMaxB || V < 1 || V > SPEC_MAX_V) return 0;
+    return sample_layout_bytes(rows, V, SPEC_F32);  // fp32 bounds both dtypes
+}
+
+spec_status spec_sample_drafts(const void* logits, spec_dtype dtype, const float* uniforms,
+                               int rows, int V, int32_t* out_tokens, float* out_logprob,
+                               int32_t* out_status, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (rows < 1 || rows > kMaxB || V < 1 || V > SPEC_MAX_V) return SPEC_EINVAL;
+    if (!logits || !uniforms || !out_tokens || !out_status) return SPEC_EINVAL;
+    if (!workspace || ((uintptr_t)workspace % 256) != 0 ||
+        workspace_bytes < sample_layout_bytes(rows, V, dtype))
+        return SPEC_EWORKSPACE;
+    Args a = {};
+    a.T = logits;
+    a.u = uniforms;
+    a.B = rows;
+    a.K = 0;
+    a.V = V;
+    a.rows_t = 1;
+    a.R = 1;
+    a.C2 = c2_of(dtype, V);
+    a.vec_t = vec_ok(logits, dtype, V);
+    a.tau = 2.f;  // unused: there is no draft to test
+    a.top_k = 0;
+    a.out_tok = out_tokens;
+    a.out_tlp = out_logprob;
+    a.out_status = out_status;
+    a.L = 1;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.out_len = reinterpret_cast<int32_t*>(
+        a.ws + make_layout(rows, 1, tpr_of(dtype, V), c2_of(dtype, V)).total);
+    return launch<kRelaxed, true>(a, dtype, static_cast<hipStream_t>(stream));
 }
 
 spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,

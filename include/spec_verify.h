@@ -191,6 +191,30 @@ spec_status spec_verify_tree(const void *target_logits, spec_dtype dtype,
                              int32_t *out_status, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * Draft-token sampler: the proposal step that feeds the verifier (spec-decode
+ * README, "How it works": the draft model samples its k tokens from its own
+ * distribution q).  One independent draw per logit row r: the token is the
+ * smallest t whose inclusive prefix of softmax(row r) exceeds uniforms[r]
+ * (ascending token order, fp64 sums), and out_logprob[r] = log q_r(token),
+ * the log-prob the exact rule later reads as log q.  Rows need at least one
+ * finite logit.
+ *
+ *   logits       [rows][V] dtype, e.g. a draft's [B][K][V] logits as B*K rows
+ *   uniforms     [rows] float in [0,1)
+ *   out_tokens   [rows] int32
+ *   out_logprob  [rows] float, or NULL (not written)
+ *   out_status   [rows] int32, always 0
+ * rows <= SPEC_MAX_B; the workspace (256-byte aligned, no initialization) must
+ * hold spec_sample_workspace_bytes(rows, V) bytes.
+ */
+size_t spec_sample_workspace_bytes(int rows, int V);
+
+spec_status spec_sample_drafts(const void *logits, spec_dtype dtype, const float *uniforms,
+                               int rows, int V, int32_t *out_tokens, float *out_logprob,
+                               int32_t *out_status, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif
