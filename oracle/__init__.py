@@ -23,7 +23,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["build", "load", "OracleResult", "OracleSample", "greedy", "exact", "relaxed", "tree",
-           "sample", "row_stats",
+           "power", "sample", "row_stats",
            "set_threads", "max_threads", "EPS_ACCEPT", "EPS_SAMPLE"]
 
 EPS_ACCEPT = 1e-6
@@ -64,6 +64,7 @@ def load():
         lib.oracle_exact.argtypes = [P, P, I, P, P, I, I, I, Dd, Dd, P, P, P, P, P, P, P]
         lib.oracle_relaxed.argtypes = [P, I, P, P, I, I, I, Dd, I, Dd, Dd, P, P, P, P, P, P, P]
         lib.oracle_sample.argtypes = [P, I, P, ctypes.c_long, I, Dd, P, P, P]
+        lib.oracle_power.argtypes = [P, P, I, P, P, I, I, I, Dd, Dd, Dd, P, P, P, P, P, P, P]
         lib.oracle_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, P, P]
         _lib = lib
     return _lib
@@ -164,6 +165,23 @@ def relaxed(target, tokens, uniforms, dtype: str, tau: float, top_k: int,
     load().oracle_relaxed(_ptr(T), _dt(dtype), _ptr(x), _ptr(u), B, K, V, float(tau), int(top_k),
                           float(eps_accept), float(eps_sample), _ptr(tok), _ptr(ln), _ptr(tlp),
                           _ptr(blp), _ptr(st), _ptr(fl), _ptr(dec))
+    return OracleResult(tok, ln, tlp, blp, st, fl, dec)
+
+
+def power(target, draft, tokens, uniforms, dtype: str, alpha: float,
+          eps_accept: float = EPS_ACCEPT, eps_sample: float = EPS_SAMPLE) -> OracleResult:
+    """Power rule: accept iff u_j < min(1, p/q)^alpha; y ~ p_n after a rejection."""
+    T = _logits(target, dtype)
+    D = _logits(draft, dtype)
+    x = _c(tokens, np.int32)
+    u = _c(uniforms, np.float32)
+    B, L, V = T.shape
+    K = L - 1
+    assert D.shape == (B, K, V) and x.shape == (B, K) and u.shape == (B, L)
+    tok, ln, tlp, blp, st, fl, dec = _outs(B, L)
+    load().oracle_power(_ptr(T), _ptr(D), _dt(dtype), _ptr(x), _ptr(u), B, K, V, float(alpha),
+                        float(eps_accept), float(eps_sample), _ptr(tok), _ptr(ln), _ptr(tlp),
+                        _ptr(blp), _ptr(st), _ptr(fl), _ptr(dec))
     return OracleResult(tok, ln, tlp, blp, st, fl, dec)
 
 

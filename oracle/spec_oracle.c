@@ -474,3 +474,91 @@ void oracle_sample(const void *X, int dt, const float *u, long rows, int V, doub
     }
 }
 
+/* ----------------------------------------------------------------- power
+ * Power acceptance (nanospec README, acceptance-rule paragraph: accept with
+ * probability min(1, p/rest)^alpha; stochastic, full support, exact
+ * weights).  Reading: "rest" is the draft probability q, so draft j is
+ * accepted iff u_j < a_j = min(1, p_j(x_j)/q_j(x_j))^alpha; at the first
+ * rejection n the sampler emits y ~ p_n (full support), and at n = K the
+ * bonus y ~ p_K, both by inverse CDF at u_K.  Behaviour log-probs: log a_j
+ * on accepted drafts, log(1 - a_n) + log p_n(y) after a rejection, and
+ * log p_K(y) for the bonus.  alpha = 0 accepts every draft.                */
+static double power_accept(double lp, double lq, double alpha)
+{
+    if (alpha == 0.0)
+        return 1.0;
+    if (lp == -INFINITY)
+        return 0.0;
+    if (lq == -INFINITY)
+        return 1.0;
+    double la = alpha * (lp - lq);
+    return la >= 0.0 ? 1.0 : exp(la);
+}
+
+void oracle_power(const void *T, const void *D, int dt, const int32_t *x, const float *u,
+                  int B, int K, int V, double alpha, double eps_accept, double eps_sample,
+                  int32_t *out_tok, int32_t *out_len, double *out_tlp, double *out_blp,
+                  int32_t *out_status, int32_t *out_flag, int32_t *out_decisions)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        const int L = K + 1;
+        int32_t *tok = out_tok + (size_t)b * L;
+        double *tlp = out_tlp + (size_t)b * L, *blp = out_blp + (size_t)b * L;
+        pad_row(tok, tlp, blp, L);
+        int status = 0, n = K, flag = -1, dec = 0;
+        double an = 0.0;
+        for (int j = 0; j < K; ++j) {
+            int32_t xj = x[(size_t)b * K + j];
+            ++dec;
+            if (xj < 0 || xj >= V) {
+                status = 1;
+                n = j;
+                an = 0.0;
+                break;
+            }
+            size_t trow = (size_t)b * L + j, drow = (size_t)b * K + j;
+            row_stats sp, sq;
+            stats(T, dt, trow, V, &sp);
+            stats(D, dt, drow, V, &sq);
+            double lp = logp(T, dt, trow, V, xj, &sp);
+            double lq = logp(D, dt, drow, V, xj, &sq);
+            double a = power_accept(lp, lq, alpha);
+            double uj = (double)u[(size_t)b * L + j];
+            if (flag < 0 && fabs(uj - a) < eps_accept)
+                flag = j;
+            if (uj < a) {
+                tok[j] = xj;
+                tlp[j] = lp;
+                blp[j] = log(a);
+            } else {
+                n = j;
+                an = a;
+                break;
+            }
+        }
+        size_t row = (size_t)b * L + n;
+        row_stats sp;
+        stats(T, dt, row, V, &sp);
+        double *w = (double *)malloc(sizeof(double) * (size_t)V);
+        double Z = 0.0;
+        for (int t = 0; t < V; ++t) {
+            w[t] = exp(logp(T, dt, row, V, t, &sp));
+            Z += w[t];
+        }
+        double lo, hi, target = (double)u[(size_t)b * L + K] * Z;
+        long y = inverse_cdf(w, V, target, &lo, &hi);
+        ++dec;
+        if (flag < 0 && sample_flag(target, lo, hi, Z, eps_sample))
+            flag = n;
+        tok[n] = (int32_t)y;
+        tlp[n] = logp(T, dt, row, V, y, &sp);
+        blp[n] = (n < K) ? log1p(-an) + tlp[n] : tlp[n];
+        free(w);
+        out_len[b] = n;
+        out_status[b] = status;
+        out_flag[b] = flag;
+        out_decisions[b] = dec;
+    }
+}
+

@@ -47,6 +47,13 @@ void oracle_tree(const void *T, int dt, const int32_t *node_tok, const int32_t *
                  int32_t *out_path, int32_t *out_tok, int32_t *out_len, double *out_tlp,
                  double *out_blp, int32_t *out_status);
 
+/* power rule: as oracle_exact's shapes, accept iff u_j < min(1, p/q)^alpha;
+ * after a rejection n the sample is y ~ p_n */
+void oracle_power(const void *T, const void *D, int dt, const int32_t *x, const float *u,
+                  int B, int K, int V, double alpha, double eps_accept, double eps_sample,
+                  int32_t *out_tok, int32_t *out_len, double *out_tlp, double *out_blp,
+                  int32_t *out_status, int32_t *out_flag, int32_t *out_decisions);
+
 /* X [rows][V]; u [rows]; out_tok, out_logq, out_flag [rows]: one inverse-CDF
  * draw per row and its log-prob; flag 1 when u*Z lies within eps_sample*Z
  * of a CDF boundary */

@@ -536,3 +536,64 @@ def test_sampler_special_cases(orc):
     r = orc.sample(e, u, "f32")
     assert list(r.tokens) == [int(math.floor(float(v) * 10)) for v in u]
     np.testing.assert_allclose(r.logq, -math.log(10.0), rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- power rule
+# nanospec README, acceptance-rule paragraph: accept with probability
+# min(1, p/rest)^alpha.  Reading: rest = q; after a rejection y ~ p_n.
+def test_power_alpha_one_accepts_like_exact(orc):
+    """alpha = 1 gives min(1, p/q): the exact rule's acceptance tests."""
+    ci = synth.chain_inputs(64, 4, 300, "f32", seed=81, useed=82)
+    pw = orc.power(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32", 1.0)
+    ex = orc.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32")
+    assert (pw.accept_len == ex.accept_len).all()
+    for b in range(64):
+        n = int(pw.accept_len[b])
+        assert (pw.tokens[b, :n] == ex.tokens[b, :n]).all()
+        np.testing.assert_allclose(pw.behavior_logprob[b, :n], ex.behavior_logprob[b, :n], atol=1e-12)
+
+
+def test_power_alpha_zero_accepts_everything(orc):
+    """alpha = 0 makes every acceptance probability 1: all K drafts, then the
+    bonus drawn from p_K as by the relaxed rule with tau <= 0."""
+    ci = synth.chain_inputs(32, 3, 200, "f32", seed=83, useed=84)
+    pw = orc.power(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32", 0.0)
+    rx = orc.relaxed(ci.target, ci.tokens, ci.uniforms, "f32", tau=-1.0, top_k=0)
+    assert (pw.accept_len == 3).all()
+    assert (pw.tokens == rx.tokens).all()
+    np.testing.assert_allclose(pw.target_logprob, rx.target_logprob, atol=1e-12)
+    assert (pw.behavior_logprob[:, :3] == 0).all()
+
+
+@pytest.mark.parametrize("alpha", [0.5, 2.0])
+def test_power_first_token_law_brute_force(orc, alpha):
+    """K = 1, V = 5: enumerate the draft token x (weight q(x)) and a midpoint
+    grid of (u_0, u_1).  The first emitted token's law is
+    q(t) a(t) + p(t) (1 - sum_x q(x) a(x)), with a = min(1, p/q)^alpha, and the
+    accept rate given x is a(x); both to within the grid's breakpoints."""
+    rng = np.random.default_rng(85)
+    V, M = 5, 160
+    t_log = rng.standard_normal(V).astype(np.float32)
+    d_log = (t_log + 0.8 * rng.standard_normal(V)).astype(np.float32)
+    p = softmax64(t_log.astype(np.float64))
+    q = softmax64(d_log.astype(np.float64))
+    a = np.minimum(1.0, (p / q) ** alpha)
+    g = (np.arange(M) + 0.5) / M
+    u0, u1 = np.meshgrid(g, g, indexing="ij")
+    U = np.stack([u0.ravel(), u1.ravel()], 1).astype(np.float32)
+    B = U.shape[0]
+    T = np.broadcast_to(t_log, (B, 2, V)).copy()
+    D = np.broadcast_to(d_log, (B, 1, V)).copy()
+    law = np.zeros(V)
+    for x in range(V):
+        r = orc.power(T, D, np.full((B, 1), x, np.int32), U, "f32", alpha)
+        first = r.tokens[:, 0]
+        law += q[x] * np.bincount(first, minlength=V) / B
+        acc = (r.accept_len == 1).mean()
+        assert abs(acc - a[x]) <= 1.0 / M + 1e-12, (x, acc, a[x])
+        rej = r.accept_len == 0
+        # after a rejection the token follows p
+        np.testing.assert_allclose(np.bincount(first[rej], minlength=V) / B, (1 - acc) * p,
+                                   atol=(V + 1) / M)
+    want = q * a + p * (1.0 - np.sum(q * a))
+    assert np.abs(law - want).max() <= (V + 1) / M, (law, want)
