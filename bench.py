@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+POWER_ALPHA = 0.5  # exponent of the power-rule measurement
 KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_verify.hip")
 
 # HBM traffic of one exact-mode streaming-kernel dispatch on this workload,
@@ -119,14 +120,14 @@ class Case:
         src = ci.draft if mode == "sample" else ci.target
         T0 = torch.from_numpy(src.view(int16)).view(torch.bfloat16).to(dev)
         D0 = (torch.from_numpy(ci.draft.view(int16)).view(torch.bfloat16).to(dev)
-              if mode == "exact" else None)
+              if mode in ("exact", "power") else None)
         x0 = torch.from_numpy(ci.tokens).to(dev)
         u0 = torch.from_numpy(ci.uniforms).to(dev)
         if mode == "sample":
             u0 = torch.from_numpy(ci.uniforms[:, :K].copy()).to(dev)
             nbytes = sv.spec_sample_workspace_bytes(B * K, V)
         else:
-            rows = 2 * K + 1 if mode == "exact" else K + 1
+            rows = 2 * K + 1 if mode in ("exact", "power") else K + 1
             nbytes = sv.spec_verify_workspace_bytes(B, rows, V)
         self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         self.inputs, self.outputs = [], []
@@ -143,7 +144,7 @@ class Case:
             out = dict(tok=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
                        ln=torch.empty(B, dtype=torch.int32, device=dev),
                        st=torch.empty(B, dtype=torch.int32, device=dev))
-            if mode == "exact":
+            if mode in ("exact", "power"):
                 out["tlp"] = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
                 out["blp"] = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
             self.outputs.append(out)
@@ -160,6 +161,11 @@ class Case:
             return (P(T.data_ptr()), 1, P(u.data_ptr()), B * K, V, P(o["tok"].data_ptr()),
                     P(o["lq"].data_ptr()), P(o["st"].data_ptr()), P(ws.data_ptr()), ws.numel(),
                     P(stream))
+        if self.mode == "power":
+            return (P(T.data_ptr()), P(D.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K,
+                    V, ctypes.c_float(POWER_ALPHA), P(o["tok"].data_ptr()), P(o["ln"].data_ptr()),
+                    P(o["tlp"].data_ptr()), P(o["blp"].data_ptr()), P(o["st"].data_ptr()),
+                    P(ws.data_ptr()), ws.numel(), P(stream))
         if self.mode == "exact":
             return (P(T.data_ptr()), P(D.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K,
                     V, P(o["tok"].data_ptr()), P(o["ln"].data_ptr()), P(o["tlp"].data_ptr()),
@@ -171,7 +177,7 @@ class Case:
 
     def fn(self):
         return {"exact": self.lib.spec_verify_exact, "greedy": self.lib.spec_verify_greedy,
-                "sample": self.lib.spec_sample_drafts}[self.mode]
+                "sample": self.lib.spec_sample_drafts, "power": self.lib.spec_verify_power}[self.mode]
 
     def run(self, n, start=0, stream=None):
         torch = self.torch
@@ -298,6 +304,9 @@ def main():
 
     lib = sv.load_library()
     lib.spec_verify_profile_next_call.argtypes = [ctypes.c_void_p] * 3
+    lib.spec_verify_power.argtypes = ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_float] +
+                                      [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p])
     lib.spec_sample_drafts.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -318,6 +327,9 @@ def main():
     gr = Case(lib, "greedy", ci, sets_greedy, torch, dev)
     r_gr = time_case(gr, args.steps, args.warmup, hip, use_graph)
     del gr
+    pw = Case(lib, "power", ci, sets_exact, torch, dev)
+    r_pw = time_case(pw, args.steps, args.warmup, hip, use_graph)
+    del pw
     sets_sample = math.ceil(2 * MALL_BYTES / ci.draft.nbytes)
     sa = Case(lib, "sample", ci, sets_sample, torch, dev)
     r_sa = time_case(sa, args.steps, args.warmup, hip, use_graph)
@@ -332,6 +344,7 @@ def main():
     achieved = stream_bytes / (k_ms * 1e-3) / 1e9
     g_ms = r_gr["graph_ms_per_step"] if use_graph else r_gr["eager_ms_per_step"]
     s_ms = r_sa["graph_ms_per_step"] if use_graph else r_sa["eager_ms_per_step"]
+    p_ms = r_pw["graph_ms_per_step"] if use_graph else r_pw["eager_ms_per_step"]
     out = {
         "metric": METRIC,
         "value": value,
@@ -368,6 +381,12 @@ def main():
             "rest_of_call_us_mean": r_gr["rest_ms_mean"] * 1e3,
             "eager_rounds_per_s": 1000.0 / r_gr["eager_ms_per_step"],
             "algorithmic_bytes": bytes_greedy, "input_sets": sets_greedy},
+        "power_c3": {
+            "alpha": POWER_ALPHA, "rounds_per_s": 1000.0 / p_ms, "ms_per_step": p_ms,
+            "hbm_gbs_call": bytes_exact / (p_ms * 1e-3) / 1e9,
+            "kernel_us_mean": r_pw["kernel_ms_mean"] * 1e3,
+            "kernel_gbs": stream_bytes / (r_pw["kernel_ms_mean"] * 1e-3) / 1e9,
+            "rest_of_call_us_mean": r_pw["rest_ms_mean"] * 1e3, "input_sets": sets_exact},
         "draft_sampler_c3_draft_rows": {
             "calls_per_s": 1000.0 / s_ms, "ms_per_call": s_ms, "rows": ci.B * ci.K,
             "hbm_gbs_call": ci.draft.nbytes / (s_ms * 1e-3) / 1e9,

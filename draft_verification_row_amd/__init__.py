@@ -17,7 +17,7 @@ from typing import NamedTuple, Optional
 import torch
 
 __all__ = ["spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed", "spec_verify_tree",
-           "spec_sample_drafts", "spec_verify_workspace_bytes", "spec_sample_workspace_bytes",
+           "spec_verify_power", "spec_sample_drafts", "spec_verify_workspace_bytes", "spec_sample_workspace_bytes",
            "VerifyResult", "TreeResult", "SampleResult", "SpecVerifyError",
            "library_path", "load_library", "SPEC_MAX_K", "SPEC_MAX_NODES"]
 
@@ -56,11 +56,12 @@ def load_library():
     lib.spec_verify_exact.argtypes = [P, P, I, P, P, I, I, I, P, P, P, P, P, P, Z, P]
     lib.spec_verify_relaxed.argtypes = [P, I, P, P, I, I, I, F, I, P, P, P, P, P, P, Z, P]
     lib.spec_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, P, P, P, Z, P]
+    lib.spec_verify_power.argtypes = [P, P, I, P, P, I, I, I, F, P, P, P, P, P, P, Z, P]
     lib.spec_sample_workspace_bytes.argtypes = [I, I]
     lib.spec_sample_workspace_bytes.restype = Z
     lib.spec_sample_drafts.argtypes = [P, I, P, I, I, P, P, P, P, Z, P]
     for fn in ("spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed", "spec_verify_tree",
-               "spec_sample_drafts"):
+               "spec_verify_power", "spec_sample_drafts"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -202,6 +203,30 @@ def spec_verify_exact(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                                _ptr(tok), _ptr(ln), _ptr(tlp), _ptr(blp), _ptr(st), _ptr(ws),
                                ws.numel(), _stream_ptr(dev))
     _raise(rc, "spec_verify_exact")
+    return VerifyResult(tok, ln, tlp, blp, st)
+
+
+def spec_verify_power(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                      draft_tokens: torch.Tensor, uniforms: torch.Tensor, alpha: float, *,
+                      logprobs: bool = True, workspace: Optional[torch.Tensor] = None
+                      ) -> VerifyResult:
+    """Power rule: accept iff u_j < min(1, p/q)^alpha; y ~ p_n after a rejection."""
+    lib = load_library()
+    T = _check(target_logits, "target_logits")
+    if T.dim() != 3:
+        raise SpecVerifyError("target_logits must be [B][K+1][V]")
+    B, L, V = T.shape
+    K = L - 1
+    D = _check(draft_logits, "draft_logits", T.dtype, (B, K, V))
+    x = _check(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    u = _check(uniforms, "uniforms", torch.float32, (B, L))
+    dev = T.device
+    ws = _workspace(dev, spec_verify_workspace_bytes(B, 2 * K + 1, V), workspace)
+    tok, ln, tlp, blp, st = _outs(B, L, dev, logprobs)
+    rc = lib.spec_verify_power(_ptr(T), _ptr(D), _dtype_code(T), _ptr(x), _ptr(u), B, K, V,
+                               ctypes.c_float(alpha), _ptr(tok), _ptr(ln), _ptr(tlp), _ptr(blp),
+                               _ptr(st), _ptr(ws), ws.numel(), _stream_ptr(dev))
+    _raise(rc, "spec_verify_power")
     return VerifyResult(tok, ln, tlp, blp, st)
 
 

@@ -86,7 +86,10 @@ static_assert(kMaxTiles <= 64, "a row's tile records must fit one wave");
 constexpr int kMaxC2 = (SPEC_MAX_V + kChunk - 1) / kChunk;
 static_assert(kMaxC2 <= 64, "a row's pass-2 chunks must fit one wave");
 
-enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3 };
+enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3, kPower = 4 };
+
+// Rules that stream the draft rows and test p/q.
+constexpr bool uses_draft(int mode) { return mode == kExact || mode == kPower; }
 
 // Statistics of one tile: max m, then the lowest index of the max (greedy,
 // tree) or the rank count (relaxed), and s = sum over the tile of
@@ -479,6 +482,7 @@ struct Args {
     int C2;      // pass-2 chunks per row
     int vec_t, vec_d;
     float tau;
+    float alpha;  // power rule exponent
     int top_k;
     int32_t* out_tok;
     int32_t* out_len;
@@ -509,7 +513,7 @@ __device__ inline const T* call_row(const Args& a, int g, int& vec, int& active)
     const int b = g / a.R, rr = g - (g / a.R) * a.R;
     active = 1;
     if (MODE == kTree && a.num_nodes) active = uniform(rr < min(max(a.num_nodes[b], 1), a.rows_t));
-    if (MODE == kExact && rr >= a.rows_t) {
+    if (uses_draft(MODE) && rr >= a.rows_t) {
         vec = a.vec_d;
         return uniform_ptr(reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + (rr - a.rows_t)) * a.V);
     }
@@ -750,7 +754,7 @@ __device__ inline void chain_load_tokens(const Args& a, int b, ChainVals& cv) {
     cv.u = 0.f;
     if (j < a.K) {
         cv.x = a.tok[b * a.K + j];
-        if (MODE == kExact) cv.u = a.u[b * (a.K + 1) + j];
+        if (uses_draft(MODE)) cv.u = a.u[b * (a.K + 1) + j];
     }
 }
 
@@ -763,7 +767,7 @@ __device__ inline void chain_load_values(const Args& a, int b, ChainVals& cv) {
         cv.bad = (unsigned)cv.x >= (unsigned)a.V;
         if (!cv.bad && MODE != kGreedy) {
             cv.lx = Elem<T>::at(reinterpret_cast<const T*>(a.T), (size_t)(b * a.rows_t + j) * a.V + cv.x);
-            if (MODE == kExact)
+            if (uses_draft(MODE))
                 cv.dx = Elem<T>::at(reinterpret_cast<const T*>(a.D), (size_t)(b * a.K + j) * a.V + cv.x);
         }
     }
@@ -772,7 +776,7 @@ __device__ inline void chain_load_values(const Args& a, int b, ChainVals& cv) {
 struct ChainDecision {
     int n, bad_n;
     int x[64];
-    double lp[64], lq[64], r[64];
+    double lp[64], lq[64], r[64], la[64];  // la: log acceptance probability (power)
 };
 
 // Wave 0: lane j < K evaluates the test of draft j in fp64; a ballot finds
@@ -781,7 +785,7 @@ template <int MODE>
 __device__ void chain_decide(const Args& a, const RowStats& rs, const ChainVals& cv, ChainDecision& cd) {
     const int j = threadIdx.x, K = a.K;
     bool acc = false;
-    double lp = 0.0, lq = 0.0, r = 0.0;  // a malformed token is rejected outright
+    double lp = 0.0, lq = 0.0, r = 0.0, la = -INFINITY;  // a malformed token is rejected outright
     if (j < K && !cv.bad) {
         if (MODE == kGreedy) {
             acc = (cv.x == rs.g[j]);
@@ -797,6 +801,19 @@ __device__ void chain_decide(const Args& a, const RowStats& rs, const ChainVals&
                 else
                     r = exp(lp - lq);
                 acc = (double)cv.u < r;
+            } else if (MODE == kPower) {
+                // accept with probability a = min(1, p/q)^alpha (alpha = 0:
+                // always); r holds a, la its log
+                lq = ((double)cv.dx - (double)rs.M[a.rows_t + j]) - rs.lnS[a.rows_t + j];
+                const double al = (double)a.alpha;
+                if (al == 0.0 || (lq == -INFINITY && lp > -INFINITY))
+                    la = 0.0;
+                else if (lp == -INFINITY)
+                    la = -INFINITY;
+                else
+                    la = fmin(0.0, al * (lp - lq));
+                r = exp(la);
+                acc = (double)cv.u < r;
             } else {
                 acc = (rs.c[j] < a.top_k) || (exp(lp) >= (double)a.tau);
             }
@@ -808,6 +825,7 @@ __device__ void chain_decide(const Args& a, const RowStats& rs, const ChainVals&
     cd.lp[j] = lp;
     cd.lq[j] = lq;
     cd.r[j] = r;
+    cd.la[j] = la;
     if (j == n) {
         cd.n = n;
         cd.bad_n = (n < K && cv.bad) ? 1 : 0;
@@ -826,7 +844,9 @@ __device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
         if (j < n) {
             otok[j] = cd.x[j];
             if (otlp) otlp[j] = (float)cd.lp[j];
-            if (oblp) oblp[j] = (MODE == kExact) ? (float)fmin(0.0, cd.lp[j] - cd.lq[j]) : 0.f;
+            if (oblp)
+                oblp[j] = (MODE == kExact) ? (float)fmin(0.0, cd.lp[j] - cd.lq[j])
+                                           : (MODE == kPower ? (float)cd.la[j] : 0.f);
         } else if (j > n) {
             otok[j] = -1;
             if (otlp) otlp[j] = 0.f;
@@ -944,9 +964,9 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
 // decision and the sweep; chunk 0 also writes the accepted prefix and the
 // decision record.  Each workgroup then sums its chunk of the row(s) the
 // terminal token is drawn from, in fp64.
-template <typename T, bool EXACT>
+template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Args a) {
-    constexpr int MODE = EXACT ? kExact : kRelaxed;
+    constexpr bool EXACT = (MODE == kExact);
     constexpr int VEC = Elem<T>::kVec;
     constexpr int NV = kRun / VEC;  // 16-byte vectors per thread per chunk
 
@@ -1051,8 +1071,9 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Ar
 // relu(p - q) (or of p), scans them and finds the chunk holding u_K * Z; the
 // workgroup (1024 threads, four consecutive tokens each) then rescans that
 // chunk with a block scan and writes the terminal token and its log-probs.
-template <typename T, bool EXACT>
+template <typename T, int MODE>
 __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
+    constexpr bool EXACT = (MODE == kExact);
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -1209,7 +1230,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
         const int L = a.L;
         a.out_tok[(size_t)b * L + n] = y;
         const double tlp = ((double)ly - Mt) - s_lnS;
-        const double blp = res ? s_l1r + log(wy) - s_lnZ : tlp;
+        // behaviour log-prob: residual draw, power-rule fallback after a
+        // rejection (1 - a_n) p_n(y), or a plain draw from p
+        const double blp = res ? s_l1r + log(wy) - s_lnZ
+                               : ((MODE == kPower && n < a.K) ? log1p(-dc.rn) + tlp : tlp);
         if (a.out_tlp) a.out_tlp[(size_t)b * L + n] = (float)tlp;
         if (a.out_blp) a.out_blp[(size_t)b * L + n] = (float)blp;
     }
@@ -1249,7 +1273,7 @@ spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
     hipEvent_t ev[3] = {g_prof[0], g_prof[1], g_prof[2]};
     g_prof[0] = g_prof[1] = g_prof[2] = nullptr;
     const dim3 grid((unsigned)a.B * (unsigned)a.R * (unsigned)a.tpr), block(kThreads);
-    const bool vecp = a.vec_t && (MODE != kExact || a.vec_d);
+    const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
     if (dt == SPEC_BF16) {
         if (vecp)
             hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
@@ -1268,16 +1292,15 @@ spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
         else
             hipLaunchKernelGGL((k_decide<float, MODE, SUM>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
     } else {
-        constexpr bool EXACT = (MODE == kExact);
         const dim3 grid2((unsigned)a.B * (unsigned)a.C2);
         if (dt == SPEC_BF16) {
-            hipLaunchKernelGGL((k_sweep<uint16_t, EXACT>), grid2, block, 0, st, a);
+            hipLaunchKernelGGL((k_sweep<uint16_t, MODE>), grid2, block, 0, st, a);
             if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-            hipLaunchKernelGGL((k_sample<uint16_t, EXACT>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
+            hipLaunchKernelGGL((k_sample<uint16_t, MODE>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
         } else {
-            hipLaunchKernelGGL((k_sweep<float, EXACT>), grid2, block, 0, st, a);
+            hipLaunchKernelGGL((k_sweep<float, MODE>), grid2, block, 0, st, a);
             if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-            hipLaunchKernelGGL((k_sample<float, EXACT>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
+            hipLaunchKernelGGL((k_sample<float, MODE>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
         }
     }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
@@ -1440,6 +1463,44 @@ spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return launch<kRelaxed, true>(a, dtype, st);
+}
+
+spec_status spec_verify_power(const void* target_logits, const void* draft_logits,
+                              spec_dtype dtype, const int32_t* draft_tokens, const float* uniforms,
+                              int B, int K, int V, float alpha, int32_t* out_tokens,
+                              int32_t* out_accept_len, float* out_target_logprob,
+                              float* out_behavior_logprob, int32_t* out_status, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !sizes_ok(B, K, V, 2 * K + 1)) return SPEC_EINVAL;
+    if (!(alpha >= 0.f) || alpha == INFINITY) return SPEC_EINVAL;
+    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
+        !out_accept_len || !out_status)
+        return SPEC_EINVAL;
+    const spec_status ws = check_ws(workspace, workspace_bytes, B, 2 * K + 1, V, dtype);
+    if (ws != SPEC_OK) return ws;
+    Args a = {};
+    a.T = target_logits;
+    a.D = draft_logits;
+    a.tok = draft_tokens;
+    a.u = uniforms;
+    a.B = B;
+    a.K = K;
+    a.V = V;
+    a.rows_t = K + 1;
+    a.R = 2 * K + 1;
+    a.C2 = c2_of(dtype, V);
+    a.vec_t = vec_ok(target_logits, dtype, V);
+    a.vec_d = vec_ok(draft_logits, dtype, V);
+    a.alpha = alpha;
+    a.out_tok = out_tokens;
+    a.out_len = out_accept_len;
+    a.out_tlp = out_target_logprob;
+    a.out_blp = out_behavior_logprob;
+    a.out_status = out_status;
+    a.L = K + 1;
+    a.ws = static_cast<unsigned char*>(workspace);
+    return launch<kPower, true>(a, dtype, static_cast<hipStream_t>(stream));
 }
 
 size_t spec_sample_workspace_bytes(int rows, int V) {

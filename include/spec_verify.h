@@ -192,6 +192,27 @@ spec_status spec_verify_tree(const void *target_logits, spec_dtype dtype,
                              void *stream);
 
 /*
+ * Power acceptance (nanospec README, acceptance rules: accept with
+ * probability min(1, p/rest)^alpha; stochastic, full support, exact
+ * weights).  Reading of "rest": the draft probability q, so draft x_j is
+ * accepted iff uniforms[b][j] < a_j = min(1, p_j(x_j)/q_j(x_j))^alpha, in
+ * order.  At the first rejection n the sampler emits y ~ p_n (the target row:
+ * full support); if all K are accepted it emits y ~ p_K; both by inverse CDF
+ * at uniforms[b][K].  Behaviour log-probs: log a_j for accepted drafts,
+ * log(1 - a_n) + log p_n(y) after a rejection, log p_K(y) for the bonus.
+ * alpha = 1 accepts exactly as spec_verify_exact (only the draw after a
+ * rejection differs); alpha = 0 accepts every draft.  alpha must be finite
+ * and >= 0.  Shapes, outputs and workspace (rows_per_request 2K+1) as for
+ * spec_verify_exact.
+ */
+spec_status spec_verify_power(const void *target_logits, const void *draft_logits,
+                              spec_dtype dtype, const int32_t *draft_tokens, const float *uniforms,
+                              int B, int K, int V, float alpha, int32_t *out_tokens,
+                              int32_t *out_accept_len, float *out_target_logprob,
+                              float *out_behavior_logprob, int32_t *out_status, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
  * Draft-token sampler: the proposal step that feeds the verifier (spec-decode
  * README, "How it works": the draft model samples its k tokens from its own
  * distribution q).  One independent draw per logit row r: the token is the

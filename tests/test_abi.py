@@ -115,3 +115,25 @@ def test_header_has_no_torch_or_hip_types():
     src = open(HEADER).read()
     assert "torch" not in src.lower().replace("torch tensors", "")
     assert "#include <hip" not in src
+
+
+def test_power_and_sampler_argument_errors(lib):
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    need = lib.spec_verify_workspace_bytes(2, 7, 100)
+    F = ctypes.c_float
+    # power: negative, NaN and infinite alpha; missing draft logits
+    for alpha in (-0.5, float("nan"), float("inf")):
+        assert lib.spec_verify_power(p, p, 1, p, p, 2, 3, 100, F(alpha), p, p, None, None, p, ws,
+                                     need, None) == SPEC_EINVAL
+    assert lib.spec_verify_power(p, None, 1, p, p, 2, 3, 100, F(1.0), p, p, None, None, p, ws, need,
+                                 None) == SPEC_EINVAL
+    assert lib.spec_verify_power(p, p, 1, p, p, 2, 3, 100, F(1.0), p, p, None, None, p, ws, 64,
+                                 None) == SPEC_EWORKSPACE
+    # sampler: bad rows, missing uniforms, small workspace
+    wsz = lib.spec_sample_workspace_bytes(10, 100)
+    assert wsz > 0 and lib.spec_sample_workspace_bytes(0, 100) == 0
+    assert lib.spec_sample_drafts(p, 1, p, 0, 100, p, None, p, ws, wsz, None) == SPEC_EINVAL
+    assert lib.spec_sample_drafts(p, 1, None, 10, 100, p, None, p, ws, wsz, None) == SPEC_EINVAL
+    assert lib.spec_sample_drafts(p, 1, p, 10, 100, p, None, p, ws, wsz - 256, None) == SPEC_EWORKSPACE
+
