@@ -18,7 +18,7 @@ calls; its algorithmic bytes (every logit read once) divided by that duration
 give the roofline figure.  The fp64 CPU oracle is
 timed on a bounded sample of the same workload on the host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counters
 """
 from __future__ import annotations
@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true", help="time the eager loop only")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (greedy B=8, tree, relaxed/exact B=64)")
     return ap.parse_args()
 
 
@@ -110,17 +112,41 @@ def copy_calibration():
 
 
 class Case:
-    """Resident input sets and prebuilt C-call arguments for one entry point."""
+    """Resident input sets and prebuilt C-call arguments for one entry point.
+
+    mode: exact, power, greedy or relaxed (chain inputs), sample (the draft
+    rows of chain inputs), tree (tree inputs)."""
 
     def __init__(self, lib, mode, ci, sets, torch, dev):
         import draft_verification_row_amd as sv
         from numpy import int16
         self.lib, self.mode, self.ci, self.sets = lib, mode, ci, sets
+        self.torch = torch
+
+        def logits(a):
+            return torch.from_numpy(a.view(int16)).view(torch.bfloat16).to(dev)
+
+        def i32(shape):
+            return torch.empty(shape, dtype=torch.int32, device=dev)
+
+        def f32(shape):
+            return torch.empty(shape, dtype=torch.float32, device=dev)
+
+        self.inputs, self.outputs = [], []
+        if mode == "tree":
+            B, N, V = ci.B, ci.N, ci.V
+            T0 = logits(ci.target)
+            small = [torch.from_numpy(a).to(dev) for a in (ci.node_tok, ci.parents, ci.num_nodes)]
+            self.ws = torch.zeros(sv.spec_verify_workspace_bytes(B, N, V), dtype=torch.uint8,
+                                  device=dev)
+            for s in range(sets):
+                self.inputs.append((T0.clone(), *[a.clone() for a in small]))
+                self.outputs.append(dict(path=i32((B, N)), tok=i32((B, N)), ln=i32(B), st=i32(B)))
+            del T0
+            return
         B, K, V = ci.B, ci.K, ci.V
-        src = ci.draft if mode == "sample" else ci.target
-        T0 = torch.from_numpy(src.view(int16)).view(torch.bfloat16).to(dev)
-        D0 = (torch.from_numpy(ci.draft.view(int16)).view(torch.bfloat16).to(dev)
-              if mode in ("exact", "power") else None)
+        T0 = logits(ci.draft if mode == "sample" else ci.target)
+        D0 = logits(ci.draft) if mode in ("exact", "power") else None
         x0 = torch.from_numpy(ci.tokens).to(dev)
         u0 = torch.from_numpy(ci.uniforms).to(dev)
         if mode == "sample":
@@ -130,53 +156,53 @@ class Case:
             rows = 2 * K + 1 if mode in ("exact", "power") else K + 1
             nbytes = sv.spec_verify_workspace_bytes(B, rows, V)
         self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-        self.inputs, self.outputs = [], []
         for s in range(sets):
-            T = T0.clone()
             D = D0.clone() if D0 is not None else None
-            self.inputs.append((T, D, x0.clone(), u0.clone()))
+            self.inputs.append((T0.clone(), D, x0.clone(), u0.clone()))
             if mode == "sample":
-                out = dict(tok=torch.empty((B, K), dtype=torch.int32, device=dev),
-                           lq=torch.empty((B, K), dtype=torch.float32, device=dev),
-                           st=torch.empty((B, K), dtype=torch.int32, device=dev))
-                self.outputs.append(out)
+                self.outputs.append(dict(tok=i32((B, K)), lq=f32((B, K)), st=i32((B, K))))
                 continue
-            out = dict(tok=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
-                       ln=torch.empty(B, dtype=torch.int32, device=dev),
-                       st=torch.empty(B, dtype=torch.int32, device=dev))
-            if mode in ("exact", "power"):
-                out["tlp"] = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
-                out["blp"] = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
+            out = dict(tok=i32((B, K + 1)), ln=i32(B), st=i32(B))
+            if mode in ("exact", "power", "relaxed"):
+                out["tlp"] = f32((B, K + 1))
+                out["blp"] = f32((B, K + 1))
             self.outputs.append(out)
         del T0, D0
-        self.torch = torch
 
     def args(self, s, stream):
+        P = ctypes.c_void_p
+        o = self.outputs[s]
+        ws = self.ws
+        if self.mode == "tree":
+            B, N, V = self.ci.B, self.ci.N, self.ci.V
+            T, nt, par, nn = self.inputs[s]
+            return (P(T.data_ptr()), 1, P(nt.data_ptr()), P(par.data_ptr()), P(nn.data_ptr()), B,
+                    N, V, P(o["path"].data_ptr()), P(o["tok"].data_ptr()), P(o["ln"].data_ptr()),
+                    None, None, P(o["st"].data_ptr()), P(ws.data_ptr()), ws.numel(), P(stream))
         B, K, V = self.ci.B, self.ci.K, self.ci.V
         T, D, x, u = self.inputs[s]
-        o = self.outputs[s]
-        P = ctypes.c_void_p
-        ws = self.ws
         if self.mode == "sample":
             return (P(T.data_ptr()), 1, P(u.data_ptr()), B * K, V, P(o["tok"].data_ptr()),
                     P(o["lq"].data_ptr()), P(o["st"].data_ptr()), P(ws.data_ptr()), ws.numel(),
                     P(stream))
+        tail = (P(o["st"].data_ptr()), P(ws.data_ptr()), ws.numel(), P(stream))
+        if self.mode == "greedy":
+            return (P(T.data_ptr()), 1, P(x.data_ptr()), B, K, V, P(o["tok"].data_ptr()),
+                    P(o["ln"].data_ptr()), None, None) + tail
+        outs = (P(o["tok"].data_ptr()), P(o["ln"].data_ptr()), P(o["tlp"].data_ptr()),
+                P(o["blp"].data_ptr()))
+        if self.mode == "relaxed":
+            return ((P(T.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K, V,
+                     ctypes.c_float(self.ci.tau), self.ci.top_k) + outs + tail)
         if self.mode == "power":
-            return (P(T.data_ptr()), P(D.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K,
-                    V, ctypes.c_float(POWER_ALPHA), P(o["tok"].data_ptr()), P(o["ln"].data_ptr()),
-                    P(o["tlp"].data_ptr()), P(o["blp"].data_ptr()), P(o["st"].data_ptr()),
-                    P(ws.data_ptr()), ws.numel(), P(stream))
-        if self.mode == "exact":
-            return (P(T.data_ptr()), P(D.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K,
-                    V, P(o["tok"].data_ptr()), P(o["ln"].data_ptr()), P(o["tlp"].data_ptr()),
-                    P(o["blp"].data_ptr()), P(o["st"].data_ptr()), P(ws.data_ptr()), ws.numel(),
-                    P(stream))
-        return (P(T.data_ptr()), 1, P(x.data_ptr()), B, K, V, P(o["tok"].data_ptr()),
-                P(o["ln"].data_ptr()), None, None, P(o["st"].data_ptr()), P(ws.data_ptr()),
-                ws.numel(), P(stream))
+            return ((P(T.data_ptr()), P(D.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K,
+                     V, ctypes.c_float(POWER_ALPHA)) + outs + tail)
+        return ((P(T.data_ptr()), P(D.data_ptr()), 1, P(x.data_ptr()), P(u.data_ptr()), B, K, V) +
+                outs + tail)
 
     def fn(self):
         return {"exact": self.lib.spec_verify_exact, "greedy": self.lib.spec_verify_greedy,
+                "relaxed": self.lib.spec_verify_relaxed, "tree": self.lib.spec_verify_tree,
                 "sample": self.lib.spec_sample_drafts, "power": self.lib.spec_verify_power}[self.mode]
 
     def run(self, n, start=0, stream=None):
@@ -253,6 +279,27 @@ def time_case(case, steps, warmup, hip, use_graph):
     hip.destroy(a)
     hip.destroy(b)
     return res
+
+
+def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, torch, dev):
+    """Call rate and streaming-kernel rate of one more workload."""
+    sets = math.ceil(2 * MALL_BYTES / nbytes)
+    case = Case(lib, mode, ci, sets, torch, dev)
+    r = time_case(case, steps, warmup, hip, use_graph)
+    del case
+    torch.cuda.synchronize()
+    ms = r["graph_ms_per_step"] if use_graph else r["eager_ms_per_step"]
+    logit_bytes = ci.target.nbytes + (ci.draft.nbytes if mode == "exact" else 0)
+    return {"workload": label, "entry_point": f"spec_verify_{mode}",
+            "rounds_per_s": 1000.0 / ms, "us_per_call": ms * 1e3,
+            "hbm_gbs_call": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac_call": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_us_mean": r["kernel_ms_mean"] * 1e3,
+            "kernel_gbs": logit_bytes / (r["kernel_ms_mean"] * 1e-3) / 1e9,
+            "kernel_frac": logit_bytes / (r["kernel_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "rest_of_call_us_mean": r["rest_ms_mean"] * 1e3,
+            "eager_us_per_call": r["eager_ms_per_step"] * 1e3,
+            "algorithmic_bytes": nbytes, "input_sets": sets}
 
 
 def kernel_source_sha256() -> str:
@@ -335,6 +382,31 @@ def main():
     r_sa = time_case(sa, args.steps, args.warmup, hip, use_graph)
     del sa
     torch.cuda.synchronize()
+    others = None
+    if not args.no_configs:
+        others = {}
+        c2 = synth.c2()
+        others["greedy_b8"] = other_workload(
+            lib, "greedy", c2, c2.algorithmic_bytes_greedy,
+            "greedy chain, B=8 K=5 V=128256 bf16, no log-probs", args.steps, args.warmup, hip,
+            use_graph, torch, dev)
+        del c2
+        c4 = synth.c4()
+        others["tree_b8_n61"] = other_workload(
+            lib, "tree", c4, c4.algorithmic_bytes,
+            "greedy tree (depth 5, top-k 4, 60 drafted nodes + root), B=8 V=128256 bf16, "
+            "no log-probs", args.steps, args.warmup, hip, use_graph, torch, dev)
+        del c4
+        c5 = synth.c5()
+        others["relaxed_b64_k8"] = other_workload(
+            lib, "relaxed", c5, c5.algorithmic_bytes_relaxed,
+            f"relaxed (p >= {c5.tau} or top-{c5.top_k}), B=64 K=8 V=151936 bf16", args.steps,
+            args.warmup, hip, use_graph, torch, dev)
+        others["exact_b64_k8"] = other_workload(
+            lib, "exact", c5, c5.algorithmic_bytes_exact,
+            "exact, B=64 K=8 V=151936 bf16, draft target+0.8*N(0,1)", args.steps, args.warmup,
+            hip, use_graph, torch, dev)
+        del c5
 
     ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
     value = 1000.0 / ms
@@ -394,6 +466,7 @@ def main():
             "kernel_gbs": ci.draft.nbytes / (r_sa["kernel_ms_mean"] * 1e-3) / 1e9,
             "rest_of_call_us_mean": r_sa["rest_ms_mean"] * 1e3,
             "logit_bytes": ci.draft.nbytes, "input_sets": sets_sample},
+        "other_workloads": others,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

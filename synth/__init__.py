@@ -98,6 +98,14 @@ class ChainInputs:
         es = 2 if self.dtype == "bf16" else 4
         return self.B * (self.K + 1) * self.V * es + self.B * self.K * 4 + _out_bytes_greedy(self.B, self.K + 1)
 
+    @property
+    def algorithmic_bytes_relaxed(self) -> int:
+        # target rows, draft tokens, the one terminal uniform per request, and
+        # the outputs with both log-prob rows
+        es = 2 if self.dtype == "bf16" else 4
+        return (self.B * (self.K + 1) * self.V * es + self.B * self.K * 4 + self.B * 4 +
+                _out_bytes(self.B, self.K + 1))
+
 
 def _out_bytes(B: int, L: int) -> int:
     # tokens + two log-prob rows (int32/fp32 [B][L]) + accept_len + status
@@ -130,6 +138,14 @@ class TreeInputs:
     num_nodes: np.ndarray
     expected_path: Optional[list] = None  # per request: list of node ids (root excluded)
     expected_bonus: Optional[np.ndarray] = None
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        # logits, node tokens, parents, node counts; path and token outputs
+        # [B][N], accepted length and status (no log-probs requested)
+        es = 2 if self.dtype == "bf16" else 4
+        B, N = self.B, self.N
+        return B * N * self.V * es + B * N * 4 * 2 + B * 4 + B * N * 4 * 2 + B * 4 * 2
 
 
 # ----------------------------------------------------------------------------
