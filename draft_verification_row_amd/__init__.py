@@ -60,8 +60,22 @@ def load_library():
     lib.spec_sample_workspace_bytes.argtypes = [I, I]
     lib.spec_sample_workspace_bytes.restype = Z
     lib.spec_sample_drafts.argtypes = [P, I, P, I, I, P, P, P, P, Z, P]
+    for fn, n in (("spec_shard_record_bytes", 5), ("spec_shard_sums_bytes", 3),
+                  ("spec_shard_workspace_bytes", 1)):
+        getattr(lib, fn).argtypes = [I] * n
+        getattr(lib, fn).restype = Z
+    lib.spec_shard_stats_greedy.argtypes = [P, I, I, I, I, I, I, I, P, Z, P]
+    lib.spec_shard_stats_tree.argtypes = [P, I, P, I, I, I, I, I, I, P, Z, P]
+    lib.spec_shard_stats_exact.argtypes = [P, P, I, P, I, I, I, I, I, P, Z, P]
+    lib.spec_shard_combine_greedy.argtypes = [P, I, P, I, I, I, I, P, P, P, P, P, P]
+    lib.spec_shard_combine_tree.argtypes = [P, I, P, P, P, I, I, I, I, P, P, P, P, P, P, P]
+    lib.spec_shard_sweep_exact.argtypes = [P, P, I, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z,
+                                           P, Z, P]
+    lib.spec_shard_sample_exact.argtypes = [P, P, I, P, P, I, I, I, I, I, P, P, P, P, P, Z, P]
     for fn in ("spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed", "spec_verify_tree",
-               "spec_verify_power", "spec_sample_drafts"):
+               "spec_verify_power", "spec_sample_drafts", "spec_shard_stats_greedy",
+               "spec_shard_stats_tree", "spec_shard_stats_exact", "spec_shard_combine_greedy",
+               "spec_shard_combine_tree", "spec_shard_sweep_exact", "spec_shard_sample_exact"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib

@@ -492,9 +492,18 @@ struct Args {
     int32_t* out_path;
     int L;  // output row length: K+1, or N for a tree
     unsigned char* ws;
-    Seg* segs;        // [B][R][tpr]
+    Seg* segs;        // [B][R][tpr]; sharded combine: G slots of these
     Decision* dec;    // [B]
-    ChunkSums* sums;  // [B][C2]
+    ChunkSums* sums;  // [B][C2]; sharded sample: G slots of these
+    // vocabulary sharding (V above is then the shard's column count)
+    int Vtot;              // vocabulary size: the bound of token ids
+    int G, shard;          // shards, and the shard this call runs for
+    size_t slot_segs;      // records between shard slots
+    size_t slot_xv;        // floats between the slots' drafted-token logits
+    const float* xv_in;    // gathered drafted-token logits, slot 0 ([B][K][2])
+    float* xv_out;         // this shard's drafted-token logits ([B][K][2])
+    size_t sums_slot;      // chunk sums between shard slots
+    int32_t* out_owner;    // [B] shard holding the terminal draw, or null
 };
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -547,7 +556,10 @@ __device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[kTileVec
 // max (or argmax, or rank compare), and for the normalizer one fma, one exp2
 // and one add against the tile max, which the workgroup agrees on first.
 // VECP: every row of the call takes the 16-byte path (chosen on the host).
-template <typename T, int MODE, bool SUM, bool VECP>
+// XV (a vocabulary shard's exact-rule statistics): the first tile's
+// workgroup of a drafted position's row also records the drafted token's
+// logit when the token is one of the shard's columns.
+template <typename T, int MODE, bool SUM, bool VECP, bool XV>
 __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const Args a) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int TILE = kThreads * kTileVecs * VEC;
@@ -653,6 +665,15 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
         sg.ic = (ARGMAX || COUNT) ? I : 0;
         sg.s = s;
         a.segs[blockIdx.x] = sg;
+        if (XV && c == 0) {
+            const int b = g / a.R, rr = g - b * a.R;
+            const bool drow = rr >= a.rows_t;
+            const int j = drow ? rr - a.rows_t : rr;
+            if (j < a.K) {
+                const int xl = a.tok[b * a.K + j] - a.shard * a.V;
+                if ((unsigned)xl < (unsigned)a.V) a.xv_out[2 * (b * a.K + j) + (drow ? 1 : 0)] = Elem<T>::at(row, (size_t)xl);
+            }
+        }
     }
 }
 
@@ -675,20 +696,32 @@ struct NoHook {
 // loads are issued before any is used, and `hook` runs once after the first
 // batch is issued (the caller's dependent loads overlap the fold).  The
 // table of exp_nonpos must be ready.  Ends with a barrier.
-template <int MODE, bool SUM, int NW, typename Hook>
+template <int MODE, bool SUM, int NW, bool SHARD, typename Hook>
 __device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const double* tab, Hook hook) {
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
     constexpr int kBatch = 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Sharded: lane l takes tile l % tpr of shard l / tpr's slot; a shard's
+    // argmax is a column of its own, offset to a vocabulary index here.
+    size_t off = lane;
+    unsigned goff = 0u;
+    int nrec = a.tpr;
+    if (SHARD) {
+        const int sl = lane / a.tpr;
+        off = (size_t)sl * a.slot_segs + (lane - sl * a.tpr);
+        goff = (unsigned)sl * (unsigned)a.V;
+        nrec = a.G * a.tpr;
+    }
     bool hooked = false;
     for (int k0 = 0; k0 == 0 || wave + NW * k0 < nrows; k0 += kBatch) {
         Seg sg[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int r = wave + NW * (k0 + j);
-            if (r < nrows && lane < a.tpr) {
-                sg[j] = a.segs[((size_t)b * a.R + r) * a.tpr + lane];
+            if (r < nrows && lane < nrec) {
+                sg[j] = a.segs[((size_t)b * a.R + r) * a.tpr + off];
+                if (SHARD && ARGMAX && sg[j].ic != INT_MAX) sg[j].ic = (int)((unsigned)sg[j].ic + goff);
             } else {
                 sg[j].m = -INFINITY;
                 sg[j].ic = ARGMAX ? INT_MAX : 0;
@@ -760,15 +793,23 @@ __device__ inline void chain_load_tokens(const Args& a, int b, ChainVals& cv) {
 
 // Logits of the drafted token in target row j (and draft row j): depends on
 // the token load, so it runs as the fold's hook.
-template <typename T, int MODE>
+// Sharded: the shard whose columns hold the token recorded both logits in its
+// slot.
+template <typename T, int MODE, bool SHARD>
 __device__ inline void chain_load_values(const Args& a, int b, ChainVals& cv) {
     const int j = threadIdx.x;
     if (j < a.K) {
-        cv.bad = (unsigned)cv.x >= (unsigned)a.V;
+        cv.bad = (unsigned)cv.x >= (unsigned)a.Vtot;
         if (!cv.bad && MODE != kGreedy) {
-            cv.lx = Elem<T>::at(reinterpret_cast<const T*>(a.T), (size_t)(b * a.rows_t + j) * a.V + cv.x);
-            if (uses_draft(MODE))
-                cv.dx = Elem<T>::at(reinterpret_cast<const T*>(a.D), (size_t)(b * a.K + j) * a.V + cv.x);
+            if (SHARD) {
+                const float* xv = a.xv_in + (size_t)(cv.x / a.V) * a.slot_xv + 2 * (b * a.K + j);
+                cv.lx = xv[0];
+                if (uses_draft(MODE)) cv.dx = xv[1];
+            } else {
+                cv.lx = Elem<T>::at(reinterpret_cast<const T*>(a.T), (size_t)(b * a.rows_t + j) * a.V + cv.x);
+                if (uses_draft(MODE))
+                    cv.dx = Elem<T>::at(reinterpret_cast<const T*>(a.D), (size_t)(b * a.K + j) * a.V + cv.x);
+            }
         }
     }
 }
@@ -862,7 +903,7 @@ __device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
 // -------------------------------------------------------------- decide
 // Greedy and tree: one workgroup (kDecideThreads) per request folds the tile
 // records (one row per wave), takes the decision and writes the outputs.
-template <typename T, int MODE, bool SUM>
+template <typename T, int MODE, bool SUM, bool SHARD>
 __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
     constexpr int NW = kDecideThreads / 64;
     const int b = blockIdx.x;
@@ -874,8 +915,8 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
         ChainVals cv;
         if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
         __syncthreads();
-        fold_rows<MODE, SUM, NW>(a, b, a.R, rs, tab, [&]() {
-            if (threadIdx.x < 64) chain_load_values<T, MODE>(a, b, cv);
+        fold_rows<MODE, SUM, NW, SHARD>(a, b, a.R, rs, tab, [&]() {
+            if (threadIdx.x < 64) chain_load_values<T, MODE, SHARD>(a, b, cv);
         });
         if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
         __syncthreads();
@@ -891,48 +932,71 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
         // tree: a node is accepted iff its token is its parent's argmax and
         // its parent is accepted; parents precede children
         __shared__ int t_par[SPEC_MAX_NODES];
-        __shared__ int t_match[SPEC_MAX_NODES];
+        __shared__ int t_tok[SPEC_MAX_NODES];
         __shared__ int t_path[SPEC_MAX_NODES];
         __shared__ int t_d, t_e, t_bad;
         const int N = a.rows_t;
-        const int nb = a.num_nodes ? min(max(a.num_nodes[b], 1), N) : N;
+        // the node count, parents and tokens are loaded together, before the
+        // fold, which takes every row of the request: records of rows past
+        // the node count are stale but never consulted (a parent index is
+        // below its child's)
+        const int nraw = a.num_nodes ? a.num_nodes[b] : N;
         int p = -1, t = -1;
-        if (threadIdx.x >= 1 && (int)threadIdx.x < nb) {  // issued before the fold
+        if (threadIdx.x >= 1 && (int)threadIdx.x < N) {
             p = a.parents[b * N + threadIdx.x];
             t = a.tok[b * N + threadIdx.x];
         }
         __syncthreads();
-        fold_rows<kTree, SUM, NW>(a, b, nb, rs, tab, NoHook());
+        fold_rows<kTree, SUM, NW, SHARD>(a, b, N, rs, tab, NoHook());
+        const int nb = min(max(nraw, 1), N);
         if (threadIdx.x < 64) {
+            // wave 0, lane i = node i.  Pointer jumping: `ok` says every node
+            // from i up to (not including) `anc` matches, `dep` counts those
+            // edges; each round doubles the span, so six rounds reach the root
+            // from any depth below 64.  A node that does not match (or is
+            // malformed, or lies beyond the tree) stops its chain with ok =
+            // false, which its descendants inherit.
             const int i = threadIdx.x;
-            bool bad = false;
+            bool bad = false, match = false;
+            int par = -1;
             if (i >= 1 && i < nb) {
-                bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.V);
-                t_par[i] = bad ? -1 : p;
-                t_match[i] = bad ? 0 : (t == rs.g[p]);
+                bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.Vtot);
+                par = bad ? -1 : p;
+                match = !bad && (t == rs.g[p]);
             }
+            t_par[i] = par;
+            t_tok[i] = t;
             const unsigned long long bm = __ballot(bad);
-            if (i == 0) t_bad = bm != 0ull;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            unsigned long long accm = 1ull;  // bit i: node i accepted
-            int depth[SPEC_MAX_NODES];
-            depth[0] = 0;
-            int e = 0;
-            for (int i = 1; i < nb; ++i) {
-                const int pi = t_par[i];
-                depth[i] = 0;
-                if (pi >= 0 && t_match[i] && ((accm >> pi) & 1ull)) {
-                    accm |= 1ull << i;
-                    depth[i] = depth[pi] + 1;
-                    if (depth[i] > depth[e]) e = i;
+            bool ok = (i == 0) || match;
+            int anc = match ? par : -1;
+            int dep = (i == 0) ? 0 : 1;
+#pragma unroll
+            for (int round = 0; round < 6; ++round) {
+                const int src = anc >= 0 ? anc : i;
+                const int ok_a = __shfl(ok ? 1 : 0, src);
+                const int dep_a = __shfl(dep, src);
+                const int anc_a = __shfl(anc, src);
+                if (anc >= 0) {
+                    ok = ok && ok_a;
+                    dep += dep_a;
+                    anc = anc_a;
                 }
             }
-            const int d = depth[e];
-            for (int v = e, k = d - 1; k >= 0; --k, v = t_par[v]) t_path[k] = v;
-            t_d = d;
-            t_e = e;
+            // deepest accepted node, ties to the lowest index (the root is
+            // always accepted at depth 0)
+            const int key = ok ? (dep << 6) | (63 - i) : -1;
+            const int kmax = wave_max_i(key);
+            const int e = 63 - (kmax & 63), d = kmax >> 6;
+            int v = e;
+            for (int k = d - 1; k >= 0; --k) {
+                if (i == 0) t_path[k] = v;
+                v = __builtin_amdgcn_readlane(par, v);
+            }
+            if (i == 0) {
+                t_bad = bm != 0ull;
+                t_d = d;
+                t_e = e;
+            }
         }
         __syncthreads();
         const int d = t_d, e = t_e;
@@ -941,7 +1005,7 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
             if (k < d) {
                 const int v = t_path[k];
                 a.out_path[(size_t)b * N + k] = v;
-                otok[k] = a.tok[b * N + v];
+                otok[k] = t_tok[v];
                 if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (float)(-rs.lnS[t_par[v]]);
             } else {
                 a.out_path[(size_t)b * N + k] = -1;
@@ -964,7 +1028,7 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
 // decision and the sweep; chunk 0 also writes the accepted prefix and the
 // decision record.  Each workgroup then sums its chunk of the row(s) the
 // terminal token is drawn from, in fp64.
-template <typename T, int MODE>
+template <typename T, int MODE, bool SHARD>
 __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Args a) {
     constexpr bool EXACT = (MODE == kExact);
     constexpr int VEC = Elem<T>::kVec;
@@ -983,8 +1047,8 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Ar
     ChainVals cv;
     if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
     __syncthreads();
-    fold_rows<MODE, true, kWaves>(a, b, a.R, rs, tab, [&]() {
-        if (threadIdx.x < 64) chain_load_values<T, MODE>(a, b, cv);
+    fold_rows<MODE, true, kWaves, SHARD>(a, b, a.R, rs, tab, [&]() {
+        if (threadIdx.x < 64) chain_load_values<T, MODE, SHARD>(a, b, cv);
     });
     if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
     __syncthreads();
@@ -1071,7 +1135,11 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Ar
 // relu(p - q) (or of p), scans them and finds the chunk holding u_K * Z; the
 // workgroup (1024 threads, four consecutive tokens each) then rescans that
 // chunk with a block scan and writes the terminal token and its log-probs.
-template <typename T, int MODE>
+//
+// Sharded: lane l of wave 0 holds chunk l % C2 of shard l / C2 (the gathered
+// slots, in shard order, tile the vocabulary in ascending order); only the
+// shard whose chunk holds the draw rescans it.
+template <typename T, int MODE, bool SHARD>
 __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     constexpr bool EXACT = (MODE == kExact);
     const int b = blockIdx.x;
@@ -1093,7 +1161,15 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     if (wave == 0) {
         // lane l holds chunk l
         ChunkSums cs = {0.0, 0.0, 0.0, 0.0};
-        if (lane < a.C2) cs = a.sums[(size_t)b * a.C2 + lane];
+        const int nchunk = SHARD ? a.G * a.C2 : a.C2;
+        if (lane < nchunk) {
+            size_t at = (size_t)b * a.C2 + lane;
+            if (SHARD) {
+                const int sl = lane / a.C2;
+                at = (size_t)sl * a.sums_slot + (size_t)b * a.C2 + (lane - sl * a.C2);
+            }
+            cs = a.sums[at];
+        }
         const double S = wave_sum(cs.sa);
         const double Sq = residual ? wave_sum(cs.sb) : 1.0;
         const double iS = 1.0 / S, iSq = 1.0 / Sq;
@@ -1109,7 +1185,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
         const double incl = wave_incl_scan(W);
         double excl = __shfl_up(incl, 1);
         if (lane == 0) excl = 0.0;  // [excl, incl) of consecutive chunks tile [0, Z)
-        const bool has = lane < a.C2 && W > 0.0;
+        const bool has = lane < nchunk && W > 0.0;
         const unsigned long long mine = __ballot(has && excl <= target && target < incl);
         const unsigned long long hasm = __ballot(has);
         // the unique chunk whose interval holds target; if rounding pushed
@@ -1133,7 +1209,13 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     }
     __syncthreads();
 
-    const int cstar = s_cstar;
+    int cstar = s_cstar;
+    if (SHARD) {
+        const int owner = cstar / a.C2;
+        if (threadIdx.x == 0 && a.out_owner) a.out_owner[b] = owner;
+        if (owner != a.shard) return;  // uniform: another shard draws
+        cstar -= owner * a.C2;
+    }
     const bool res = s_res;
     const double iS = s_iS, iSq = s_iSq, target = s_target;
     const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
@@ -1228,7 +1310,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
             if (res && xa - xb > cls) wy = fmax(exp_nonpos(xa, tab) * iS - exp_nonpos(xb, tab) * iSq, 0.0);
         }
         const int L = a.L;
-        a.out_tok[(size_t)b * L + n] = y;
+        a.out_tok[(size_t)b * L + n] = SHARD ? y + a.shard * a.V : y;
         const double tlp = ((double)ly - Mt) - s_lnS;
         // behaviour log-prob: residual draw, power-rule fallback after a
         // rejection (1 - a_n) p_n(y), or a plain draw from p
@@ -1259,6 +1341,34 @@ spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt)
 // this thread.
 thread_local hipEvent_t g_prof[3] = {nullptr, nullptr, nullptr};
 
+// The streaming kernel over B * R rows of a.V logits, with the dispatch's
+// own start and stop events when given.
+template <int MODE, bool SUM, bool XV>
+spec_status launch_stream(const Args& a, spec_dtype dt, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    const dim3 grid((unsigned)a.B * (unsigned)a.R * (unsigned)a.tpr), block(kThreads);
+    const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
+    if (dt == SPEC_BF16) {
+        if (vecp)
+            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true, XV>), grid, block, 0, st, e0, e1, 0, a);
+        else
+            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false, XV>), grid, block, 0, st, e0, e1, 0, a);
+    } else {
+        if (vecp)
+            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, true, XV>), grid, block, 0, st, e0, e1, 0, a);
+        else
+            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, false, XV>), grid, block, 0, st, e0, e1, 0, a);
+    }
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+// Takes the one-shot profiling events, clearing them.
+inline void take_prof(hipEvent_t (&ev)[3]) {
+    for (int i = 0; i < 3; ++i) {
+        ev[i] = g_prof[i];
+        g_prof[i] = nullptr;
+    }
+}
+
 // Streaming kernel, then the per-request kernels: decide (greedy, tree), or
 // sweep and sample (exact, relaxed).  With the profiling hook set, the
 // streaming kernel is launched with start/stop events that the dispatch
@@ -1266,43 +1376,113 @@ thread_local hipEvent_t g_prof[3] = {nullptr, nullptr, nullptr};
 template <int MODE, bool SUM>
 spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
     a.tpr = tpr_of(dt, a.V);
+    a.Vtot = a.V;
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
     a.segs = reinterpret_cast<Seg*>(a.ws + lay.seg);
     a.dec = reinterpret_cast<Decision*>(a.ws + lay.dec);
     a.sums = reinterpret_cast<ChunkSums*>(a.ws + lay.sums);
-    hipEvent_t ev[3] = {g_prof[0], g_prof[1], g_prof[2]};
-    g_prof[0] = g_prof[1] = g_prof[2] = nullptr;
-    const dim3 grid((unsigned)a.B * (unsigned)a.R * (unsigned)a.tpr), block(kThreads);
-    const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
-    if (dt == SPEC_BF16) {
-        if (vecp)
-            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
-        else
-            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
-    } else {
-        if (vecp)
-            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
-        else
-            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
-    }
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    hipEvent_t ev[3];
+    take_prof(ev);
+    if (launch_stream<MODE, SUM, false>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
+    const dim3 block(kThreads);
     if constexpr (MODE == kGreedy || MODE == kTree) {
         if (dt == SPEC_BF16)
-            hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM, false>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((k_decide<float, MODE, SUM>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decide<float, MODE, SUM, false>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
     } else {
         const dim3 grid2((unsigned)a.B * (unsigned)a.C2);
         if (dt == SPEC_BF16) {
-            hipLaunchKernelGGL((k_sweep<uint16_t, MODE>), grid2, block, 0, st, a);
+            hipLaunchKernelGGL((k_sweep<uint16_t, MODE, false>), grid2, block, 0, st, a);
             if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-            hipLaunchKernelGGL((k_sample<uint16_t, MODE>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
+            hipLaunchKernelGGL((k_sample<uint16_t, MODE, false>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
         } else {
-            hipLaunchKernelGGL((k_sweep<float, MODE>), grid2, block, 0, st, a);
+            hipLaunchKernelGGL((k_sweep<float, MODE, false>), grid2, block, 0, st, a);
             if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-            hipLaunchKernelGGL((k_sample<float, MODE>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
+            hipLaunchKernelGGL((k_sample<float, MODE, false>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
         }
     }
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+// ------------------------------------------------------ vocabulary shards
+// One shard's record slot: the tile records of its B * R rows, then the
+// drafted-token logits ([B][K][2] floats, sized [B][R][2]).
+struct ShardLayout {
+    size_t xv, slot;
+};
+inline ShardLayout shard_layout(spec_dtype dt, int B, int R, int Vs) {
+    ShardLayout L;
+    L.xv = align_up((size_t)B * R * tpr_of(dt, Vs) * sizeof(Seg), 256);
+    L.slot = align_up(L.xv + (size_t)B * R * 2 * sizeof(float), 256);
+    return L;
+}
+inline size_t shard_sums_slot(int B, int Vs) { return align_up((size_t)B * c2_of(SPEC_F32, Vs) * sizeof(ChunkSums), 256); }
+inline size_t shard_ws_bytes(int B) { return align_up((size_t)B * 64, 256); }
+
+bool sizes_ok(int B, int K, int V, long rows_per_req);
+
+// Shard count, shard index and the one-wave limits of the combine and the
+// sample scan.
+bool shard_ok(spec_dtype dt, int B, int K, int V, int G, int shard, long rows) {
+    if (G < 1 || V < 1 || V % G != 0 || shard < 0 || shard >= G) return false;
+    if (!sizes_ok(B, K, V, rows)) return false;
+    const int Vs = V / G;
+    return (long)G * tpr_of(dt, Vs) <= 64 && (long)G * c2_of(dt, Vs) <= 64;
+}
+
+inline bool buf_ok(const void* p, size_t bytes, size_t need) {
+    return p && ((uintptr_t)p % 256) == 0 && bytes >= need;
+}
+
+// Shard-local argument block: V is the shard's column count, Vtot the
+// vocabulary.
+inline Args shard_args(spec_dtype dt, int B, int K, int V, int G, int shard, int rows_t, int R) {
+    Args a = {};
+    a.B = B;
+    a.K = K;
+    a.V = V / G;
+    a.Vtot = V;
+    a.G = G;
+    a.shard = shard;
+    a.rows_t = rows_t;
+    a.R = R;
+    a.tpr = tpr_of(dt, a.V);
+    a.C2 = c2_of(dt, a.V);
+    a.L = rows_t;
+    return a;
+}
+
+// Points the combine at the G gathered record slots.
+inline void gathered_records(Args& a, spec_dtype dt, const void* records) {
+    const ShardLayout L = shard_layout(dt, a.B, a.R, a.V);
+    a.segs = reinterpret_cast<Seg*>(const_cast<void*>(records));
+    a.slot_segs = L.slot / sizeof(Seg);
+    a.xv_in = reinterpret_cast<const float*>(static_cast<const unsigned char*>(records) + L.xv);
+    a.slot_xv = L.slot / sizeof(float);
+}
+
+template <int MODE, bool SUM>
+spec_status shard_stats(Args a, spec_dtype dt, void* out_record, hipStream_t st) {
+    const ShardLayout L = shard_layout(dt, a.B, a.R, a.V);
+    a.segs = reinterpret_cast<Seg*>(out_record);
+    a.xv_out = reinterpret_cast<float*>(static_cast<unsigned char*>(out_record) + L.xv);
+    hipEvent_t ev[3];
+    take_prof(ev);
+    if (launch_stream<MODE, SUM, uses_draft(MODE)>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
+    if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+// One per-request kernel of a sharded step, with the profiling events around
+// its dispatch when set.
+template <typename K>
+spec_status shard_launch(K kernel, dim3 grid, dim3 block, const Args& a, hipStream_t st) {
+    hipEvent_t ev[3];
+    take_prof(ev);
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev[0], ev[1], 0, a);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
@@ -1577,6 +1757,199 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out_target_logprob) return launch<kTree, true>(a, dtype, st);
     return launch<kTree, false>(a, dtype, st);
+}
+
+// ------------------------------------------------------ vocabulary shards
+size_t spec_shard_record_bytes(spec_dtype dtype, int B, int rows_per_request, int V, int G) {
+    if (!dtype_ok(dtype) || !shard_ok(dtype, B, 1, V, G, 0, rows_per_request)) return 0;
+    return shard_layout(dtype, B, rows_per_request, V / G).slot;
+}
+
+size_t spec_shard_sums_bytes(int B, int V, int G) {
+    if (B < 1 || B > kMaxB || G < 1 || V < 1 || V > SPEC_MAX_V || V % G != 0) return 0;
+    return shard_sums_slot(B, V / G);
+}
+
+size_t spec_shard_workspace_bytes(int B) {
+    if (B < 1 || B > kMaxB) return 0;
+    return shard_ws_bytes(B);
+}
+
+spec_status spec_shard_stats_greedy(const void* target_shard, spec_dtype dtype, int B, int K,
+                                    int V, int G, int shard, int logprobs, void* out_record,
+                                    size_t record_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, K + 1) || !target_shard)
+        return SPEC_EINVAL;
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, K + 1);
+    if (!buf_ok(out_record, record_bytes, shard_layout(dtype, B, a.R, a.V).slot)) return SPEC_EWORKSPACE;
+    a.T = target_shard;
+    a.vec_t = vec_ok(target_shard, dtype, a.V);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (logprobs) return shard_stats<kGreedy, true>(a, dtype, out_record, st);
+    return shard_stats<kGreedy, false>(a, dtype, out_record, st);
+}
+
+spec_status spec_shard_stats_tree(const void* target_shard, spec_dtype dtype,
+                                  const int32_t* num_nodes, int B, int N, int V, int G, int shard,
+                                  int logprobs, void* out_record, size_t record_bytes,
+                                  void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (N < 1 || N > SPEC_MAX_NODES || !shard_ok(dtype, B, 1, V, G, shard, N) || !target_shard)
+        return SPEC_EINVAL;
+    Args a = shard_args(dtype, B, 0, V, G, shard, N, N);
+    if (!buf_ok(out_record, record_bytes, shard_layout(dtype, B, a.R, a.V).slot)) return SPEC_EWORKSPACE;
+    a.T = target_shard;
+    a.num_nodes = num_nodes;
+    a.vec_t = vec_ok(target_shard, dtype, a.V);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (logprobs) return shard_stats<kTree, true>(a, dtype, out_record, st);
+    return shard_stats<kTree, false>(a, dtype, out_record, st);
+}
+
+spec_status spec_shard_stats_exact(const void* target_shard, const void* draft_shard,
+                                   spec_dtype dtype, const int32_t* draft_tokens, int B, int K,
+                                   int V, int G, int shard, void* out_record, size_t record_bytes,
+                                   void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, 2 * K + 1)) return SPEC_EINVAL;
+    if (!target_shard || !draft_shard || !draft_tokens) return SPEC_EINVAL;
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, 2 * K + 1);
+    if (!buf_ok(out_record, record_bytes, shard_layout(dtype, B, a.R, a.V).slot)) return SPEC_EWORKSPACE;
+    a.T = target_shard;
+    a.D = draft_shard;
+    a.tok = draft_tokens;
+    a.vec_t = vec_ok(target_shard, dtype, a.V);
+    a.vec_d = vec_ok(draft_shard, dtype, a.V);
+    return shard_stats<kExact, true>(a, dtype, out_record, static_cast<hipStream_t>(stream));
+}
+
+spec_status spec_shard_combine_greedy(const void* records, spec_dtype dtype,
+                                      const int32_t* draft_tokens, int B, int K, int V, int G,
+                                      int32_t* out_tokens, int32_t* out_accept_len,
+                                      float* out_target_logprob, float* out_behavior_logprob,
+                                      int32_t* out_status, void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, 0, K + 1)) return SPEC_EINVAL;
+    if (!draft_tokens || !out_tokens || !out_accept_len || !out_status) return SPEC_EINVAL;
+    if (!records || ((uintptr_t)records % 256) != 0) return SPEC_EWORKSPACE;
+    Args a = shard_args(dtype, B, K, V, G, 0, K + 1, K + 1);
+    gathered_records(a, dtype, records);
+    a.tok = draft_tokens;
+    a.out_tok = out_tokens;
+    a.out_len = out_accept_len;
+    a.out_tlp = out_target_logprob;
+    a.out_blp = out_behavior_logprob;
+    a.out_status = out_status;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid(B), block(kDecideThreads);
+    if (dtype == SPEC_BF16) {
+        if (out_target_logprob) return shard_launch(k_decide<uint16_t, kGreedy, true, true>, grid, block, a, st);
+        return shard_launch(k_decide<uint16_t, kGreedy, false, true>, grid, block, a, st);
+    }
+    if (out_target_logprob) return shard_launch(k_decide<float, kGreedy, true, true>, grid, block, a, st);
+    return shard_launch(k_decide<float, kGreedy, false, true>, grid, block, a, st);
+}
+
+spec_status spec_shard_combine_tree(const void* records, spec_dtype dtype,
+                                    const int32_t* node_tokens, const int32_t* parents,
+                                    const int32_t* num_nodes, int B, int N, int V, int G,
+                                    int32_t* out_path_nodes, int32_t* out_tokens,
+                                    int32_t* out_accept_len, float* out_target_logprob,
+                                    float* out_behavior_logprob, int32_t* out_status,
+                                    void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (N < 1 || N > SPEC_MAX_NODES || !shard_ok(dtype, B, 1, V, G, 0, N)) return SPEC_EINVAL;
+    if (!node_tokens || !parents || !out_path_nodes || !out_tokens || !out_accept_len || !out_status)
+        return SPEC_EINVAL;
+    if (!records || ((uintptr_t)records % 256) != 0) return SPEC_EWORKSPACE;
+    Args a = shard_args(dtype, B, 0, V, G, 0, N, N);
+    gathered_records(a, dtype, records);
+    a.tok = node_tokens;
+    a.parents = parents;
+    a.num_nodes = num_nodes;
+    a.out_path = out_path_nodes;
+    a.out_tok = out_tokens;
+    a.out_len = out_accept_len;
+    a.out_tlp = out_target_logprob;
+    a.out_blp = out_behavior_logprob;
+    a.out_status = out_status;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid(B), block(kDecideThreads);
+    if (dtype == SPEC_BF16) {
+        if (out_target_logprob) return shard_launch(k_decide<uint16_t, kTree, true, true>, grid, block, a, st);
+        return shard_launch(k_decide<uint16_t, kTree, false, true>, grid, block, a, st);
+    }
+    if (out_target_logprob) return shard_launch(k_decide<float, kTree, true, true>, grid, block, a, st);
+    return shard_launch(k_decide<float, kTree, false, true>, grid, block, a, st);
+}
+
+spec_status spec_shard_sweep_exact(const void* target_shard, const void* draft_shard,
+                                   spec_dtype dtype, const void* records,
+                                   const int32_t* draft_tokens, const float* uniforms, int B,
+                                   int K, int V, int G, int shard, int32_t* out_tokens,
+                                   int32_t* out_accept_len, float* out_target_logprob,
+                                   float* out_behavior_logprob, int32_t* out_status,
+                                   void* out_sums, size_t sums_bytes, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, 2 * K + 1)) return SPEC_EINVAL;
+    if (!target_shard || !draft_shard || !draft_tokens || !uniforms || !out_tokens ||
+        !out_accept_len || !out_status)
+        return SPEC_EINVAL;
+    if (!records || ((uintptr_t)records % 256) != 0) return SPEC_EWORKSPACE;
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, 2 * K + 1);
+    if (!buf_ok(out_sums, sums_bytes, shard_sums_slot(B, a.V)) ||
+        !buf_ok(workspace, workspace_bytes, shard_ws_bytes(B)))
+        return SPEC_EWORKSPACE;
+    gathered_records(a, dtype, records);
+    a.T = target_shard;
+    a.D = draft_shard;
+    a.tok = draft_tokens;
+    a.u = uniforms;
+    a.vec_t = vec_ok(target_shard, dtype, a.V);
+    a.vec_d = vec_ok(draft_shard, dtype, a.V);
+    a.out_tok = out_tokens;
+    a.out_len = out_accept_len;
+    a.out_tlp = out_target_logprob;
+    a.out_blp = out_behavior_logprob;
+    a.out_status = out_status;
+    a.sums = static_cast<ChunkSums*>(out_sums);
+    a.dec = static_cast<Decision*>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)B * (unsigned)a.C2), block(kThreads);
+    if (dtype == SPEC_BF16) return shard_launch(k_sweep<uint16_t, kExact, true>, grid, block, a, st);
+    return shard_launch(k_sweep<float, kExact, true>, grid, block, a, st);
+}
+
+spec_status spec_shard_sample_exact(const void* target_shard, const void* draft_shard,
+                                    spec_dtype dtype, const void* sums, const float* uniforms,
+                                    int B, int K, int V, int G, int shard, int32_t* out_tokens,
+                                    float* out_target_logprob, float* out_behavior_logprob,
+                                    int32_t* out_sample_shard, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, 2 * K + 1)) return SPEC_EINVAL;
+    if (!target_shard || !draft_shard || !uniforms || !out_tokens) return SPEC_EINVAL;
+    if (!sums || ((uintptr_t)sums % 256) != 0 || !buf_ok(workspace, workspace_bytes, shard_ws_bytes(B)))
+        return SPEC_EWORKSPACE;
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, 2 * K + 1);
+    a.T = target_shard;
+    a.D = draft_shard;
+    a.u = uniforms;
+    a.vec_t = vec_ok(target_shard, dtype, a.V);
+    a.vec_d = vec_ok(draft_shard, dtype, a.V);
+    a.sums = static_cast<ChunkSums*>(const_cast<void*>(sums));
+    a.sums_slot = shard_sums_slot(B, a.V) / sizeof(ChunkSums);
+    a.dec = static_cast<Decision*>(workspace);
+    a.out_tok = out_tokens;
+    a.out_tlp = out_target_logprob;
+    a.out_blp = out_behavior_logprob;
+    a.out_owner = out_sample_shard;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid(B), block(kSampleThreads);
+    if (dtype == SPEC_BF16) return shard_launch(k_sample<uint16_t, kExact, true>, grid, block, a, st);
+    return shard_launch(k_sample<float, kExact, true>, grid, block, a, st);
 }
 
 }  // extern "C"

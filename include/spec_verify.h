@@ -236,6 +236,111 @@ spec_status spec_sample_drafts(const void *logits, spec_dtype dtype, const float
                                int32_t *out_status, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/*
+ * ------------------------------------------------------------------------
+ * Vocabulary-sharded verification.  When the target's (and draft's) output
+ * layer is split over G devices by vocabulary columns, shard s holds columns
+ * [s*Vs, (s+1)*Vs) of every logit row, Vs = V / G (V must be a multiple of
+ * G).  The rules are the same as above (greedy: mini-sglang PR #134,
+ * "Modifications"; exact: spec-decode README, "How it works"; tree: nanospec
+ * README); only the data each device holds changes.  Each shard streams its
+ * own columns once and exchanges small per-row records instead of logits:
+ *
+ *   1. stats    every shard: its columns -> one "record slot" (tile maxima,
+ *               argmaxes, exp sums; for the exact rule also the logits of
+ *               drafted tokens that fall in its columns).
+ *   -- exchange 1: all-gather of the G record slots, in shard order, into one
+ *               buffer of G * spec_shard_record_bytes(...) bytes.
+ *   2. combine  greedy/tree: every shard folds the gathered records, decides
+ *               and writes the complete outputs (identical on every shard).
+ *      sweep    exact: every shard folds, decides, writes the accepted prefix,
+ *               and sums its columns of the row(s) the terminal token is drawn
+ *               from into one "sums slot".
+ *   -- exchange 2 (exact): all-gather of the G sums slots, in shard order.
+ *   3. sample   exact: every shard finds which shard's columns hold the
+ *               terminal draw; that shard alone writes the terminal token and
+ *               its log-probs; all write that shard's index.
+ *   -- exchange 3 (exact): broadcast of the terminal token and its two
+ *               log-probs from the owning shard.
+ *
+ * The exchanges are the caller's (e.g. collectives over the devices); on one
+ * device the G shards may share the gathered buffers and the outputs, each
+ * call writing its own slot.  Results equal the unsharded entry points' up
+ * to floating-point summation order (identical decisions away from near
+ * ties); with G = 1 they are bitwise identical.
+ *
+ * Shapes: the shard's logits are [B][rows][Vs] (rows as above: K+1 target,
+ * K draft, N tree), row-major, the shard's own columns only.  Token ids,
+ * parents, uniforms and outputs are global (0..V-1) and identical on every
+ * shard.  Limits: 1 <= G, V % G == 0, G * ceil(Vs / (16384 / element size))
+ * <= 64 and G * ceil(Vs / 4096) <= 64, besides the unsharded limits for V.
+ * Record and sums buffers are 256-byte aligned; they need no initialization.
+ * Errors as above (SPEC_EINVAL also for a shard index outside [0, G) and
+ * for G or V outside the limits; SPEC_EWORKSPACE for a record, sums or
+ * workspace buffer that is null, misaligned or too small).
+ */
+
+/* Host-only sizes; 0 for invalid arguments.  rows_per_request as for
+ * spec_verify_workspace_bytes (K+1 greedy, 2K+1 exact, N tree). */
+size_t spec_shard_record_bytes(spec_dtype dtype, int B, int rows_per_request, int V, int G);
+size_t spec_shard_sums_bytes(int B, int V, int G);
+size_t spec_shard_workspace_bytes(int B);
+
+/* Step 1.  out_record: this shard's slot (record_bytes >= the query).
+ * logprobs != 0 adds the exp sums the combine needs for log-probs; the
+ * combine may ask for log-probs only if every shard's stats call did. */
+spec_status spec_shard_stats_greedy(const void *target_shard, spec_dtype dtype, int B, int K,
+                                    int V, int G, int shard, int logprobs, void *out_record,
+                                    size_t record_bytes, void *stream);
+spec_status spec_shard_stats_tree(const void *target_shard, spec_dtype dtype,
+                                  const int32_t *num_nodes, int B, int N, int V, int G, int shard,
+                                  int logprobs, void *out_record, size_t record_bytes,
+                                  void *stream);
+spec_status spec_shard_stats_exact(const void *target_shard, const void *draft_shard,
+                                   spec_dtype dtype, const int32_t *draft_tokens, int B, int K,
+                                   int V, int G, int shard, void *out_record, size_t record_bytes,
+                                   void *stream);
+
+/* Step 2, greedy and tree: records = the G gathered slots.  Outputs as for
+ * spec_verify_greedy / spec_verify_tree. */
+spec_status spec_shard_combine_greedy(const void *records, spec_dtype dtype,
+                                      const int32_t *draft_tokens, int B, int K, int V, int G,
+                                      int32_t *out_tokens, int32_t *out_accept_len,
+                                      float *out_target_logprob, float *out_behavior_logprob,
+                                      int32_t *out_status, void *stream);
+spec_status spec_shard_combine_tree(const void *records, spec_dtype dtype,
+                                    const int32_t *node_tokens, const int32_t *parents,
+                                    const int32_t *num_nodes, int B, int N, int V, int G,
+                                    int32_t *out_path_nodes, int32_t *out_tokens,
+                                    int32_t *out_accept_len, float *out_target_logprob,
+                                    float *out_behavior_logprob, int32_t *out_status,
+                                    void *stream);
+
+/* Step 2, exact: writes outputs 0..accept_len-1 (and the padding after the
+ * terminal position), accept_len and status, this shard's sums slot
+ * (out_sums, sums_bytes >= spec_shard_sums_bytes) and the decision into the
+ * workspace (spec_shard_workspace_bytes(B) bytes, one per shard: step 3 of
+ * the same shard reads it). */
+spec_status spec_shard_sweep_exact(const void *target_shard, const void *draft_shard,
+                                   spec_dtype dtype, const void *records,
+                                   const int32_t *draft_tokens, const float *uniforms, int B,
+                                   int K, int V, int G,
+                                   int shard, int32_t *out_tokens, int32_t *out_accept_len,
+                                   float *out_target_logprob, float *out_behavior_logprob,
+                                   int32_t *out_status, void *out_sums, size_t sums_bytes,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step 3, exact: sums = the G gathered sums slots.  The owning shard writes
+ * out_tokens[b][accept_len[b]] and the two log-probs there (NULL log-prob
+ * arrays are skipped); every shard writes out_sample_shard[b] = the owning
+ * shard (NULL: not written). */
+spec_status spec_shard_sample_exact(const void *target_shard, const void *draft_shard,
+                                    spec_dtype dtype, const void *sums, const float *uniforms,
+                                    int B, int K, int V, int G, int shard, int32_t *out_tokens,
+                                    float *out_target_logprob, float *out_behavior_logprob,
+                                    int32_t *out_sample_shard, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -137,3 +137,72 @@ def test_power_and_sampler_argument_errors(lib):
     assert lib.spec_sample_drafts(p, 1, None, 10, 100, p, None, p, ws, wsz, None) == SPEC_EINVAL
     assert lib.spec_sample_drafts(p, 1, p, 10, 100, p, None, p, ws, wsz - 256, None) == SPEC_EWORKSPACE
 
+
+
+def test_shard_size_queries(lib):
+    rb, sb, wb = lib.spec_shard_record_bytes, lib.spec_shard_sums_bytes, lib.spec_shard_workspace_bytes
+    # 32 requests x 11 rows x 2 bf16 tiles of 16032 columns, then the drafted-token logits
+    assert rb(1, 32, 11, 128256, 8) == 14080
+    assert rb(1, 32, 11, 128256, 7) == 0        # 128256 is not a multiple of 7
+    assert rb(1, 32, 11, 128256, 0) == 0
+    assert rb(2, 32, 11, 128256, 8) == 0        # bad dtype
+    assert rb(1, 0, 11, 128256, 8) == 0 and rb(1, 32, 128, 128256, 8) == 0
+    assert rb(0, 2, 13, 262144, 64) > 0         # fp32, one tile per shard row
+    assert rb(0, 2, 13, 262144, 128) == 0       # 128 shard slots exceed one wave
+    assert rb(1, 2, 13, 262144, 16) > 0         # 16 x 4 chunks: exactly one wave
+    assert rb(1, 2, 13, 33 * 4100, 33) == 0     # 33 x 2 chunks exceed one wave
+    assert sb(32, 128256, 8) == 4096 and sb(32, 128256, 7) == 0
+    assert wb(32) == 2048 and wb(0) == 0
+    for v in (rb(1, 32, 11, 128256, 8), sb(32, 128256, 8), wb(32)):
+        assert v % 256 == 0
+
+
+P4K = ctypes.c_void_p(4096)
+PWS = ctypes.c_void_p(1 << 20)
+
+
+def test_shard_argument_errors(lib):
+    rec = lib.spec_shard_record_bytes(1, 2, 7, 1000, 4)
+
+    def stats(**over):
+        a = dict(T=P4K, D=P4K, dt=1, x=P4K, B=2, K=3, V=1000, G=4, s=0, rec=PWS, rb=rec, st=None)
+        a.update(over)
+        return lib.spec_shard_stats_exact(*a.values())
+
+    assert stats(dt=5) == SPEC_EDTYPE
+    assert stats(G=3) == SPEC_EINVAL           # 1000 % 3 != 0
+    assert stats(s=4) == SPEC_EINVAL and stats(s=-1) == SPEC_EINVAL
+    assert stats(K=0) == SPEC_EINVAL
+    assert stats(D=None) == SPEC_EINVAL and stats(x=None) == SPEC_EINVAL
+    assert stats(rec=None) == SPEC_EWORKSPACE
+    assert stats(rec=ctypes.c_void_p((1 << 20) + 16)) == SPEC_EWORKSPACE
+    assert stats(rb=rec - 256) == SPEC_EWORKSPACE
+    g = lib.spec_shard_stats_greedy
+    assert g(P4K, 1, 2, 3, 1000, 4, 4, 1, PWS, 1 << 20, None) == SPEC_EINVAL   # shard = G
+    t = lib.spec_shard_stats_tree
+    assert t(P4K, 1, None, 2, 65, 1000, 4, 0, 1, PWS, 1 << 20, None) == SPEC_EINVAL  # N > 64
+    cg = lib.spec_shard_combine_greedy
+    assert cg(ctypes.c_void_p((1 << 20) + 64), 1, P4K, 2, 3, 1000, 4, P4K, P4K, None, None, P4K,
+              None) == SPEC_EWORKSPACE
+    assert cg(PWS, 1, None, 2, 3, 1000, 4, P4K, P4K, None, None, P4K, None) == SPEC_EINVAL
+    ct = lib.spec_shard_combine_tree
+    assert ct(PWS, 1, P4K, None, None, 2, 8, 1000, 4, P4K, P4K, P4K, None, None, P4K,
+              None) == SPEC_EINVAL
+    sw = lib.spec_shard_sweep_exact
+    sums, ws = lib.spec_shard_sums_bytes(2, 1000, 4), lib.spec_shard_workspace_bytes(2)
+    base = [P4K, P4K, 1, PWS, P4K, P4K, 2, 3, 1000, 4, 1, P4K, P4K, None, None, P4K, PWS, sums,
+            PWS, ws, None]
+    bad_sums = list(base)
+    bad_sums[17] = sums - 256
+    assert sw(*bad_sums) == SPEC_EWORKSPACE
+    bad_ws = list(base)
+    bad_ws[19] = 0
+    assert sw(*bad_ws) == SPEC_EWORKSPACE
+    bad_u = list(base)
+    bad_u[5] = None
+    assert sw(*bad_u) == SPEC_EINVAL
+    sa = lib.spec_shard_sample_exact
+    assert sa(P4K, P4K, 1, ctypes.c_void_p((1 << 20) + 32), P4K, 2, 3, 1000, 4, 1, P4K, None, None,
+              None, PWS, ws, None) == SPEC_EWORKSPACE
+    assert sa(P4K, P4K, 1, PWS, P4K, 2, 3, 1000, 4, 9, P4K, None, None, None, PWS, ws,
+              None) == SPEC_EINVAL

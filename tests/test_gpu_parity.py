@@ -177,6 +177,41 @@ def test_tree_chain_equals_greedy_on_gpu():
         np.testing.assert_array_equal(tt[b, : ln[b] + 1], gt[b, : ln[b] + 1])
 
 
+@pytest.mark.parametrize("shape", ["chain64", "broom", "random", "bushy_ties"])
+def test_tree_deep_and_irregular_shapes(shape):
+    """Trees up to the 64-node limit: a full chain (depth 63), a long handle
+    with a fan of leaves, random parents, and many equal-depth leaves (ties go
+    to the lowest node index).  Tokens match the parent's argmax 90% of the
+    time, so accepted paths run deep."""
+    print(f"tree shape {shape}", flush=True)
+    B, N, V = 6, 64, 3001
+    rng = np.random.default_rng({"chain64": 81, "broom": 82, "random": 83, "bushy_ties": 84}[shape])
+    par = np.full((B, N), -1, np.int32)
+    for i in range(1, N):
+        if shape == "chain64":
+            par[:, i] = i - 1
+        elif shape == "broom":
+            par[:, i] = i - 1 if i < 40 else 39
+        elif shape == "random":
+            par[:, i] = rng.integers(max(0, i - 4), i, size=B)
+        else:
+            par[:, i] = (i - 1) // 3
+    target = synth.bf16_rne(3.0 * rng.standard_normal((B, N, V), dtype=np.float32))
+    g = np.argmax(synth.bf16_to_f32(target), -1)
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            p = par[b, i]
+            tok[b, i] = g[b, p] if rng.random() < 0.9 else (g[b, p] + 1 + rng.integers(V - 1)) % V
+    nn = np.full(B, N, np.int32)
+    nn[-1] = 37
+    ti = synth.TreeInputs(shape, "bf16", B, N, V, target, tok, par, nn)
+    o = oracle.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes)
+    if shape == "chain64":
+        assert o.accept_len.max() >= 5
+    compare_tree(_tree(ti), o, what=f"tree {shape}")
+
+
 def test_tree_partial_node_counts_and_bad_parents():
     ti = synth.tree_inputs(B=6, V=3001, seed=75)
     ti.num_nodes = np.array([61, 1, 2, 30, 60, 17], np.int32)
