@@ -302,6 +302,130 @@ def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, 
             "algorithmic_bytes": nbytes, "input_sets": sets}
 
 
+def sharded_block(lib, ci, G, steps, warmup, hip, torch, dev):
+    """One shard's kernels of a vocabulary-sharded call at the workload's shape
+    (G shards of V/G columns), all shards run on this device in turn.  Each
+    step's kernel is timed by its own dispatch events; the exchanges between
+    the steps (a few KB) are not part of this measurement."""
+    import draft_verification_row_amd.sharded as sh
+    from numpy import int16
+    B, K, V = ci.B, ci.K, ci.V
+    Vs = V // G
+    sets = math.ceil(2 * MALL_BYTES / ci.algorithmic_bytes_exact)
+
+    def split(a):
+        t = torch.from_numpy(a.view(int16)).view(torch.bfloat16).to(dev)
+        return [t[:, :, s * Vs:(s + 1) * Vs].contiguous() for s in range(G)]
+
+    T0, D0 = split(ci.target), split(ci.draft)
+    Ts = [[t.clone() for t in T0] for _ in range(sets)]
+    Ds = [[d.clone() for d in D0] for _ in range(sets)]
+    del T0, D0
+    x = torch.from_numpy(ci.tokens).to(dev)
+    u = torch.from_numpy(ci.uniforms).to(dev)
+    slot = sh.shard_record_bytes(torch.bfloat16, B, 2 * K + 1, V, G)
+    gslot = sh.shard_record_bytes(torch.bfloat16, B, K + 1, V, G)
+    sslot = sh.shard_sums_bytes(B, V, G)
+    rec = torch.empty(G * slot, dtype=torch.uint8, device=dev)
+    grec = torch.empty(G * gslot, dtype=torch.uint8, device=dev)
+    sums = torch.empty(G * sslot, dtype=torch.uint8, device=dev)
+    ws = [torch.empty(sh.shard_workspace_bytes(B), dtype=torch.uint8, device=dev) for _ in range(G)]
+    import draft_verification_row_amd as sv
+    out = sv.VerifyResult(*sv._outs(B, K + 1, dev, True))
+    own = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def stats(i, s):
+        sh.shard_stats_exact(Ts[i][s], Ds[i][s], x, G, s, rec[s * slot:(s + 1) * slot])
+
+    def sweep(i, s):
+        sh.shard_sweep_exact(Ts[i][s], Ds[i][s], rec, x, u, G, s, out,
+                             sums[s * sslot:(s + 1) * sslot], ws[s])
+
+    def sample(i, s):
+        sh.shard_sample_exact(Ts[i][s], Ds[i][s], sums, u, G, s, out, own, ws[s])
+
+    def gstats(i, s):
+        sh.shard_stats_greedy(Ts[i][s], G, s, grec[s * gslot:(s + 1) * gslot], logprobs=False)
+
+    def gcombine(i, s):
+        sh.shard_combine_greedy(grec, torch.bfloat16, x, V, G, logprobs=False)
+
+    def timed(fn, i, s):
+        e = (hip.event(), hip.event(), hip.event())
+        lib.spec_verify_profile_next_call(*e)
+        fn(i, s)
+        return e
+
+    evs = {k: [] for k in ("stats", "sweep", "sample")}
+    for it in range(warmup + steps):
+        i = it % sets
+        for s in range(G):
+            if it >= warmup:
+                evs["stats"].append(timed(stats, i, s))
+            else:
+                stats(i, s)
+        for s in range(G):
+            if it >= warmup:
+                evs["sweep"].append(timed(sweep, i, s))
+            else:
+                sweep(i, s)
+        for s in range(G):
+            if it >= warmup:
+                evs["sample"].append(timed(sample, i, s))
+            else:
+                sample(i, s)
+    torch.cuda.synchronize()
+    res = {}
+    for k, lst in evs.items():
+        d = [hip.elapsed_ms(a, b) for a, b, _ in lst]
+        res[k] = sum(d) / len(d) * 1e3
+        for e in lst:
+            for h in e:
+                hip.destroy(h)
+    # greedy, no log-probs: the greedy rows are the target rows of the same shards
+    gevs = {"stats": [], "combine": []}
+    for it in range(warmup + steps):
+        i = it % sets
+        for s in range(G):
+            if it >= warmup:
+                gevs["stats"].append(timed(gstats, i, s))
+            else:
+                gstats(i, s)
+        if it >= warmup:
+            gevs["combine"].append(timed(gcombine, i, 0))
+        else:
+            gcombine(i, 0)
+    torch.cuda.synchronize()
+    gres = {}
+    for k, lst in gevs.items():
+        d = [hip.elapsed_ms(a, b) for a, b, _ in lst]
+        gres[k] = sum(d) / len(d) * 1e3
+        for e in lst:
+            for h in e:
+                hip.destroy(h)
+    shard_bytes = (ci.target.nbytes + ci.draft.nbytes) // G
+    del Ts, Ds
+    torch.cuda.synchronize()
+    return {
+        "workload": f"exact and greedy, B={B} K={K} V={V} bf16 split over {G} vocabulary shards of "
+                    f"{Vs} columns; one shard's kernels, all shards run on this device in turn",
+        "shards": G, "columns_per_shard": Vs,
+        "exact": {"stats_kernel_us": res["stats"],
+                  "stats_gbs": shard_bytes / (res["stats"] * 1e-6) / 1e9,
+                  "sweep_kernel_us": res["sweep"], "sample_kernel_us": res["sample"],
+                  "kernel_us_per_shard": res["stats"] + res["sweep"] + res["sample"],
+                  "logit_bytes_per_shard": shard_bytes,
+                  "exchange_bytes_per_shard": [slot, sslot, B * 12]},
+        "greedy_no_logprobs": {"stats_kernel_us": gres["stats"],
+                               "stats_gbs": ci.target.nbytes // G / (gres["stats"] * 1e-6) / 1e9,
+                               "combine_kernel_us": gres["combine"],
+                               "kernel_us_per_shard": gres["stats"] + gres["combine"],
+                               "exchange_bytes_per_shard": [gslot]},
+        "not_measured": "exchange latency (all-gathers of the slots, broadcast of the draw)",
+        "input_sets": sets,
+    }
+
+
 def kernel_source_sha256() -> str:
     import hashlib
     with open(KERNEL_SRC, "rb") as f:
@@ -407,6 +531,8 @@ def main():
             "exact, B=64 K=8 V=151936 bf16, draft target+0.8*N(0,1)", args.steps, args.warmup,
             hip, use_graph, torch, dev)
         del c5
+        others["sharded_exact_greedy_g8"] = sharded_block(lib, ci, 8, min(args.steps, 200),
+                                                         min(args.warmup, 20), hip, torch, dev)
 
     ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
     value = 1000.0 / ms

@@ -73,6 +73,8 @@ constexpr int kStreamWavesPerSimd = 8;                   // k_stream occupancy t
 constexpr int kChunk = 4096;                             // pass-2 tokens per workgroup
 constexpr int kPass2WavesPerSimd = 4;                    // k_pass2 occupancy target
 constexpr int kRun = kChunk / kThreads;                  // pass-2 tokens per thread
+constexpr int kSweepGroups = 2;                          // pass-2 chunks per workgroup
+constexpr int kSweepThreads = kThreads * kSweepGroups;   // k_sweep workgroup
 constexpr int kSampleThreads = 1024;                     // k_sample workgroup
 constexpr int kDecideThreads = 1024;                     // k_decide workgroup
 constexpr int kSampleRun = kChunk / kSampleThreads;      // k_sample tokens per thread
@@ -120,20 +122,22 @@ struct alignas(16) ChunkSums {
 };
 
 struct Layout {
-    size_t seg, dec, sums, total;
+    size_t seg, dec, sums, xv, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// [tile records B*R*tpr][decisions B][chunk sums B*C2]; every region is
-// written before it is read within a call, so the workspace needs no
-// initialization and keeps nothing between calls.
+// [tile records B*R*tpr][decisions B][chunk sums B*C2][drafted-token logits
+// B*K*2, sized B*R*2]; every region is written before it is read within a
+// call, so the workspace needs no initialization and keeps nothing between
+// calls.
 inline Layout make_layout(int B, int R, int tpr, int C2) {
     Layout L;
     L.seg = 0;
     L.dec = align_up(L.seg + (size_t)B * R * tpr * 16, 256);
     L.sums = align_up(L.dec + (size_t)B * 64, 256);
-    L.total = align_up(L.sums + (size_t)B * C2 * 32, 256);
+    L.xv = align_up(L.sums + (size_t)B * C2 * 32, 256);
+    L.total = align_up(L.xv + (size_t)B * R * 8, 256);
     return L;
 }
 
@@ -279,10 +283,12 @@ struct Elem<float> {
 // past c1 read as -inf.  `vec` selects the 16-byte path (row start and size
 // 16-byte aligned); otherwise each element is loaded on its own.  Values stay
 // packed (bf16: two per register) until they are used.
+// Thread tid (of kThreads) of the chunk [c0, c1): vector k covers tokens
+// c0 + (k*kThreads + tid)*VEC + [0, VEC); tokens past c1 are masked.
 template <typename T, int NV>
-__device__ inline void load_chunk(__amdgpu_buffer_rsrc_t r, int c0, int c1, bool vec, u32x4 (&q)[NV]) {
+__device__ inline void load_chunk(__amdgpu_buffer_rsrc_t r, int c0, int c1, bool vec, int tid, u32x4 (&q)[NV]) {
     constexpr int VEC = Elem<T>::kVec;
-    const int t0 = c0 + (int)threadIdx.x * VEC;
+    const int t0 = c0 + tid * VEC;
 #pragma unroll
     for (int k = 0; k < NV; ++k)
         q[k] = vec ? Elem<T>::vraw(r, t0 + k * kThreads * VEC) : Elem<T>::sgather(r, t0 + k * kThreads * VEC);
@@ -556,9 +562,11 @@ __device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[kTileVec
 // max (or argmax, or rank compare), and for the normalizer one fma, one exp2
 // and one add against the tile max, which the workgroup agrees on first.
 // VECP: every row of the call takes the 16-byte path (chosen on the host).
-// XV (a vocabulary shard's exact-rule statistics): the first tile's
-// workgroup of a drafted position's row also records the drafted token's
-// logit when the token is one of the shard's columns.
+// XV: the first workgroups (dispatched first, so the extra latency hides
+// behind the rest of the grid) also record the drafted tokens' target and
+// draft logits, one (request, position, row kind) each, for the decision
+// kernels to load beside the tile records.  On a vocabulary shard only the
+// shard whose columns hold the token records it.
 template <typename T, int MODE, bool SUM, bool VECP, bool XV>
 __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const Args a) {
     constexpr int VEC = Elem<T>::kVec;
@@ -665,13 +673,17 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
         sg.ic = (ARGMAX || COUNT) ? I : 0;
         sg.s = s;
         a.segs[blockIdx.x] = sg;
-        if (XV && c == 0) {
-            const int b = g / a.R, rr = g - b * a.R;
-            const bool drow = rr >= a.rows_t;
-            const int j = drow ? rr - a.rows_t : rr;
-            if (j < a.K) {
-                const int xl = a.tok[b * a.K + j] - a.shard * a.V;
-                if ((unsigned)xl < (unsigned)a.V) a.xv_out[2 * (b * a.K + j) + (drow ? 1 : 0)] = Elem<T>::at(row, (size_t)xl);
+        // one workgroup per (position, row kind): 2*B*K <= B*(2K+1) workgroups
+        // for the draft rules, B*K <= B*(K+1) for the target-only rule
+        constexpr int kinds = uses_draft(MODE) ? 2 : 1;
+        if (XV && (int)blockIdx.x < kinds * a.B * a.K) {
+            const int i = (int)blockIdx.x / kinds, drow = (int)blockIdx.x - i * kinds;
+            const int b = i / a.K, j = i - b * a.K;
+            const int xl = a.tok[i] - a.shard * a.V;
+            if ((unsigned)xl < (unsigned)a.V) {
+                const T* src = drow ? reinterpret_cast<const T*>(a.D) + (size_t)i * a.V
+                                    : reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + j) * a.V;
+                a.xv_out[2 * i + drow] = Elem<T>::at(src, (size_t)xl);
             }
         }
     }
@@ -687,15 +699,12 @@ struct RowStats {
     double lnS[kMaxRows];
 };
 
-struct NoHook {
-    __device__ void operator()() const {}
-};
-
 // Folds the tile records of rows [0, nrows) of request b.  Wave w of NW takes
 // rows w, w + NW, ... in batches of four, one tile record per lane; every batch's
-// loads are issued before any is used, and `hook` runs once after the first
-// batch is issued (the caller's dependent loads overlap the fold).  The
-// table of exp_nonpos must be ready.  Ends with a barrier.
+// loads are issued before any is used, and `hook` runs once in every thread
+// after the first batch is issued, before any record is used: the caller's
+// own loads go there, and the barrier that publishes the exp_nonpos table, so
+// that all of them share one memory round trip.  Ends with a barrier.
 template <int MODE, bool SUM, int NW, bool SHARD, typename Hook>
 __device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const double* tab, Hook hook) {
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
@@ -793,23 +802,27 @@ __device__ inline void chain_load_tokens(const Args& a, int b, ChainVals& cv) {
 
 // Logits of the drafted token in target row j (and draft row j): depends on
 // the token load, so it runs as the fold's hook.
-// Sharded: the shard whose columns hold the token recorded both logits in its
-// slot.
+// The streaming kernel recorded both logits (XV); on vocabulary shards, in
+// the slot of the shard whose columns hold the token.  Unsharded, the load
+// does not depend on the token, so it overlaps the record loads.
 template <typename T, int MODE, bool SHARD>
 __device__ inline void chain_load_values(const Args& a, int b, ChainVals& cv) {
     const int j = threadIdx.x;
     if (j < a.K) {
         cv.bad = (unsigned)cv.x >= (unsigned)a.Vtot;
-        if (!cv.bad && MODE != kGreedy) {
-            if (SHARD) {
-                const float* xv = a.xv_in + (size_t)(cv.x / a.V) * a.slot_xv + 2 * (b * a.K + j);
-                cv.lx = xv[0];
-                if (uses_draft(MODE)) cv.dx = xv[1];
-            } else {
-                cv.lx = Elem<T>::at(reinterpret_cast<const T*>(a.T), (size_t)(b * a.rows_t + j) * a.V + cv.x);
-                if (uses_draft(MODE))
-                    cv.dx = Elem<T>::at(reinterpret_cast<const T*>(a.D), (size_t)(b * a.K + j) * a.V + cv.x);
-            }
+        if (MODE == kGreedy) return;
+        const float* xv = a.xv_in + 2 * (b * a.K + j);
+        if (SHARD) {
+            if (cv.bad) return;
+            xv += (size_t)(cv.x / a.V) * a.slot_xv;
+        }
+        // unsharded: loaded whatever the token (a malformed token's entry is
+        // stale and unused), so the load need not wait for it
+        const float lx = xv[0];
+        const float dx = uses_draft(MODE) ? xv[1] : -INFINITY;
+        if (!cv.bad) {
+            cv.lx = lx;
+            cv.dx = dx;
         }
     }
 }
@@ -914,9 +927,9 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
         __shared__ ChainDecision cd;
         ChainVals cv;
         if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
-        __syncthreads();
         fold_rows<MODE, SUM, NW, SHARD>(a, b, a.R, rs, tab, [&]() {
             if (threadIdx.x < 64) chain_load_values<T, MODE, SHARD>(a, b, cv);
+            __syncthreads();  // the exp table; every load above is in flight
         });
         if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
         __syncthreads();
@@ -946,8 +959,9 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
             p = a.parents[b * N + threadIdx.x];
             t = a.tok[b * N + threadIdx.x];
         }
-        __syncthreads();
-        fold_rows<kTree, SUM, NW, SHARD>(a, b, N, rs, tab, NoHook());
+        fold_rows<kTree, SUM, NW, SHARD>(a, b, N, rs, tab, [] {
+            __syncthreads();  // the exp table; every load above is in flight
+        });
         const int nb = min(max(nraw, 1), N);
         if (threadIdx.x < 64) {
             // wave 0, lane i = node i.  Pointer jumping: `ok` says every node
@@ -1029,26 +1043,31 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
 // decision record.  Each workgroup then sums its chunk of the row(s) the
 // terminal token is drawn from, in fp64.
 template <typename T, int MODE, bool SHARD>
-__global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Args a) {
+__global__ __launch_bounds__(kSweepThreads, kPass2WavesPerSimd) void k_sweep(const Args a) {
     constexpr bool EXACT = (MODE == kExact);
     constexpr int VEC = Elem<T>::kVec;
     constexpr int NV = kRun / VEC;  // 16-byte vectors per thread per chunk
+    constexpr int NW = kSweepThreads / 64;
 
-    const int b = blockIdx.x / a.C2;
-    const int c = blockIdx.x - b * a.C2;
+    // kSweepGroups consecutive chunks per workgroup, one 256-thread group each
+    const int wpr = (a.C2 + kSweepGroups - 1) / kSweepGroups;
+    const int b = blockIdx.x / wpr;
+    const int grp = (int)threadIdx.x / kThreads;
+    const int c = (blockIdx.x - b * wpr) * kSweepGroups + grp;
+    const int tid = (int)threadIdx.x - grp * kThreads;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
     __shared__ double tab[kExpTab];
     __shared__ RowStats rs;
     __shared__ ChainDecision cd;
-    __shared__ double red[kWaves][4];
+    __shared__ double red[NW][4];
     fill_exp_table(tab);
     ChainVals cv;
     if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
-    __syncthreads();
-    fold_rows<MODE, true, kWaves, SHARD>(a, b, a.R, rs, tab, [&]() {
+    fold_rows<MODE, true, NW, SHARD>(a, b, a.R, rs, tab, [&]() {
         if (threadIdx.x < 64) chain_load_values<T, MODE, SHARD>(a, b, cv);
+        __syncthreads();  // the exp table; every load above is in flight
     });
     if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
     __syncthreads();
@@ -1077,13 +1096,15 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Ar
     const __amdgpu_buffer_rsrc_t rt = row_rsrc(trow, a.V);
     const __amdgpu_buffer_rsrc_t rd = row_rsrc(drow, a.V);
 
+    // a group past the row's last chunk reads nothing (its loads return zeros
+    // and are masked) and writes nothing
     const int c0 = c * kChunk;
     const int c1 = min(c0 + kChunk, a.V);
     u32x4 qt[NV], qd[NV];
     double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0;
     if (residual) {  // uniform: one loop per case, no per-token branch
-        load_chunk<T, NV>(rt, c0, c1, a.vec_t, qt);
-        load_chunk<T, NV>(rd, c0, c1, a.vec_d, qd);
+        load_chunk<T, NV>(rt, c0, c1, a.vec_t, tid, qt);
+        load_chunk<T, NV>(rd, c0, c1, a.vec_d, tid, qd);
 #pragma unroll
         for (int k = 0; k < NV; ++k)
 #pragma unroll
@@ -1099,7 +1120,7 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Ar
                 pb = fma(eb, pq, pb);
             }
     } else {
-        load_chunk<T, NV>(rt, c0, c1, a.vec_t, qt);
+        load_chunk<T, NV>(rt, c0, c1, a.vec_t, tid, qt);
 #pragma unroll
         for (int k = 0; k < NV; ++k)
 #pragma unroll
@@ -1118,9 +1139,9 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_sweep(const Ar
         red[wave][3] = pb;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid == 0 && c < a.C2) {
         ChunkSums cs = {0.0, 0.0, 0.0, 0.0};
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = grp * kWaves; w < (grp + 1) * kWaves; ++w) {
             cs.sa += red[w][0];
             cs.sb += red[w][1];
             cs.pa += red[w][2];
@@ -1381,23 +1402,27 @@ spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
     a.segs = reinterpret_cast<Seg*>(a.ws + lay.seg);
     a.dec = reinterpret_cast<Decision*>(a.ws + lay.dec);
     a.sums = reinterpret_cast<ChunkSums*>(a.ws + lay.sums);
+    a.xv_out = reinterpret_cast<float*>(a.ws + lay.xv);
+    a.xv_in = a.xv_out;
     hipEvent_t ev[3];
     take_prof(ev);
-    if (launch_stream<MODE, SUM, false>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
-    const dim3 block(kThreads);
+    // the rules that test drafted-token values record them in the stream
+    constexpr bool XV = (MODE == kExact || MODE == kPower || MODE == kRelaxed);
+    if (launch_stream<MODE, SUM, XV>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
     if constexpr (MODE == kGreedy || MODE == kTree) {
         if (dt == SPEC_BF16)
             hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM, false>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
         else
             hipLaunchKernelGGL((k_decide<float, MODE, SUM, false>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
     } else {
-        const dim3 grid2((unsigned)a.B * (unsigned)a.C2);
+        const dim3 grid2((unsigned)a.B * (unsigned)((a.C2 + kSweepGroups - 1) / kSweepGroups));
+        const dim3 block2(kSweepThreads);
         if (dt == SPEC_BF16) {
-            hipLaunchKernelGGL((k_sweep<uint16_t, MODE, false>), grid2, block, 0, st, a);
+            hipLaunchKernelGGL((k_sweep<uint16_t, MODE, false>), grid2, block2, 0, st, a);
             if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
             hipLaunchKernelGGL((k_sample<uint16_t, MODE, false>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
         } else {
-            hipLaunchKernelGGL((k_sweep<float, MODE, false>), grid2, block, 0, st, a);
+            hipLaunchKernelGGL((k_sweep<float, MODE, false>), grid2, block2, 0, st, a);
             if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
             hipLaunchKernelGGL((k_sample<float, MODE, false>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
         }
@@ -1917,7 +1942,7 @@ spec_status spec_shard_sweep_exact(const void* target_shard, const void* draft_s
     a.sums = static_cast<ChunkSums*>(out_sums);
     a.dec = static_cast<Decision*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)B * (unsigned)a.C2), block(kThreads);
+    const dim3 grid((unsigned)B * (unsigned)((a.C2 + kSweepGroups - 1) / kSweepGroups)), block(kSweepThreads);
     if (dtype == SPEC_BF16) return shard_launch(k_sweep<uint16_t, kExact, true>, grid, block, a, st);
     return shard_launch(k_sweep<float, kExact, true>, grid, block, a, st);
 }
