@@ -45,8 +45,8 @@ KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_veri
 # plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Reported only while the kernel source is the one the counters were taken
 # on.
-TRAFFIC = {"source_sha256": "a77d4483c25c56080ce041ac03830445f443ebf47923a45ffaf8821b46a791a3",
-           "fetch_kib": 44122.9, "write_kib": 176.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"source_sha256": "179fad12d30ee5ed8f17e854a8305e910aeff9be3ac5617402335dda89d576f0",
+           "fetch_kib": 44140.1, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 MALL_BYTES = 256 * 1024 * 1024
 METRIC = "verify rounds/s + achieved HBM GB/s (% of peak), B=32 K=5 V=128256 bf16"
