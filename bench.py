@@ -426,6 +426,43 @@ def sharded_block(lib, ci, G, steps, warmup, hip, torch, dev):
     }
 
 
+def markov_block(torch, dev, rounds, with_cpu):
+    """The multi-round driver with toy Markov models (V=4096, B=32, K=4): the
+    GPU loop's rate and the run's acceptance statistics; the oracle's driver on
+    a few rounds of the same inputs beside it."""
+    import draft_verification_row_amd.markov as mk
+    import synth
+    from numpy import int16
+    V, B, K = 4096, 32, 4
+    m = synth.markov_inputs(V, B, K, rounds, "bf16", seed=4096)
+    P = torch.from_numpy(m.target.view(int16)).view(torch.bfloat16).to(dev)
+    Q = torch.from_numpy(m.draft.view(int16)).view(torch.bfloat16).to(dev)
+    st = torch.from_numpy(m.start).to(dev)
+    ud = torch.from_numpy(m.u_draft).to(dev)
+    uv = torch.from_numpy(m.u_verify).to(dev)
+    warm = min(10, rounds)
+    mk.generate_speculative(P, Q, st, ud[:warm].contiguous(), uv[:warm].contiguous())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tr = mk.generate_speculative(P, Q, st, ud, uv)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    res = {"workload": f"multi-round speculative sampling, toy Markov models V={V} (target "
+                       f"2*N(0,1) logits per state, draft target+0.7*N(0,1)), B={B} sequences, "
+                       f"K={K}, {rounds} rounds; per round K draft draws (spec_sample_drafts) and "
+                       f"one exact verification",
+           "rounds_per_s": rounds / el, "tokens_per_s": None, "ms_per_round": el / rounds * 1e3,
+           **mk.trace_stats(tr.accept_len, K, 0.1), "cpu_oracle_rounds_per_s": None}
+    res["tokens_per_s"] = res["tokens"] / el
+    if with_cpu:
+        import oracle
+        n = min(20, rounds)
+        t0 = time.perf_counter()
+        oracle.speculative_generate(m.target, m.draft, m.start, m.u_draft[:n], m.u_verify[:n], "bf16")
+        res["cpu_oracle_rounds_per_s"] = n / (time.perf_counter() - t0)
+    return res
+
+
 def kernel_source_sha256() -> str:
     import hashlib
     with open(KERNEL_SRC, "rb") as f:
@@ -533,6 +570,8 @@ def main():
         del c5
         others["sharded_exact_greedy_g8"] = sharded_block(lib, ci, 8, min(args.steps, 200),
                                                          min(args.warmup, 20), hip, torch, dev)
+        others["markov_driver"] = markov_block(torch, dev, min(args.steps, 200),
+                                               not args.no_cpu_baseline)
 
     ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
     value = 1000.0 / ms

@@ -22,8 +22,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["build", "load", "OracleResult", "OracleSample", "greedy", "exact", "relaxed", "tree",
-           "power", "sample", "row_stats",
+__all__ = ["build", "load", "OracleResult", "OracleSample", "OracleTrace", "greedy", "exact",
+           "relaxed", "tree", "power", "sample", "speculative_generate", "row_stats",
            "set_threads", "max_threads", "EPS_ACCEPT", "EPS_SAMPLE"]
 
 EPS_ACCEPT = 1e-6
@@ -228,3 +228,47 @@ def tree(target, node_tok, parents, dtype: str, num_nodes=None) -> OracleResult:
                        _ptr(tlp), _ptr(blp), _ptr(st))
     return OracleResult(tok, ln, tlp, blp, st, np.full(B, -1, np.int32),
                         ln.copy(), path=path)
+
+
+@dataclass
+class OracleTrace:
+    """A multi-round run: per round and sequence the emitted tokens (-1 padded)
+    and the accepted-draft count; per sequence the first round holding a
+    flagged near tie (a draft draw or a verification decision), or -1."""
+    emitted: np.ndarray     # int32 [rounds][B][K+1]
+    accept_len: np.ndarray  # int32 [rounds][B]
+    flag_round: np.ndarray  # int32 [B]
+
+
+def speculative_generate(target_table, draft_table, start, u_draft, u_verify,
+                         dtype: str) -> OracleTrace:
+    """Speculative sampling over several rounds with toy Markov models, in the
+    order of the spec-decode README ("How it works", and generate_speculative
+    under "Use it"): each round the draft proposes K tokens one after another
+    from its own next-token distribution, the target scores all K+1 positions
+    at once, the exact rule accepts a prefix and emits one more token, and the
+    next round continues from the last emitted token.  A model's next_dist is
+    the row of its table picked by the last token.  Every draw and decision
+    is sample() and exact() above; uniforms u_draft[r][b][i] drive draft draw
+    i and u_verify[r][b] the verification of round r."""
+    T, D = np.asarray(target_table), np.asarray(draft_table)
+    rounds, B, K = u_draft.shape
+    emitted = np.full((rounds, B, K + 1), -1, np.int32)
+    accept_len = np.zeros((rounds, B), np.int32)
+    flag_round = np.full(B, -1, np.int32)
+    cur = np.asarray(start, np.int32).copy()
+    for r in range(rounds):
+        prev = [cur]
+        hit = np.zeros(B, bool)
+        for i in range(K):
+            s = sample(D[prev[-1]], u_draft[r, :, i], dtype)
+            hit |= s.flag != 0  # 1: the draw sits within the window of a boundary
+            prev.append(s.tokens)
+        x = np.stack(prev[1:], 1)
+        o = exact(T[np.stack(prev, 1)], D[np.stack(prev[:K], 1)], x, u_verify[r], dtype)
+        hit |= o.flag >= 0
+        flag_round[(flag_round < 0) & hit] = r
+        emitted[r] = o.tokens
+        accept_len[r] = o.accept_len
+        cur = o.tokens[np.arange(B), o.accept_len].astype(np.int32)
+    return OracleTrace(emitted, accept_len, flag_round)

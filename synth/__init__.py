@@ -383,3 +383,49 @@ def tree_inputs(B: int = 8, V: int = 128256, dtype: str = "bf16", *, seed: int =
 def c4(seed: int = 4, rnd: int = 0, B: int = 8, V: int = 128256) -> TreeInputs:
     """Greedy tree verify: B=8, 61 rows (root + 60 drafted nodes), V=128256 bf16."""
     return tree_inputs(B=B, V=V, dtype="bf16", seed=seed, rnd=rnd, name="c4")
+
+
+# ----------------------------------------------------------------------------
+# toy Markov language models for the multi-round driver
+# ----------------------------------------------------------------------------
+@dataclass
+class MarkovInputs:
+    """Toy Markov models (a model is next_dist(prefix) = a table row picked by
+    the last token) and the randomness of a multi-round run.
+
+    target    [V][V]          logits of the next token after token s, row s
+    draft     [V][V]          the draft model's logits, same layout
+    start     [B]             int32 first token of each sequence
+    u_draft   [rounds][B][K]  float32 uniforms of the K draft draws per round
+    u_verify  [rounds][B][K+1] float32 uniforms of the verification per round
+    """
+    name: str
+    dtype: str
+    V: int
+    B: int
+    K: int
+    rounds: int
+    target: np.ndarray
+    draft: np.ndarray
+    start: np.ndarray
+    u_draft: np.ndarray
+    u_verify: np.ndarray
+
+
+def markov_inputs(V: int, B: int, K: int, rounds: int, dtype: str = "bf16", *, seed: int,
+                  t_scale: float = 2.0, d_noise: float = 0.7, name: str = "markov") -> MarkovInputs:
+    """Per state the tiny exact config's recipe: target logits t_scale*N(0,1),
+    draft = target + d_noise*N(0,1)."""
+    rng = np.random.default_rng(seed)
+    t32 = _normal(rng, (V, V), t_scale)
+    if dtype == "bf16":
+        target = bf16_rne(t32)
+        tw = bf16_to_f32(target)
+    else:
+        target, tw = t32, t32
+    d32 = (tw + _normal(rng, (V, V), d_noise)).astype(np.float32)
+    draft = bf16_rne(d32) if dtype == "bf16" else d32
+    start = rng.integers(0, V, size=B).astype(np.int32)
+    u_draft = rng.random((rounds, B, K), dtype=np.float32)
+    u_verify = rng.random((rounds, B, K + 1), dtype=np.float32)
+    return MarkovInputs(name, dtype, V, B, K, rounds, target, draft, start, u_draft, u_verify)
