@@ -45,10 +45,11 @@ KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_veri
 # plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Reported only while the kernel source is the one the counters were taken
 # on.
-TRAFFIC = {"source_sha256": "179fad12d30ee5ed8f17e854a8305e910aeff9be3ac5617402335dda89d576f0",
-           "fetch_kib": 44140.1, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"source_sha256": "f9e4b057368a1b68fa0cd65c08bec9cd837c331be92b8644f0366560f7f777e8",
+           "fetch_kib": 44146.6, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 MALL_BYTES = 256 * 1024 * 1024
+RUNS = 3  # timed replays of the captured steps; the median is reported
 METRIC = "verify rounds/s + achieved HBM GB/s (% of peak), B=32 K=5 V=128256 bf16"
 
 
@@ -244,14 +245,18 @@ def time_case(case, steps, warmup, hip, use_graph):
             case.run(steps, stream=torch.cuda.current_stream().cuda_stream)
         g.replay()  # untimed: first replay uploads the graph
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record()
-        g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        res["graph_ms_per_step"] = t0.elapsed_time(t1) / steps
+        runs = []
+        for _ in range(RUNS):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record()
+            g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            runs.append(t0.elapsed_time(t1) / steps)
+        res["graph_ms_per_step"] = sorted(runs)[len(runs) // 2]
+        res["graph_ms_per_step_runs"] = runs
         # the timed replays must reproduce the eager results bit for bit
         for o1, o2 in zip(eager_out, case.snapshot()):
             for k in o1:
@@ -281,8 +286,53 @@ def time_case(case, steps, warmup, hip, use_graph):
     return res
 
 
-def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, torch, dev):
-    """Call rate and streaming-kernel rate of one more workload."""
+def read_ceiling(lib, nbytes, steps, hip, torch, dev):
+    """The library's read-only kernel (the streaming kernel's tiles and loads,
+    no arithmetic) over nbytes, rotating over enough buffers to defeat the
+    last-level cache: its mean dispatch duration and rate."""
+    sets = math.ceil(2 * MALL_BYTES / nbytes)
+    bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device=dev) for _ in range(sets)]
+    words = lib.spec_read_ceiling_out_words(nbytes)
+    out = torch.empty(words, dtype=torch.int32, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(20):
+        assert lib.spec_read_ceiling(ctypes.c_void_p(bufs[i % sets].data_ptr()), nbytes,
+                                     ctypes.c_void_p(out.data_ptr()), st) == 0
+    evs = [(hip.event(), hip.event(), hip.event()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        lib.spec_verify_profile_next_call(*evs[i])
+        assert lib.spec_read_ceiling(ctypes.c_void_p(bufs[i % sets].data_ptr()), nbytes,
+                                     ctypes.c_void_p(out.data_ptr()), st) == 0
+    torch.cuda.synchronize()
+    d = [hip.elapsed_ms(a, b) for a, b, _ in evs]
+    for e in evs:
+        for h in e:
+            hip.destroy(h)
+    del bufs
+    us = sum(d) / len(d) * 1e3
+    return {"kernel": "k_read: the streaming kernel's 16 KiB tiles and non-temporal 16-byte loads, "
+                      "no arithmetic", "bytes": nbytes, "kernel_us_mean": us,
+            "gbs": nbytes / (us * 1e-6) / 1e9, "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "input_sets": sets}
+
+
+def oracle_rate(fn, seconds, max_calls):
+    """Calls per second of an oracle call, over about `seconds` (at least one call)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= max_calls:
+            return n / el
+
+
+def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, torch, dev,
+                   cpu=False):
+    """Call rate and streaming-kernel rate of one more workload; with cpu, the
+    oracle's rate on the same inputs beside it (a bounded sample)."""
     sets = math.ceil(2 * MALL_BYTES / nbytes)
     case = Case(lib, mode, ci, sets, torch, dev)
     r = time_case(case, steps, warmup, hip, use_graph)
@@ -299,7 +349,24 @@ def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, 
             "kernel_frac": logit_bytes / (r["kernel_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "rest_of_call_us_mean": r["rest_ms_mean"] * 1e3,
             "eager_us_per_call": r["eager_ms_per_step"] * 1e3,
-            "algorithmic_bytes": nbytes, "input_sets": sets}
+            "graph_us_per_call_runs": [x * 1e3 for x in r.get("graph_ms_per_step_runs", [])],
+            "algorithmic_bytes": nbytes, "input_sets": sets,
+            "cpu_oracle_rounds_per_s": oracle_call_rate(mode, ci) if cpu else None}
+
+
+def oracle_call_rate(mode, ci):
+    import oracle
+    if mode == "tree":
+        fn = lambda: oracle.tree(ci.target, ci.node_tok, ci.parents, "bf16",  # noqa: E731
+                                 num_nodes=ci.num_nodes)
+    elif mode == "greedy":
+        fn = lambda: oracle.greedy(ci.target, ci.tokens, "bf16")  # noqa: E731
+    elif mode == "relaxed":
+        fn = lambda: oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", ci.tau,  # noqa: E731
+                                    ci.top_k)
+    else:
+        fn = lambda: oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")  # noqa: E731
+    return oracle_rate(fn, 2.0, 50)
 
 
 def sharded_block(lib, ci, G, steps, warmup, hip, torch, dev):
@@ -478,8 +545,20 @@ def traffic_bytes():
                TRAFFIC["write_kib"] * TRAFFIC["write_scale"] * 1024)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(ci, seconds):
     import oracle
+    import synth
     oracle.load()
     t0 = time.perf_counter()
     n = 0
@@ -489,10 +568,21 @@ def cpu_baseline(ci, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": n / el, "unit": "rounds/s", "cores": oracle.max_threads(), "kind": "oracle",
+    threads = oracle.max_threads()
+    oracle.set_threads(1)
+    one = oracle_rate(lambda: oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
+                      3.0, 100)
+    oracle.set_threads(threads)
+    c1 = synth.c1()
+    c1_rate = c1.B * oracle_rate(lambda: oracle.exact(c1.target, c1.draft, c1.tokens, c1.uniforms,
+                                                      "f32"), 1.0, 1000)
+    return {"value": n / el, "unit": "rounds/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} exact verification calls of the benchmark batch (B=32, K=5, "
                       f"V=128256 bf16) on the same inputs, {el:.1f} s, fp64 C oracle, "
-                      f"OpenMP over requests"}
+                      f"OpenMP over requests",
+            "cpu_model": cpu_model(), "single_thread_value": one,
+            "gbs_equivalent": n / el * ci.algorithmic_bytes_exact / 1e9,
+            "tiny_exact_b1_k4_v32_rounds_per_s": c1_rate}
 
 
 def main():
@@ -543,6 +633,9 @@ def main():
     r_sa = time_case(sa, args.steps, args.warmup, hip, use_graph)
     del sa
     torch.cuda.synchronize()
+    ceiling = read_ceiling(lib, ci.target.nbytes + ci.draft.nbytes, args.steps, hip, torch, dev)
+    ceiling_g = read_ceiling(lib, ci.target.nbytes, args.steps, hip, torch, dev)
+    cpu = not args.no_cpu_baseline
     others = None
     if not args.no_configs:
         others = {}
@@ -550,23 +643,23 @@ def main():
         others["greedy_b8"] = other_workload(
             lib, "greedy", c2, c2.algorithmic_bytes_greedy,
             "greedy chain, B=8 K=5 V=128256 bf16, no log-probs", args.steps, args.warmup, hip,
-            use_graph, torch, dev)
+            use_graph, torch, dev, cpu)
         del c2
         c4 = synth.c4()
         others["tree_b8_n61"] = other_workload(
             lib, "tree", c4, c4.algorithmic_bytes,
             "greedy tree (depth 5, top-k 4, 60 drafted nodes + root), B=8 V=128256 bf16, "
-            "no log-probs", args.steps, args.warmup, hip, use_graph, torch, dev)
+            "no log-probs", args.steps, args.warmup, hip, use_graph, torch, dev, cpu)
         del c4
         c5 = synth.c5()
         others["relaxed_b64_k8"] = other_workload(
             lib, "relaxed", c5, c5.algorithmic_bytes_relaxed,
             f"relaxed (p >= {c5.tau} or top-{c5.top_k}), B=64 K=8 V=151936 bf16", args.steps,
-            args.warmup, hip, use_graph, torch, dev)
+            args.warmup, hip, use_graph, torch, dev, cpu)
         others["exact_b64_k8"] = other_workload(
             lib, "exact", c5, c5.algorithmic_bytes_exact,
             "exact, B=64 K=8 V=151936 bf16, draft target+0.8*N(0,1)", args.steps, args.warmup,
-            hip, use_graph, torch, dev)
+            hip, use_graph, torch, dev, cpu)
         del c5
         others["sharded_exact_greedy_g8"] = sharded_block(lib, ci, 8, min(args.steps, 200),
                                                          min(args.warmup, 20), hip, torch, dev)
@@ -606,7 +699,11 @@ def main():
                      "kernel": "k_stream<bf16, exact> (reads every logit once)",
                      "kernel_us_mean": k_ms * 1e3, "kernel_us_min": r_ex["kernel_ms_min"] * 1e3,
                      "algorithmic_bytes_per_launch": stream_bytes,
-                     "rest_of_call_us_mean": r_ex["rest_ms_mean"] * 1e3},
+                     "rest_of_call_us_mean": r_ex["rest_ms_mean"] * 1e3,
+                     "frac_of_read_ceiling": achieved / ceiling["gbs"],
+                     "call_gbs_on_kernel_time": bytes_exact / ((k_ms + r_ex["rest_ms_mean"]) * 1e-3) / 1e9},
+        "read_ceiling": ceiling,
+        "graph_ms_per_step_runs": r_ex.get("graph_ms_per_step_runs"),
         "eager": {"rounds_per_s": 1000.0 / r_ex["eager_ms_per_step"],
                   "ms_per_step": r_ex["eager_ms_per_step"]},
         "greedy_c3_shape": {
@@ -615,6 +712,9 @@ def main():
             "kernel_us_mean": r_gr["kernel_ms_mean"] * 1e3,
             "kernel_gbs": ci.target.nbytes / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9,
             "kernel_frac": ci.target.nbytes / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_frac_of_read_ceiling": ci.target.nbytes / (r_gr["kernel_ms_mean"] * 1e-3) / 1e9
+                                           / ceiling_g["gbs"],
+            "read_ceiling": ceiling_g,
             "rest_of_call_us_mean": r_gr["rest_ms_mean"] * 1e3,
             "eager_rounds_per_s": 1000.0 / r_gr["eager_ms_per_step"],
             "algorithmic_bytes": bytes_greedy, "input_sets": sets_greedy},

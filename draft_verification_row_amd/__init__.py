@@ -64,6 +64,10 @@ def load_library():
                   ("spec_shard_workspace_bytes", 1)):
         getattr(lib, fn).argtypes = [I] * n
         getattr(lib, fn).restype = Z
+    lib.spec_read_ceiling_out_words.argtypes = [Z]
+    lib.spec_read_ceiling_out_words.restype = Z
+    lib.spec_read_ceiling.argtypes = [P, Z, P, P]
+    lib.spec_read_ceiling.restype = I
     lib.spec_shard_stats_greedy.argtypes = [P, I, I, I, I, I, I, I, P, Z, P]
     lib.spec_shard_stats_tree.argtypes = [P, I, P, I, I, I, I, I, I, P, Z, P]
     lib.spec_shard_stats_exact.argtypes = [P, P, I, P, I, I, I, I, I, P, Z, P]

@@ -689,6 +689,30 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     }
 }
 
+// ------------------------------------------------------- read ceiling
+// The streaming kernel's memory access with no arithmetic: one workgroup per
+// 16 KiB tile, four non-temporal 16-byte loads per thread, an xor of the
+// words so the loads stay live, one word written per workgroup.  Its rate is
+// the practical ceiling the streaming kernel is measured against.
+__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_read(const unsigned char* data, size_t nvec,
+                                                                      uint32_t* out) {
+    const size_t v0 = (size_t)blockIdx.x * (kThreads * kTileVecs) + threadIdx.x;
+    u32x4 q[kTileVecs];
+#pragma unroll
+    for (int k = 0; k < kTileVecs; ++k) {
+        const size_t v = min(v0 + (size_t)k * kThreads, nvec - 1);
+        q[k] = __builtin_nontemporal_load((const gu32x4*)(data + v * 16));
+    }
+    uint32_t x = 0u;
+#pragma unroll
+    for (int k = 0; k < kTileVecs; ++k) x ^= q[k].x ^ q[k].y ^ q[k].z ^ q[k].w;
+    x = (uint32_t)wave_max_i((int)(x & 0x7fffffffu));
+    __shared__ uint32_t s_x[kWaves];
+    if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3];
+}
+
 // ------------------------------------------------------- row statistics
 // Row max M, argmax g (lowest index), rank count c and log normalizer
 // lnS = log sum exp(l - M) of the rows of one request, in LDS.
@@ -1782,6 +1806,24 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out_target_logprob) return launch<kTree, true>(a, dtype, st);
     return launch<kTree, false>(a, dtype, st);
+}
+
+size_t spec_read_ceiling_out_words(size_t bytes) {
+    if (bytes < 16 || bytes % 16 != 0) return 0;
+    return (bytes + kTileBytes - 1) / kTileBytes;
+}
+
+spec_status spec_read_ceiling(const void* data, size_t bytes, uint32_t* out, void* stream) {
+    const size_t words = spec_read_ceiling_out_words(bytes);
+    if (!data || !out || words == 0 || words > (size_t)INT_MAX || ((uintptr_t)data % 16) != 0)
+        return SPEC_EINVAL;
+    hipEvent_t ev[3];
+    take_prof(ev);
+    hipExtLaunchKernelGGL(k_read, dim3((unsigned)words), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                          ev[0], ev[1], 0, static_cast<const unsigned char*>(data), bytes / 16, out);
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    if (ev[2] && hipEventRecord(ev[2], static_cast<hipStream_t>(stream)) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
 }
 
 // ------------------------------------------------------ vocabulary shards

@@ -113,6 +113,19 @@ const char *spec_status_string(int status);
 void spec_verify_profile_next_call(void *before_stream, void *after_stream, void *after_call);
 
 /*
+ * Host-only benchmarking aid: the practical read ceiling.  spec_read_ceiling
+ * reads `bytes` bytes (a multiple of 16, from a 16-byte aligned device
+ * pointer) with the streaming kernel's access pattern and no arithmetic: one
+ * workgroup per 16 KiB, non-temporal 16-byte loads; it writes one word per
+ * 16 KiB to out (spec_read_ceiling_out_words(bytes) words, device memory;
+ * their values carry no meaning).  The profiling hook above applies to it
+ * (its only kernel).  SPEC_EINVAL for a null pointer, a misaligned pointer
+ * or a size that is zero or not a multiple of 16.
+ */
+size_t spec_read_ceiling_out_words(size_t bytes);
+spec_status spec_read_ceiling(const void *data, size_t bytes, uint32_t *out, void *stream);
+
+/*
  * Greedy chain verification (mini-sglang PR #134, "Modifications",
  * verify_drafts): draft j is accepted while it equals the argmax of target
  * row j (lowest index among equal maxima); the first unmatched row (row K if

@@ -206,3 +206,14 @@ def test_shard_argument_errors(lib):
               None, PWS, ws, None) == SPEC_EWORKSPACE
     assert sa(P4K, P4K, 1, PWS, P4K, 2, 3, 1000, 4, 9, P4K, None, None, None, PWS, ws,
               None) == SPEC_EINVAL
+
+
+def test_read_ceiling_argument_errors(lib):
+    w = lib.spec_read_ceiling_out_words
+    assert w(0) == 0 and w(15) == 0 and w(24) == 0
+    assert w(16) == 1 and w(16384) == 1 and w(16400) == 2
+    r = lib.spec_read_ceiling
+    assert r(None, 16384, P4K, None) == SPEC_EINVAL
+    assert r(P4K, 16384, None, None) == SPEC_EINVAL
+    assert r(P4K, 100, P4K, None) == SPEC_EINVAL                  # not a multiple of 16
+    assert r(ctypes.c_void_p(4100), 16384, P4K, None) == SPEC_EINVAL  # misaligned
