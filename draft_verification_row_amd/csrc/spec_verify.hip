@@ -15,7 +15,8 @@
 //     README, intro and benchmark section).
 //
 // How it is computed here (no kernel design comes from the pages): two or
-// three kernels per call on the caller's stream.
+// three kernels per call on the caller's stream.  Vocabulary-sharded calls
+// run the same kernels one step at a time (spec_shard_*).
 //
 //   k_stream  one workgroup per (logit row, 16 KB tile).  Each thread issues
 //             its four 16-byte loads at once; the workgroup reduces the tile
@@ -46,6 +47,9 @@
 //             them and finds the chunk holding u_K * Z; the workgroup rescans
 //             that chunk with a block scan and writes the terminal token and
 //             its log-probs.
+//
+//   The draft sampler (one draw per row) streams with k_stream_rows, which
+//   leaves the fp64 chunk sums in the one pass, then runs k_sample.
 //
 // Every reduction runs in a fixed order, so results are bitwise
 // reproducible.  No atomics are used: data passes between workgroups only
@@ -88,7 +92,7 @@ static_assert(kMaxTiles <= 64, "a row's tile records must fit one wave");
 constexpr int kMaxC2 = (SPEC_MAX_V + kChunk - 1) / kChunk;
 static_assert(kMaxC2 <= 64, "a row's pass-2 chunks must fit one wave");
 
-enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3, kPower = 4 };
+enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3, kPower = 4, kSample = 5 };
 
 // Rules that stream the draft rows and test p/q.
 constexpr bool uses_draft(int mode) { return mode == kExact || mode == kPower; }
@@ -689,6 +693,79 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     }
 }
 
+// ------------------------------------------------------ sampler stream
+// The draft sampler draws from every row it streams, so the fp64 chunk sums
+// its inverse CDF needs are taken in the one pass: one workgroup per 16 KiB
+// tile finds the tile max M, then sums exp(l - M) in fp64 (the Cody-Waite exp
+// above) over each 4096-token chunk of the tile.  Each chunk's record is
+// {sum, M}; the sampling kernel rescales them to the row max.
+template <typename T, bool VECP>
+__global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_stream_rows(const Args a) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int TILE = kThreads * kTileVecs * VEC;
+    constexpr int CPT = TILE / kChunk;  // chunks per tile: 2 (bf16) or 1 (fp32)
+    static_assert(CPT * kChunk == TILE && kTileVecs % CPT == 0, "a tile holds whole chunks");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    __shared__ double tab[kExpTab];
+    __shared__ float s_m[kWaves];
+    __shared__ double s_s[kWaves][CPT];
+    fill_exp_table(tab);
+
+    const int g = uniform((int)(blockIdx.x / (unsigned)a.tpr));
+    const int c = (int)blockIdx.x - g * a.tpr;
+    int vec, act;
+    const T* row = call_row<T, kRelaxed>(a, g, vec, act);
+    u32x4 q[kTileVecs];
+    load_tile<T, true, VECP>(row, a.V, c, q);
+    const int t0 = c * TILE + (int)threadIdx.x * VEC;
+    if (c == a.tpr - 1 && a.V % TILE != 0) {
+#pragma unroll
+        for (int k = 0; k < kTileVecs; ++k) Elem<T>::mask_tail(q[k], t0 + k * kThreads * VEC, a.V);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kTileVecs; ++k) {
+        float v[VEC];
+        Elem<T>::unpack(q[k], v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) m = fmaxf(m, v[i]);
+    }
+    m = wave_max(m);
+    if (lane == 0) s_m[wave] = m;
+    __syncthreads();  // also publishes the exp table
+    const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    // vector k of a thread lies in chunk k / (kTileVecs / CPT) of the tile
+    double acc[CPT];
+#pragma unroll
+    for (int h = 0; h < CPT; ++h) acc[h] = 0.0;
+    if (M > -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < kTileVecs; ++k) {
+            float v[VEC];
+            Elem<T>::unpack(q[k], v);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[k / (kTileVecs / CPT)] += exp_nonpos((double)v[i] - (double)M, tab);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < CPT; ++h) {
+        acc[h] = wave_sum(acc[h]);
+        if (lane == 0) s_s[wave][h] = acc[h];
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < CPT) {
+        const int h = threadIdx.x, ch = c * CPT + h;
+        if (ch < a.C2) {
+            ChunkSums cs;
+            cs.sa = ((s_s[0][h] + s_s[1][h]) + s_s[2][h]) + s_s[3][h];
+            cs.sb = (double)M;
+            cs.pa = cs.pb = 0.0;
+            a.sums[(size_t)g * a.C2 + ch] = cs;
+        }
+    }
+}
+
 // ------------------------------------------------------- read ceiling
 // The streaming kernel's memory access with no arithmetic: one workgroup per
 // 16 KiB tile, four non-temporal 16-byte loads per thread, an xor of the
@@ -1199,10 +1276,16 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     __shared__ int s_pick[kSampleWaves][3];
     fill_exp_table(tab);
 
-    const Decision dc = a.dec[b];
+    // The draft sampler (kSample) has no decision: it draws from its only row,
+    // whose max and chunk masses it takes from the chunk records.
+    constexpr bool ROWS = (MODE == kSample);
+    __shared__ double s_Mt;
+    Decision dc = {};
+    if (!ROWS) dc = a.dec[b];
     const int n = dc.n;
     const bool residual = EXACT && dc.residual;
-    const double Mt = dc.Mt, Md = dc.Md, cls = dc.cls;
+    const double Md = dc.Md, cls = dc.cls;
+    if (ROWS) __syncthreads();  // the exp table, used by wave 0 below
     if (wave == 0) {
         // lane l holds chunk l
         ChunkSums cs = {0.0, 0.0, 0.0, 0.0};
@@ -1214,6 +1297,13 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
                 at = (size_t)sl * a.sums_slot + (size_t)b * a.C2 + (lane - sl * a.C2);
             }
             cs = a.sums[at];
+        }
+        if (ROWS) {
+            // chunk records {sum of exp(l - m), m}: rescale to the row max
+            const float mc = lane < nchunk ? (float)cs.sb : -INFINITY;
+            const float Mr = wave_max(mc);
+            cs.sa = mc > -INFINITY ? cs.sa * exp_nonpos((double)mc - (double)Mr, tab) : 0.0;
+            if (lane == 0) s_Mt = (double)Mr;
         }
         const double S = wave_sum(cs.sa);
         const double Sq = residual ? wave_sum(cs.sb) : 1.0;
@@ -1254,6 +1344,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     }
     __syncthreads();
 
+    const double Mt = ROWS ? s_Mt : dc.Mt;
+    if (ROWS && t == 0) a.out_status[b] = 0;
     int cstar = s_cstar;
     if (SHARD) {
         const int owner = cstar / a.C2;
@@ -1539,9 +1631,9 @@ spec_status shard_launch(K kernel, dim3 grid, dim3 block, const Args& a, hipStre
 
 bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
 
-// The draft sampler runs the relaxed path with no drafts: each row is a
-// request whose only row is sampled at its uniform.  Its accept lengths (all
-// zero) go to the workspace after the layout.
+// The draft sampler's workspace: the layout of one row per request (it uses
+// the chunk-sum region) and a row-count tail that the size query has always
+// included.
 size_t sample_layout_bytes(int rows, int V, spec_dtype dt) {
     return make_layout(rows, 1, tpr_of(dt, V), c2_of(dt, V)).total + align_up((size_t)rows * 4, 256);
 }
@@ -1764,9 +1856,32 @@ spec_status spec_sample_drafts(const void* logits, spec_dtype dtype, const float
     a.out_status = out_status;
     a.L = 1;
     a.ws = static_cast<unsigned char*>(workspace);
-    a.out_len = reinterpret_cast<int32_t*>(
-        a.ws + make_layout(rows, 1, tpr_of(dtype, V), c2_of(dtype, V)).total);
-    return launch<kRelaxed, true>(a, dtype, static_cast<hipStream_t>(stream));
+    a.tpr = tpr_of(dtype, V);
+    a.Vtot = V;
+    a.sums = reinterpret_cast<ChunkSums*>(a.ws + make_layout(rows, 1, a.tpr, a.C2).sums);
+    // one pass that leaves fp64 chunk sums, then the draw
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[3];
+    take_prof(ev);
+    const dim3 grid((unsigned)rows * (unsigned)a.tpr), block(kThreads);
+    if (dtype == SPEC_BF16) {
+        if (a.vec_t)
+            hipExtLaunchKernelGGL((k_stream_rows<uint16_t, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        else
+            hipExtLaunchKernelGGL((k_stream_rows<uint16_t, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+        hipLaunchKernelGGL((k_sample<uint16_t, kSample, false>), dim3(rows), dim3(kSampleThreads), 0, st, a);
+    } else {
+        if (a.vec_t)
+            hipExtLaunchKernelGGL((k_stream_rows<float, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        else
+            hipExtLaunchKernelGGL((k_stream_rows<float, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+        hipLaunchKernelGGL((k_sample<float, kSample, false>), dim3(rows), dim3(kSampleThreads), 0, st, a);
+    }
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
 }
 
 spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
