@@ -43,9 +43,9 @@ KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_veri
 # from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch,
 # averaged over dispatches), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
-# Reported only while the kernel source is the one the counters were taken
-# on.
-TRAFFIC = {"source_sha256": "3a7c469e4aaa4427d4acbe8fe7e8c957b3c977d450fde0aabb117d085d88e6d6",
+# Reported only while the source of the streaming kernel (the file up to its
+# end) is the one the counters were taken on.
+TRAFFIC = {"source_sha256": "63594638e89db8ae78b295a3c8ace46028a5efa37d4b85d53bd469511fd12a78",
            "fetch_kib": 44146.8, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 MALL_BYTES = 256 * 1024 * 1024
@@ -530,16 +530,27 @@ def markov_block(torch, dev, rounds, with_cpu):
     return res
 
 
-def kernel_source_sha256() -> str:
+# The streaming kernel can only depend on source above its end; the section
+# that follows it in the file starts with this line.
+KERNEL_END_MARKER = "// ------------------------------------------------------ sampler stream"
+
+
+def kernel_source_sha256():
+    """SHA-256 of the kernel source up to the end of the streaming kernel
+    (everything it can depend on), or None if the layout has changed."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        src = f.read()
+    i = src.find(KERNEL_END_MARKER)
+    if i < 0 or "void k_stream(" not in src[:i]:
+        return None
+    return hashlib.sha256(src[:i].encode()).hexdigest()
 
 
 def traffic_bytes():
     """HBM bytes per streaming-kernel dispatch from the recorded counters, or
     None when none are recorded for the current kernel source."""
-    if not TRAFFIC or TRAFFIC["source_sha256"] != kernel_source_sha256():
+    if not TRAFFIC or kernel_source_sha256() is None or TRAFFIC["source_sha256"] != kernel_source_sha256():
         return None
     return int(TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] * 1024 +
                TRAFFIC["write_kib"] * TRAFFIC["write_scale"] * 1024)

@@ -2066,16 +2066,20 @@ spec_status spec_shard_combine_tree(const void* records, spec_dtype dtype,
     return shard_launch(k_decide<float, kTree, false, true>, grid, block, a, st);
 }
 
-spec_status spec_shard_sweep_exact(const void* target_shard, const void* draft_shard,
-                                   spec_dtype dtype, const void* records,
-                                   const int32_t* draft_tokens, const float* uniforms, int B,
-                                   int K, int V, int G, int shard, int32_t* out_tokens,
-                                   int32_t* out_accept_len, float* out_target_logprob,
-                                   float* out_behavior_logprob, int32_t* out_status,
-                                   void* out_sums, size_t sums_bytes, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+template <int MODE>
+spec_status shard_sweep(const void* target_shard, const void* draft_shard, spec_dtype dtype,
+                        const void* records, const int32_t* draft_tokens, const float* uniforms,
+                        int B, int K, int V, int G, int shard, float alpha, int32_t* out_tokens,
+                        int32_t* out_accept_len, float* out_target_logprob,
+                        float* out_behavior_logprob, int32_t* out_status, void* out_sums,
+                        size_t sums_bytes, void* workspace, size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
     if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, 2 * K + 1)) return SPEC_EINVAL;
+    if (MODE == kPower && (!(alpha >= 0.f) || alpha == INFINITY)) return SPEC_EINVAL;
     if (!target_shard || !draft_shard || !draft_tokens || !uniforms || !out_tokens ||
         !out_accept_len || !out_status)
         return SPEC_EINVAL;
@@ -2089,6 +2093,7 @@ spec_status spec_shard_sweep_exact(const void* target_shard, const void* draft_s
     a.D = draft_shard;
     a.tok = draft_tokens;
     a.u = uniforms;
+    a.alpha = alpha;
     a.vec_t = vec_ok(target_shard, dtype, a.V);
     a.vec_d = vec_ok(draft_shard, dtype, a.V);
     a.out_tok = out_tokens;
@@ -2100,16 +2105,16 @@ spec_status spec_shard_sweep_exact(const void* target_shard, const void* draft_s
     a.dec = static_cast<Decision*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)B * (unsigned)((a.C2 + kSweepGroups - 1) / kSweepGroups)), block(kSweepThreads);
-    if (dtype == SPEC_BF16) return shard_launch(k_sweep<uint16_t, kExact, true>, grid, block, a, st);
-    return shard_launch(k_sweep<float, kExact, true>, grid, block, a, st);
+    if (dtype == SPEC_BF16) return shard_launch(k_sweep<uint16_t, MODE, true>, grid, block, a, st);
+    return shard_launch(k_sweep<float, MODE, true>, grid, block, a, st);
 }
 
-spec_status spec_shard_sample_exact(const void* target_shard, const void* draft_shard,
-                                    spec_dtype dtype, const void* sums, const float* uniforms,
-                                    int B, int K, int V, int G, int shard, int32_t* out_tokens,
-                                    float* out_target_logprob, float* out_behavior_logprob,
-                                    int32_t* out_sample_shard, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+template <int MODE>
+spec_status shard_sample(const void* target_shard, const void* draft_shard, spec_dtype dtype,
+                         const void* sums, const float* uniforms, int B, int K, int V, int G,
+                         int shard, int32_t* out_tokens, float* out_target_logprob,
+                         float* out_behavior_logprob, int32_t* out_sample_shard, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
     if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, 2 * K + 1)) return SPEC_EINVAL;
     if (!target_shard || !draft_shard || !uniforms || !out_tokens) return SPEC_EINVAL;
@@ -2130,8 +2135,62 @@ spec_status spec_shard_sample_exact(const void* target_shard, const void* draft_
     a.out_owner = out_sample_shard;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(B), block(kSampleThreads);
-    if (dtype == SPEC_BF16) return shard_launch(k_sample<uint16_t, kExact, true>, grid, block, a, st);
-    return shard_launch(k_sample<float, kExact, true>, grid, block, a, st);
+    if (dtype == SPEC_BF16) return shard_launch(k_sample<uint16_t, MODE, true>, grid, block, a, st);
+    return shard_launch(k_sample<float, MODE, true>, grid, block, a, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+spec_status spec_shard_sweep_exact(const void* target_shard, const void* draft_shard,
+                                   spec_dtype dtype, const void* records,
+                                   const int32_t* draft_tokens, const float* uniforms, int B,
+                                   int K, int V, int G, int shard, int32_t* out_tokens,
+                                   int32_t* out_accept_len, float* out_target_logprob,
+                                   float* out_behavior_logprob, int32_t* out_status,
+                                   void* out_sums, size_t sums_bytes, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    return shard_sweep<kExact>(target_shard, draft_shard, dtype, records, draft_tokens, uniforms, B, K, V, G,
+                               shard, 0.f, out_tokens, out_accept_len, out_target_logprob,
+                               out_behavior_logprob, out_status, out_sums, sums_bytes, workspace,
+                               workspace_bytes, stream);
+}
+
+spec_status spec_shard_sweep_power(const void* target_shard, const void* draft_shard,
+                                   spec_dtype dtype, const void* records,
+                                   const int32_t* draft_tokens, const float* uniforms, int B,
+                                   int K, int V, int G, int shard, float alpha, int32_t* out_tokens,
+                                   int32_t* out_accept_len, float* out_target_logprob,
+                                   float* out_behavior_logprob, int32_t* out_status,
+                                   void* out_sums, size_t sums_bytes, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    return shard_sweep<kPower>(target_shard, draft_shard, dtype, records, draft_tokens, uniforms, B, K, V, G,
+                               shard, alpha, out_tokens, out_accept_len, out_target_logprob,
+                               out_behavior_logprob, out_status, out_sums, sums_bytes, workspace,
+                               workspace_bytes, stream);
+}
+
+spec_status spec_shard_sample_exact(const void* target_shard, const void* draft_shard,
+                                    spec_dtype dtype, const void* sums, const float* uniforms,
+                                    int B, int K, int V, int G, int shard, int32_t* out_tokens,
+                                    float* out_target_logprob, float* out_behavior_logprob,
+                                    int32_t* out_sample_shard, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return shard_sample<kExact>(target_shard, draft_shard, dtype, sums, uniforms, B, K, V, G, shard,
+                                out_tokens, out_target_logprob, out_behavior_logprob, out_sample_shard,
+                                workspace, workspace_bytes, stream);
+}
+
+spec_status spec_shard_sample_power(const void* target_shard, const void* draft_shard,
+                                    spec_dtype dtype, const void* sums, const float* uniforms,
+                                    int B, int K, int V, int G, int shard, int32_t* out_tokens,
+                                    float* out_target_logprob, float* out_behavior_logprob,
+                                    int32_t* out_sample_shard, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return shard_sample<kPower>(target_shard, draft_shard, dtype, sums, uniforms, B, K, V, G, shard,
+                                out_tokens, out_target_logprob, out_behavior_logprob, out_sample_shard,
+                                workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

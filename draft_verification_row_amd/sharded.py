@@ -28,8 +28,9 @@ from . import (SpecVerifyError, TreeResult, VerifyResult, _check, _dtype_code, _
 __all__ = ["shard_record_bytes", "shard_sums_bytes", "shard_workspace_bytes",
            "shard_stats_greedy", "shard_stats_tree", "shard_stats_exact",
            "shard_combine_greedy", "shard_combine_tree", "shard_sweep_exact",
-           "shard_sample_exact", "verify_greedy_sharded", "verify_tree_sharded",
-           "verify_exact_sharded", "ShardedExactResult"]
+           "shard_sample_exact", "shard_sweep_power", "shard_sample_power",
+           "verify_greedy_sharded", "verify_tree_sharded", "verify_exact_sharded",
+           "verify_power_sharded", "ShardedExactResult"]
 
 
 def shard_record_bytes(dtype: torch.dtype, B: int, rows_per_request: int, V: int, G: int) -> int:
@@ -123,6 +124,41 @@ def shard_combine_tree(records: torch.Tensor, dtype: torch.dtype, node_tokens, p
     return TreeResult(path, tok, ln, tlp, blp, st)
 
 
+def shard_sweep_power(target_shard, draft_shard, records: torch.Tensor, draft_tokens, uniforms,
+                      G: int, shard: int, alpha: float, out: VerifyResult, out_sums: torch.Tensor,
+                      workspace: torch.Tensor):
+    """The power rule's step 2; its records come from shard_stats_exact."""
+    B, L, V = _shard_logits(target_shard, "target_shard", G)
+    K = L - 1
+    _check(draft_shard, "draft_shard", target_shard.dtype, (B, K, V // G))
+    x = _check(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    u = _check(uniforms, "uniforms", torch.float32, (B, L))
+    rec, sums, ws = _slot(records, "records"), _slot(out_sums, "out_sums"), _slot(workspace, "workspace")
+    rc = load_library().spec_shard_sweep_power(
+        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(rec), _ptr(x),
+        _ptr(u), B, K, V, G, shard, ctypes.c_float(alpha), _ptr(out.tokens), _ptr(out.accept_len),
+        _ptr(out.target_logprob), _ptr(out.behavior_logprob), _ptr(out.status), _ptr(sums),
+        sums.numel(), _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
+    _raise(rc, "spec_shard_sweep_power")
+
+
+def shard_sample_power(target_shard, draft_shard, sums: torch.Tensor, uniforms, G: int,
+                       shard: int, out: VerifyResult, out_sample_shard: Optional[torch.Tensor],
+                       workspace: torch.Tensor):
+    B, L, V = _shard_logits(target_shard, "target_shard", G)
+    K = L - 1
+    _check(draft_shard, "draft_shard", target_shard.dtype, (B, K, V // G))
+    u = _check(uniforms, "uniforms", torch.float32, (B, L))
+    sm, ws = _slot(sums, "sums"), _slot(workspace, "workspace")
+    own = None if out_sample_shard is None else _check(out_sample_shard, "out_sample_shard",
+                                                       torch.int32, (B,))
+    rc = load_library().spec_shard_sample_power(
+        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(sm), _ptr(u), B, K,
+        V, G, shard, _ptr(out.tokens), _ptr(out.target_logprob), _ptr(out.behavior_logprob),
+        _ptr(own), _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
+    _raise(rc, "spec_shard_sample_power")
+
+
 def shard_sweep_exact(target_shard, draft_shard, records: torch.Tensor, draft_tokens, uniforms,
                       G: int, shard: int, out: VerifyResult, out_sums: torch.Tensor,
                       workspace: torch.Tensor):
@@ -207,6 +243,17 @@ class ShardedExactResult(NamedTuple):
 def verify_exact_sharded(target_shards: Sequence[torch.Tensor],
                          draft_shards: Sequence[torch.Tensor], draft_tokens, uniforms, *,
                          logprobs: bool = True) -> ShardedExactResult:
+    return _verify_pq_sharded(target_shards, draft_shards, draft_tokens, uniforms, None, logprobs)
+
+
+def verify_power_sharded(target_shards: Sequence[torch.Tensor],
+                         draft_shards: Sequence[torch.Tensor], draft_tokens, uniforms,
+                         alpha: float, *, logprobs: bool = True) -> ShardedExactResult:
+    return _verify_pq_sharded(target_shards, draft_shards, draft_tokens, uniforms, alpha, logprobs)
+
+
+def _verify_pq_sharded(target_shards, draft_shards, draft_tokens, uniforms, alpha, logprobs):
+    """The exact rule (alpha None) or the power rule over G shards on one device."""
     G = len(target_shards)
     if len(draft_shards) != G:
         raise SpecVerifyError("one draft shard per target shard")
@@ -225,8 +272,15 @@ def verify_exact_sharded(target_shards: Sequence[torch.Tensor],
         shard_stats_exact(target_shards[s], draft_shards[s], draft_tokens, G, s,
                           rec[s * slot:(s + 1) * slot])
     for s in range(G):
-        shard_sweep_exact(target_shards[s], draft_shards[s], rec, draft_tokens, uniforms, G, s,
-                          out, sums[s * sslot:(s + 1) * sslot], ws[s])
+        if alpha is None:
+            shard_sweep_exact(target_shards[s], draft_shards[s], rec, draft_tokens, uniforms, G, s,
+                              out, sums[s * sslot:(s + 1) * sslot], ws[s])
+        else:
+            shard_sweep_power(target_shards[s], draft_shards[s], rec, draft_tokens, uniforms, G, s,
+                              alpha, out, sums[s * sslot:(s + 1) * sslot], ws[s])
     for s in range(G):
-        shard_sample_exact(target_shards[s], draft_shards[s], sums, uniforms, G, s, out, own, ws[s])
+        if alpha is None:
+            shard_sample_exact(target_shards[s], draft_shards[s], sums, uniforms, G, s, out, own, ws[s])
+        else:
+            shard_sample_power(target_shards[s], draft_shards[s], sums, uniforms, G, s, out, own, ws[s])
     return ShardedExactResult(out, own)

@@ -343,6 +343,24 @@ spec_status spec_shard_sweep_exact(const void *target_shard, const void *draft_s
                                    int32_t *out_status, void *out_sums, size_t sums_bytes,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Steps 2 and 3 of the power rule (spec_verify_power's rule and outputs; alpha
+ * finite and >= 0).  Its statistics are the exact rule's: step 1 is
+ * spec_shard_stats_exact, with record and sums slots sized alike. */
+spec_status spec_shard_sweep_power(const void *target_shard, const void *draft_shard,
+                                   spec_dtype dtype, const void *records,
+                                   const int32_t *draft_tokens, const float *uniforms, int B,
+                                   int K, int V, int G, int shard, float alpha,
+                                   int32_t *out_tokens, int32_t *out_accept_len,
+                                   float *out_target_logprob, float *out_behavior_logprob,
+                                   int32_t *out_status, void *out_sums, size_t sums_bytes,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+spec_status spec_shard_sample_power(const void *target_shard, const void *draft_shard,
+                                    spec_dtype dtype, const void *sums, const float *uniforms,
+                                    int B, int K, int V, int G, int shard, int32_t *out_tokens,
+                                    float *out_target_logprob, float *out_behavior_logprob,
+                                    int32_t *out_sample_shard, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 /* Step 3, exact: sums = the G gathered sums slots.  The owning shard writes
  * out_tokens[b][accept_len[b]] and the two log-probs there (NULL log-prob
  * arrays are skipped); every shard writes out_sample_shard[b] = the owning

@@ -217,3 +217,18 @@ def test_read_ceiling_argument_errors(lib):
     assert r(P4K, 16384, None, None) == SPEC_EINVAL
     assert r(P4K, 100, P4K, None) == SPEC_EINVAL                  # not a multiple of 16
     assert r(ctypes.c_void_p(4100), 16384, P4K, None) == SPEC_EINVAL  # misaligned
+
+
+def test_shard_power_argument_errors(lib):
+    sums, ws = lib.spec_shard_sums_bytes(2, 1000, 4), lib.spec_shard_workspace_bytes(2)
+    base = [P4K, P4K, 1, PWS, P4K, P4K, 2, 3, 1000, 4, 1, ctypes.c_float(0.5), P4K, P4K, None, None,
+            P4K, PWS, sums, PWS, ws, None]
+    for alpha in (-1.0, float("inf"), float("nan")):
+        bad = list(base)
+        bad[11] = ctypes.c_float(alpha)
+        assert lib.spec_shard_sweep_power(*bad) == SPEC_EINVAL
+    bad = list(base)
+    bad[8] = 1001                     # not a multiple of G
+    assert lib.spec_shard_sweep_power(*bad) == SPEC_EINVAL
+    assert lib.spec_shard_sample_power(P4K, P4K, 1, PWS, P4K, 2, 3, 1000, 4, 4, P4K, None, None,
+                                       None, PWS, ws, None) == SPEC_EINVAL   # shard = G

@@ -341,3 +341,20 @@ def test_first_token_histogram_matches_target():
     chi2 = ((obs - exp) ** 2 / exp).sum()
     # chi-square with 31 degrees of freedom: P(chi2 > 70) < 1e-4
     assert chi2 < 70, chi2
+
+
+def test_read_ceiling_kernel_runs_on_odd_sizes():
+    """The benchmarking read kernel reads any multiple of 16 bytes and writes
+    one word per 16 KiB; its ragged last tile stays inside the buffer."""
+    import ctypes
+    lib = sv.load_library()
+    for nbytes in (16, 16384, 16400, 3 * 16384 + 48):
+        buf = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda")
+        words = lib.spec_read_ceiling_out_words(nbytes)
+        assert words == (nbytes + 16383) // 16384
+        out = torch.full((words + 1,), -1, dtype=torch.int32, device="cuda")
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert lib.spec_read_ceiling(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                     ctypes.c_void_p(out.data_ptr()), st) == 0
+        torch.cuda.synchronize()
+        assert int(out[words]) == -1  # nothing written past the last word

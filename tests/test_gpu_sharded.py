@@ -174,3 +174,44 @@ def test_tree_sharded_partial_counts_and_bad_parents():
     ti.node_tok[4, 7] = 10 ** 6
     o = oracle.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes)
     compare_tree(_tree_sharded(ti, 4), o, what="sharded tree edge")
+
+
+# ------------------------------------------------------------------ power
+@pytest.mark.parametrize("alpha", [0.5, 2.0])
+def test_power_c3_eight_shards(alpha):
+    print(f"sharded power c3 g8 alpha={alpha}", flush=True)
+    ci = synth.c3()
+    o = oracle.power(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16", alpha)
+    T = _split(dev_logits(ci.target, "bf16"), 8)
+    D = _split(dev_logits(ci.draft, "bf16"), 8)
+    res = sh.verify_power_sharded(T, D, dev(ci.tokens), dev(ci.uniforms), alpha)
+    torch.cuda.synchronize()
+    t = compare_chain(res.result, o, what=f"sharded power {alpha}")
+    assert t.within_budget(), t
+    _check_owner(res, 8, ci.V)
+
+
+def test_power_one_shard_is_the_unsharded_call():
+    ci = synth.chain_inputs(8, 5, 30000, "bf16", seed=101, useed=102)
+    T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
+    x, u = dev(ci.tokens), dev(ci.uniforms)
+    a = sv.spec_verify_power(T, D, x, u, 0.7)
+    b = sh.verify_power_sharded([T], [D], x, u, 0.7).result
+    torch.cuda.synchronize()
+    for f in ("tokens", "accept_len", "target_logprob", "behavior_logprob", "status"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+def test_power_sharded_ragged_fp32():
+    ci = synth.chain_inputs(5, 3, 3 * 2999, "f32", seed=103, useed=104)
+    o = oracle.power(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32", 1.5)
+    res = _pq_power(ci, 3, 1.5)
+    compare_chain(res.result, o, what="sharded power fp32 ragged")
+
+
+def _pq_power(ci, G, alpha):
+    T = _split(dev_logits(ci.target, ci.dtype), G)
+    D = _split(dev_logits(ci.draft, ci.dtype), G)
+    r = sh.verify_power_sharded(T, D, dev(ci.tokens), dev(ci.uniforms), alpha)
+    torch.cuda.synchronize()
+    return r
