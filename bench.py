@@ -45,8 +45,8 @@ KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_veri
 # plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Reported only while the source of the streaming kernel (the file up to its
 # end) is the one the counters were taken on.
-TRAFFIC = {"source_sha256": "63594638e89db8ae78b295a3c8ace46028a5efa37d4b85d53bd469511fd12a78",
-           "fetch_kib": 44146.8, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"source_sha256": "53ff20b08bad37dd58ec8c2ae4d13c6e1d34858b924e8a25714ffb433e01c9fc",
+           "fetch_kib": 44147.3, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 MALL_BYTES = 256 * 1024 * 1024
 RUNS = 3  # timed replays of the captured steps; the median is reported

@@ -571,7 +571,10 @@ __device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[kTileVec
 // draft logits, one (request, position, row kind) each, for the decision
 // kernels to load beside the tile records.  On a vocabulary shard only the
 // shard whose columns hold the token records it.
-template <typename T, int MODE, bool SUM, bool VECP, bool XV>
+// SHARD (a vocabulary shard's relaxed-rule statistics): the rank count's
+// threshold l_x comes from the gathered drafted-token logits, since the token
+// may be another shard's column.
+template <typename T, int MODE, bool SUM, bool VECP, bool XV, bool SHARD>
 __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const Args a) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int TILE = kThreads * kTileVecs * VEC;
@@ -600,7 +603,11 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
         const int b = g / a.R, rr = g - b * a.R;
         if (rr < a.K) {
             const int x = a.tok[b * a.K + rr];
-            if ((unsigned)x < (unsigned)a.V) thr = Elem<T>::at(row, (size_t)x);
+            if (SHARD) {
+                if ((unsigned)x < (unsigned)a.Vtot) thr = a.xv_in[(size_t)(x / a.V) * a.slot_xv + b * a.K + rr];
+            } else if ((unsigned)x < (unsigned)a.V) {
+                thr = Elem<T>::at(row, (size_t)x);
+            }
         }
     }
 
@@ -764,6 +771,19 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_stream_rows(co
             a.sums[(size_t)g * a.C2 + ch] = cs;
         }
     }
+}
+
+// ------------------------------------------- drafted-token logits (shards)
+// Step 0 of a sharded relaxed call: the logit of each drafted token in its
+// target row, written by the shard whose columns hold the token.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_values(const Args a, float* out) {
+    const int i = (int)(blockIdx.x * kThreads + threadIdx.x);
+    if (i >= a.B * a.K) return;
+    const int b = i / a.K, j = i - b * a.K;
+    const int xl = a.tok[i] - a.shard * a.V;
+    if ((unsigned)xl < (unsigned)a.V)
+        out[i] = Elem<T>::at(reinterpret_cast<const T*>(a.T), (size_t)(b * a.rows_t + j) * a.V + xl);
 }
 
 // ------------------------------------------------------- read ceiling
@@ -1480,20 +1500,20 @@ thread_local hipEvent_t g_prof[3] = {nullptr, nullptr, nullptr};
 
 // The streaming kernel over B * R rows of a.V logits, with the dispatch's
 // own start and stop events when given.
-template <int MODE, bool SUM, bool XV>
+template <int MODE, bool SUM, bool XV, bool SHARD = false>
 spec_status launch_stream(const Args& a, spec_dtype dt, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid((unsigned)a.B * (unsigned)a.R * (unsigned)a.tpr), block(kThreads);
     const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
     if (dt == SPEC_BF16) {
         if (vecp)
-            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true, XV>), grid, block, 0, st, e0, e1, 0, a);
+            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true, XV, SHARD>), grid, block, 0, st, e0, e1, 0, a);
         else
-            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false, XV>), grid, block, 0, st, e0, e1, 0, a);
+            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false, XV, SHARD>), grid, block, 0, st, e0, e1, 0, a);
     } else {
         if (vecp)
-            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, true, XV>), grid, block, 0, st, e0, e1, 0, a);
+            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, true, XV, SHARD>), grid, block, 0, st, e0, e1, 0, a);
         else
-            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, false, XV>), grid, block, 0, st, e0, e1, 0, a);
+            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, false, XV, SHARD>), grid, block, 0, st, e0, e1, 0, a);
     }
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
@@ -1612,7 +1632,8 @@ spec_status shard_stats(Args a, spec_dtype dt, void* out_record, hipStream_t st)
     a.xv_out = reinterpret_cast<float*>(static_cast<unsigned char*>(out_record) + L.xv);
     hipEvent_t ev[3];
     take_prof(ev);
-    if (launch_stream<MODE, SUM, uses_draft(MODE)>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
+    constexpr bool XV = uses_draft(MODE) || MODE == kRelaxed;
+    if (launch_stream<MODE, SUM, XV, MODE == kRelaxed>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
 }
@@ -2070,21 +2091,26 @@ spec_status spec_shard_combine_tree(const void* records, spec_dtype dtype,
 
 namespace {
 
+// Rows per request of a chain rule: target K+1, plus draft K for the rules
+// that test p/q.
+constexpr int chain_rows(int mode, int K) { return uses_draft(mode) ? 2 * K + 1 : K + 1; }
+
 template <int MODE>
 spec_status shard_sweep(const void* target_shard, const void* draft_shard, spec_dtype dtype,
                         const void* records, const int32_t* draft_tokens, const float* uniforms,
-                        int B, int K, int V, int G, int shard, float alpha, int32_t* out_tokens,
-                        int32_t* out_accept_len, float* out_target_logprob,
+                        int B, int K, int V, int G, int shard, float alpha, float tau, int top_k,
+                        int32_t* out_tokens, int32_t* out_accept_len, float* out_target_logprob,
                         float* out_behavior_logprob, int32_t* out_status, void* out_sums,
                         size_t sums_bytes, void* workspace, size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, 2 * K + 1)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, chain_rows(MODE, K))) return SPEC_EINVAL;
     if (MODE == kPower && (!(alpha >= 0.f) || alpha == INFINITY)) return SPEC_EINVAL;
-    if (!target_shard || !draft_shard || !draft_tokens || !uniforms || !out_tokens ||
-        !out_accept_len || !out_status)
+    if (MODE == kRelaxed && (tau != tau || top_k < 0)) return SPEC_EINVAL;
+    if (!target_shard || (uses_draft(MODE) && !draft_shard) || !draft_tokens || !uniforms ||
+        !out_tokens || !out_accept_len || !out_status)
         return SPEC_EINVAL;
     if (!records || ((uintptr_t)records % 256) != 0) return SPEC_EWORKSPACE;
-    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, 2 * K + 1);
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, chain_rows(MODE, K));
     if (!buf_ok(out_sums, sums_bytes, shard_sums_slot(B, a.V)) ||
         !buf_ok(workspace, workspace_bytes, shard_ws_bytes(B)))
         return SPEC_EWORKSPACE;
@@ -2094,8 +2120,10 @@ spec_status shard_sweep(const void* target_shard, const void* draft_shard, spec_
     a.tok = draft_tokens;
     a.u = uniforms;
     a.alpha = alpha;
+    a.tau = tau;
+    a.top_k = top_k;
     a.vec_t = vec_ok(target_shard, dtype, a.V);
-    a.vec_d = vec_ok(draft_shard, dtype, a.V);
+    a.vec_d = uses_draft(MODE) && vec_ok(draft_shard, dtype, a.V);
     a.out_tok = out_tokens;
     a.out_len = out_accept_len;
     a.out_tlp = out_target_logprob;
@@ -2116,16 +2144,16 @@ spec_status shard_sample(const void* target_shard, const void* draft_shard, spec
                          float* out_behavior_logprob, int32_t* out_sample_shard, void* workspace,
                          size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, 2 * K + 1)) return SPEC_EINVAL;
-    if (!target_shard || !draft_shard || !uniforms || !out_tokens) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, chain_rows(MODE, K))) return SPEC_EINVAL;
+    if (!target_shard || (uses_draft(MODE) && !draft_shard) || !uniforms || !out_tokens) return SPEC_EINVAL;
     if (!sums || ((uintptr_t)sums % 256) != 0 || !buf_ok(workspace, workspace_bytes, shard_ws_bytes(B)))
         return SPEC_EWORKSPACE;
-    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, 2 * K + 1);
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, chain_rows(MODE, K));
     a.T = target_shard;
     a.D = draft_shard;
     a.u = uniforms;
     a.vec_t = vec_ok(target_shard, dtype, a.V);
-    a.vec_d = vec_ok(draft_shard, dtype, a.V);
+    a.vec_d = uses_draft(MODE) && vec_ok(draft_shard, dtype, a.V);
     a.sums = static_cast<ChunkSums*>(const_cast<void*>(sums));
     a.sums_slot = shard_sums_slot(B, a.V) / sizeof(ChunkSums);
     a.dec = static_cast<Decision*>(workspace);
@@ -2152,7 +2180,7 @@ spec_status spec_shard_sweep_exact(const void* target_shard, const void* draft_s
                                    void* out_sums, size_t sums_bytes, void* workspace,
                                    size_t workspace_bytes, void* stream) {
     return shard_sweep<kExact>(target_shard, draft_shard, dtype, records, draft_tokens, uniforms, B, K, V, G,
-                               shard, 0.f, out_tokens, out_accept_len, out_target_logprob,
+                               shard, 0.f, 0.f, 0, out_tokens, out_accept_len, out_target_logprob,
                                out_behavior_logprob, out_status, out_sums, sums_bytes, workspace,
                                workspace_bytes, stream);
 }
@@ -2166,7 +2194,7 @@ spec_status spec_shard_sweep_power(const void* target_shard, const void* draft_s
                                    void* out_sums, size_t sums_bytes, void* workspace,
                                    size_t workspace_bytes, void* stream) {
     return shard_sweep<kPower>(target_shard, draft_shard, dtype, records, draft_tokens, uniforms, B, K, V, G,
-                               shard, alpha, out_tokens, out_accept_len, out_target_logprob,
+                               shard, alpha, 0.f, 0, out_tokens, out_accept_len, out_target_logprob,
                                out_behavior_logprob, out_status, out_sums, sums_bytes, workspace,
                                workspace_bytes, stream);
 }
@@ -2191,6 +2219,73 @@ spec_status spec_shard_sample_power(const void* target_shard, const void* draft_
     return shard_sample<kPower>(target_shard, draft_shard, dtype, sums, uniforms, B, K, V, G, shard,
                                 out_tokens, out_target_logprob, out_behavior_logprob, out_sample_shard,
                                 workspace, workspace_bytes, stream);
+}
+
+size_t spec_shard_values_bytes(int B, int K) {
+    if (B < 1 || B > kMaxB || K < 1 || K > SPEC_MAX_K) return 0;
+    return align_up((size_t)B * K * sizeof(float), 256);
+}
+
+spec_status spec_shard_values_relaxed(const void* target_shard, spec_dtype dtype,
+                                      const int32_t* draft_tokens, int B, int K, int V, int G,
+                                      int shard, void* out_values, size_t values_bytes,
+                                      void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, K + 1)) return SPEC_EINVAL;
+    if (!target_shard || !draft_tokens) return SPEC_EINVAL;
+    if (!buf_ok(out_values, values_bytes, spec_shard_values_bytes(B, K))) return SPEC_EWORKSPACE;
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, K + 1);
+    a.T = target_shard;
+    a.tok = draft_tokens;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)((B * K + kThreads - 1) / kThreads)), block(kThreads);
+    float* out = static_cast<float*>(out_values);
+    if (dtype == SPEC_BF16)
+        hipLaunchKernelGGL((k_values<uint16_t>), grid, block, 0, st, a, out);
+    else
+        hipLaunchKernelGGL((k_values<float>), grid, block, 0, st, a, out);
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+spec_status spec_shard_stats_relaxed(const void* target_shard, spec_dtype dtype,
+                                     const int32_t* draft_tokens, const void* values, int B, int K,
+                                     int V, int G, int shard, void* out_record, size_t record_bytes,
+                                     void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, K + 1)) return SPEC_EINVAL;
+    if (!target_shard || !draft_tokens) return SPEC_EINVAL;
+    if (!values || ((uintptr_t)values % 256) != 0) return SPEC_EWORKSPACE;
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, K + 1);
+    if (!buf_ok(out_record, record_bytes, shard_layout(dtype, B, a.R, a.V).slot)) return SPEC_EWORKSPACE;
+    a.T = target_shard;
+    a.tok = draft_tokens;
+    a.vec_t = vec_ok(target_shard, dtype, a.V);
+    a.xv_in = static_cast<const float*>(values);
+    a.slot_xv = spec_shard_values_bytes(B, K) / sizeof(float);
+    return shard_stats<kRelaxed, true>(a, dtype, out_record, static_cast<hipStream_t>(stream));
+}
+
+spec_status spec_shard_sweep_relaxed(const void* target_shard, spec_dtype dtype, const void* records,
+                                     const int32_t* draft_tokens, const float* uniforms, int B,
+                                     int K, int V, int G, int shard, float tau, int top_k,
+                                     int32_t* out_tokens, int32_t* out_accept_len,
+                                     float* out_target_logprob, float* out_behavior_logprob,
+                                     int32_t* out_status, void* out_sums, size_t sums_bytes,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    return shard_sweep<kRelaxed>(target_shard, nullptr, dtype, records, draft_tokens, uniforms, B, K, V, G,
+                                 shard, 0.f, tau, top_k, out_tokens, out_accept_len, out_target_logprob,
+                                 out_behavior_logprob, out_status, out_sums, sums_bytes, workspace,
+                                 workspace_bytes, stream);
+}
+
+spec_status spec_shard_sample_relaxed(const void* target_shard, spec_dtype dtype, const void* sums,
+                                      const float* uniforms, int B, int K, int V, int G, int shard,
+                                      int32_t* out_tokens, float* out_target_logprob,
+                                      float* out_behavior_logprob, int32_t* out_sample_shard,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    return shard_sample<kRelaxed>(target_shard, nullptr, dtype, sums, uniforms, B, K, V, G, shard,
+                                  out_tokens, out_target_logprob, out_behavior_logprob, out_sample_shard,
+                                  workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

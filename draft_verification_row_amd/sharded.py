@@ -30,7 +30,9 @@ __all__ = ["shard_record_bytes", "shard_sums_bytes", "shard_workspace_bytes",
            "shard_combine_greedy", "shard_combine_tree", "shard_sweep_exact",
            "shard_sample_exact", "shard_sweep_power", "shard_sample_power",
            "verify_greedy_sharded", "verify_tree_sharded", "verify_exact_sharded",
-           "verify_power_sharded", "ShardedExactResult"]
+           "verify_power_sharded", "verify_relaxed_sharded", "shard_values_bytes",
+           "shard_values_relaxed", "shard_stats_relaxed", "shard_sweep_relaxed",
+           "shard_sample_relaxed", "ShardedExactResult"]
 
 
 def shard_record_bytes(dtype: torch.dtype, B: int, rows_per_request: int, V: int, G: int) -> int:
@@ -283,4 +285,91 @@ def _verify_pq_sharded(target_shards, draft_shards, draft_tokens, uniforms, alph
             shard_sample_exact(target_shards[s], draft_shards[s], sums, uniforms, G, s, out, own, ws[s])
         else:
             shard_sample_power(target_shards[s], draft_shards[s], sums, uniforms, G, s, out, own, ws[s])
+    return ShardedExactResult(out, own)
+
+
+# ---------------------------------------------------------------- relaxed
+def shard_values_bytes(B: int, K: int) -> int:
+    return int(load_library().spec_shard_values_bytes(B, K))
+
+
+def shard_values_relaxed(target_shard, draft_tokens, G: int, shard: int, out_values: torch.Tensor):
+    B, L, V = _shard_logits(target_shard, "target_shard", G)
+    x = _check(draft_tokens, "draft_tokens", torch.int32, (B, L - 1))
+    out = _slot(out_values, "out_values")
+    rc = load_library().spec_shard_values_relaxed(
+        _ptr(target_shard), _dtype_code(target_shard), _ptr(x), B, L - 1, V, G, shard, _ptr(out),
+        out.numel(), _stream_ptr(target_shard.device))
+    _raise(rc, "spec_shard_values_relaxed")
+
+
+def shard_stats_relaxed(target_shard, draft_tokens, values: torch.Tensor, G: int, shard: int,
+                        out_record: torch.Tensor):
+    B, L, V = _shard_logits(target_shard, "target_shard", G)
+    x = _check(draft_tokens, "draft_tokens", torch.int32, (B, L - 1))
+    vals, rec = _slot(values, "values"), _slot(out_record, "out_record")
+    rc = load_library().spec_shard_stats_relaxed(
+        _ptr(target_shard), _dtype_code(target_shard), _ptr(x), _ptr(vals), B, L - 1, V, G, shard,
+        _ptr(rec), rec.numel(), _stream_ptr(target_shard.device))
+    _raise(rc, "spec_shard_stats_relaxed")
+
+
+def shard_sweep_relaxed(target_shard, records: torch.Tensor, draft_tokens, uniforms, G: int,
+                        shard: int, tau: float, top_k: int, out: VerifyResult,
+                        out_sums: torch.Tensor, workspace: torch.Tensor):
+    B, L, V = _shard_logits(target_shard, "target_shard", G)
+    K = L - 1
+    x = _check(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    u = _check(uniforms, "uniforms", torch.float32, (B, L))
+    rec, sums, ws = _slot(records, "records"), _slot(out_sums, "out_sums"), _slot(workspace, "workspace")
+    rc = load_library().spec_shard_sweep_relaxed(
+        _ptr(target_shard), _dtype_code(target_shard), _ptr(rec), _ptr(x), _ptr(u), B, K, V, G,
+        shard, ctypes.c_float(tau), int(top_k), _ptr(out.tokens), _ptr(out.accept_len),
+        _ptr(out.target_logprob), _ptr(out.behavior_logprob), _ptr(out.status), _ptr(sums),
+        sums.numel(), _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
+    _raise(rc, "spec_shard_sweep_relaxed")
+
+
+def shard_sample_relaxed(target_shard, sums: torch.Tensor, uniforms, G: int, shard: int,
+                         out: VerifyResult, out_sample_shard: Optional[torch.Tensor],
+                         workspace: torch.Tensor):
+    B, L, V = _shard_logits(target_shard, "target_shard", G)
+    u = _check(uniforms, "uniforms", torch.float32, (B, L))
+    sm, ws = _slot(sums, "sums"), _slot(workspace, "workspace")
+    own = None if out_sample_shard is None else _check(out_sample_shard, "out_sample_shard",
+                                                       torch.int32, (B,))
+    rc = load_library().spec_shard_sample_relaxed(
+        _ptr(target_shard), _dtype_code(target_shard), _ptr(sm), _ptr(u), B, L - 1, V, G, shard,
+        _ptr(out.tokens), _ptr(out.target_logprob), _ptr(out.behavior_logprob), _ptr(own),
+        _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
+    _raise(rc, "spec_shard_sample_relaxed")
+
+
+def verify_relaxed_sharded(target_shards: Sequence[torch.Tensor], draft_tokens, uniforms,
+                           tau: float, top_k: int, *, logprobs: bool = True) -> ShardedExactResult:
+    """The relaxed rule over G shards on one device: values, stats, sweep and
+    sample steps, each writing its own slot of the shared gathered buffers."""
+    G = len(target_shards)
+    B, L, V = _shapes(target_shards, "target_shards")
+    K = L - 1
+    dt = target_shards[0].dtype
+    dev = target_shards[0].device
+    vslot = shard_values_bytes(B, K)
+    slot = shard_record_bytes(dt, B, K + 1, V, G)
+    sslot = shard_sums_bytes(B, V, G)
+    vals = _gathered(vslot, G, dev)
+    rec = _gathered(slot, G, dev)
+    sums = _gathered(sslot, G, dev)
+    ws = [torch.empty(shard_workspace_bytes(B), dtype=torch.uint8, device=dev) for _ in range(G)]
+    out = VerifyResult(*_outs(B, L, dev, logprobs))
+    own = torch.empty(B, dtype=torch.int32, device=dev)
+    for s in range(G):
+        shard_values_relaxed(target_shards[s], draft_tokens, G, s, vals[s * vslot:(s + 1) * vslot])
+    for s in range(G):
+        shard_stats_relaxed(target_shards[s], draft_tokens, vals, G, s, rec[s * slot:(s + 1) * slot])
+    for s in range(G):
+        shard_sweep_relaxed(target_shards[s], rec, draft_tokens, uniforms, G, s, tau, top_k, out,
+                            sums[s * sslot:(s + 1) * sslot], ws[s])
+    for s in range(G):
+        shard_sample_relaxed(target_shards[s], sums, uniforms, G, s, out, own, ws[s])
     return ShardedExactResult(out, own)

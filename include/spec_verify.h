@@ -361,6 +361,40 @@ spec_status spec_shard_sample_power(const void *target_shard, const void *draft_
                                     int32_t *out_sample_shard, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
+/* The relaxed rule over shards (spec_verify_relaxed's rule and outputs; tau
+ * not NaN, top_k >= 0).  Its rank count #{t : l_t > l_x} needs the drafted
+ * token's logit on every shard, so it takes one more exchange first:
+ *   0. spec_shard_values_relaxed: the shard whose columns hold a drafted token
+ *      writes that token's target logit into its values slot ([B][K] floats,
+ *      spec_shard_values_bytes(B, K) bytes; entries of other shards' tokens
+ *      are left as they are and never read).
+ *   -- exchange 0: all-gather of the G values slots, in shard order.
+ *   1. spec_shard_stats_relaxed (values = the gathered slots; record slot as
+ *      above with rows_per_request K+1).
+ *   2, 3. spec_shard_sweep_relaxed and spec_shard_sample_relaxed, as for the
+ *      exact rule (no draft logits). */
+size_t spec_shard_values_bytes(int B, int K);
+spec_status spec_shard_values_relaxed(const void *target_shard, spec_dtype dtype,
+                                      const int32_t *draft_tokens, int B, int K, int V, int G,
+                                      int shard, void *out_values, size_t values_bytes,
+                                      void *stream);
+spec_status spec_shard_stats_relaxed(const void *target_shard, spec_dtype dtype,
+                                     const int32_t *draft_tokens, const void *values, int B, int K,
+                                     int V, int G, int shard, void *out_record, size_t record_bytes,
+                                     void *stream);
+spec_status spec_shard_sweep_relaxed(const void *target_shard, spec_dtype dtype, const void *records,
+                                     const int32_t *draft_tokens, const float *uniforms, int B,
+                                     int K, int V, int G, int shard, float tau, int top_k,
+                                     int32_t *out_tokens, int32_t *out_accept_len,
+                                     float *out_target_logprob, float *out_behavior_logprob,
+                                     int32_t *out_status, void *out_sums, size_t sums_bytes,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+spec_status spec_shard_sample_relaxed(const void *target_shard, spec_dtype dtype, const void *sums,
+                                      const float *uniforms, int B, int K, int V, int G, int shard,
+                                      int32_t *out_tokens, float *out_target_logprob,
+                                      float *out_behavior_logprob, int32_t *out_sample_shard,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Step 3, exact: sums = the G gathered sums slots.  The owning shard writes
  * out_tokens[b][accept_len[b]] and the two log-probs there (NULL log-prob
  * arrays are skipped); every shard writes out_sample_shard[b] = the owning

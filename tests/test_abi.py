@@ -232,3 +232,30 @@ def test_shard_power_argument_errors(lib):
     assert lib.spec_shard_sweep_power(*bad) == SPEC_EINVAL
     assert lib.spec_shard_sample_power(P4K, P4K, 1, PWS, P4K, 2, 3, 1000, 4, 4, P4K, None, None,
                                        None, PWS, ws, None) == SPEC_EINVAL   # shard = G
+
+
+def test_shard_relaxed_argument_errors(lib):
+    assert lib.spec_shard_values_bytes(32, 5) == 768 and lib.spec_shard_values_bytes(0, 5) == 0
+    assert lib.spec_shard_values_bytes(2, 64) == 0
+    vb = lib.spec_shard_values_bytes(2, 3)
+    v = lib.spec_shard_values_relaxed
+    assert v(P4K, 1, P4K, 2, 3, 1000, 3, 0, PWS, vb, None) == SPEC_EINVAL      # 1000 % 3
+    assert v(P4K, 1, None, 2, 3, 1000, 4, 0, PWS, vb, None) == SPEC_EINVAL
+    assert v(P4K, 1, P4K, 2, 3, 1000, 4, 0, PWS, vb - 256, None) == SPEC_EWORKSPACE
+    rb = lib.spec_shard_record_bytes(1, 2, 4, 1000, 4)
+    st = lib.spec_shard_stats_relaxed
+    assert st(P4K, 1, P4K, ctypes.c_void_p((1 << 20) + 8), 2, 3, 1000, 4, 0, PWS, rb, None) == SPEC_EWORKSPACE
+    assert st(P4K, 1, P4K, PWS, 2, 3, 1000, 4, 4, PWS, rb, None) == SPEC_EINVAL   # shard = G
+    assert st(P4K, 1, P4K, PWS, 2, 3, 1000, 4, 0, PWS, rb - 256, None) == SPEC_EWORKSPACE
+    sums, ws = lib.spec_shard_sums_bytes(2, 1000, 4), lib.spec_shard_workspace_bytes(2)
+    sw = lib.spec_shard_sweep_relaxed
+    base = [P4K, 1, PWS, P4K, P4K, 2, 3, 1000, 4, 0, ctypes.c_float(0.1), 4, P4K, P4K, None, None,
+            P4K, PWS, sums, PWS, ws, None]
+    bad = list(base)
+    bad[10] = ctypes.c_float(float("nan"))
+    assert sw(*bad) == SPEC_EINVAL
+    bad = list(base)
+    bad[11] = -1
+    assert sw(*bad) == SPEC_EINVAL
+    sa = lib.spec_shard_sample_relaxed
+    assert sa(P4K, 1, PWS, None, 2, 3, 1000, 4, 0, P4K, None, None, None, PWS, ws, None) == SPEC_EINVAL

@@ -215,3 +215,51 @@ def _pq_power(ci, G, alpha):
     r = sh.verify_power_sharded(T, D, dev(ci.tokens), dev(ci.uniforms), alpha)
     torch.cuda.synchronize()
     return r
+
+
+# ---------------------------------------------------------------- relaxed
+def _relaxed_sharded(ci, G):
+    T = _split(dev_logits(ci.target, ci.dtype), G)
+    r = sh.verify_relaxed_sharded(T, dev(ci.tokens), dev(ci.uniforms), ci.tau, ci.top_k)
+    torch.cuda.synchronize()
+    return r
+
+
+def test_relaxed_c5_eight_shards():
+    """B=64, K=8, V=151936 bf16 over 8 shards of 18992 columns."""
+    print("sharded relaxed c5 g8", flush=True)
+    ci = synth.c5()
+    o = oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", ci.tau, ci.top_k)
+    res = _relaxed_sharded(ci, 8)
+    t = compare_chain(res.result, o, what="sharded relaxed c5")
+    assert t.within_budget(), t
+    _check_owner(res, 8, ci.V)
+
+
+@pytest.mark.parametrize("tau,k,G", [(2.0, 0, 4), (-1.0, 0, 4), (2.0, 1, 5), (0.05, 2, 2),
+                                     (0.5, 10, 8)])
+def test_relaxed_sharded_special_cases(tau, k, G):
+    """Reject-all, accept-all, greedy-like, and rank tests whose top-k members
+    lie in other shards than the drafted token."""
+    ci = synth.chain_inputs(16, 6, 20000, "bf16", seed=61, useed=62, d_noise=0.3)
+    ci.tau, ci.top_k = tau, k
+    o = oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", tau, k)
+    compare_chain(_relaxed_sharded(ci, G).result, o, what=f"sharded relaxed tau={tau} k={k} G={G}")
+
+
+def test_relaxed_one_shard_is_the_unsharded_call():
+    ci = synth.chain_inputs(8, 5, 30000, "bf16", seed=105, useed=106)
+    T, x, u = dev_logits(ci.target, "bf16"), dev(ci.tokens), dev(ci.uniforms)
+    a = sv.spec_verify_relaxed(T, x, u, 0.1, 4)
+    b = sh.verify_relaxed_sharded([T], x, u, 0.1, 4).result
+    torch.cuda.synchronize()
+    for f in ("tokens", "accept_len", "target_logprob", "behavior_logprob", "status"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+def test_relaxed_sharded_malformed_and_fp32():
+    ci = synth.chain_inputs(5, 4, 4 * 1501, "f32", seed=107, useed=108)
+    ci.tokens = ci.tokens.copy()
+    ci.tokens[2, 0] = ci.V + 5
+    o = oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "f32", ci.tau, ci.top_k)
+    compare_chain(_relaxed_sharded(ci, 4).result, o, what="sharded relaxed fp32 malformed")
