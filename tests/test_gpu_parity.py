@@ -358,3 +358,42 @@ def test_read_ceiling_kernel_runs_on_odd_sizes():
                                      ctypes.c_void_p(out.data_ptr()), st) == 0
         torch.cuda.synchronize()
         assert int(out[words]) == -1  # nothing written past the last word
+
+
+def test_graph_capture_replays_match_eager():
+    """Calls captured in a HIP graph: every replay equals the eager result bit
+    for bit, with other eager calls (reusing the same workspace) between the
+    replays."""
+    ci = synth.chain_inputs(16, 5, 50000, "bf16", seed=111, useed=112)
+    T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
+    x, u = dev(ci.tokens), dev(ci.uniforms)
+    B, K, V = ci.B, ci.K, ci.V
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(B, 2 * K + 1, V), dtype=torch.uint8,
+                     device="cuda")
+    ws_s = torch.zeros(sv.spec_sample_workspace_bytes(B * K, V), dtype=torch.uint8, device="cuda")
+    ud = u[:, :K].contiguous()
+
+    def calls():
+        return (sv.spec_verify_exact(T, D, x, u, workspace=ws),
+                sv.spec_verify_greedy(T, x, workspace=ws),
+                sv.spec_sample_drafts(D, ud, workspace=ws_s))
+
+    eager = [[t.clone() for t in r if t is not None] for r in calls()]
+    torch.cuda.synchronize()
+    other = synth.chain_inputs(16, 5, 50000, "bf16", seed=113, useed=114)
+    T2, x2 = dev_logits(other.target, "bf16"), dev(other.tokens)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        captured = calls()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for r_eager, r_cap in zip(eager, captured):
+            for a, b in zip(r_eager, [t for t in r_cap if t is not None]):
+                assert torch.equal(a, b), f"replay {rep}"
+        sv.spec_verify_greedy(T2, x2, workspace=ws)  # eager work on the same workspace
+        sv.spec_verify_exact(T2, dev_logits(other.draft, "bf16"), x2, dev(other.uniforms),
+                             workspace=ws)
+        torch.cuda.synchronize()
