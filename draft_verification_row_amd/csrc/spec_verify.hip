@@ -1306,6 +1306,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     const bool residual = EXACT && dc.residual;
     const double Md = dc.Md, cls = dc.cls;
     if (ROWS) __syncthreads();  // the exp table, used by wave 0 below
+    double S0 = 1.0, Z0 = 1.0;  // wave 0: the normalizer and the terminal draw's total
     if (wave == 0) {
         // lane l holds chunk l
         ChunkSums cs = {0.0, 0.0, 0.0, 0.0};
@@ -1347,9 +1348,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
         // target past the last boundary, the last chunk with mass
         const int cstar = mine ? __builtin_ctzll(mine) : (hasm ? 63 - __builtin_clzll(hasm) : 0);
         const double base = readlane_d(excl, cstar);
-        const double lg = log(lane == 0 ? S : Z);  // lane 0: log S, lane 1: log Z
-        const double lgz = readlane_d(lg, 1);
-        const double l1r = res ? log1p(-dc.rn) : 0.0;
+        S0 = S;
+        Z0 = Z;
         if (lane == 0) {
             s_cstar = cstar;
             s_base = base;
@@ -1357,9 +1357,6 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
             s_iS = iS;
             s_iSq = iSq;
             s_res = res;
-            s_lnS = lg;
-            s_lnZ = lgz;
-            s_l1r = l1r;
         }
     }
     __syncthreads();
@@ -1381,6 +1378,13 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     float lt[kSampleRun], ld[kSampleRun];
     Elem<T>::load4(row_rsrc(trow, a.V), e0, a.V, a.vec_t, lt);
     Elem<T>::load4(row_rsrc(drow, a.V), e0, a.V, residual ? a.vec_d : a.vec_t, ld);
+    // the logs of the outputs, while the chunk loads are in flight (the last
+    // barrier below publishes them)
+    if (t == 0) {
+        s_lnS = log(S0);
+        s_lnZ = log(Z0);
+        s_l1r = res ? log1p(-dc.rn) : 0.0;
+    }
     double w[kSampleRun];
     double tsum = 0.0;
     unsigned pos = 0u, fin = 0u;  // bit i: token i has mass / a finite logit
