@@ -397,3 +397,42 @@ def test_graph_capture_replays_match_eager():
         sv.spec_verify_exact(T2, dev_logits(other.draft, "bf16"), x2, dev(other.uniforms),
                              workspace=ws)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_largest_vocabulary(dtype):
+    """V = 262144: in fp32 a row has 64 tile records and 64 pass-2 chunks, so
+    the fold and the chunk scan use every lane of a wave."""
+    print(f"largest vocabulary {dtype}", flush=True)
+    ci = synth.chain_inputs(2, 3, 262144, dtype, seed=121, useed=122)
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, dtype)
+    compare_chain(_exact(ci), o, what=f"exact V max {dtype}")
+    compare_chain(_greedy(ci), oracle.greedy(ci.target, ci.tokens, dtype), what=f"greedy V max {dtype}")
+    ci.tau, ci.top_k = 0.1, 4
+    compare_chain(_relaxed(ci), oracle.relaxed(ci.target, ci.tokens, ci.uniforms, dtype, 0.1, 4),
+                  what=f"relaxed V max {dtype}")
+    po = oracle.power(ci.target, ci.draft, ci.tokens, ci.uniforms, dtype, 0.5)
+    pr = sv.spec_verify_power(dev_logits(ci.target, dtype), dev_logits(ci.draft, dtype),
+                              dev(ci.tokens), dev(ci.uniforms), 0.5)
+    torch.cuda.synchronize()
+    compare_chain(pr, po, what=f"power V max {dtype}")
+    s = sv.spec_sample_drafts(dev_logits(ci.draft, dtype), dev(ci.uniforms[:, :3].copy()))
+    os_ = oracle.sample(ci.draft, ci.uniforms[:, :3].copy(), dtype)
+    ok = os_.flag == 0
+    np.testing.assert_array_equal(s.tokens.cpu().numpy()[ok], os_.tokens[ok])
+
+
+def test_largest_batch():
+    """B = 65536 requests (the library's limit), K = 1, V = 40."""
+    print("largest batch", flush=True)
+    ci = synth.chain_inputs(65536, 1, 40, "bf16", seed=123, useed=124)
+    o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")
+    t = compare_chain(_exact(ci), o, what="exact B max")
+    assert t.within_budget(), t
+    compare_chain(_greedy(ci), oracle.greedy(ci.target, ci.tokens, "bf16"), what="greedy B max")
+    rows = ci.draft.reshape(65536, 40)
+    u = ci.uniforms[:, 0].copy()
+    s = sv.spec_sample_drafts(dev_logits(rows, "bf16"), dev(u))
+    os_ = oracle.sample(rows, u, "bf16")
+    ok = os_.flag == 0
+    np.testing.assert_array_equal(s.tokens.cpu().numpy()[ok], os_.tokens[ok])
