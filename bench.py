@@ -340,18 +340,23 @@ def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, 
     torch.cuda.synchronize()
     ms = r["graph_ms_per_step"] if use_graph else r["eager_ms_per_step"]
     logit_bytes = ci.target.nbytes + (ci.draft.nbytes if mode == "exact" else 0)
-    return {"workload": label, "entry_point": f"spec_verify_{mode}",
-            "rounds_per_s": 1000.0 / ms, "us_per_call": ms * 1e3,
-            "hbm_gbs_call": nbytes / (ms * 1e-3) / 1e9,
-            "hbm_frac_call": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "kernel_us_mean": r["kernel_ms_mean"] * 1e3,
-            "kernel_gbs": logit_bytes / (r["kernel_ms_mean"] * 1e-3) / 1e9,
-            "kernel_frac": logit_bytes / (r["kernel_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "rest_of_call_us_mean": r["rest_ms_mean"] * 1e3,
-            "eager_us_per_call": r["eager_ms_per_step"] * 1e3,
-            "graph_us_per_call_runs": [x * 1e3 for x in r.get("graph_ms_per_step_runs", [])],
-            "algorithmic_bytes": nbytes, "input_sets": sets,
-            "cpu_oracle_rounds_per_s": oracle_call_rate(mode, ci) if cpu else None}
+    out = {"workload": label, "entry_point": f"spec_verify_{mode}",
+           "rounds_per_s": 1000.0 / ms, "us_per_call": ms * 1e3,
+           "hbm_gbs_call": nbytes / (ms * 1e-3) / 1e9,
+           "hbm_frac_call": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "kernel_us_mean": r["kernel_ms_mean"] * 1e3,
+           "kernel_gbs": logit_bytes / (r["kernel_ms_mean"] * 1e-3) / 1e9,
+           "kernel_frac": logit_bytes / (r["kernel_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "rest_of_call_us_mean": r["rest_ms_mean"] * 1e3,
+           "eager_us_per_call": r["eager_ms_per_step"] * 1e3,
+           "graph_us_per_call_runs": [x * 1e3 for x in r.get("graph_ms_per_step_runs", [])],
+           "algorithmic_bytes": nbytes, "input_sets": sets,
+           "cpu_oracle_rounds_per_s": None, "cpu_oracle_gbs_equivalent": None}
+    if cpu:
+        rate = oracle_call_rate(mode, ci)
+        out["cpu_oracle_rounds_per_s"] = rate
+        out["cpu_oracle_gbs_equivalent"] = rate * nbytes / 1e9
+    return out
 
 
 def oracle_call_rate(mode, ci):
