@@ -1587,13 +1587,13 @@ inline ShardLayout shard_layout(spec_dtype dt, int B, int R, int Vs) {
 inline size_t shard_sums_slot(int B, int Vs) { return align_up((size_t)B * c2_of(SPEC_F32, Vs) * sizeof(ChunkSums), 256); }
 inline size_t shard_ws_bytes(int B) { return align_up((size_t)B * 64, 256); }
 
-bool sizes_ok(int B, int K, int V, long rows_per_req);
+bool sizes_ok(spec_dtype dt, int B, int K, int V, long rows_per_req);
 
 // Shard count, shard index and the one-wave limits of the combine and the
 // sample scan.
 bool shard_ok(spec_dtype dt, int B, int K, int V, int G, int shard, long rows) {
     if (G < 1 || V < 1 || V % G != 0 || shard < 0 || shard >= G) return false;
-    if (!sizes_ok(B, K, V, rows)) return false;
+    if (!sizes_ok(dt, B, K, V, rows)) return false;
     const int Vs = V / G;
     return (long)G * tpr_of(dt, Vs) <= 64 && (long)G * c2_of(dt, Vs) <= 64;
 }
@@ -1663,12 +1663,14 @@ size_t sample_layout_bytes(int rows, int V, spec_dtype dt) {
     return make_layout(rows, 1, tpr_of(dt, V), c2_of(dt, V)).total + align_up((size_t)rows * 4, 256);
 }
 
-bool sizes_ok(int B, int K, int V, long rows_per_req) {
+bool sizes_ok(spec_dtype dt, int B, int K, int V, long rows_per_req) {
     if (B < 1 || B > kMaxB || K < 1 || V < 1 || V > SPEC_MAX_V) return false;
     if (rows_per_req < 1 || rows_per_req > kMaxRows) return false;
-    // streaming grid (fp32 has the most tiles) and element offsets
-    const long long tiles = (V + 4095) / 4096;
-    return (long long)B * rows_per_req * tiles < (1ll << 31) && (long long)B * rows_per_req * V < (1ll << 40);
+    // The streaming grid's size in threads is a 32-bit quantity: one 16 KiB
+    // tile per workgroup of kThreads, so at most 2^24 tiles (256 GiB of
+    // logits) per call.  Element offsets stay far inside 64 bits.
+    const long long tiles = (long long)B * rows_per_req * tpr_of(dt, V);
+    return tiles * kThreads < (1ll << 32) && (long long)B * rows_per_req * V < (1ll << 40);
 }
 
 }  // namespace
@@ -1709,7 +1711,7 @@ spec_status spec_verify_greedy(const void* target_logits, spec_dtype dtype,
                                int32_t* out_status, void* workspace, size_t workspace_bytes,
                                void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !sizes_ok(B, K, V, K + 1)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, K + 1)) return SPEC_EINVAL;
     if (!target_logits || !draft_tokens || !out_tokens || !out_accept_len || !out_status)
         return SPEC_EINVAL;
     const spec_status ws = check_ws(workspace, workspace_bytes, B, K + 1, V, dtype);
@@ -1743,7 +1745,7 @@ spec_status spec_verify_exact(const void* target_logits, const void* draft_logit
                               int32_t* out_status, void* workspace, size_t workspace_bytes,
                               void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !sizes_ok(B, K, V, 2 * K + 1)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, 2 * K + 1)) return SPEC_EINVAL;
     if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
         !out_accept_len || !out_status)
         return SPEC_EINVAL;
@@ -1780,7 +1782,7 @@ spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
                                 float* out_behavior_logprob, int32_t* out_status, void* workspace,
                                 size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !sizes_ok(B, K, V, K + 1)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, K + 1)) return SPEC_EINVAL;
     if (tau != tau || top_k < 0) return SPEC_EINVAL;
     if (!target_logits || !draft_tokens || !uniforms || !out_tokens || !out_accept_len ||
         !out_status)
@@ -1818,7 +1820,7 @@ spec_status spec_verify_power(const void* target_logits, const void* draft_logit
                               float* out_behavior_logprob, int32_t* out_status, void* workspace,
                               size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !sizes_ok(B, K, V, 2 * K + 1)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, 2 * K + 1)) return SPEC_EINVAL;
     if (!(alpha >= 0.f) || alpha == INFINITY) return SPEC_EINVAL;
     if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
         !out_accept_len || !out_status)
@@ -1917,7 +1919,7 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
                              int32_t* out_status, void* workspace, size_t workspace_bytes,
                              void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (N < 1 || N > SPEC_MAX_NODES || !sizes_ok(B, 1, V, N)) return SPEC_EINVAL;
+    if (N < 1 || N > SPEC_MAX_NODES || !sizes_ok(dtype, B, 1, V, N)) return SPEC_EINVAL;
     if (!target_logits || !node_tokens || !parents || !out_path_nodes || !out_tokens ||
         !out_accept_len || !out_status)
         return SPEC_EINVAL;

@@ -83,7 +83,11 @@ typedef enum {
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 
 /* Largest K (drafts per request), N (tree nodes per request), V (vocabulary)
- * and B (requests per call). */
+ * and B (requests per call).  A call's logits must also span fewer than 2^24
+ * tiles of 16 KiB, counted per row (B * rows_per_request * ceil(V * element
+ * size / 16 KiB)), since the streaming launch runs one 256-thread workgroup
+ * per tile and a launch holds fewer than 2^32 threads; larger calls return
+ * SPEC_EINVAL. */
 #define SPEC_MAX_K 63
 #define SPEC_MAX_NODES 64
 #define SPEC_MAX_V 262144

@@ -77,6 +77,16 @@ def test_greedy_argument_errors(lib):
     assert _greedy(lib, wsb=need - 256) == SPEC_EWORKSPACE                      # too small
 
 
+def test_streaming_grid_limit(lib):
+    # one 256-thread workgroup per 16 KiB tile, at most 2^32 threads a launch:
+    # B * (K + 1) * tiles < 2^24.  bf16 V = 262144 has 32 tiles a row, fp32 64.
+    big = dict(B=65536, V=262144)
+    assert _greedy(lib, K=7, **big) == SPEC_EINVAL                  # 2^24 bf16 tiles
+    assert _greedy(lib, K=6, **big) == SPEC_EWORKSPACE              # sizes pass, no workspace
+    assert _greedy(lib, dt=0, K=3, **big) == SPEC_EINVAL            # 2^24 fp32 tiles
+    assert _greedy(lib, dt=0, K=2, **big) == SPEC_EWORKSPACE
+
+
 def test_exact_relaxed_tree_argument_errors(lib):
     p = ctypes.c_void_p(4096)
     ws = ctypes.c_void_p(1 << 20)
