@@ -498,10 +498,11 @@ def sharded_block(lib, ci, G, steps, warmup, hip, torch, dev):
     }
 
 
-def markov_block(torch, dev, rounds, with_cpu):
+def markov_block(torch, dev, rounds, with_cpu, use_graph=True):
     """The multi-round driver with toy Markov models (V=4096, B=32, K=4): the
-    GPU loop's rate and the run's acceptance statistics; the oracle's driver on
-    a few rounds of the same inputs beside it."""
+    GPU loop's rate (all rounds in one captured graph, and the eager loop),
+    the run's acceptance statistics, and the oracle's driver on a few rounds
+    of the same inputs beside it."""
     import draft_verification_row_amd.markov as mk
     import synth
     from numpy import int16
@@ -518,12 +519,38 @@ def markov_block(torch, dev, rounds, with_cpu):
     t0 = time.perf_counter()
     tr = mk.generate_speculative(P, Q, st, ud, uv)
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+    eager_s = time.perf_counter() - t0
+    # every round captured in one HIP graph: the first replay uploads it, the
+    # median of RUNS timed replays is reported, and each replay must equal the
+    # eager loop's tokens bit for bit
+    el = eager_s
+    if use_graph:
+        g = mk.SpeculativeGraph(P, Q, B, K, rounds)
+        g.run(st, ud, uv)
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(RUNS):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            gt = g.run(st, ud, uv)
+            e1.record()
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1) * 1e-3)
+            if not (torch.equal(gt.emitted, tr.emitted) and torch.equal(gt.accept_len, tr.accept_len)):
+                raise RuntimeError("the graph-captured driver differs from the eager loop")
+        el = sorted(runs)[len(runs) // 2]
+        del g
+    timed = (f"all rounds captured in one HIP graph (rounds_per_s: median of {RUNS} replays, "
+             f"input copies included) and the eager loop (eager_rounds_per_s)" if use_graph
+             else "the eager loop")
     res = {"workload": f"multi-round speculative sampling, toy Markov models V={V} (target "
                        f"2*N(0,1) logits per state, draft target+0.7*N(0,1)), B={B} sequences, "
                        f"K={K}, {rounds} rounds; per round K draft draws (spec_sample_drafts) and "
-                       f"one exact verification",
+                       f"one exact verification; timed: {timed}",
            "rounds_per_s": rounds / el, "tokens_per_s": None, "ms_per_round": el / rounds * 1e3,
+           "eager_rounds_per_s": rounds / eager_s, "eager_ms_per_round": eager_s / rounds * 1e3,
            **mk.trace_stats(tr.accept_len, K, 0.1), "cpu_oracle_rounds_per_s": None}
     res["tokens_per_s"] = res["tokens"] / el
     if with_cpu:
@@ -680,7 +707,7 @@ def main():
         others["sharded_exact_greedy_g8"] = sharded_block(lib, ci, 8, min(args.steps, 200),
                                                          min(args.warmup, 20), hip, torch, dev)
         others["markov_driver"] = markov_block(torch, dev, min(args.steps, 200),
-                                               not args.no_cpu_baseline)
+                                               not args.no_cpu_baseline, use_graph)
 
     ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
     value = 1000.0 / ms

@@ -50,3 +50,31 @@ def test_driver_transitions_follow_the_target_chain():
     stats = mk.trace_stats(ln, m.K)
     assert stats["tokens"] == int(C.sum())
     assert 1.0 <= stats["tokens_per_target_pass"] <= m.K + 1
+
+
+def test_graph_replays_match_the_eager_driver():
+    """SpeculativeGraph: each replay, with new start tokens and uniforms
+    copied in and eager driver runs between the replays, equals the eager
+    driver on the same inputs bit for bit."""
+    V, B, K, rounds = 512, 16, 3, 12
+    m = synth.markov_inputs(V, B, K, rounds, "bf16", seed=31)
+    other = synth.markov_inputs(V, B, K, rounds, "bf16", seed=32)
+    P, Q = dev_logits(m.target, "bf16"), dev_logits(m.draft, "bf16")
+    inputs = [(dev(m.start), dev(m.u_draft), dev(m.u_verify)),
+              (dev(other.start), dev(other.u_draft), dev(other.u_verify))]
+    eager = []
+    for st, ud, uv in inputs:
+        tr = mk.generate_speculative(P, Q, st, ud, uv)
+        eager.append((tr.emitted.clone(), tr.accept_len.clone()))
+    torch.cuda.synchronize()
+    g = mk.SpeculativeGraph(P, Q, B, K, rounds)
+    for rep, i in enumerate([0, 1, 0]):
+        print(f"graph replay {rep} inputs {i}", flush=True)
+        tr = g.run(*inputs[i])
+        torch.cuda.synchronize()
+        assert torch.equal(tr.emitted, eager[i][0]), f"replay {rep}"
+        assert torch.equal(tr.accept_len, eager[i][1]), f"replay {rep}"
+        # eager work between replays, on the other tables
+        mk.generate_speculative(dev_logits(other.target, "bf16"), dev_logits(other.draft, "bf16"),
+                                *inputs[1 - i])
+        torch.cuda.synchronize()
