@@ -45,7 +45,7 @@ KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_veri
 # plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Reported only while the source of the streaming kernel (the file up to its
 # end) is the one the counters were taken on.
-TRAFFIC = {"source_sha256": "85092abb0a704806f1324687e40fc495faa0e3d8384f76e4a4d739bf80861651",
+TRAFFIC = {"source_sha256": "1557ea0b3998e00b7f8e7a0efa48b1901244e1d1ac7eb5e740d41935de2e0b83",
            "fetch_kib": 44143.4, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 MALL_BYTES = 256 * 1024 * 1024
@@ -287,7 +287,7 @@ def time_case(case, steps, warmup, hip, use_graph):
 
 
 def stream_alone(lib, case, steps, hip, torch):
-    """The exact rule's streaming kernel launched back to back with nothing
+    """The exact call's streaming kernel launched back to back with nothing
     between its launches (the vocabulary-sharded statistics step at one shard
     launches exactly this kernel), rotating over the case's input sets: the
     mean of the dispatches' own durations.  Inside a call the same kernel

@@ -73,6 +73,13 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTileBytes = 16384;                        // streaming tile
 constexpr int kTileVecs = kTileBytes / (kThreads * 16);  // 16-byte loads per thread
+// The greedy rule's stream without log-probs reads bf16 rows in 8 KiB tiles:
+// twice the workgroups, each with half the loads (measured: 8.68 vs 8.86 us
+// for the [32][6][128256] target rows launched alone, 10.1 vs 10.4 us inside
+// calls; the normalizer streams are no faster with them, and the tree's
+// 61-row stream is slower, 23.8 vs 21.6 us).  A row then has as many tiles as
+// an fp32 row of 16 KiB tiles.
+constexpr int kSmallTileVecs = kTileVecs / 2;
 constexpr int kStreamWavesPerSimd = 8;                   // k_stream occupancy target
 constexpr int kChunk = 4096;                             // pass-2 tokens per workgroup
 constexpr int kPass2WavesPerSimd = 4;                    // k_pass2 occupancy target
@@ -552,21 +559,21 @@ __device__ inline const T* call_row(const Args& a, int g, int& vec, int& active)
 // Issues this thread's loads of tile c of a row: vector k covers tokens
 // c*TILE + (k*kThreads + tid)*VEC + [0, VEC).  Indices are clamped into the
 // row and the caller masks tokens past V, so no load leaves the row.
-template <typename T, bool NT, bool VECP>
-__device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[kTileVecs]) {
+template <typename T, bool NT, bool VECP, int NV>
+__device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[NV]) {
     constexpr int VEC = Elem<T>::kVec;
-    constexpr int TILE = kThreads * kTileVecs * VEC;
+    constexpr int TILE = kThreads * NV * VEC;
     const int t0 = c * TILE + (int)threadIdx.x * VEC;
     if (VECP) {  // V is a multiple of VEC and every row is 16-byte aligned
 #pragma unroll
-        for (int k = 0; k < kTileVecs; ++k) {
+        for (int k = 0; k < NV; ++k) {
             // global (not flat) address space: these loads wait on vmcnt only
             const gu32x4* p = (const gu32x4*)(row + min(t0 + k * kThreads * VEC, V - VEC));
             q[k] = NT ? __builtin_nontemporal_load(p) : *p;
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < kTileVecs; ++k) q[k] = Elem<T>::gather_clamped(row, t0 + k * kThreads * VEC, V);
+        for (int k = 0; k < NV; ++k) q[k] = Elem<T>::gather_clamped(row, t0 + k * kThreads * VEC, V);
     }
 }
 
@@ -583,10 +590,10 @@ __device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[kTileVec
 // SHARD (a vocabulary shard's relaxed-rule statistics): the rank count's
 // threshold l_x comes from the gathered drafted-token logits, since the token
 // may be another shard's column.
-template <typename T, int MODE, bool SUM, bool VECP, bool XV, bool SHARD>
+template <typename T, int MODE, bool SUM, bool VECP, bool XV, bool SHARD, int NV>
 __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const Args a) {
     constexpr int VEC = Elem<T>::kVec;
-    constexpr int TILE = kThreads * kTileVecs * VEC;
+    constexpr int TILE = kThreads * NV * VEC;
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
     // Non-temporal loads: the stream touches every line once.  (The one or
@@ -622,8 +629,8 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     int xt = 0;
     if (xvw) xt = a.tok[xi];
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 q[kTileVecs];
-    load_tile<T, NT, VECP>(row, a.V, c, q);
+    u32x4 q[NV];
+    load_tile<T, NT, VECP, NV>(row, a.V, c, q);
     __builtin_amdgcn_sched_barrier(0);
     int xl = -1;
     uint32_t xraw = 0u;
@@ -652,14 +659,14 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     const int t0 = c * TILE + (int)threadIdx.x * VEC;
     if (c == a.tpr - 1 && a.V % TILE != 0) {  // ragged last tile: clamped lanes
 #pragma unroll
-        for (int k = 0; k < kTileVecs; ++k) Elem<T>::mask_tail(q[k], t0 + k * kThreads * VEC, a.V);
+        for (int k = 0; k < NV; ++k) Elem<T>::mask_tail(q[k], t0 + k * kThreads * VEC, a.V);
     }
     // Values are unpacked from the packed vectors where they are used, so
     // only the 16-byte vectors stay live between the phases.
     float m = -INFINITY;
     int cnt = 0;
 #pragma unroll
-    for (int k = 0; k < kTileVecs; ++k) {
+    for (int k = 0; k < NV; ++k) {
         float v[VEC];
         Elem<T>::unpack(q[k], v);
 #pragma unroll
@@ -683,7 +690,7 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     int idx = INT_MAX;
     if (ARGMAX && m == M && M > -INFINITY) {
 #pragma unroll
-        for (int k = kTileVecs - 1; k >= 0; --k) {
+        for (int k = NV - 1; k >= 0; --k) {
             float v[VEC];
             Elem<T>::unpack(q[k], v);
 #pragma unroll
@@ -700,7 +707,7 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
         const float mL = M * kLog2e;
         float acc = 0.f;
 #pragma unroll
-        for (int k = 0; k < kTileVecs; ++k) {
+        for (int k = 0; k < NV; ++k) {
             float v[VEC];
             Elem<T>::unpack(q[k], v);
 #pragma unroll
@@ -756,7 +763,7 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_stream_rows(co
     int vec, act;
     const T* row = call_row<T, kRelaxed>(a, g, vec, act);
     u32x4 q[kTileVecs];
-    load_tile<T, true, VECP>(row, a.V, c, q);
+    load_tile<T, true, VECP, kTileVecs>(row, a.V, c, q);
     const int t0 = c * TILE + (int)threadIdx.x * VEC;
     if (c == a.tpr - 1 && a.V % TILE != 0) {
 #pragma unroll
@@ -1518,15 +1525,27 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
 inline int esize(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
 inline int tile_elems(spec_dtype dt) { return kTileBytes / esize(dt); }
 inline int tpr_of(spec_dtype dt, int V) { return (V + tile_elems(dt) - 1) / tile_elems(dt); }
+constexpr int kSmallTileElems = kThreads * kSmallTileVecs * 8;  // bf16 elements of an 8 KiB tile
+// Whether a call's stream reads 8 KiB tiles: the greedy rule without
+// log-probs on bf16 rows, where the doubled grid still fits in 2^32 threads.
+inline bool small_tiles(spec_dtype dt, int V, long long rows, bool greedy_no_logprobs) {
+    if (!greedy_no_logprobs || dt != SPEC_BF16) return false;
+    return rows * ((V + kSmallTileElems - 1) / kSmallTileElems) * kThreads < (1ll << 32);
+}
+// Tiles per row of the stream (8 KiB tiles have as many as an fp32 row's 16
+// KiB tiles, so the workspace query, sized for fp32, covers them).
+inline int stream_tpr(spec_dtype dt, int V, bool small) {
+    return small ? (V + kSmallTileElems - 1) / kSmallTileElems : tpr_of(dt, V);
+}
 inline int c2_of(spec_dtype, int V) { return (V + kChunk - 1) / kChunk; }
 
 inline bool vec_ok(const void* p, spec_dtype dt, int V) {
     return ((uintptr_t)p % 16 == 0) && (((size_t)V * esize(dt)) % 16 == 0);
 }
 
-spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt) {
+spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt, bool small = false) {
     if (!ws || ((uintptr_t)ws % 256) != 0) return SPEC_EWORKSPACE;
-    const Layout L = make_layout(B, R, tpr_of(dt, V), c2_of(dt, V));
+    const Layout L = make_layout(B, R, stream_tpr(dt, V, small), c2_of(dt, V));
     return bytes >= L.total ? SPEC_OK : SPEC_EWORKSPACE;
 }
 
@@ -1536,20 +1555,24 @@ thread_local hipEvent_t g_prof[3] = {nullptr, nullptr, nullptr};
 
 // The streaming kernel over B * R rows of a.V logits, with the dispatch's
 // own start and stop events when given.
-template <int MODE, bool SUM, bool XV, bool SHARD = false>
+// NV: 16-byte loads per thread, kTileVecs (16 KiB tiles) or kSmallTileVecs
+// (8 KiB tiles, bf16 only); a.tpr must match it.
+template <int MODE, bool SUM, bool XV, bool SHARD = false, int NV = kTileVecs>
 spec_status launch_stream(const Args& a, spec_dtype dt, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid((unsigned)a.B * (unsigned)a.R * (unsigned)a.tpr), block(kThreads);
     const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
     if (dt == SPEC_BF16) {
         if (vecp)
-            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true, XV, SHARD>), grid, block, 0, st, e0, e1, 0, a);
+            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, true, XV, SHARD, NV>), grid, block, 0, st, e0, e1, 0, a);
         else
-            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false, XV, SHARD>), grid, block, 0, st, e0, e1, 0, a);
-    } else {
+            hipExtLaunchKernelGGL((k_stream<uint16_t, MODE, SUM, false, XV, SHARD, NV>), grid, block, 0, st, e0, e1, 0, a);
+    } else if constexpr (NV == kTileVecs) {
         if (vecp)
-            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, true, XV, SHARD>), grid, block, 0, st, e0, e1, 0, a);
+            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, true, XV, SHARD, NV>), grid, block, 0, st, e0, e1, 0, a);
         else
-            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, false, XV, SHARD>), grid, block, 0, st, e0, e1, 0, a);
+            hipExtLaunchKernelGGL((k_stream<float, MODE, SUM, false, XV, SHARD, NV>), grid, block, 0, st, e0, e1, 0, a);
+    } else {
+        return SPEC_EINVAL;  // small tiles are bf16 only (never chosen for fp32)
     }
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
@@ -1568,7 +1591,9 @@ inline void take_prof(hipEvent_t (&ev)[3]) {
 // itself timestamps, so their interval is the kernel's own duration.
 template <int MODE, bool SUM>
 spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
-    a.tpr = tpr_of(dt, a.V);
+    constexpr bool SMALL_OK = !SUM && MODE == kGreedy;
+    const bool small = small_tiles(dt, a.V, (long long)a.B * a.R, SMALL_OK);
+    a.tpr = stream_tpr(dt, a.V, small);
     a.Vtot = a.V;
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
     a.segs = reinterpret_cast<Seg*>(a.ws + lay.seg);
@@ -1580,7 +1605,14 @@ spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
     take_prof(ev);
     // the rules that test drafted-token values record them in the stream
     constexpr bool XV = (MODE == kExact || MODE == kPower || MODE == kRelaxed);
-    if (launch_stream<MODE, SUM, XV>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
+    spec_status ls;
+    if constexpr (SMALL_OK) {
+        ls = small ? launch_stream<MODE, SUM, XV, false, kSmallTileVecs>(a, dt, st, ev[0], ev[1])
+                   : launch_stream<MODE, SUM, XV>(a, dt, st, ev[0], ev[1]);
+    } else {
+        ls = launch_stream<MODE, SUM, XV>(a, dt, st, ev[0], ev[1]);
+    }
+    if (ls != SPEC_OK) return SPEC_EHIP;
     if constexpr (MODE == kGreedy || MODE == kTree) {
         if (dt == SPEC_BF16)
             hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM, false>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
@@ -1746,7 +1778,8 @@ spec_status spec_verify_greedy(const void* target_logits, spec_dtype dtype,
     if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, K + 1)) return SPEC_EINVAL;
     if (!target_logits || !draft_tokens || !out_tokens || !out_accept_len || !out_status)
         return SPEC_EINVAL;
-    const spec_status ws = check_ws(workspace, workspace_bytes, B, K + 1, V, dtype);
+    const spec_status ws = check_ws(workspace, workspace_bytes, B, K + 1, V, dtype,
+                                    small_tiles(dtype, V, (long long)B * (K + 1), !out_target_logprob));
     if (ws != SPEC_OK) return ws;
     Args a = {};
     a.T = target_logits;
