@@ -168,6 +168,17 @@ __device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const T* row, int V) {
                                              kRsrcWord3);
 }
 
+// Workgroup-uniform reads of inputs through the scalar cache (constant
+// address space).  They are counted apart from the vector loads, so waiting
+// for one does not wait for a tile in flight.  Only memory that no kernel of
+// the call writes is read this way.
+__device__ inline int32_t sload_i32(const int32_t* p) {
+    return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
+__device__ inline float sload_f32(const float* p) {
+    return *(const __attribute__((address_space(4))) float*)(uintptr_t)p;
+}
+
 template <typename T>
 struct Elem;
 
@@ -177,9 +188,13 @@ struct Elem<uint16_t> {  // bf16 bit patterns
     __device__ static inline float at(const uint16_t* p, size_t i) {
         return __uint_as_float((uint32_t)p[i] << 16);
     }
-    // element i's bits, widened later by from_bits
-    __device__ static inline uint32_t bits(const uint16_t* p, int i) {
-        return (uint32_t)((const __attribute__((address_space(1))) uint16_t*)p)[i];
+    // element i's bits by a scalar load of the aligned dword that holds it
+    // (that dword lies in the same allocation: device allocations are
+    // aligned far beyond 4 bytes); widened by from_bits
+    __device__ static inline uint32_t sbits(const uint16_t* p, int i) {
+        const uintptr_t at = (uintptr_t)(p + i);
+        const uint32_t w = *(const __attribute__((address_space(4))) uint32_t*)(at & ~(uintptr_t)3);
+        return (at & 2) ? (w >> 16) : (w & 0xffffu);
     }
     __device__ static inline float from_bits(uint32_t w) { return __uint_as_float(w << 16); }
     template <int AUX = 0>
@@ -252,8 +267,8 @@ template <>
 struct Elem<float> {
     static constexpr int kVec = 4;
     __device__ static inline float at(const float* p, size_t i) { return p[i]; }
-    __device__ static inline uint32_t bits(const float* p, int i) {
-        return __float_as_uint(((const __attribute__((address_space(1))) float*)p)[i]);
+    __device__ static inline uint32_t sbits(const float* p, int i) {
+        return *(const __attribute__((address_space(4))) uint32_t*)(uintptr_t)(p + i);
     }
     __device__ static inline float from_bits(uint32_t w) { return __uint_as_float(w); }
     template <int AUX = 0>
@@ -616,18 +631,22 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     int vec, act;
     const T* row = call_row<T, MODE>(a, g, vec, act);
     if (!act) return;  // tree node past num_nodes: never read
-    // XV: the drafted token's id is loaded ahead of the tile and its logit
-    // right behind it, so both round trips overlap the tile's.  All of it is
-    // workgroup-uniform.  The empty asm statements only pin where the
-    // compiler waits for each value: the id once the tile's loads are issued,
-    // the logit's raw bits when the record is written.
+    // Drafted-token reads, all workgroup-uniform and by scalar loads: the
+    // token id goes out ahead of the tile's loads and its logit right behind
+    // them, so both round trips overlap the tile's.
+    // XV: the first workgroups record the drafted token's logits, one
+    // (position, row kind) each: 2*B*K <= B*(2K+1) workgroups for the draft
+    // rules, B*K <= B*(K+1) for the others.
     constexpr int kinds = uses_draft(MODE) ? 2 : 1;
     const bool xvw = XV && (int)blockIdx.x < kinds * a.B * a.K;
-    // one workgroup per (position, row kind): 2*B*K <= B*(2K+1) workgroups
-    // for the draft rules, B*K <= B*(K+1) for the others
     const int xi = uniform((int)blockIdx.x / kinds), xslot = 2 * xi + ((int)blockIdx.x - xi * kinds);
-    int xt = 0;
-    if (xvw) xt = a.tok[xi];
+    // COUNT: a target row j < K counts the tokens strictly above l_x of its
+    // drafted token x
+    const int cb = COUNT ? g / a.R : 0, cr = COUNT ? g - cb * a.R : 0;
+    const bool cw = COUNT && cr < a.K;
+    int xt = 0, ct = 0;
+    if (xvw) xt = sload_i32(a.tok + xi);
+    if (cw) ct = sload_i32(a.tok + cb * a.K + cr);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 q[NV];
     load_tile<T, NT, VECP, NV>(row, a.V, c, q);
@@ -635,26 +654,22 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     int xl = -1;
     uint32_t xraw = 0u;
     if (xvw) {
-        __asm__ volatile("" : "+v"(xt));
         xl = xt - a.shard * a.V;
         const int b = xi / a.K, j = xi - b * a.K;
         const T* xsrc = xslot & 1 ? reinterpret_cast<const T*>(a.D) + (size_t)xi * a.V
                                   : reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + j) * a.V;
-        if ((unsigned)xl < (unsigned)a.V) xraw = Elem<T>::bits(xsrc, xl);
+        if ((unsigned)xl < (unsigned)a.V) xraw = Elem<T>::sbits(xsrc, xl);
     }
-    __builtin_amdgcn_s_setprio(0);
     float thr = INFINITY;  // relaxed: count the tokens strictly above l_x
-    if (COUNT) {
-        const int b = g / a.R, rr = g - b * a.R;
-        if (rr < a.K) {
-            const int x = a.tok[b * a.K + rr];
-            if (SHARD) {
-                if ((unsigned)x < (unsigned)a.Vtot) thr = a.xv_in[(size_t)(x / a.V) * a.slot_xv + b * a.K + rr];
-            } else if ((unsigned)x < (unsigned)a.V) {
-                thr = Elem<T>::at(row, (size_t)x);
-            }
+    if (cw) {
+        if (SHARD) {
+            if ((unsigned)ct < (unsigned)a.Vtot)
+                thr = sload_f32(a.xv_in + (size_t)(ct / a.V) * a.slot_xv + cb * a.K + cr);
+        } else if ((unsigned)ct < (unsigned)a.V) {
+            thr = Elem<T>::from_bits(Elem<T>::sbits(row, ct));
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 
     const int t0 = c * TILE + (int)threadIdx.x * VEC;
     if (c == a.tpr - 1 && a.V % TILE != 0) {  // ragged last tile: clamped lanes
@@ -732,10 +747,7 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
         sg.ic = (ARGMAX || COUNT) ? I : 0;
         sg.s = s;
         a.segs[blockIdx.x] = sg;
-        if (xvw && (unsigned)xl < (unsigned)a.V) {
-            __asm__ volatile("" : "+v"(xraw));
-            a.xv_out[xslot] = Elem<T>::from_bits(xraw);
-        }
+        if (xvw && (unsigned)xl < (unsigned)a.V) a.xv_out[xslot] = Elem<T>::from_bits(xraw);
     }
 }
 
