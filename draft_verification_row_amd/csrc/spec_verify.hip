@@ -87,7 +87,7 @@ constexpr int kRun = kChunk / kThreads;                  // pass-2 tokens per th
 constexpr int kSweepGroups = 2;                          // pass-2 chunks per workgroup
 constexpr int kSweepThreads = kThreads * kSweepGroups;   // k_sweep workgroup
 constexpr int kSampleThreads = 1024;                     // k_sample workgroup
-constexpr int kDecideThreads = 1024;                     // k_decide workgroup
+constexpr int kDecideThreads = 1024;                     // k_decide workgroup (tree)
 constexpr int kSampleRun = kChunk / kSampleThreads;      // k_sample tokens per thread
 constexpr int kSampleWaves = kSampleThreads / 64;
 static_assert(kSampleRun == 4, "k_sample loads four tokens per thread");
@@ -1086,11 +1086,16 @@ __device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
 }
 
 // -------------------------------------------------------------- decide
-// Greedy and tree: one workgroup (kDecideThreads) per request folds the tile
+// The greedy rule's decide workgroup folds only K + 1 rows: eight waves take
+// them in one batch for K < 8 and launch faster than sixteen.
+constexpr int decide_threads(int mode) { return mode == kGreedy ? 512 : kDecideThreads; }
+
+// Greedy and tree: one workgroup (decide_threads) per request folds the tile
 // records (one row per wave), takes the decision and writes the outputs.
 template <typename T, int MODE, bool SUM, bool SHARD>
-__global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
-    constexpr int NW = kDecideThreads / 64;
+__global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
+    constexpr int NT = decide_threads(MODE);
+    constexpr int NW = NT / 64;
     const int b = blockIdx.x;
     __shared__ double tab[kExpTab];
     __shared__ RowStats rs;
@@ -1186,7 +1191,7 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const Args a) {
         }
         __syncthreads();
         const int d = t_d, e = t_e;
-        for (int k = threadIdx.x; k < N; k += kDecideThreads) {
+        for (int k = threadIdx.x; k < N; k += NT) {
             int32_t* otok = a.out_tok + (size_t)b * N;
             if (k < d) {
                 const int v = t_path[k];
@@ -1627,9 +1632,9 @@ spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
     if (ls != SPEC_OK) return SPEC_EHIP;
     if constexpr (MODE == kGreedy || MODE == kTree) {
         if (dt == SPEC_BF16)
-            hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM, false>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM, false>), dim3(a.B), dim3(decide_threads(MODE)), 0, st, a);
         else
-            hipLaunchKernelGGL((k_decide<float, MODE, SUM, false>), dim3(a.B), dim3(kDecideThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decide<float, MODE, SUM, false>), dim3(a.B), dim3(decide_threads(MODE)), 0, st, a);
     } else {
         const dim3 grid2((unsigned)a.B * (unsigned)((a.C2 + kSweepGroups - 1) / kSweepGroups));
         const dim3 block2(kSweepThreads);
@@ -2128,7 +2133,7 @@ spec_status spec_shard_combine_greedy(const void* records, spec_dtype dtype,
     a.out_blp = out_behavior_logprob;
     a.out_status = out_status;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(B), block(kDecideThreads);
+    const dim3 grid(B), block(decide_threads(kGreedy));
     if (dtype == SPEC_BF16) {
         if (out_target_logprob) return shard_launch(k_decide<uint16_t, kGreedy, true, true>, grid, block, a, st);
         return shard_launch(k_decide<uint16_t, kGreedy, false, true>, grid, block, a, st);
