@@ -87,7 +87,7 @@ constexpr int kRun = kChunk / kThreads;                  // pass-2 tokens per th
 constexpr int kSweepGroups = 2;                          // pass-2 chunks per workgroup
 constexpr int kSweepThreads = kThreads * kSweepGroups;   // k_sweep workgroup
 constexpr int kSampleThreads = 1024;                     // k_sample workgroup
-constexpr int kDecideThreads = 1024;                     // k_decide workgroup (tree)
+constexpr int kDecideThreads = 1024;                     // k_decide workgroup
 constexpr int kSampleRun = kChunk / kSampleThreads;      // k_sample tokens per thread
 constexpr int kSampleWaves = kSampleThreads / 64;
 static_assert(kSampleRun == 4, "k_sample loads four tokens per thread");
