@@ -17,7 +17,9 @@
  *   (b * rows + r) * V.  dtype is SPEC_BF16 (16-bit brain float, read as the
  *   top half of an fp32) or SPEC_F32.  Every array is aligned to its element
  *   size (2 bytes for bf16, 4 for fp32 and int32), as any tensor or array of
- *   that type is.  Rows whose start is 16-byte aligned
+ *   that type is.  No output, record, sums or workspace buffer may overlap
+ *   an input of the same call (inputs are read through caches that a call's
+ *   own writes do not update).  Rows whose start is 16-byte aligned
  *   (pointer % 16 == 0 and V * element size % 16 == 0) take the vector fast
  *   path; any other V is handled element by element.  Logit rows must hold
  *   at least one finite value; -inf entries are allowed and have probability
