@@ -258,6 +258,11 @@ def test_misaligned_rows_take_element_path():
     torch.cuda.synchronize()
     compare_chain(r, oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
                   what="misaligned")
+    og = oracle.greedy(ci.target, ci.tokens, "bf16")
+    for lp in (True, False):  # 16 KiB and 8 KiB tiles
+        g = sv.spec_verify_greedy(T, dev(ci.tokens), logprobs=lp)
+        torch.cuda.synchronize()
+        compare_chain(g, og, logprobs=lp, what=f"misaligned greedy logprobs={lp}")
 
 
 def test_out_of_range_draft_tokens_set_status():
@@ -407,7 +412,10 @@ def test_largest_vocabulary(dtype):
     ci = synth.chain_inputs(2, 3, 262144, dtype, seed=121, useed=122)
     o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, dtype)
     compare_chain(_exact(ci), o, what=f"exact V max {dtype}")
-    compare_chain(_greedy(ci), oracle.greedy(ci.target, ci.tokens, dtype), what=f"greedy V max {dtype}")
+    og = oracle.greedy(ci.target, ci.tokens, dtype)
+    compare_chain(_greedy(ci), og, what=f"greedy V max {dtype}")
+    # bf16 without log-probs: 8 KiB tiles, 64 tile records a row (one per lane)
+    compare_chain(_greedy(ci, logprobs=False), og, logprobs=False, what=f"greedy V max {dtype} no-logprob")
     ci.tau, ci.top_k = 0.1, 4
     compare_chain(_relaxed(ci), oracle.relaxed(ci.target, ci.tokens, ci.uniforms, dtype, 0.1, 4),
                   what=f"relaxed V max {dtype}")

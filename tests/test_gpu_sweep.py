@@ -59,8 +59,8 @@ def _sync(r):
 
 @pytest.mark.parametrize("c", CHAIN, ids=lambda c: f"{c['i']}-B{c['B']}-K{c['K']}-V{c['V']}-{c['dtype']}")
 def test_chain_rules_sweep(c):
-    """Exact, greedy, relaxed and power on one batch, and the draft sampler on
-    its draft rows."""
+    """Exact, greedy (with and without log-probs), relaxed and power on one
+    batch, and the draft sampler on its draft rows."""
     print(f"sweep {c}", flush=True)
     B, K, V, dt = c["B"], c["K"], c["V"], c["dtype"]
     ci = synth.chain_inputs(B, K, V, dt, seed=5000 + c["i"], useed=6000 + c["i"],
@@ -72,8 +72,11 @@ def test_chain_rules_sweep(c):
     t.add(compare_chain(_sync(sv.spec_verify_exact(T, D, x, u)),
                         oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, dt),
                         what=f"{what} exact"))
-    t.add(compare_chain(_sync(sv.spec_verify_greedy(T, x)),
-                        oracle.greedy(ci.target, ci.tokens, dt), what=f"{what} greedy"))
+    og = oracle.greedy(ci.target, ci.tokens, dt)
+    t.add(compare_chain(_sync(sv.spec_verify_greedy(T, x)), og, what=f"{what} greedy"))
+    # without log-probs the bf16 stream reads 8 KiB tiles
+    t.add(compare_chain(_sync(sv.spec_verify_greedy(T, x, logprobs=False)), og, logprobs=False,
+                        what=f"{what} greedy no-logprob"))
     t.add(compare_chain(_sync(sv.spec_verify_relaxed(T, x, u, c["tau"], c["top_k"])),
                         oracle.relaxed(ci.target, ci.tokens, ci.uniforms, dt, c["tau"], c["top_k"]),
                         what=f"{what} relaxed"))
