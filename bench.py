@@ -644,8 +644,8 @@ def cpu_baseline(ci, seconds):
     one = oracle_rate(lambda: oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
                       3.0, 100)
     oracle.set_threads(threads)
-    c1 = synth.c1()
-    c1_rate = c1.B * oracle_rate(lambda: oracle.exact(c1.target, c1.draft, c1.tokens, c1.uniforms,
+    tiny = synth.tiny_exact_v32()
+    tiny_rate = tiny.B * oracle_rate(lambda: oracle.exact(tiny.target, tiny.draft, tiny.tokens, tiny.uniforms,
                                                       "f32"), 1.0, 1000)
     return {"value": n / el, "unit": "rounds/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} exact verification calls of the benchmark batch (B=32, K=5, "
@@ -653,7 +653,7 @@ def cpu_baseline(ci, seconds):
                       f"OpenMP over requests",
             "cpu_model": cpu_model(), "single_thread_value": one,
             "gbs_equivalent": n / el * ci.algorithmic_bytes_exact / 1e9,
-            "tiny_exact_b1_k4_v32_rounds_per_s": c1_rate}
+            "tiny_exact_b1_k4_v32_rounds_per_s": tiny_rate}
 
 
 def main():
@@ -683,7 +683,7 @@ def main():
     lib.spec_verify_profile_next_call.restype = None
     dev = torch.device("cuda:0")
     hip = Hip()
-    ci = synth.c3()
+    ci = synth.exact_b32_k5()
     bytes_exact = ci.algorithmic_bytes_exact
     bytes_greedy = ci.algorithmic_bytes_greedy
     sets_exact = math.ceil(2 * MALL_BYTES / bytes_exact)
@@ -711,28 +711,28 @@ def main():
     others = None
     if not args.no_configs:
         others = {}
-        c2 = synth.c2()
+        greedy8 = synth.greedy_chain_b8()
         others["greedy_b8"] = other_workload(
-            lib, "greedy", c2, c2.algorithmic_bytes_greedy,
+            lib, "greedy", greedy8, greedy8.algorithmic_bytes_greedy,
             "greedy chain, B=8 K=5 V=128256 bf16, no log-probs", args.steps, args.warmup, hip,
             use_graph, torch, dev, cpu)
-        del c2
-        c4 = synth.c4()
+        del greedy8
+        tree8 = synth.tree_b8_n61()
         others["tree_b8_n61"] = other_workload(
-            lib, "tree", c4, c4.algorithmic_bytes,
+            lib, "tree", tree8, tree8.algorithmic_bytes,
             "greedy tree (depth 5, top-k 4, 60 drafted nodes + root), B=8 V=128256 bf16, "
             "no log-probs", args.steps, args.warmup, hip, use_graph, torch, dev, cpu)
-        del c4
-        c5 = synth.c5()
+        del tree8
+        large = synth.large_b64_k8()
         others["relaxed_b64_k8"] = other_workload(
-            lib, "relaxed", c5, c5.algorithmic_bytes_relaxed,
-            f"relaxed (p >= {c5.tau} or top-{c5.top_k}), B=64 K=8 V=151936 bf16", args.steps,
+            lib, "relaxed", large, large.algorithmic_bytes_relaxed,
+            f"relaxed (p >= {large.tau} or top-{large.top_k}), B=64 K=8 V=151936 bf16", args.steps,
             args.warmup, hip, use_graph, torch, dev, cpu)
         others["exact_b64_k8"] = other_workload(
-            lib, "exact", c5, c5.algorithmic_bytes_exact,
+            lib, "exact", large, large.algorithmic_bytes_exact,
             "exact, B=64 K=8 V=151936 bf16, draft target+0.8*N(0,1)", args.steps, args.warmup,
             hip, use_graph, torch, dev, cpu)
-        del c5
+        del large
         others["sharded_exact_greedy_g8"] = sharded_block(lib, ci, 8, min(args.steps, 200),
                                                          min(args.warmup, 20), hip, torch, dev)
         others["markov_driver"] = markov_block(torch, dev, min(args.steps, 200),
@@ -783,7 +783,7 @@ def main():
         "graph_ms_per_step_runs": r_ex.get("graph_ms_per_step_runs"),
         "eager": {"rounds_per_s": 1000.0 / r_ex["eager_ms_per_step"],
                   "ms_per_step": r_ex["eager_ms_per_step"]},
-        "greedy_c3_shape": {
+        "greedy_b32_k5": {
             "rounds_per_s": 1000.0 / g_ms, "ms_per_step": g_ms,
             "hbm_gbs_call": bytes_greedy / (g_ms * 1e-3) / 1e9,
             "kernel_us_mean": r_gr["kernel_ms_mean"] * 1e3,
@@ -795,13 +795,13 @@ def main():
             "rest_of_call_us_mean": r_gr["rest_ms_mean"] * 1e3,
             "eager_rounds_per_s": 1000.0 / r_gr["eager_ms_per_step"],
             "algorithmic_bytes": bytes_greedy, "input_sets": sets_greedy},
-        "power_c3": {
+        "power_b32_k5": {
             "alpha": POWER_ALPHA, "rounds_per_s": 1000.0 / p_ms, "ms_per_step": p_ms,
             "hbm_gbs_call": bytes_exact / (p_ms * 1e-3) / 1e9,
             "kernel_us_mean": r_pw["kernel_ms_mean"] * 1e3,
             "kernel_gbs": stream_bytes / (r_pw["kernel_ms_mean"] * 1e-3) / 1e9,
             "rest_of_call_us_mean": r_pw["rest_ms_mean"] * 1e3, "input_sets": sets_exact},
-        "draft_sampler_c3_draft_rows": {
+        "draft_sampler_b32_k5_draft_rows": {
             "calls_per_s": 1000.0 / s_ms, "ms_per_call": s_ms, "rows": ci.B * ci.K,
             "hbm_gbs_call": ci.draft.nbytes / (s_ms * 1e-3) / 1e9,
             "kernel_us_mean": r_sa["kernel_ms_mean"] * 1e3,

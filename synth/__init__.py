@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "bf16_rne", "bf16_to_f32", "ChainInputs", "TreeInputs", "chain_inputs",
-    "c1", "c2", "c3", "c5", "c4", "tree_inputs", "make_tree", "widen",
+    "tiny_exact_v32", "greedy_chain_b8", "exact_b32_k5", "large_b64_k8", "tree_b8_n61", "tree_inputs", "make_tree", "widen",
     "gumbel_max_tokens",
 ]
 
@@ -208,7 +208,7 @@ def chain_inputs(B: int, K: int, V: int, dtype: str = "bf16", *, seed: int, usee
 # ----------------------------------------------------------------------------
 # the five workloads
 # ----------------------------------------------------------------------------
-def c1(rounds: int = 1000, seed: int = 1) -> ChainInputs:
+def tiny_exact_v32(rounds: int = 1000, seed: int = 1) -> ChainInputs:
     """Tiny exact rejection sampling: B=1, K=4, V=32, fp32, many rounds.
 
     Target ~ 2*N(0,1), draft = target + 0.7*N(0,1), x ~ softmax(draft).  Each
@@ -221,11 +221,11 @@ def c1(rounds: int = 1000, seed: int = 1) -> ChainInputs:
     d = (t[:, :K, :] + _normal(rng, (rounds, K, V), 0.7)).astype(np.float32)
     tokens = gumbel_max_tokens(d.astype(np.float64), rng)
     u = np.random.default_rng(0).random((rounds, 1, K + 1), dtype=np.float32).reshape(rounds, K + 1)
-    return ChainInputs(name="c1", dtype="f32", B=rounds, K=K, V=V, target=t, draft=d,
+    return ChainInputs(name="tiny_exact_v32", dtype="f32", B=rounds, K=K, V=V, target=t, draft=d,
                        tokens=tokens, uniforms=u)
 
 
-def c2(seed: int = 2, rnd: int = 0, B: int = 8, K: int = 5, V: int = 128256) -> ChainInputs:
+def greedy_chain_b8(seed: int = 2, rnd: int = 0, B: int = 8, K: int = 5, V: int = 128256) -> ChainInputs:
     """Greedy chain verify: bf16 3*N(0,1) target [B][K+1][V].
 
     For request b, j_b ~ U{0..K}; drafts 0..j_b-1 equal the row argmax (lowest
@@ -249,24 +249,24 @@ def c2(seed: int = 2, rnd: int = 0, B: int = 8, K: int = 5, V: int = 128256) -> 
             tokens[b, jb[b]] = below[rng.integers(0, below.size)]
     urng = _rng(102, rnd)
     uniforms = urng.random((B, K + 1), dtype=np.float32)
-    ci = ChainInputs(name="c2", dtype="bf16", B=B, K=K, V=V, target=target, draft=None,
+    ci = ChainInputs(name="greedy_chain_b8", dtype="bf16", B=B, K=K, V=V, target=target, draft=None,
                      tokens=tokens, uniforms=uniforms, expected_accept_len=jb.astype(np.int32))
     ci.extra["expected_bonus"] = np.array([g[b, jb[b]] for b in range(B)], dtype=np.int32)
     return ci
 
 
-def c3(seed: int = 3, useed: int = 103, rnd: int = 0, B: int = 32, K: int = 5,
+def exact_b32_k5(seed: int = 3, useed: int = 103, rnd: int = 0, B: int = 32, K: int = 5,
        V: int = 128256) -> ChainInputs:
     """Exact stochastic verify: B=32, K=5, V=128256 bf16; target 3*N(0,1), draft + 0.5*N(0,1)."""
     return chain_inputs(B, K, V, "bf16", seed=seed, useed=useed, t_scale=3.0, d_noise=0.5,
-                        rnd=rnd, name="c3")
+                        rnd=rnd, name="exact_b32_k5")
 
 
-def c5(seed: int = 5, useed: int = 105, rnd: int = 0, B: int = 64, K: int = 8,
+def large_b64_k8(seed: int = 5, useed: int = 105, rnd: int = 0, B: int = 64, K: int = 8,
        V: int = 151936) -> ChainInputs:
     """Relaxed + exact: B=64, K=8, V=151936 bf16; draft + 0.8*N(0,1); tau=0.1, top-4."""
     return chain_inputs(B, K, V, "bf16", seed=seed, useed=useed, t_scale=3.0, d_noise=0.8,
-                        rnd=rnd, tau=0.1, top_k=4, name="c5")
+                        rnd=rnd, tau=0.1, top_k=4, name="large_b64_k8")
 
 
 # ----------------------------------------------------------------------------
@@ -380,9 +380,9 @@ def tree_inputs(B: int = 8, V: int = 128256, dtype: str = "bf16", *, seed: int =
                       expected_path=paths, expected_bonus=bonus)
 
 
-def c4(seed: int = 4, rnd: int = 0, B: int = 8, V: int = 128256) -> TreeInputs:
+def tree_b8_n61(seed: int = 4, rnd: int = 0, B: int = 8, V: int = 128256) -> TreeInputs:
     """Greedy tree verify: B=8, 61 rows (root + 60 drafted nodes), V=128256 bf16."""
-    return tree_inputs(B=B, V=V, dtype="bf16", seed=seed, rnd=rnd, name="c4")
+    return tree_inputs(B=B, V=V, dtype="bf16", seed=seed, rnd=rnd, name="tree_b8_n61")
 
 
 # ----------------------------------------------------------------------------

@@ -45,22 +45,22 @@ def _tree(ti, **kw):
 
 # ------------------------------------------------------------------ greedy
 @pytest.mark.parametrize("rnd", range(6))
-def test_greedy_c2_full_size(rnd):
+def test_greedy_b8_full_size(rnd):
     """B=8, K=5, V=128256 bf16; the accepted length equals the construction."""
-    ci = synth.c2(rnd=rnd)
-    print(f"greedy c2 round {rnd}", flush=True)
+    ci = synth.greedy_chain_b8(rnd=rnd)
+    print(f"greedy B=8 round {rnd}", flush=True)
     o = oracle.greedy(ci.target, ci.tokens, "bf16")
     np.testing.assert_array_equal(o.accept_len, ci.expected_accept_len)
-    compare_chain(_greedy(ci), o, what=f"c2 r{rnd}")
+    compare_chain(_greedy(ci), o, what=f"greedy B=8 r{rnd}")
     r = _greedy(ci, logprobs=False)
     assert r.target_logprob is None
-    compare_chain(r, o, logprobs=False, what=f"c2 r{rnd} no-logprob")
+    compare_chain(r, o, logprobs=False, what=f"greedy B=8 r{rnd} no-logprob")
 
 
-def test_greedy_c3_shape():
-    ci = synth.c3()
+def test_greedy_b32_k5():
+    ci = synth.exact_b32_k5()
     o = oracle.greedy(ci.target, ci.tokens, "bf16")
-    compare_chain(_greedy(ci), o, what="c3-shape greedy")
+    compare_chain(_greedy(ci), o, what="greedy B=32")
 
 
 @pytest.mark.parametrize("K", [1, 2, 5, 8, 63])
@@ -84,55 +84,55 @@ def test_greedy_scenarios(K):
 
 
 # ------------------------------------------------------------------- exact
-def test_exact_c1_batched():
+def test_exact_tiny_v32_batched():
     """1000 rounds of B=1, K=4, V=32 fp32, run as one B=1000 call."""
-    ci = synth.c1()
+    ci = synth.tiny_exact_v32()
     o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32")
-    t = compare_chain(_exact(ci), o, what="c1 batched")
+    t = compare_chain(_exact(ci), o, what="tiny exact batched")
     assert t.within_budget(), t
     og = oracle.greedy(ci.target, ci.tokens, "f32")
-    compare_chain(_greedy(ci), og, what="c1 greedy")
+    compare_chain(_greedy(ci), og, what="tiny greedy")
 
 
-def test_exact_c1_single_requests():
+def test_exact_tiny_v32_single_requests():
     """The same rounds as individual B=1 calls (first 100)."""
-    ci = synth.c1()
+    ci = synth.tiny_exact_v32()
     o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32")
     tot = Tally()
     for r in range(100):
-        sub = synth.ChainInputs("c1", "f32", 1, 4, 32, ci.target[r:r + 1], ci.draft[r:r + 1],
+        sub = synth.ChainInputs("tiny_exact_v32", "f32", 1, 4, 32, ci.target[r:r + 1], ci.draft[r:r + 1],
                                 ci.tokens[r:r + 1], ci.uniforms[r:r + 1])
         osub = oracle.OracleResult(*(getattr(o, f)[r:r + 1] for f in
                                      ("tokens", "accept_len", "target_logprob",
                                       "behavior_logprob", "status", "flag", "decisions")))
-        tot.add(compare_chain(_exact(sub), osub, what=f"c1 round {r}"))
+        tot.add(compare_chain(_exact(sub), osub, what=f"tiny exact round {r}"))
     assert tot.within_budget(), tot
 
 
 @pytest.mark.parametrize("rnd", range(4))
-def test_exact_c3_full_size(rnd):
+def test_exact_b32_full_size(rnd):
     """B=32, K=5, V=128256 bf16 -- the benchmarked configuration."""
-    print(f"exact c3 round {rnd}", flush=True)
-    ci = synth.c3(rnd=rnd)
+    print(f"exact B=32 round {rnd}", flush=True)
+    ci = synth.exact_b32_k5(rnd=rnd)
     o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")
-    t = compare_chain(_exact(ci), o, what=f"c3 r{rnd}")
+    t = compare_chain(_exact(ci), o, what=f"exact B=32 r{rnd}")
     assert t.within_budget(), t
 
 
-def test_exact_c5_full_size():
-    print("exact c5", flush=True)
-    ci = synth.c5()
+def test_exact_b64_full_size():
+    print("exact B=64 K=8", flush=True)
+    ci = synth.large_b64_k8()
     o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")
-    t = compare_chain(_exact(ci), o, what="c5 exact")
+    t = compare_chain(_exact(ci), o, what="exact B=64")
     assert t.within_budget(), t
 
 
 # ----------------------------------------------------------------- relaxed
-def test_relaxed_c5_full_size():
-    print("relaxed c5", flush=True)
-    ci = synth.c5()
+def test_relaxed_b64_full_size():
+    print("relaxed B=64 K=8", flush=True)
+    ci = synth.large_b64_k8()
     o = oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", ci.tau, ci.top_k)
-    t = compare_chain(_relaxed(ci), o, what="c5 relaxed")
+    t = compare_chain(_relaxed(ci), o, what="relaxed B=64")
     assert t.within_budget(), t
 
 
@@ -146,15 +146,15 @@ def test_relaxed_special_cases(tau, k):
 
 # -------------------------------------------------------------------- tree
 @pytest.mark.parametrize("rnd", range(3))
-def test_tree_c4_full_size(rnd):
-    print(f"tree c4 round {rnd}", flush=True)
-    ti = synth.c4(rnd=rnd)
+def test_tree_b8_n61_full_size(rnd):
+    print(f"tree B=8 N=61 round {rnd}", flush=True)
+    ti = synth.tree_b8_n61(rnd=rnd)
     o = oracle.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes)
     for b in range(ti.B):
         assert list(o.path[b, : o.accept_len[b]]) == ti.expected_path[b]
-    compare_tree(_tree(ti), o, what=f"c4 r{rnd}")
+    compare_tree(_tree(ti), o, what=f"tree B=8 r{rnd}")
     r = _tree(ti, logprobs=False)
-    compare_tree(r, o, logprobs=False, what=f"c4 r{rnd} no-logprob")
+    compare_tree(r, o, logprobs=False, what=f"tree B=8 r{rnd} no-logprob")
 
 
 def test_tree_chain_equals_greedy_on_gpu():

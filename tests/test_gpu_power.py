@@ -28,14 +28,14 @@ def _check(ci, alpha, what):
 
 
 @pytest.mark.parametrize("alpha", [0.5, 1.0, 2.0])
-def test_power_c3(alpha):
+def test_power_b32(alpha):
     """The benchmark batch, B=32 K=5 V=128256 bf16, at three exponents."""
-    t, o = _check(synth.c3(), alpha, f"c3 power alpha={alpha}")
+    t, o = _check(synth.exact_b32_k5(), alpha, f"power B=32 alpha={alpha}")
     assert t.flagged <= NEAR_TIE_BUDGET * max(t.decisions, 1) + 3
 
 
-def test_power_c5():
-    t, o = _check(synth.c5(), 0.7, "c5 power")
+def test_power_b64():
+    t, o = _check(synth.large_b64_k8(), 0.7, "power B=64")
     assert t.flagged <= NEAR_TIE_BUDGET * max(t.decisions, 1) + 3
 
 
@@ -57,8 +57,8 @@ def test_power_alpha_one_accepts_as_exact():
 
 
 def test_power_small_fp32_many_requests():
-    ci = synth.c1()
-    _check(ci, 1.5, "c1 power")
+    ci = synth.tiny_exact_v32()
+    _check(ci, 1.5, "power tiny V=32")
 
 
 @pytest.mark.parametrize("B,K,V,dtype", [(3, 1, 1, "f32"), (5, 3, 7, "bf16"), (2, 5, 8193, "bf16"),

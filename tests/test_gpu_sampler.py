@@ -40,24 +40,24 @@ def _compare(x, u, dtype, what, max_flags=None):
     return tok
 
 
-def test_sampler_c3_draft_rows():
+def test_sampler_b32_draft_rows():
     """The benchmark batch's draft logits, [32][5][128256] bf16, one draw per row."""
-    ci = synth.c3()
+    ci = synth.exact_b32_k5()
     u = np.random.default_rng(203).random(ci.tokens.shape, dtype=np.float32)
-    _compare(ci.draft, u, "bf16", "c3 draft rows")
+    _compare(ci.draft, u, "bf16", "B=32 draft rows")
 
 
-def test_sampler_c5_draft_rows():
-    ci = synth.c5()
+def test_sampler_b64_draft_rows():
+    ci = synth.large_b64_k8()
     u = np.random.default_rng(205).random(ci.tokens.shape, dtype=np.float32)
-    _compare(ci.draft, u, "bf16", "c5 draft rows")
+    _compare(ci.draft, u, "bf16", "B=64 draft rows")
 
 
 def test_sampler_small_fp32_many_rows():
-    """C1's shape: V=32 fp32, 1000 x 4 rows."""
-    ci = synth.c1()
+    """The tiny exact workload's shape: V=32 fp32, 1000 x 4 rows."""
+    ci = synth.tiny_exact_v32()
     u = np.random.default_rng(201).random(ci.tokens.shape, dtype=np.float32)
-    _compare(ci.draft, u, "f32", "c1 draft rows")
+    _compare(ci.draft, u, "f32", "tiny V=32 draft rows")
 
 
 @pytest.mark.parametrize("V", [1, 2, 7, 8, 4095, 4097, 8193, 128257])

@@ -55,13 +55,13 @@ def _check_owner(res, G, V):
 
 
 # ------------------------------------------------------------------ exact
-def test_exact_c3_eight_shards():
+def test_exact_b32_eight_shards():
     """B=32, K=5, V=128256 bf16 split over 8 shards of 16032 columns."""
-    print("sharded exact c3 g8", flush=True)
-    ci = synth.c3()
+    print("sharded exact B=32 g8", flush=True)
+    ci = synth.exact_b32_k5()
     o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")
     res = _exact_sharded(ci, 8)
-    t = compare_chain(res.result, o, what="sharded c3 g8")
+    t = compare_chain(res.result, o, what="sharded exact B=32 g8")
     assert t.within_budget(), t
     _check_owner(res, 8, ci.V)
 
@@ -115,9 +115,9 @@ def test_exact_sharded_reuses_buffers_across_calls():
 
 # ----------------------------------------------------------------- greedy
 @pytest.mark.parametrize("G", [1, 2, 8])
-def test_greedy_c2_sharded(G):
-    print(f"sharded greedy c2 G={G}", flush=True)
-    ci = synth.c2()
+def test_greedy_b8_sharded(G):
+    print(f"sharded greedy B=8 G={G}", flush=True)
+    ci = synth.greedy_chain_b8()
     o = oracle.greedy(ci.target, ci.tokens, "bf16")
     np.testing.assert_array_equal(o.accept_len, ci.expected_accept_len)
     compare_chain(_greedy_sharded(ci, G), o, what=f"sharded greedy G={G}")
@@ -156,9 +156,9 @@ def test_greedy_one_shard_is_the_unsharded_call():
 
 # ------------------------------------------------------------------- tree
 @pytest.mark.parametrize("G", [1, 8])
-def test_tree_c4_sharded(G):
-    print(f"sharded tree c4 G={G}", flush=True)
-    ti = synth.c4()
+def test_tree_b8_sharded(G):
+    print(f"sharded tree B=8 G={G}", flush=True)
+    ti = synth.tree_b8_n61()
     o = oracle.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes)
     compare_tree(_tree_sharded(ti, G), o, what=f"sharded tree G={G}")
     compare_tree(_tree_sharded(ti, G, logprobs=False), o, logprobs=False,
@@ -178,9 +178,9 @@ def test_tree_sharded_partial_counts_and_bad_parents():
 
 # ------------------------------------------------------------------ power
 @pytest.mark.parametrize("alpha", [0.5, 2.0])
-def test_power_c3_eight_shards(alpha):
-    print(f"sharded power c3 g8 alpha={alpha}", flush=True)
-    ci = synth.c3()
+def test_power_b32_eight_shards(alpha):
+    print(f"sharded power B=32 g8 alpha={alpha}", flush=True)
+    ci = synth.exact_b32_k5()
     o = oracle.power(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16", alpha)
     T = _split(dev_logits(ci.target, "bf16"), 8)
     D = _split(dev_logits(ci.draft, "bf16"), 8)
@@ -225,13 +225,13 @@ def _relaxed_sharded(ci, G):
     return r
 
 
-def test_relaxed_c5_eight_shards():
+def test_relaxed_b64_eight_shards():
     """B=64, K=8, V=151936 bf16 over 8 shards of 18992 columns."""
-    print("sharded relaxed c5 g8", flush=True)
-    ci = synth.c5()
+    print("sharded relaxed B=64 g8", flush=True)
+    ci = synth.large_b64_k8()
     o = oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", ci.tau, ci.top_k)
     res = _relaxed_sharded(ci, 8)
-    t = compare_chain(res.result, o, what="sharded relaxed c5")
+    t = compare_chain(res.result, o, what="sharded relaxed B=64")
     assert t.within_budget(), t
     _check_owner(res, 8, ci.V)
 

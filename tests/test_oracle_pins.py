@@ -143,8 +143,8 @@ def test_greedy_scenarios(orc, K):
         np.testing.assert_array_equal(r.behavior_logprob[0], 0.0)
 
 
-def test_greedy_c2_construction(orc):
-    ci = synth.c2(V=4099)
+def test_greedy_b8_construction(orc):
+    ci = synth.greedy_chain_b8(V=4099)
     r = orc.greedy(ci.target, ci.tokens, "bf16")
     np.testing.assert_array_equal(r.accept_len, ci.expected_accept_len)
     np.testing.assert_array_equal(r.tokens[np.arange(ci.B), r.accept_len], ci.extra["expected_bonus"])
@@ -168,7 +168,7 @@ def test_argmax_lowest_index_among_ties(orc):
     M, g, S = orc.row_stats(h, "bf16")
     np.testing.assert_array_equal(g, np.argmax(vals, axis=-1))
     np.testing.assert_array_equal(M, vals.max(-1))
-    # c3-like bf16 rows at V = 128256: about 5% of rows tie at the max
+    # bf16 3*N(0,1) rows at V = 128256: about 5% of rows tie at the max
     t = synth.bf16_rne(3.0 * np.random.default_rng(8).standard_normal((40, 128256), dtype=np.float32))
     M, g, S = orc.row_stats(t, "bf16")
     np.testing.assert_array_equal(g, np.argmax(synth.bf16_to_f32(t), axis=-1))
@@ -363,10 +363,10 @@ def test_exact_identical_draft_accepts_everything(orc):
     np.testing.assert_allclose(r.behavior_logprob[:, :4], 0.0, atol=1e-12)
 
 
-def test_exact_c1_acceptance_rate_matches_tv(orc):
+def test_exact_tiny_acceptance_rate_matches_tv(orc):
     """Mean acceptance of test j equals 1 - TV(p_j, q_j) in expectation; checked
     on the tiny exact workload (1000 rounds) within a binomial 5-sigma band."""
-    ci = synth.c1()
+    ci = synth.tiny_exact_v32()
     r = orc.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32")
     P = softmax64(synth.widen(ci.target, "f32")[:, 0, :])
     Q = softmax64(synth.widen(ci.draft, "f32")[:, 0, :])
@@ -461,7 +461,7 @@ def test_tree_brute_force_all_root_paths(orc):
         assert r.tokens[b, d] == bonus
 
 
-def test_tree_c4_construction(orc):
+def test_tree_b8_construction(orc):
     ti = synth.tree_inputs(B=4, V=3001, seed=4)
     r = orc.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes)
     for b in range(ti.B):

@@ -39,8 +39,8 @@ def test_chain_inputs_deterministic_and_shaped():
     assert not np.array_equal(a.target, c.target)
 
 
-def test_c1_shapes():
-    ci = synth.c1(rounds=1000)
+def test_tiny_exact_shapes():
+    ci = synth.tiny_exact_v32(rounds=1000)
     assert ci.target.shape == (1000, 5, 32) and ci.target.dtype == np.float32
     assert ci.draft.shape == (1000, 4, 32)
     np.testing.assert_array_equal(
@@ -72,8 +72,8 @@ def test_tree_inputs_sibling_tokens_distinct():
             assert len(toks) == len(set(toks))
 
 
-def test_c2_construction_facts():
-    ci = synth.c2(V=2000)
+def test_greedy_b8_construction_facts():
+    ci = synth.greedy_chain_b8(V=2000)
     g = np.argmax(synth.bf16_to_f32(ci.target), -1)
     for b in range(ci.B):
         j = int(ci.expected_accept_len[b])
