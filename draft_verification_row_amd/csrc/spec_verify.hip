@@ -18,15 +18,16 @@
 // three kernels per call on the caller's stream.  Vocabulary-sharded calls
 // run the same kernels one step at a time (spec_shard_*).
 //
-//   k_stream  one workgroup per (logit row, 16 KB tile).  Each thread issues
-//             its four 16-byte loads at once; the workgroup reduces the tile
-//             max (with the lowest index among equal maxima for the greedy
-//             rules, and the rank count #{t : l_t > l_x} for the relaxed
-//             rule) and, where a normalizer is needed, the sum of
-//             exp(l - tile max): v_exp_f32 per logit, fp32 within a vector,
-//             fp64 beyond.  One 16-byte record per tile goes to the
-//             workspace.  This kernel reads every logit once and carries all
-//             of the call's HBM traffic.
+//   k_stream  one workgroup per (logit row, 16 KB tile; 8 KB for the greedy
+//             rule without log-probs).  Each thread issues its 16-byte loads
+//             at once; the workgroup reduces the tile max (with the lowest
+//             index among equal maxima for the greedy rules, and the rank
+//             count #{t : l_t > l_x} for the relaxed rule) and, where a
+//             normalizer is needed, the sum of exp(l - tile max): v_exp_f32
+//             per logit, fp32 over a thread's terms, fp64 beyond.  One
+//             16-byte record per tile goes to the workspace.  This kernel
+//             reads every logit once and carries all of the call's HBM
+//             traffic.
 //
 //   k_decide  (greedy, tree) one workgroup per request.  A wave folds the
 //             tile records of a row, one record per lane: max and argmax by
