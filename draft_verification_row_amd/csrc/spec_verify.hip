@@ -189,15 +189,22 @@ struct Elem<uint16_t> {  // bf16 bit patterns
     __device__ static inline float at(const uint16_t* p, size_t i) {
         return __uint_as_float((uint32_t)p[i] << 16);
     }
-    // element i's bits by a scalar load of the aligned dword that holds it
-    // (that dword lies in the same allocation: device allocations are
-    // aligned far beyond 4 bytes); widened by from_bits
-    __device__ static inline uint32_t sbits(const uint16_t* p, int i) {
-        const uintptr_t at = (uintptr_t)(p + i);
-        const uint32_t w = *(const __attribute__((address_space(4))) uint32_t*)(at & ~(uintptr_t)3);
-        return (at & 2) ? (w >> 16) : (w & 0xffffu);
+    // element i's bits: sword loads the aligned dword that holds it by a
+    // scalar load (that dword lies in the same allocation: device
+    // allocations are aligned far beyond 4 bytes), half picks the element;
+    // from_bits widens it
+    __device__ static inline uint32_t sword(const uint16_t* p, int i) {
+        return *(const __attribute__((address_space(4))) uint32_t*)((uintptr_t)(p + i) & ~(uintptr_t)3);
+    }
+    __device__ static inline uint32_t half(const uint16_t* p, int i, uint32_t w) {
+        return ((uintptr_t)(p + i) & 2) ? (w >> 16) : (w & 0xffffu);
     }
     __device__ static inline float from_bits(uint32_t w) { return __uint_as_float(w << 16); }
+    // element i's bits by a vector buffer load: 0, with no memory access, at
+    // or past the descriptor's size
+    __device__ static inline uint32_t bbits(__amdgpu_buffer_rsrc_t r, int i) {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, i * 2, 0, 0);
+    }
     template <int AUX = 0>
     __device__ static inline u32x4 vraw(__amdgpu_buffer_rsrc_t r, int e) {
         return __builtin_amdgcn_raw_buffer_load_b128(r, e * 2, 0, AUX);
@@ -268,10 +275,14 @@ template <>
 struct Elem<float> {
     static constexpr int kVec = 4;
     __device__ static inline float at(const float* p, size_t i) { return p[i]; }
-    __device__ static inline uint32_t sbits(const float* p, int i) {
+    __device__ static inline uint32_t sword(const float* p, int i) {
         return *(const __attribute__((address_space(4))) uint32_t*)(uintptr_t)(p + i);
     }
+    __device__ static inline uint32_t half(const float*, int, uint32_t w) { return w; }
     __device__ static inline float from_bits(uint32_t w) { return __uint_as_float(w); }
+    __device__ static inline uint32_t bbits(__amdgpu_buffer_rsrc_t r, int i) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0);
+    }
     template <int AUX = 0>
     __device__ static inline u32x4 vraw(__amdgpu_buffer_rsrc_t r, int e) {
         return __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, AUX);
@@ -620,7 +631,7 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     __shared__ float s_m[kWaves];
-    __shared__ int s_i[kWaves], s_j[kWaves];
+    __shared__ int s_j[kWaves];
     __shared__ double s_s[kWaves];
 
     // Waves issuing their loads take precedence over waves reducing a tile
@@ -632,43 +643,48 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     int vec, act;
     const T* row = call_row<T, MODE>(a, g, vec, act);
     if (!act) return;  // tree node past num_nodes: never read
-    // Drafted-token reads, all workgroup-uniform and by scalar loads: the
-    // token id goes out ahead of the tile's loads and its logit right behind
-    // them, so both round trips overlap the tile's.
+    // Drafted-token reads.  The token ids are workgroup-uniform scalar loads
+    // issued right behind the tile's loads (their waits count apart from the
+    // tile's vector loads, and nothing delays the tile's issue).
     // XV: the first workgroups record the drafted token's logits, one
     // (position, row kind) each: 2*B*K <= B*(2K+1) workgroups for the draft
-    // rules, B*K <= B*(K+1) for the others.
+    // rules, B*K <= B*(K+1) for the others.  The logit is a vector load issued
+    // right behind the tile's and consumed only when the record is written, so
+    // nothing waits for it; every workgroup issues it, with a descriptor of
+    // size 0 (no memory access) outside the recording workgroups and for an
+    // out-of-range token.
     constexpr int kinds = uses_draft(MODE) ? 2 : 1;
     const bool xvw = XV && (int)blockIdx.x < kinds * a.B * a.K;
     const int xi = uniform((int)blockIdx.x / kinds), xslot = 2 * xi + ((int)blockIdx.x - xi * kinds);
     // COUNT: a target row j < K counts the tokens strictly above l_x of its
-    // drafted token x
+    // drafted token x; l_x is needed from the second pass over the tile on
     const int cb = COUNT ? g / a.R : 0, cr = COUNT ? g - cb * a.R : 0;
     const bool cw = COUNT && cr < a.K;
-    int xt = 0, ct = 0;
-    if (xvw) xt = sload_i32(a.tok + xi);
-    if (cw) ct = sload_i32(a.tok + cb * a.K + cr);
-    __builtin_amdgcn_sched_barrier(0);
     u32x4 q[NV];
     load_tile<T, NT, VECP, NV>(row, a.V, c, q);
     __builtin_amdgcn_sched_barrier(0);
-    int xl = -1;
+    int xt = 0, ct = 0;
+    if (xvw) xt = sload_i32(a.tok + xi);
+    if (cw) ct = sload_i32(a.tok + cb * a.K + cr);
     uint32_t xraw = 0u;
-    if (xvw) {
-        xl = xt - a.shard * a.V;
+    int xl = -1;
+    if (XV) {
         const int b = xi / a.K, j = xi - b * a.K;
         const T* xsrc = xslot & 1 ? reinterpret_cast<const T*>(a.D) + (size_t)xi * a.V
                                   : reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + j) * a.V;
-        if ((unsigned)xl < (unsigned)a.V) xraw = Elem<T>::sbits(xsrc, xl);
+        xl = xvw ? xt - a.shard * a.V : -1;
+        const bool xin = (unsigned)xl < (unsigned)a.V;
+        xraw = Elem<T>::bbits(row_rsrc(uniform_ptr(xsrc), xin ? a.V : 0), xin ? xl : 0);
     }
-    float thr = INFINITY;  // relaxed: count the tokens strictly above l_x
-    if (cw) {
-        if (SHARD) {
-            if ((unsigned)ct < (unsigned)a.Vtot)
-                thr = sload_f32(a.xv_in + (size_t)(ct / a.V) * a.slot_xv + cb * a.K + cr);
-        } else if ((unsigned)ct < (unsigned)a.V) {
-            thr = Elem<T>::from_bits(Elem<T>::sbits(row, ct));
-        }
+    // relaxed: the raw word holding l_x, turned into the threshold after the
+    // first barrier (so that its wait falls there)
+    uint32_t tword = 0u;
+    const bool tin = cw && (SHARD ? (unsigned)ct < (unsigned)a.Vtot : (unsigned)ct < (unsigned)a.V);
+    if (tin) {
+        if (SHARD)
+            tword = (uint32_t)__float_as_uint(sload_f32(a.xv_in + (size_t)(ct / a.V) * a.slot_xv + cb * a.K + cr));
+        else
+            tword = Elem<T>::sword(row, ct);
     }
     __builtin_amdgcn_s_setprio(0);
 
@@ -680,26 +696,20 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     // Values are unpacked from the packed vectors where they are used, so
     // only the 16-byte vectors stay live between the phases.
     float m = -INFINITY;
-    int cnt = 0;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         float v[VEC];
         Elem<T>::unpack(q[k], v);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            m = fmaxf(m, v[i]);
-            if (COUNT) cnt += (v[i] > thr) ? 1 : 0;
-        }
+        for (int i = 0; i < VEC; ++i) m = fmaxf(m, v[i]);
     }
     float M = wave_max(m);
-    if (COUNT) cnt = wave_sum_i(cnt);
-    if (lane == 0) {
-        s_m[wave] = M;
-        s_i[wave] = cnt;
-    }
+    if (lane == 0) s_m[wave] = M;
     __syncthreads();
     M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-    int I = COUNT ? ((s_i[0] + s_i[1]) + s_i[2]) + s_i[3] : 0;
+    int I = 0;
+    // relaxed: count the tokens strictly above l_x
+    const float thr = !tin ? INFINITY : SHARD ? __uint_as_float(tword) : Elem<T>::from_bits(Elem<T>::half(row, ct, tword));
     // Greedy rules: the lowest index holding the tile max.  Only threads whose
     // own max is the tile max search their tokens (ascending, first hit), so
     // the common path pays one max per token.
@@ -715,6 +725,16 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
         }
     }
     double s = 0.0;
+    int cnt = 0;
+    if (COUNT && !SUM) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            float v[VEC];
+            Elem<T>::unpack(q[k], v);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) cnt += (v[i] > thr) ? 1 : 0;
+        }
+    }
     if (SUM && M > -INFINITY) {
         // 2^(l*L - mL) with the reference mL = fl(M*L): every term <= 1.  A
         // thread's 32 (bf16) or 16 (fp32) terms are summed in fp32 (relative
@@ -727,20 +747,25 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
             float v[VEC];
             Elem<T>::unpack(q[k], v);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc += __builtin_amdgcn_exp2f(fmaf(v[i], kLog2e, -mL));
+            for (int i = 0; i < VEC; ++i) {
+                acc += __builtin_amdgcn_exp2f(fmaf(v[i], kLog2e, -mL));
+                if (COUNT) cnt += (v[i] > thr) ? 1 : 0;
+            }
         }
         s = (double)acc;
     }
-    if (SUM || ARGMAX) {
+    if (SUM || ARGMAX || COUNT) {
         if (SUM) s = wave_sum(s);
         if (ARGMAX) idx = wave_min_i(idx);
+        if (COUNT) cnt = wave_sum_i(cnt);
         if (lane == 0) {
             s_s[wave] = s;
-            s_j[wave] = idx;
+            s_j[wave] = ARGMAX ? idx : cnt;
         }
         __syncthreads();
         s = ((s_s[0] + s_s[1]) + s_s[2]) + s_s[3];
         if (ARGMAX) I = min(min(s_j[0], s_j[1]), min(s_j[2], s_j[3]));
+        if (COUNT) I = ((s_j[0] + s_j[1]) + s_j[2]) + s_j[3];
     }
     if (threadIdx.x == 0) {
         Seg sg;
