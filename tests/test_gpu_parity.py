@@ -263,6 +263,12 @@ def test_misaligned_rows_take_element_path():
         g = sv.spec_verify_greedy(T, dev(ci.tokens), logprobs=lp)
         torch.cuda.synchronize()
         compare_chain(g, og, logprobs=lp, what=f"misaligned greedy logprobs={lp}")
+    # the relaxed rule reads each drafted token's logit as the 4-byte word that
+    # holds it; here rows start 2 bytes past a word boundary
+    rr = sv.spec_verify_relaxed(T, dev(ci.tokens), dev(ci.uniforms), 0.05, 3)
+    torch.cuda.synchronize()
+    compare_chain(rr, oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", 0.05, 3),
+                  what="misaligned relaxed")
 
 
 def test_out_of_range_draft_tokens_set_status():

@@ -152,6 +152,13 @@ def test_greedy_one_shard_is_the_unsharded_call():
     torch.cuda.synchronize()
     for f in ("tokens", "accept_len", "target_logprob", "behavior_logprob", "status"):
         assert torch.equal(getattr(a, f), getattr(b, f)), f
+    # without log-probs the unsharded stream reads 8 KiB tiles, the shard's
+    # 16 KiB: the argmax (exact) and so every output still agree
+    a = sv.spec_verify_greedy(T, x, logprobs=False)
+    b = sh.verify_greedy_sharded([T], x, logprobs=False)
+    torch.cuda.synchronize()
+    for f in ("tokens", "accept_len", "status"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
 
 
 # ------------------------------------------------------------------- tree
