@@ -15,8 +15,10 @@ then cost no host time); the same loop run eagerly is reported alongside.
 The streaming kernel's duration is measured with HIP start/stop events that
 its dispatch timestamps itself (spec_verify_profile_next_call) over K further
 calls; its algorithmic bytes (every logit read once) divided by that duration
-give the roofline figure.  The fp64 CPU oracle is
-timed on a bounded sample of the same workload on the host's cores.
+give the roofline figure.  The same kernel is also timed launched back to back
+with nothing between its launches (kernel_alone_*), which shows what starting
+it after the previous call's last kernel costs.  The fp64 CPU oracle is timed
+on a bounded sample of the same workload on the host's cores.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counters
