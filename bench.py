@@ -658,6 +658,14 @@ def cpu_baseline(ci, seconds):
             "tiny_exact_b1_k4_v32_rounds_per_s": tiny_rate}
 
 
+def progress(msg: str) -> None:
+    """One line per finished block on stderr (stdout carries only the result)."""
+    print(f"bench: {msg} ({time.time() - _T0:.0f} s)", file=sys.stderr, flush=True)
+
+
+_T0 = time.time()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -696,19 +704,24 @@ def main():
     r_ex = time_case(ex, args.steps, args.warmup, hip, use_graph)
     alone_ms = stream_alone(lib, ex, args.steps, hip, torch)
     del ex
+    progress("exact timed")
     gr = Case(lib, "greedy", ci, sets_greedy, torch, dev)
     r_gr = time_case(gr, args.steps, args.warmup, hip, use_graph)
     del gr
+    progress("greedy timed")
     pw = Case(lib, "power", ci, sets_exact, torch, dev)
     r_pw = time_case(pw, args.steps, args.warmup, hip, use_graph)
     del pw
+    progress("power timed")
     sets_sample = math.ceil(2 * MALL_BYTES / ci.draft.nbytes)
     sa = Case(lib, "sample", ci, sets_sample, torch, dev)
     r_sa = time_case(sa, args.steps, args.warmup, hip, use_graph)
     del sa
+    progress("draft sampler timed")
     torch.cuda.synchronize()
     ceiling = read_ceiling(lib, ci.target.nbytes + ci.draft.nbytes, args.steps, hip, torch, dev)
     ceiling_g = read_ceiling(lib, ci.target.nbytes, args.steps, hip, torch, dev)
+    progress("read ceiling timed")
     cpu = not args.no_cpu_baseline
     others = None
     if not args.no_configs:
@@ -719,12 +732,14 @@ def main():
             "greedy chain, B=8 K=5 V=128256 bf16, no log-probs", args.steps, args.warmup, hip,
             use_graph, torch, dev, cpu)
         del greedy8
+        progress("greedy B=8 timed")
         tree8 = synth.tree_b8_n61()
         others["tree_b8_n61"] = other_workload(
             lib, "tree", tree8, tree8.algorithmic_bytes,
             "greedy tree (depth 5, top-k 4, 60 drafted nodes + root), B=8 V=128256 bf16, "
             "no log-probs", args.steps, args.warmup, hip, use_graph, torch, dev, cpu)
         del tree8
+        progress("tree timed")
         large = synth.large_b64_k8()
         others["relaxed_b64_k8"] = other_workload(
             lib, "relaxed", large, large.algorithmic_bytes_relaxed,
@@ -735,10 +750,13 @@ def main():
             "exact, B=64 K=8 V=151936 bf16, draft target+0.8*N(0,1)", args.steps, args.warmup,
             hip, use_graph, torch, dev, cpu)
         del large
+        progress("B=64 relaxed and exact timed")
         others["sharded_exact_greedy_g8"] = sharded_block(lib, ci, 8, min(args.steps, 200),
                                                          min(args.warmup, 20), hip, torch, dev)
+        progress("vocabulary shards timed")
         others["markov_driver"] = markov_block(torch, dev, min(args.steps, 200),
                                                not args.no_cpu_baseline, use_graph)
+        progress("multi-round driver timed")
 
     ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
     value = 1000.0 / ms
@@ -814,6 +832,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
+        progress("CPU baseline starts")
         out["cpu_baseline"] = cpu_baseline(ci, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
