@@ -387,6 +387,7 @@ def test_graph_capture_replays_match_eager():
     def calls():
         return (sv.spec_verify_exact(T, D, x, u, workspace=ws),
                 sv.spec_verify_greedy(T, x, workspace=ws),
+                sv.spec_verify_greedy(T, x, logprobs=False, workspace=ws),  # 8 KiB tiles
                 sv.spec_sample_drafts(D, ud, workspace=ws_s))
 
     eager = [[t.clone() for t in r if t is not None] for r in calls()]
