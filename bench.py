@@ -669,7 +669,7 @@ _T0 = time.time()
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(requests shard across GPUs with no exchange, see the design notes)",
               file=sys.stderr)
         sys.exit(2)
