@@ -24,6 +24,7 @@ import numpy as np
 
 __all__ = ["build", "load", "OracleResult", "OracleSample", "OracleTrace", "greedy", "exact",
            "relaxed", "tree", "power", "sample", "speculative_generate", "row_stats",
+           "terminal_weights", "TerminalWeights",
            "set_threads", "max_threads", "EPS_ACCEPT", "EPS_SAMPLE"]
 
 EPS_ACCEPT = 1e-6
@@ -66,6 +67,7 @@ def load():
         lib.oracle_sample.argtypes = [P, I, P, ctypes.c_long, I, Dd, P, P, P]
         lib.oracle_power.argtypes = [P, P, I, P, P, I, I, I, Dd, Dd, Dd, P, P, P, P, P, P, P]
         lib.oracle_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, P, P]
+        lib.oracle_terminal_weights.argtypes = [I, P, P, I, P, I, I, I, P, P, P]
         _lib = lib
     return _lib
 
@@ -208,6 +210,45 @@ def sample(logits, uniforms, dtype: str, eps_sample: float = EPS_SAMPLE) -> Orac
     load().oracle_sample(_ptr(X), _dt(dtype), _ptr(u), rows, V, float(eps_sample), _ptr(tok),
                          _ptr(lq), _ptr(fl))
     return OracleSample(tok, lq, fl)
+
+
+@dataclass
+class TerminalWeights:
+    """The weights a terminal draw inverts: w [B][V] (not normalized), their
+    sum Z [B], and for the exact rule whether w is the relu(p - q) residual."""
+    w: np.ndarray
+    Z: np.ndarray
+    residual: np.ndarray
+
+
+_RULES = {"exact": 0, "target": 1, "sampler": 2}
+
+
+def terminal_weights(rule: str, target, dtype: str, n=None, draft=None) -> TerminalWeights:
+    """Weights of the terminal draw at first-rejection position n[b]:
+    rule "exact" (target [B][K+1][V], draft [B][K][V]), "target" (the
+    relaxed and power rules' draw from p_n), or "sampler" (target is the
+    [rows][V] logits, n unused).  The draw picks the smallest t whose
+    running sum of w exceeds u * Z."""
+    T = _logits(target, dtype)
+    V = T.shape[-1]
+    if rule == "sampler":
+        B, K = T.size // V, 0
+        nn = np.zeros(B, np.int32)
+    else:
+        B, L, _ = T.shape
+        K = L - 1
+        nn = _c(n, np.int32)
+        assert nn.shape == (B,) and (nn >= 0).all() and (nn <= K).all()
+    Dr = _logits(draft, dtype) if draft is not None else None
+    if rule == "exact":
+        assert Dr is not None and Dr.shape == (B, K, V)
+    w = np.empty((B, V), np.float64)
+    Z = np.empty(B, np.float64)
+    res = np.empty(B, np.int32)
+    load().oracle_terminal_weights(_RULES[rule], _ptr(T), None if Dr is None else _ptr(Dr),
+                                   _dt(dtype), _ptr(nn), B, K, V, _ptr(w), _ptr(Z), _ptr(res))
+    return TerminalWeights(w, Z, res)
 
 
 def tree(target, node_tok, parents, dtype: str, num_nodes=None) -> OracleResult:

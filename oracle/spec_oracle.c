@@ -146,6 +146,65 @@ static void pad_row(int32_t *tok, double *tlp, double *blp, int L)
     }
 }
 
+/* ------------------------------------------------------ terminal weights
+ * The weights each rule's terminal draw inverts (spec-decode README, "How it
+ * works": after the first rejection n the sampler draws from
+ * normalize(relu(p_n - q_n)); with every draft accepted, from the last target
+ * row).  Returns Z = sum_t w[t].                                          */
+
+/* exact rule: relu(p_n - q_n) when n < K and it has mass, else p_n */
+static double exact_terminal(const void *T, const void *D, int dt, int b, int K, int V, int n,
+                             const row_stats *sp, double *w, int *residual)
+{
+    const int L = K + 1;
+    double Z = 0.0;
+    *residual = 0;
+    if (n < K) {
+        row_stats sq;
+        stats(D, dt, (size_t)b * K + n, V, &sq);
+        for (int t = 0; t < V; ++t) {
+            double p = exp(logp(T, dt, (size_t)b * L + n, V, t, sp));
+            double q = exp(logp(D, dt, (size_t)b * K + n, V, t, &sq));
+            double d = p - q;
+            w[t] = d > 0.0 ? d : 0.0;
+            Z += w[t];
+        }
+        *residual = Z > 0.0;
+    }
+    if (!*residual) { /* bonus (n == K) or a residual with no mass */
+        Z = 0.0;
+        for (int t = 0; t < V; ++t) {
+            w[t] = exp(logp(T, dt, (size_t)b * L + n, V, t, sp));
+            Z += w[t];
+        }
+    }
+    return Z;
+}
+
+/* p over one target row: the relaxed and power rules' terminal draw */
+static double target_terminal(const void *T, int dt, size_t row, int V, const row_stats *sp,
+                              double *w)
+{
+    double Z = 0.0;
+    for (int t = 0; t < V; ++t) {
+        w[t] = exp(logp(T, dt, row, V, t, sp));
+        Z += w[t];
+    }
+    return Z;
+}
+
+/* exp(l - M) over one row (unnormalized q): the draft sampler's weights */
+static double sampler_weights(const void *X, int dt, size_t r, int V, const row_stats *sq,
+                              double *w)
+{
+    double Z = 0.0;
+    for (int t = 0; t < V; ++t) {
+        w[t] = exp(ld(X, dt, r * (size_t)V + t) - sq->M);
+        Z += w[t];
+    }
+    return Z;
+}
+
 /* --------------------------------------------------------------- threads */
 void oracle_set_threads(int n)
 {
@@ -271,27 +330,8 @@ void oracle_exact(const void *T, const void *D, int dt, const int32_t *x, const 
         double *w = (double *)malloc(sizeof(double) * (size_t)V);
         row_stats sp;
         stats(T, dt, (size_t)b * L + n, V, &sp);
-        double Z = 0.0;
-        int residual = 0;
-        if (n < K) {
-            row_stats sq;
-            stats(D, dt, (size_t)b * K + n, V, &sq);
-            for (int t = 0; t < V; ++t) {
-                double p = exp(logp(T, dt, (size_t)b * L + n, V, t, &sp));
-                double q = exp(logp(D, dt, (size_t)b * K + n, V, t, &sq));
-                double d = p - q;
-                w[t] = d > 0.0 ? d : 0.0;
-                Z += w[t];
-            }
-            residual = Z > 0.0;
-        }
-        if (!residual) { /* bonus (n == K) or a residual with no mass */
-            Z = 0.0;
-            for (int t = 0; t < V; ++t) {
-                w[t] = exp(logp(T, dt, (size_t)b * L + n, V, t, &sp));
-                Z += w[t];
-            }
-        }
+        int residual;
+        double Z = exact_terminal(T, D, dt, b, K, V, n, &sp, w, &residual);
         double lo, hi, target = uK * Z;
         long y = inverse_cdf(w, V, target, &lo, &hi);
         ++dec;
@@ -358,11 +398,7 @@ void oracle_relaxed(const void *T, int dt, const int32_t *x, const float *u, int
         row_stats sp;
         stats(T, dt, row, V, &sp);
         double *w = (double *)malloc(sizeof(double) * (size_t)V);
-        double Z = 0.0;
-        for (int t = 0; t < V; ++t) {
-            w[t] = exp(logp(T, dt, row, V, t, &sp));
-            Z += w[t];
-        }
+        double Z = target_terminal(T, dt, row, V, &sp, w);
         double uK = (double)u[(size_t)b * L + K];
         double lo, hi, target = uK * Z;
         long y = inverse_cdf(w, V, target, &lo, &hi);
@@ -460,11 +496,7 @@ void oracle_sample(const void *X, int dt, const float *u, long rows, int V, doub
         row_stats sq;
         stats(X, dt, (size_t)r, V, &sq);
         double *w = (double *)malloc(sizeof(double) * (size_t)V);
-        double Z = 0.0;
-        for (int t = 0; t < V; ++t) {
-            w[t] = exp(ld(X, dt, (size_t)r * V + t) - sq.M);
-            Z += w[t];
-        }
+        double Z = sampler_weights(X, dt, (size_t)r, V, &sq, w);
         double lo, hi, target = (double)u[r] * Z;
         long y = inverse_cdf(w, V, target, &lo, &hi);
         out_tok[r] = (int32_t)y;
@@ -541,11 +573,7 @@ void oracle_power(const void *T, const void *D, int dt, const int32_t *x, const 
         row_stats sp;
         stats(T, dt, row, V, &sp);
         double *w = (double *)malloc(sizeof(double) * (size_t)V);
-        double Z = 0.0;
-        for (int t = 0; t < V; ++t) {
-            w[t] = exp(logp(T, dt, row, V, t, &sp));
-            Z += w[t];
-        }
+        double Z = target_terminal(T, dt, row, V, &sp, w);
         double lo, hi, target = (double)u[(size_t)b * L + K] * Z;
         long y = inverse_cdf(w, V, target, &lo, &hi);
         ++dec;
@@ -562,3 +590,34 @@ void oracle_power(const void *T, const void *D, int dt, const int32_t *x, const 
     }
 }
 
+
+/* ------------------------------------------------------ terminal weights
+ * The weights a rule's terminal draw inverts, for a given first-rejection
+ * position n[b], exactly as the rules above form them: rule 0 the exact rule
+ * (relu(p_n - q_n), or p_n at n = K or when the residual has no mass), rule 1
+ * target row n (relaxed and power rules), rule 2 the draft sampler (row b of
+ * T, n and D unused).  Used by tests to place uniforms next to CDF
+ * boundaries.                                                             */
+void oracle_terminal_weights(int rule, const void *T, const void *D, int dt, const int32_t *n,
+                             int B, int K, int V, double *out_w, double *out_Z,
+                             int32_t *out_residual)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        double *w = out_w + (size_t)b * V;
+        row_stats st;
+        int residual = 0;
+        if (rule == 2) {
+            stats(T, dt, (size_t)b, V, &st);
+            out_Z[b] = sampler_weights(T, dt, (size_t)b, V, &st, w);
+        } else {
+            size_t row = (size_t)b * (K + 1) + n[b];
+            stats(T, dt, row, V, &st);
+            if (rule == 0)
+                out_Z[b] = exact_terminal(T, D, dt, b, K, V, n[b], &st, w, &residual);
+            else
+                out_Z[b] = target_terminal(T, dt, row, V, &st, w);
+        }
+        out_residual[b] = residual;
+    }
+}

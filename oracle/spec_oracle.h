@@ -60,6 +60,14 @@ void oracle_power(const void *T, const void *D, int dt, const int32_t *x, const 
 void oracle_sample(const void *X, int dt, const float *u, long rows, int V, double eps_sample,
                    int32_t *out_tok, double *out_logq, int32_t *out_flag);
 
+/* the weights w [B][V] and their sum Z [B] that a rule's terminal draw
+ * inverts at first-rejection position n[b]: rule 0 exact (out_residual[b] = 1
+ * when w = relu(p_n - q_n)), 1 target row n (relaxed, power), 2 the draft
+ * sampler's row b of T */
+void oracle_terminal_weights(int rule, const void *T, const void *D, int dt, const int32_t *n,
+                             int B, int K, int V, double *out_w, double *out_Z,
+                             int32_t *out_residual);
+
 #ifdef __cplusplus
 }
 #endif
