@@ -128,9 +128,13 @@ struct alignas(16) Decision {
 };
 
 // Fp64 sums of one pass-2 chunk: exp(l - Mt) and exp(d - Md) over the chunk,
-// and over its tokens with p > q.
+// and over its tokens classified p > q with the streamed normalizers; dmin is
+// the smallest distance of a token's (l - Mt) - (d - Md) from that
+// classification threshold (+inf when nothing was classified), so the
+// sampling kernel can tell whether the exact fp64 threshold would classify
+// any token of the chunk otherwise.
 struct alignas(16) ChunkSums {
-    double sa, sb, pa, pb;
+    double sa, sb, pa, pb, dmin, pad;
 };
 
 struct Layout {
@@ -148,7 +152,7 @@ inline Layout make_layout(int B, int R, int tpr, int C2) {
     L.seg = 0;
     L.dec = align_up(L.seg + (size_t)B * R * tpr * 16, 256);
     L.sums = align_up(L.dec + (size_t)B * 64, 256);
-    L.xv = align_up(L.sums + (size_t)B * C2 * 32, 256);
+    L.xv = align_up(L.sums + (size_t)B * C2 * sizeof(ChunkSums), 256);
     L.total = align_up(L.xv + (size_t)B * R * 8, 256);
     return L;
 }
@@ -358,7 +362,7 @@ __device__ inline void load_run(__amdgpu_buffer_rsrc_t r, int e0, int V, bool ve
 
 // ------------------------------------------------------------ fp64 exp(x<=0)
 // Reduction x = k ln2/256 + r with k = rint(x * 256/ln2) and |r| <= ln2/512,
-// a degree-3 Taylor polynomial (truncation error r^4/24 < 1.5e-13 relative)
+// a degree-4 Taylor polynomial (truncation error r^5/120 < 4e-17 relative)
 // and 2^(k/256) = 2^(k>>8) * tab[k & 255], the power of two applied by
 // v_ldexp.  r uses the double nearest ln2/256 in one fma: its error,
 // |k| * 2^-61, stays below 3e-15 relative for x >= -30 and below 2e-13 at the
@@ -373,7 +377,8 @@ __device__ inline double exp_nonpos(double x, const double* tab) {
     const double kd = __builtin_rint(xc * kInvLn2x256);
     const int k = (int)kd;
     const double r = fma(-kd, kLn2o256, xc);
-    double p = fma(r, 1.0 / 6.0, 0.5);
+    double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+    p = fma(p, r, 0.5);
     p = fma(p, r, 1.0);
     p = fma(p, r, 1.0);
     return ldexp(tab[k & (kExpTab - 1)] * p, k >> 8);
@@ -499,6 +504,17 @@ __device__ inline double wave_incl_scan(double v) {
     return s;
 }
 
+// Smallest double over the wave, in every lane.
+__device__ inline double wave_min_d(double v) {
+    v = fmin(v, dpp_d<kDppXor1>(v, v));
+    v = fmin(v, dpp_d<kDppXor2>(v, v));
+    v = fmin(v, dpp_d<kDppHalfMirror>(v, v));
+    v = fmin(v, dpp_d<kDppMirror>(v, v));
+    v = fmin(v, dpp_d<kDppBcast15, 0xA>(v, v));
+    v = fmin(v, dpp_d<kDppBcast31, 0xC>(v, v));
+    return readlane_d(v, 63);
+}
+
 // Smallest / largest int over the wave, in every lane.
 __device__ inline int wave_min_i(int v) {
     v = min(v, dpp_i<kDppXor1>(v, v));
@@ -555,7 +571,7 @@ struct Args {
     size_t slot_xv;        // floats between the slots' drafted-token logits
     const float* xv_in;    // gathered drafted-token logits, slot 0 ([B][K][2])
     float* xv_out;         // this shard's drafted-token logits ([B][K][2])
-    size_t sums_slot;      // chunk sums between shard slots
+    size_t sums_slot;      // bytes between the shard slots of chunk sums
     int32_t* out_owner;    // [B] shard holding the terminal draw, or null
 };
 
@@ -845,6 +861,8 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_stream_rows(co
             cs.sa = ((s_s[0][h] + s_s[1][h]) + s_s[2][h]) + s_s[3][h];
             cs.sb = (double)M;
             cs.pa = cs.pb = 0.0;
+            cs.dmin = INFINITY;
+            cs.pad = 0.0;
             a.sums[(size_t)g * a.C2 + ch] = cs;
         }
     }
@@ -1264,7 +1282,7 @@ __global__ __launch_bounds__(kSweepThreads, kPass2WavesPerSimd) void k_sweep(con
     __shared__ double tab[kExpTab];
     __shared__ RowStats rs;
     __shared__ ChainDecision cd;
-    __shared__ double red[NW][4];
+    __shared__ double red[NW][5];
     fill_exp_table(tab);
     ChainVals cv;
     if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
@@ -1304,7 +1322,7 @@ __global__ __launch_bounds__(kSweepThreads, kPass2WavesPerSimd) void k_sweep(con
     const int c0 = c * kChunk;
     const int c1 = min(c0 + kChunk, a.V);
     u32x4 qt[NV], qd[NV];
-    double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0;
+    double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0, dmin = INFINITY;
     if (residual) {  // uniform: one loop per case, no per-token branch
         load_chunk<T, NV>(rt, c0, c1, a.vec_t, tid, qt);
         load_chunk<T, NV>(rd, c0, c1, a.vec_d, tid, qd);
@@ -1318,9 +1336,11 @@ __global__ __launch_bounds__(kSweepThreads, kPass2WavesPerSimd) void k_sweep(con
                 const double eb = exp_nonpos(xb, tab);
                 sa += ea;
                 sb += eb;
-                const double pq = (xa - xb > cls) ? 1.0 : 0.0;  // p > q
+                const double dd = (xa - xb) - cls;
+                const double pq = (dd > 0.0) ? 1.0 : 0.0;  // p > q
                 pa = fma(ea, pq, pa);
                 pb = fma(eb, pq, pb);
+                dmin = fmin(dmin, fabs(dd));
             }
     } else {
         load_chunk<T, NV>(rt, c0, c1, a.vec_t, tid, qt);
@@ -1334,21 +1354,24 @@ __global__ __launch_bounds__(kSweepThreads, kPass2WavesPerSimd) void k_sweep(con
         sb = wave_sum(sb);
         pa = wave_sum(pa);
         pb = wave_sum(pb);
+        dmin = wave_min_d(dmin);
     }
     if (lane == 0) {
         red[wave][0] = sa;
         red[wave][1] = sb;
         red[wave][2] = pa;
         red[wave][3] = pb;
+        red[wave][4] = dmin;
     }
     __syncthreads();
     if (tid == 0 && c < a.C2) {
-        ChunkSums cs = {0.0, 0.0, 0.0, 0.0};
+        ChunkSums cs = {0.0, 0.0, 0.0, 0.0, INFINITY, 0.0};
         for (int w = grp * kWaves; w < (grp + 1) * kWaves; ++w) {
             cs.sa += red[w][0];
             cs.sb += red[w][1];
             cs.pa += red[w][2];
             cs.pb += red[w][3];
+            cs.dmin = fmin(cs.dmin, red[w][4]);
         }
         a.sums[(size_t)b * a.C2 + c] = cs;
     }
@@ -1388,36 +1411,21 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     const bool residual = EXACT && dc.residual;
     const double Md = dc.Md, cls = dc.cls;
     if (ROWS) __syncthreads();  // the exp table, used by wave 0 below
+    // Chunk masses of a residual draw whose classification must be redone
+    // (see below), the exact threshold, and the chunks concerned.
+    __shared__ double s_W[64];
+    __shared__ double s_cls;
+    __shared__ unsigned long long s_sus;
     double S0 = 1.0, Z0 = 1.0;  // wave 0: the normalizer and the terminal draw's total
-    if (wave == 0) {
-        // lane l holds chunk l
-        ChunkSums cs = {0.0, 0.0, 0.0, 0.0};
-        const int nchunk = SHARD ? a.G * a.C2 : a.C2;
-        if (lane < nchunk) {
-            size_t at = (size_t)b * a.C2 + lane;
-            if (SHARD) {
-                const int sl = lane / a.C2;
-                at = (size_t)sl * a.sums_slot + (size_t)b * a.C2 + (lane - sl * a.C2);
-            }
-            cs = a.sums[at];
-        }
-        if (ROWS) {
-            // chunk records {sum of exp(l - m), m}: rescale to the row max
-            const float mc = lane < nchunk ? (float)cs.sb : -INFINITY;
-            const float Mr = wave_max(mc);
-            cs.sa = mc > -INFINITY ? cs.sa * exp_nonpos((double)mc - (double)Mr, tab) : 0.0;
-            if (lane == 0) s_Mt = (double)Mr;
-        }
-        const double S = wave_sum(cs.sa);
-        const double Sq = residual ? wave_sum(cs.sb) : 1.0;
-        const double iS = 1.0 / S, iSq = 1.0 / Sq;
-        // residual mass of the chunk (clamped: tokens classified with the
-        // streamed normalizers can leave a rounding-size negative); fall back
-        // to p when relu(p - q) has no mass
-        double W = residual ? fmax(cs.pa * iS - cs.pb * iSq, 0.0) : cs.sa;
+    const int nchunk = SHARD ? a.G * a.C2 : a.C2;
+    ChunkSums cs = {0.0, 0.0, 0.0, 0.0, INFINITY, 0.0};  // wave 0, lane l: chunk l
+    double S = 1.0, iS = 1.0, iSq = 1.0;
+    // Wave 0: the draw's total Z from the chunk masses W (lane = chunk), a wave
+    // scan, and the chunk whose interval holds u_K * Z.
+    auto pick = [&](double W) {
         const double Zr = residual ? wave_sum(W) : 0.0;
         const bool res = residual && (Zr > 0.0);
-        if (residual && !res) W = cs.sa;
+        if (residual && !res) W = cs.sa;  // relu(p - q) has no mass: draw from p
         const double Z = res ? Zr : S;
         const double target = (double)a.u[b * (a.K + 1) + a.K] * Z;
         const double incl = wave_incl_scan(W);
@@ -1436,12 +1444,89 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
             s_cstar = cstar;
             s_base = base;
             s_target = target;
+            s_res = res;
+        }
+    };
+    if (wave == 0) {
+        if (lane < nchunk) {
+            const ChunkSums* src = a.sums + (size_t)b * a.C2 + lane;
+            if (SHARD) {  // slot sl starts sl * sums_slot bytes in
+                const int sl = lane / a.C2;
+                src = reinterpret_cast<const ChunkSums*>(reinterpret_cast<const unsigned char*>(a.sums) +
+                                                         (size_t)sl * a.sums_slot) +
+                      (size_t)b * a.C2 + (lane - sl * a.C2);
+            }
+            cs = *src;
+        }
+        if (ROWS) {
+            // chunk records {sum of exp(l - m), m}: rescale to the row max
+            const float mc = lane < nchunk ? (float)cs.sb : -INFINITY;
+            const float Mr = wave_max(mc);
+            cs.sa = mc > -INFINITY ? cs.sa * exp_nonpos((double)mc - (double)Mr, tab) : 0.0;
+            if (lane == 0) s_Mt = (double)Mr;
+        }
+        S = wave_sum(cs.sa);
+        const double Sq = residual ? wave_sum(cs.sb) : 1.0;
+        iS = 1.0 / S;
+        iSq = 1.0 / Sq;
+        // residual mass of the chunk (clamped: rounding can leave a
+        // rounding-size negative)
+        const double W = residual ? fmax(cs.pa * iS - cs.pb * iSq, 0.0) : cs.sa;
+        // The sweep classified tokens p > q against the streamed normalizers;
+        // the exact threshold comes from the fp64 sums just formed.  A token
+        // the two thresholds classify differently lies between them, so only
+        // chunks with a token that close (plus a rounding allowance) need
+        // their mass recomputed.  Vocabulary shards keep the streamed
+        // threshold (their columns are not all here).
+        double clsx = cls;
+        unsigned long long sus = 0ull;
+        if (EXACT && !SHARD && residual) {
+            clsx = log(S) - log(Sq);
+            const double gap = fabs(clsx - cls) + 1e-12;
+            sus = __ballot(lane < nchunk && cs.dmin <= gap);
+        }
+        if (lane == 0) {
+            s_cls = clsx;
+            s_sus = sus;
             s_iS = iS;
             s_iSq = iSq;
-            s_res = res;
+        }
+        if (sus) {
+            s_W[lane] = W;
+        } else {
+            pick(W);
         }
     }
     __syncthreads();
+    if (s_sus) {  // workgroup-uniform and rare: recompute those chunks' masses
+        const T* tr = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
+        const T* dr = reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V;
+        const double clsx = s_cls, jS = s_iS, jSq = s_iSq;
+        for (unsigned long long m = s_sus; m; m &= m - 1) {
+            const int c = __builtin_ctzll(m);
+            const int e = c * kChunk + t * kSampleRun;
+            float lt[kSampleRun], ld[kSampleRun];
+            Elem<T>::load4(row_rsrc(tr, a.V), e, a.V, a.vec_t, lt);
+            Elem<T>::load4(row_rsrc(dr, a.V), e, a.V, a.vec_d, ld);
+            double sum = 0.0;
+#pragma unroll
+            for (int i = 0; i < kSampleRun; ++i) {
+                const double xa = (double)lt[i] - dc.Mt, xb = (double)ld[i] - Md;
+                if (xa - xb > clsx) sum += fmax(exp_nonpos(xa, tab) * jS - exp_nonpos(xb, tab) * jSq, 0.0);
+            }
+            sum = wave_sum(sum);
+            if (lane == 0) s_wtot[wave] = sum;
+            __syncthreads();
+            if (t == 0) {
+                double z = 0.0;
+                for (int ww = 0; ww < kSampleWaves; ++ww) z += s_wtot[ww];
+                s_W[c] = z;
+            }
+            __syncthreads();
+        }
+        if (wave == 0) pick(s_W[lane]);
+        __syncthreads();
+    }
 
     const double Mt = ROWS ? s_Mt : dc.Mt;
     if (ROWS && t == 0) a.out_status[b] = 0;
@@ -1453,7 +1538,9 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
         cstar -= owner * a.C2;
     }
     const bool res = s_res;
-    const double iS = s_iS, iSq = s_iSq, target = s_target;
+    const double target = s_target, clsx = s_cls;
+    iS = s_iS;
+    iSq = s_iSq;
     const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
     const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
     const int e0 = cstar * kChunk + t * kSampleRun;
@@ -1478,7 +1565,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
         if (res) {
             const double xb = (double)ld[i] - Md;
             const double eb = exp_nonpos(xb, tab);
-            wi = (xa - xb > cls) ? fmax(ea * iS - eb * iSq, 0.0) : 0.0;
+            wi = (xa - xb > clsx) ? fmax(ea * iS - eb * iSq, 0.0) : 0.0;
         }
         w[i] = wi;
         tsum += wi;
@@ -1550,7 +1637,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
             const float dy = Elem<T>::at(drow, (size_t)y);
             const double xa = (double)ly - Mt, xb = (double)dy - Md;
             wy = 0.0;
-            if (res && xa - xb > cls) wy = fmax(exp_nonpos(xa, tab) * iS - exp_nonpos(xb, tab) * iSq, 0.0);
+            if (res && xa - xb > clsx) wy = fmax(exp_nonpos(xa, tab) * iS - exp_nonpos(xb, tab) * iSq, 0.0);
         }
         const int L = a.L;
         a.out_tok[(size_t)b * L + n] = SHARD ? y + a.shard * a.V : y;
@@ -2269,7 +2356,7 @@ spec_status shard_sample(const void* target_shard, const void* draft_shard, spec
     a.vec_t = vec_ok(target_shard, dtype, a.V);
     a.vec_d = uses_draft(MODE) && vec_ok(draft_shard, dtype, a.V);
     a.sums = static_cast<ChunkSums*>(const_cast<void*>(sums));
-    a.sums_slot = shard_sums_slot(B, a.V) / sizeof(ChunkSums);
+    a.sums_slot = shard_sums_slot(B, a.V);
     a.dec = static_cast<Decision*>(workspace);
     a.out_tok = out_tokens;
     a.out_tlp = out_target_logprob;

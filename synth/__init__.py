@@ -33,7 +33,7 @@ import numpy as np
 __all__ = [
     "bf16_rne", "bf16_to_f32", "ChainInputs", "TreeInputs", "chain_inputs",
     "tiny_exact_v32", "greedy_chain_b8", "exact_b32_k5", "large_b64_k8", "tree_b8_n61", "tree_inputs", "make_tree", "widen",
-    "gumbel_max_tokens",
+    "gumbel_max_tokens", "redraw_draft_tokens",
 ]
 
 
@@ -158,6 +158,20 @@ def gumbel_max_tokens(logits64: np.ndarray, rng: np.random.Generator) -> np.ndar
     u = np.maximum(u, np.finfo(np.float64).tiny)
     g = -np.log(-np.log(u))
     return np.argmax(logits64 + g, axis=-1).astype(np.int32)
+
+
+def redraw_draft_tokens(draft: np.ndarray, dtype: str, rng: np.random.Generator) -> np.ndarray:
+    """Fresh draft tokens x ~ softmax(row) for every row of stored draft
+    logits [..., V], by Gumbel-max with float32 noise: cheap enough to draw a
+    new set of tokens for every round of a long run on the same logits (the
+    law differs from the exact one only by the float32 rounding of the
+    noise)."""
+    d = bf16_to_f32(draft) if dtype == "bf16" else np.asarray(draft, np.float32)
+    u = rng.random(d.shape, dtype=np.float32)
+    np.maximum(u, np.float32(1e-30), out=u)
+    g = -np.log(-np.log(u))
+    g += d
+    return np.argmax(g, axis=-1).astype(np.int32)
 
 
 def _rng(seed: int, rnd: int) -> np.random.Generator:

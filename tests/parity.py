@@ -19,6 +19,7 @@ import torch
 
 LOGPROB_TOL = 1e-4
 NEAR_TIE_BUDGET = 1e-4
+U_REJECT = np.float32(1.0 - 2.0 ** -24)  # the largest float32 below 1: rejects any r < 1 - 6e-8
 
 
 def dev_logits(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -43,9 +44,9 @@ class Tally:
         self.flagged += other.flagged
 
     def within_budget(self) -> bool:
-        if self.decisions >= 1.0 / NEAR_TIE_BUDGET:
-            return self.flagged < NEAR_TIE_BUDGET * self.decisions
-        return self.flagged <= 1
+        """Flagged near-ties strictly under NEAR_TIE_BUDGET of the decisions
+        (below 1e4 decisions: none at all)."""
+        return self.flagged < NEAR_TIE_BUDGET * self.decisions
 
 
 def compare_chain(res, orc, *, logprobs=True, what="") -> Tally:
@@ -101,3 +102,34 @@ def compare_tree(res, orc, *, logprobs=True, what=""):
         if tlp is not None:
             assert np.abs(tlp[b, : d + 1] - orc.target_logprob[b, : d + 1]).max() < LOGPROB_TOL, ctx
             assert (tlp[b, d + 1:] == 0).all() and (blp[b] == 0).all(), ctx
+
+
+# ----------------------------------------------- uniforms next to boundaries
+def near_boundary_uniforms(w, Z, bins, per_bin, rng):
+    """Float32 uniforms u lying next to boundaries of the inverse CDF of w:
+    boundary t sits at cumsum(w)[t] / Z (the running sum through token t).
+    The distance of u*Z from that boundary, relative to Z, falls in each
+    [lo, hi) of `bins`; per bin at most `per_bin` picks.  The boundaries are
+    taken from an extended-precision running sum, the reference here.
+    Returns (u, dist, want): want is the smallest t whose extended-precision
+    running sum exceeds u * Z."""
+    wl = w.astype(np.longdouble)
+    c = np.cumsum(wl)
+    Zl = c[-1]
+    pos = np.flatnonzero(w > 0)
+    beta = c[pos[:-1]] / Zl                      # boundaries between drawn tokens
+    u = beta.astype(np.float32)
+    dist = (u.astype(np.longdouble) - beta).astype(np.float64)  # u*Z - boundary, / Z
+    out = []
+    for lo, hi in bins:
+        sel = np.flatnonzero((np.abs(dist) >= lo) & (np.abs(dist) < hi) & (u > 0) & (u < 1))
+        if sel.size > per_bin:
+            sel = rng.choice(sel, per_bin, replace=False)
+        for k in sel:
+            want = int(np.searchsorted(c, u[k].astype(np.longdouble) * Zl, side="right"))
+            out.append((u[k], dist[k], want))
+    return out
+
+
+BINS = [(1e-14, 1e-13), (1e-13, 1e-12), (1e-12, 1e-11), (1e-11, 1e-10), (1e-10, 1e-9),
+        (1e-9, 1e-7)]

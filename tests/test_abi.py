@@ -161,7 +161,7 @@ def test_shard_size_queries(lib):
     assert rb(0, 2, 13, 262144, 128) == 0       # 128 shard slots exceed one wave
     assert rb(1, 2, 13, 262144, 16) > 0         # 16 x 4 chunks: exactly one wave
     assert rb(1, 2, 13, 33 * 4100, 33) == 0     # 33 x 2 chunks exceed one wave
-    assert sb(32, 128256, 8) == 4096 and sb(32, 128256, 7) == 0
+    assert sb(32, 128256, 8) == 32 * 4 * 48 and sb(32, 128256, 7) == 0  # 48-byte chunk records
     assert wb(32) == 2048 and wb(0) == 0
     for v in (rb(1, 32, 11, 128256, 8), sb(32, 128256, 8), wb(32)):
         assert v % 256 == 0

@@ -95,11 +95,11 @@ def test_exact_tiny_v32_batched():
 
 
 def test_exact_tiny_v32_single_requests():
-    """The same rounds as individual B=1 calls (first 100)."""
+    """The same 1000 rounds as individual B=1 calls."""
     ci = synth.tiny_exact_v32()
     o = oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "f32")
     tot = Tally()
-    for r in range(100):
+    for r in range(1000):
         sub = synth.ChainInputs("tiny_exact_v32", "f32", 1, 4, 32, ci.target[r:r + 1], ci.draft[r:r + 1],
                                 ci.tokens[r:r + 1], ci.uniforms[r:r + 1])
         osub = oracle.OracleResult(*(getattr(o, f)[r:r + 1] for f in

@@ -12,18 +12,18 @@ softmax of the same logits.
 
 None of these tests calls the HIP library.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
-import json
-import os
-
 import oracle
 import synth
+from parity import BINS, U_REJECT, near_boundary_uniforms
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
-U_REJECT = np.float32(1.0 - 2.0 ** -24)  # the largest float32 below 1
 
 
 def softmax64(a):
@@ -173,36 +173,6 @@ def test_terminal_weights_match_numpy():
 
 
 # ------------------------------------------- inverse CDF at full vocabulary
-def near_boundary_uniforms(w, Z, bins, per_bin, rng):
-    """Float32 uniforms u lying next to boundaries of the inverse CDF of w:
-    boundary t sits at cumsum(w)[t] / Z (the running sum through token t).
-    The distance of u*Z from that boundary, relative to Z, falls in each
-    [lo, hi) of `bins`; per bin at most `per_bin` picks.  The boundaries are
-    taken from an extended-precision running sum, the reference here.
-    Returns (u, dist, want): want is the smallest t whose extended-precision
-    running sum exceeds u * Z."""
-    wl = w.astype(np.longdouble)
-    c = np.cumsum(wl)
-    Zl = c[-1]
-    pos = np.flatnonzero(w > 0)
-    beta = c[pos[:-1]] / Zl                      # boundaries between drawn tokens
-    u = beta.astype(np.float32)
-    dist = (u.astype(np.longdouble) - beta).astype(np.float64)  # u*Z - boundary, / Z
-    out = []
-    for lo, hi in bins:
-        sel = np.flatnonzero((np.abs(dist) >= lo) & (np.abs(dist) < hi) & (u > 0) & (u < 1))
-        if sel.size > per_bin:
-            sel = rng.choice(sel, per_bin, replace=False)
-        for k in sel:
-            want = int(np.searchsorted(c, u[k].astype(np.longdouble) * Zl, side="right"))
-            out.append((u[k], dist[k], want))
-    return out
-
-
-BINS = [(1e-14, 1e-13), (1e-13, 1e-12), (1e-12, 1e-11), (1e-11, 1e-10), (1e-10, 1e-9),
-        (1e-9, 1e-7)]
-
-
 def test_oracle_inverse_cdf_precision_at_full_vocab():
     """At V = 128256 the oracle's draw agrees with the extended-precision
     inverse CDF whenever u*Z lies at least 1e-13*Z from a boundary: the
