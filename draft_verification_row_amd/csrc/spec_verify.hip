@@ -1796,6 +1796,11 @@ inline bool buf_ok(const void* p, size_t bytes, size_t need) {
     return p && ((uintptr_t)p % 256) == 0 && bytes >= need;
 }
 
+// G gathered slots of `slot` bytes each (slot 0 for invalid sizes).
+inline bool gathered_ok(const void* p, size_t bytes, int G, size_t slot) {
+    return slot > 0 && G >= 1 && buf_ok(p, bytes, (size_t)G * slot);
+}
+
 // Shard-local argument block: V is the shard's column count, Vtot the
 // vocabulary.
 inline Args shard_args(spec_dtype dt, int B, int K, int V, int G, int shard, int rows_t, int R) {
@@ -2228,16 +2233,16 @@ spec_status spec_shard_stats_exact(const void* target_shard, const void* draft_s
     return shard_stats<kExact, true>(a, dtype, out_record, static_cast<hipStream_t>(stream));
 }
 
-spec_status spec_shard_combine_greedy(const void* records, spec_dtype dtype,
+spec_status spec_shard_combine_greedy(const void* records, size_t records_bytes, spec_dtype dtype,
                                       const int32_t* draft_tokens, int B, int K, int V, int G,
                                       int32_t* out_tokens, int32_t* out_accept_len,
                                       float* out_target_logprob, float* out_behavior_logprob,
                                       int32_t* out_status, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
     if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, 0, K + 1)) return SPEC_EINVAL;
-    if (!draft_tokens || !out_tokens || !out_accept_len || !out_status) return SPEC_EINVAL;
-    if (!records || ((uintptr_t)records % 256) != 0) return SPEC_EWORKSPACE;
     Args a = shard_args(dtype, B, K, V, G, 0, K + 1, K + 1);
+    if (!gathered_ok(records, records_bytes, G, shard_layout(dtype, B, a.R, a.V).slot)) return SPEC_EWORKSPACE;
+    if (!draft_tokens || !out_tokens || !out_accept_len || !out_status) return SPEC_EINVAL;
     gathered_records(a, dtype, records);
     a.tok = draft_tokens;
     a.out_tok = out_tokens;
@@ -2255,7 +2260,7 @@ spec_status spec_shard_combine_greedy(const void* records, spec_dtype dtype,
     return shard_launch(k_decide<float, kGreedy, false, true>, grid, block, a, st);
 }
 
-spec_status spec_shard_combine_tree(const void* records, spec_dtype dtype,
+spec_status spec_shard_combine_tree(const void* records, size_t records_bytes, spec_dtype dtype,
                                     const int32_t* node_tokens, const int32_t* parents,
                                     const int32_t* num_nodes, int B, int N, int V, int G,
                                     int32_t* out_path_nodes, int32_t* out_tokens,
@@ -2264,10 +2269,10 @@ spec_status spec_shard_combine_tree(const void* records, spec_dtype dtype,
                                     void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
     if (N < 1 || N > SPEC_MAX_NODES || !shard_ok(dtype, B, 1, V, G, 0, N)) return SPEC_EINVAL;
+    Args a = shard_args(dtype, B, 0, V, G, 0, N, N);
+    if (!gathered_ok(records, records_bytes, G, shard_layout(dtype, B, a.R, a.V).slot)) return SPEC_EWORKSPACE;
     if (!node_tokens || !parents || !out_path_nodes || !out_tokens || !out_accept_len || !out_status)
         return SPEC_EINVAL;
-    if (!records || ((uintptr_t)records % 256) != 0) return SPEC_EWORKSPACE;
-    Args a = shard_args(dtype, B, 0, V, G, 0, N, N);
     gathered_records(a, dtype, records);
     a.tok = node_tokens;
     a.parents = parents;
@@ -2298,7 +2303,7 @@ constexpr int chain_rows(int mode, int K) { return uses_draft(mode) ? 2 * K + 1 
 
 template <int MODE>
 spec_status shard_sweep(const void* target_shard, const void* draft_shard, spec_dtype dtype,
-                        const void* records, const int32_t* draft_tokens, const float* uniforms,
+                        const void* records, size_t records_bytes, const int32_t* draft_tokens, const float* uniforms,
                         int B, int K, int V, int G, int shard, float alpha, float tau, int top_k,
                         int32_t* out_tokens, int32_t* out_accept_len, float* out_target_logprob,
                         float* out_behavior_logprob, int32_t* out_status, void* out_sums,
@@ -2307,11 +2312,11 @@ spec_status shard_sweep(const void* target_shard, const void* draft_shard, spec_
     if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, chain_rows(MODE, K))) return SPEC_EINVAL;
     if (MODE == kPower && (!(alpha >= 0.f) || alpha == INFINITY)) return SPEC_EINVAL;
     if (MODE == kRelaxed && (tau != tau || top_k < 0)) return SPEC_EINVAL;
+    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, chain_rows(MODE, K));
+    if (!gathered_ok(records, records_bytes, G, shard_layout(dtype, B, a.R, a.V).slot)) return SPEC_EWORKSPACE;
     if (!target_shard || (uses_draft(MODE) && !draft_shard) || !draft_tokens || !uniforms ||
         !out_tokens || !out_accept_len || !out_status)
         return SPEC_EINVAL;
-    if (!records || ((uintptr_t)records % 256) != 0) return SPEC_EWORKSPACE;
-    Args a = shard_args(dtype, B, K, V, G, shard, K + 1, chain_rows(MODE, K));
     if (!buf_ok(out_sums, sums_bytes, shard_sums_slot(B, a.V)) ||
         !buf_ok(workspace, workspace_bytes, shard_ws_bytes(B)))
         return SPEC_EWORKSPACE;
@@ -2340,16 +2345,16 @@ spec_status shard_sweep(const void* target_shard, const void* draft_shard, spec_
 
 template <int MODE>
 spec_status shard_sample(const void* target_shard, const void* draft_shard, spec_dtype dtype,
-                         const void* sums, const float* uniforms, int B, int K, int V, int G,
+                         const void* sums, size_t sums_bytes, const float* uniforms, int B, int K, int V, int G,
                          int shard, int32_t* out_tokens, float* out_target_logprob,
                          float* out_behavior_logprob, int32_t* out_sample_shard, void* workspace,
                          size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
     if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, chain_rows(MODE, K))) return SPEC_EINVAL;
-    if (!target_shard || (uses_draft(MODE) && !draft_shard) || !uniforms || !out_tokens) return SPEC_EINVAL;
-    if (!sums || ((uintptr_t)sums % 256) != 0 || !buf_ok(workspace, workspace_bytes, shard_ws_bytes(B)))
-        return SPEC_EWORKSPACE;
     Args a = shard_args(dtype, B, K, V, G, shard, K + 1, chain_rows(MODE, K));
+    if (!gathered_ok(sums, sums_bytes, G, shard_sums_slot(B, a.V))) return SPEC_EWORKSPACE;
+    if (!target_shard || (uses_draft(MODE) && !draft_shard) || !uniforms || !out_tokens) return SPEC_EINVAL;
+    if (!buf_ok(workspace, workspace_bytes, shard_ws_bytes(B))) return SPEC_EWORKSPACE;
     a.T = target_shard;
     a.D = draft_shard;
     a.u = uniforms;
@@ -2373,51 +2378,53 @@ spec_status shard_sample(const void* target_shard, const void* draft_shard, spec
 extern "C" {
 
 spec_status spec_shard_sweep_exact(const void* target_shard, const void* draft_shard,
-                                   spec_dtype dtype, const void* records,
+                                   spec_dtype dtype, const void* records, size_t records_bytes,
                                    const int32_t* draft_tokens, const float* uniforms, int B,
                                    int K, int V, int G, int shard, int32_t* out_tokens,
                                    int32_t* out_accept_len, float* out_target_logprob,
                                    float* out_behavior_logprob, int32_t* out_status,
                                    void* out_sums, size_t sums_bytes, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-    return shard_sweep<kExact>(target_shard, draft_shard, dtype, records, draft_tokens, uniforms, B, K, V, G,
+    return shard_sweep<kExact>(target_shard, draft_shard, dtype, records, records_bytes, draft_tokens, uniforms, B, K, V, G,
                                shard, 0.f, 0.f, 0, out_tokens, out_accept_len, out_target_logprob,
                                out_behavior_logprob, out_status, out_sums, sums_bytes, workspace,
                                workspace_bytes, stream);
 }
 
 spec_status spec_shard_sweep_power(const void* target_shard, const void* draft_shard,
-                                   spec_dtype dtype, const void* records,
+                                   spec_dtype dtype, const void* records, size_t records_bytes,
                                    const int32_t* draft_tokens, const float* uniforms, int B,
                                    int K, int V, int G, int shard, float alpha, int32_t* out_tokens,
                                    int32_t* out_accept_len, float* out_target_logprob,
                                    float* out_behavior_logprob, int32_t* out_status,
                                    void* out_sums, size_t sums_bytes, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-    return shard_sweep<kPower>(target_shard, draft_shard, dtype, records, draft_tokens, uniforms, B, K, V, G,
+    return shard_sweep<kPower>(target_shard, draft_shard, dtype, records, records_bytes, draft_tokens, uniforms, B, K, V, G,
                                shard, alpha, 0.f, 0, out_tokens, out_accept_len, out_target_logprob,
                                out_behavior_logprob, out_status, out_sums, sums_bytes, workspace,
                                workspace_bytes, stream);
 }
 
 spec_status spec_shard_sample_exact(const void* target_shard, const void* draft_shard,
-                                    spec_dtype dtype, const void* sums, const float* uniforms,
+                                    spec_dtype dtype, const void* sums, size_t sums_bytes,
+                                    const float* uniforms,
                                     int B, int K, int V, int G, int shard, int32_t* out_tokens,
                                     float* out_target_logprob, float* out_behavior_logprob,
                                     int32_t* out_sample_shard, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-    return shard_sample<kExact>(target_shard, draft_shard, dtype, sums, uniforms, B, K, V, G, shard,
+    return shard_sample<kExact>(target_shard, draft_shard, dtype, sums, sums_bytes, uniforms, B, K, V, G, shard,
                                 out_tokens, out_target_logprob, out_behavior_logprob, out_sample_shard,
                                 workspace, workspace_bytes, stream);
 }
 
 spec_status spec_shard_sample_power(const void* target_shard, const void* draft_shard,
-                                    spec_dtype dtype, const void* sums, const float* uniforms,
+                                    spec_dtype dtype, const void* sums, size_t sums_bytes,
+                                    const float* uniforms,
                                     int B, int K, int V, int G, int shard, int32_t* out_tokens,
                                     float* out_target_logprob, float* out_behavior_logprob,
                                     int32_t* out_sample_shard, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-    return shard_sample<kPower>(target_shard, draft_shard, dtype, sums, uniforms, B, K, V, G, shard,
+    return shard_sample<kPower>(target_shard, draft_shard, dtype, sums, sums_bytes, uniforms, B, K, V, G, shard,
                                 out_tokens, out_target_logprob, out_behavior_logprob, out_sample_shard,
                                 workspace, workspace_bytes, stream);
 }
@@ -2449,13 +2456,14 @@ spec_status spec_shard_values_relaxed(const void* target_shard, spec_dtype dtype
 }
 
 spec_status spec_shard_stats_relaxed(const void* target_shard, spec_dtype dtype,
-                                     const int32_t* draft_tokens, const void* values, int B, int K,
+                                     const int32_t* draft_tokens, const void* values,
+                                     size_t values_bytes, int B, int K,
                                      int V, int G, int shard, void* out_record, size_t record_bytes,
                                      void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
     if (K > SPEC_MAX_K || !shard_ok(dtype, B, K, V, G, shard, K + 1)) return SPEC_EINVAL;
+    if (!gathered_ok(values, values_bytes, G, spec_shard_values_bytes(B, K))) return SPEC_EWORKSPACE;
     if (!target_shard || !draft_tokens) return SPEC_EINVAL;
-    if (!values || ((uintptr_t)values % 256) != 0) return SPEC_EWORKSPACE;
     Args a = shard_args(dtype, B, K, V, G, shard, K + 1, K + 1);
     if (!buf_ok(out_record, record_bytes, shard_layout(dtype, B, a.R, a.V).slot)) return SPEC_EWORKSPACE;
     a.T = target_shard;
@@ -2467,24 +2475,24 @@ spec_status spec_shard_stats_relaxed(const void* target_shard, spec_dtype dtype,
 }
 
 spec_status spec_shard_sweep_relaxed(const void* target_shard, spec_dtype dtype, const void* records,
-                                     const int32_t* draft_tokens, const float* uniforms, int B,
+                                     size_t records_bytes, const int32_t* draft_tokens, const float* uniforms, int B,
                                      int K, int V, int G, int shard, float tau, int top_k,
                                      int32_t* out_tokens, int32_t* out_accept_len,
                                      float* out_target_logprob, float* out_behavior_logprob,
                                      int32_t* out_status, void* out_sums, size_t sums_bytes,
                                      void* workspace, size_t workspace_bytes, void* stream) {
-    return shard_sweep<kRelaxed>(target_shard, nullptr, dtype, records, draft_tokens, uniforms, B, K, V, G,
+    return shard_sweep<kRelaxed>(target_shard, nullptr, dtype, records, records_bytes, draft_tokens, uniforms, B, K, V, G,
                                  shard, 0.f, tau, top_k, out_tokens, out_accept_len, out_target_logprob,
                                  out_behavior_logprob, out_status, out_sums, sums_bytes, workspace,
                                  workspace_bytes, stream);
 }
 
 spec_status spec_shard_sample_relaxed(const void* target_shard, spec_dtype dtype, const void* sums,
-                                      const float* uniforms, int B, int K, int V, int G, int shard,
+                                      size_t sums_bytes, const float* uniforms, int B, int K, int V, int G, int shard,
                                       int32_t* out_tokens, float* out_target_logprob,
                                       float* out_behavior_logprob, int32_t* out_sample_shard,
                                       void* workspace, size_t workspace_bytes, void* stream) {
-    return shard_sample<kRelaxed>(target_shard, nullptr, dtype, sums, uniforms, B, K, V, G, shard,
+    return shard_sample<kRelaxed>(target_shard, nullptr, dtype, sums, sums_bytes, uniforms, B, K, V, G, shard,
                                   out_tokens, out_target_logprob, out_behavior_logprob, out_sample_shard,
                                   workspace, workspace_bytes, stream);
 }

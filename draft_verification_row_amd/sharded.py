@@ -102,7 +102,7 @@ def shard_combine_greedy(records: torch.Tensor, dtype: torch.dtype, draft_tokens
     code = 1 if dtype == torch.bfloat16 else 0
     tok, ln, tlp, blp, st = _outs(B, K + 1, x.device, logprobs)
     rc = load_library().spec_shard_combine_greedy(
-        _ptr(rec), code, _ptr(x), B, K, V, G, _ptr(tok), _ptr(ln), _ptr(tlp), _ptr(blp), _ptr(st),
+        _ptr(rec), rec.numel(), code, _ptr(x), B, K, V, G, _ptr(tok), _ptr(ln), _ptr(tlp), _ptr(blp), _ptr(st),
         _stream_ptr(x.device))
     _raise(rc, "spec_shard_combine_greedy")
     return VerifyResult(tok, ln, tlp, blp, st)
@@ -120,7 +120,7 @@ def shard_combine_tree(records: torch.Tensor, dtype: torch.dtype, node_tokens, p
     tok, ln, tlp, blp, st = _outs(B, N, nt.device, logprobs)
     path = torch.empty((B, N), dtype=torch.int32, device=nt.device)
     rc = load_library().spec_shard_combine_tree(
-        _ptr(rec), code, _ptr(nt), _ptr(par), _ptr(nn), B, N, V, G, _ptr(path), _ptr(tok),
+        _ptr(rec), rec.numel(), code, _ptr(nt), _ptr(par), _ptr(nn), B, N, V, G, _ptr(path), _ptr(tok),
         _ptr(ln), _ptr(tlp), _ptr(blp), _ptr(st), _stream_ptr(nt.device))
     _raise(rc, "spec_shard_combine_tree")
     return TreeResult(path, tok, ln, tlp, blp, st)
@@ -137,7 +137,8 @@ def shard_sweep_power(target_shard, draft_shard, records: torch.Tensor, draft_to
     u = _check(uniforms, "uniforms", torch.float32, (B, L))
     rec, sums, ws = _slot(records, "records"), _slot(out_sums, "out_sums"), _slot(workspace, "workspace")
     rc = load_library().spec_shard_sweep_power(
-        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(rec), _ptr(x),
+        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(rec), rec.numel(),
+        _ptr(x),
         _ptr(u), B, K, V, G, shard, ctypes.c_float(alpha), _ptr(out.tokens), _ptr(out.accept_len),
         _ptr(out.target_logprob), _ptr(out.behavior_logprob), _ptr(out.status), _ptr(sums),
         sums.numel(), _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
@@ -155,7 +156,8 @@ def shard_sample_power(target_shard, draft_shard, sums: torch.Tensor, uniforms, 
     own = None if out_sample_shard is None else _check(out_sample_shard, "out_sample_shard",
                                                        torch.int32, (B,))
     rc = load_library().spec_shard_sample_power(
-        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(sm), _ptr(u), B, K,
+        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(sm), sm.numel(),
+        _ptr(u), B, K,
         V, G, shard, _ptr(out.tokens), _ptr(out.target_logprob), _ptr(out.behavior_logprob),
         _ptr(own), _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
     _raise(rc, "spec_shard_sample_power")
@@ -171,7 +173,8 @@ def shard_sweep_exact(target_shard, draft_shard, records: torch.Tensor, draft_to
     u = _check(uniforms, "uniforms", torch.float32, (B, L))
     rec, sums, ws = _slot(records, "records"), _slot(out_sums, "out_sums"), _slot(workspace, "workspace")
     rc = load_library().spec_shard_sweep_exact(
-        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(rec), _ptr(x),
+        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(rec), rec.numel(),
+        _ptr(x),
         _ptr(u), B, K, V, G, shard, _ptr(out.tokens), _ptr(out.accept_len),
         _ptr(out.target_logprob), _ptr(out.behavior_logprob), _ptr(out.status), _ptr(sums),
         sums.numel(), _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
@@ -189,7 +192,8 @@ def shard_sample_exact(target_shard, draft_shard, sums: torch.Tensor, uniforms, 
     own = None if out_sample_shard is None else _check(out_sample_shard, "out_sample_shard",
                                                        torch.int32, (B,))
     rc = load_library().spec_shard_sample_exact(
-        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(sm), _ptr(u), B, K,
+        _ptr(target_shard), _ptr(draft_shard), _dtype_code(target_shard), _ptr(sm), sm.numel(),
+        _ptr(u), B, K,
         V, G, shard, _ptr(out.tokens), _ptr(out.target_logprob), _ptr(out.behavior_logprob),
         _ptr(own), _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
     _raise(rc, "spec_shard_sample_exact")
@@ -309,7 +313,8 @@ def shard_stats_relaxed(target_shard, draft_tokens, values: torch.Tensor, G: int
     x = _check(draft_tokens, "draft_tokens", torch.int32, (B, L - 1))
     vals, rec = _slot(values, "values"), _slot(out_record, "out_record")
     rc = load_library().spec_shard_stats_relaxed(
-        _ptr(target_shard), _dtype_code(target_shard), _ptr(x), _ptr(vals), B, L - 1, V, G, shard,
+        _ptr(target_shard), _dtype_code(target_shard), _ptr(x), _ptr(vals), vals.numel(), B, L - 1,
+        V, G, shard,
         _ptr(rec), rec.numel(), _stream_ptr(target_shard.device))
     _raise(rc, "spec_shard_stats_relaxed")
 
@@ -323,7 +328,8 @@ def shard_sweep_relaxed(target_shard, records: torch.Tensor, draft_tokens, unifo
     u = _check(uniforms, "uniforms", torch.float32, (B, L))
     rec, sums, ws = _slot(records, "records"), _slot(out_sums, "out_sums"), _slot(workspace, "workspace")
     rc = load_library().spec_shard_sweep_relaxed(
-        _ptr(target_shard), _dtype_code(target_shard), _ptr(rec), _ptr(x), _ptr(u), B, K, V, G,
+        _ptr(target_shard), _dtype_code(target_shard), _ptr(rec), rec.numel(), _ptr(x), _ptr(u), B,
+        K, V, G,
         shard, ctypes.c_float(tau), int(top_k), _ptr(out.tokens), _ptr(out.accept_len),
         _ptr(out.target_logprob), _ptr(out.behavior_logprob), _ptr(out.status), _ptr(sums),
         sums.numel(), _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
@@ -339,7 +345,8 @@ def shard_sample_relaxed(target_shard, sums: torch.Tensor, uniforms, G: int, sha
     own = None if out_sample_shard is None else _check(out_sample_shard, "out_sample_shard",
                                                        torch.int32, (B,))
     rc = load_library().spec_shard_sample_relaxed(
-        _ptr(target_shard), _dtype_code(target_shard), _ptr(sm), _ptr(u), B, L - 1, V, G, shard,
+        _ptr(target_shard), _dtype_code(target_shard), _ptr(sm), sm.numel(), _ptr(u), B, L - 1, V,
+        G, shard,
         _ptr(out.tokens), _ptr(out.target_logprob), _ptr(out.behavior_logprob), _ptr(own),
         _ptr(ws), ws.numel(), _stream_ptr(target_shard.device))
     _raise(rc, "spec_shard_sample_relaxed")

@@ -296,9 +296,11 @@ spec_status spec_sample_drafts(const void *logits, spec_dtype dtype, const float
  * shard.  Limits: 1 <= G, V % G == 0, G * ceil(Vs / (16384 / element size))
  * <= 64 and G * ceil(Vs / 4096) <= 64, besides the unsharded limits for V.
  * Record and sums buffers are 256-byte aligned; they need no initialization.
- * Errors as above (SPEC_EINVAL also for a shard index outside [0, G) and
- * for G or V outside the limits; SPEC_EWORKSPACE for a record, sums or
- * workspace buffer that is null, misaligned or too small).
+ * Every buffer comes with its size in bytes, gathered inputs included, and
+ * is checked before anything is enqueued.  Errors as above (SPEC_EINVAL also
+ * for a shard index outside [0, G) and for G or V outside the limits;
+ * SPEC_EWORKSPACE for a record, sums, values or workspace buffer that is
+ * null, misaligned or too small).
  */
 
 /* Host-only sizes; 0 for invalid arguments.  rows_per_request as for
@@ -322,14 +324,15 @@ spec_status spec_shard_stats_exact(const void *target_shard, const void *draft_s
                                    int V, int G, int shard, void *out_record, size_t record_bytes,
                                    void *stream);
 
-/* Step 2, greedy and tree: records = the G gathered slots.  Outputs as for
- * spec_verify_greedy / spec_verify_tree. */
-spec_status spec_shard_combine_greedy(const void *records, spec_dtype dtype,
+/* Step 2, greedy and tree: records = the G gathered slots (records_bytes >=
+ * G * spec_shard_record_bytes(...), else SPEC_EWORKSPACE before any launch).
+ * Outputs as for spec_verify_greedy / spec_verify_tree. */
+spec_status spec_shard_combine_greedy(const void *records, size_t records_bytes, spec_dtype dtype,
                                       const int32_t *draft_tokens, int B, int K, int V, int G,
                                       int32_t *out_tokens, int32_t *out_accept_len,
                                       float *out_target_logprob, float *out_behavior_logprob,
                                       int32_t *out_status, void *stream);
-spec_status spec_shard_combine_tree(const void *records, spec_dtype dtype,
+spec_status spec_shard_combine_tree(const void *records, size_t records_bytes, spec_dtype dtype,
                                     const int32_t *node_tokens, const int32_t *parents,
                                     const int32_t *num_nodes, int B, int N, int V, int G,
                                     int32_t *out_path_nodes, int32_t *out_tokens,
@@ -337,13 +340,14 @@ spec_status spec_shard_combine_tree(const void *records, spec_dtype dtype,
                                     float *out_behavior_logprob, int32_t *out_status,
                                     void *stream);
 
-/* Step 2, exact: writes outputs 0..accept_len-1 (and the padding after the
+/* Step 2, exact: records = the G gathered record slots (records_bytes >= G *
+ * the record query).  Writes outputs 0..accept_len-1 (and the padding after the
  * terminal position), accept_len and status, this shard's sums slot
  * (out_sums, sums_bytes >= spec_shard_sums_bytes) and the decision into the
  * workspace (spec_shard_workspace_bytes(B) bytes, one per shard: step 3 of
  * the same shard reads it). */
 spec_status spec_shard_sweep_exact(const void *target_shard, const void *draft_shard,
-                                   spec_dtype dtype, const void *records,
+                                   spec_dtype dtype, const void *records, size_t records_bytes,
                                    const int32_t *draft_tokens, const float *uniforms, int B,
                                    int K, int V, int G,
                                    int shard, int32_t *out_tokens, int32_t *out_accept_len,
@@ -355,7 +359,7 @@ spec_status spec_shard_sweep_exact(const void *target_shard, const void *draft_s
  * finite and >= 0).  Its statistics are the exact rule's: step 1 is
  * spec_shard_stats_exact, with record and sums slots sized alike. */
 spec_status spec_shard_sweep_power(const void *target_shard, const void *draft_shard,
-                                   spec_dtype dtype, const void *records,
+                                   spec_dtype dtype, const void *records, size_t records_bytes,
                                    const int32_t *draft_tokens, const float *uniforms, int B,
                                    int K, int V, int G, int shard, float alpha,
                                    int32_t *out_tokens, int32_t *out_accept_len,
@@ -363,7 +367,8 @@ spec_status spec_shard_sweep_power(const void *target_shard, const void *draft_s
                                    int32_t *out_status, void *out_sums, size_t sums_bytes,
                                    void *workspace, size_t workspace_bytes, void *stream);
 spec_status spec_shard_sample_power(const void *target_shard, const void *draft_shard,
-                                    spec_dtype dtype, const void *sums, const float *uniforms,
+                                    spec_dtype dtype, const void *sums, size_t sums_bytes,
+                                    const float *uniforms,
                                     int B, int K, int V, int G, int shard, int32_t *out_tokens,
                                     float *out_target_logprob, float *out_behavior_logprob,
                                     int32_t *out_sample_shard, void *workspace,
@@ -377,8 +382,9 @@ spec_status spec_shard_sample_power(const void *target_shard, const void *draft_
  *      spec_shard_values_bytes(B, K) bytes; entries of other shards' tokens
  *      are left as they are and never read).
  *   -- exchange 0: all-gather of the G values slots, in shard order.
- *   1. spec_shard_stats_relaxed (values = the gathered slots; record slot as
- *      above with rows_per_request K+1).
+ *   1. spec_shard_stats_relaxed (values = the gathered slots, values_bytes >=
+ *      G * spec_shard_values_bytes(B, K); record slot as above with
+ *      rows_per_request K+1).
  *   2, 3. spec_shard_sweep_relaxed and spec_shard_sample_relaxed, as for the
  *      exact rule (no draft logits). */
 size_t spec_shard_values_bytes(int B, int K);
@@ -387,28 +393,31 @@ spec_status spec_shard_values_relaxed(const void *target_shard, spec_dtype dtype
                                       int shard, void *out_values, size_t values_bytes,
                                       void *stream);
 spec_status spec_shard_stats_relaxed(const void *target_shard, spec_dtype dtype,
-                                     const int32_t *draft_tokens, const void *values, int B, int K,
+                                     const int32_t *draft_tokens, const void *values,
+                                     size_t values_bytes, int B, int K,
                                      int V, int G, int shard, void *out_record, size_t record_bytes,
                                      void *stream);
 spec_status spec_shard_sweep_relaxed(const void *target_shard, spec_dtype dtype, const void *records,
-                                     const int32_t *draft_tokens, const float *uniforms, int B,
+                                     size_t records_bytes, const int32_t *draft_tokens, const float *uniforms, int B,
                                      int K, int V, int G, int shard, float tau, int top_k,
                                      int32_t *out_tokens, int32_t *out_accept_len,
                                      float *out_target_logprob, float *out_behavior_logprob,
                                      int32_t *out_status, void *out_sums, size_t sums_bytes,
                                      void *workspace, size_t workspace_bytes, void *stream);
 spec_status spec_shard_sample_relaxed(const void *target_shard, spec_dtype dtype, const void *sums,
-                                      const float *uniforms, int B, int K, int V, int G, int shard,
+                                      size_t sums_bytes, const float *uniforms, int B, int K, int V, int G, int shard,
                                       int32_t *out_tokens, float *out_target_logprob,
                                       float *out_behavior_logprob, int32_t *out_sample_shard,
                                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* Step 3, exact: sums = the G gathered sums slots.  The owning shard writes
+/* Step 3, exact: sums = the G gathered sums slots (sums_bytes >= G *
+ * spec_shard_sums_bytes(...), else SPEC_EWORKSPACE).  The owning shard writes
  * out_tokens[b][accept_len[b]] and the two log-probs there (NULL log-prob
  * arrays are skipped); every shard writes out_sample_shard[b] = the owning
  * shard (NULL: not written). */
 spec_status spec_shard_sample_exact(const void *target_shard, const void *draft_shard,
-                                    spec_dtype dtype, const void *sums, const float *uniforms,
+                                    spec_dtype dtype, const void *sums, size_t sums_bytes,
+                                    const float *uniforms,
                                     int B, int K, int V, int G, int shard, int32_t *out_tokens,
                                     float *out_target_logprob, float *out_behavior_logprob,
                                     int32_t *out_sample_shard, void *workspace,

@@ -192,30 +192,84 @@ def test_shard_argument_errors(lib):
     t = lib.spec_shard_stats_tree
     assert t(P4K, 1, None, 2, 65, 1000, 4, 0, 1, PWS, 1 << 20, None) == SPEC_EINVAL  # N > 64
     cg = lib.spec_shard_combine_greedy
-    assert cg(ctypes.c_void_p((1 << 20) + 64), 1, P4K, 2, 3, 1000, 4, P4K, P4K, None, None, P4K,
-              None) == SPEC_EWORKSPACE
-    assert cg(PWS, 1, None, 2, 3, 1000, 4, P4K, P4K, None, None, P4K, None) == SPEC_EINVAL
+    grec = 4 * lib.spec_shard_record_bytes(1, 2, 4, 1000, 4)   # G gathered greedy slots
+    assert cg(ctypes.c_void_p((1 << 20) + 64), grec, 1, P4K, 2, 3, 1000, 4, P4K, P4K, None, None,
+              P4K, None) == SPEC_EWORKSPACE
+    assert cg(PWS, grec, 1, None, 2, 3, 1000, 4, P4K, P4K, None, None, P4K, None) == SPEC_EINVAL
     ct = lib.spec_shard_combine_tree
-    assert ct(PWS, 1, P4K, None, None, 2, 8, 1000, 4, P4K, P4K, P4K, None, None, P4K,
+    assert ct(PWS, 1 << 30, 1, P4K, None, None, 2, 8, 1000, 4, P4K, P4K, P4K, None, None, P4K,
               None) == SPEC_EINVAL
     sw = lib.spec_shard_sweep_exact
     sums, ws = lib.spec_shard_sums_bytes(2, 1000, 4), lib.spec_shard_workspace_bytes(2)
-    base = [P4K, P4K, 1, PWS, P4K, P4K, 2, 3, 1000, 4, 1, P4K, P4K, None, None, P4K, PWS, sums,
-            PWS, ws, None]
+    base = [P4K, P4K, 1, PWS, 4 * rec, P4K, P4K, 2, 3, 1000, 4, 1, P4K, P4K, None, None, P4K, PWS,
+            sums, PWS, ws, None]
     bad_sums = list(base)
-    bad_sums[17] = sums - 256
+    bad_sums[18] = sums - 256
     assert sw(*bad_sums) == SPEC_EWORKSPACE
     bad_ws = list(base)
-    bad_ws[19] = 0
+    bad_ws[20] = 0
     assert sw(*bad_ws) == SPEC_EWORKSPACE
     bad_u = list(base)
-    bad_u[5] = None
+    bad_u[6] = None
     assert sw(*bad_u) == SPEC_EINVAL
     sa = lib.spec_shard_sample_exact
-    assert sa(P4K, P4K, 1, ctypes.c_void_p((1 << 20) + 32), P4K, 2, 3, 1000, 4, 1, P4K, None, None,
-              None, PWS, ws, None) == SPEC_EWORKSPACE
-    assert sa(P4K, P4K, 1, PWS, P4K, 2, 3, 1000, 4, 9, P4K, None, None, None, PWS, ws,
+    assert sa(P4K, P4K, 1, ctypes.c_void_p((1 << 20) + 32), 4 * sums, P4K, 2, 3, 1000, 4, 1, P4K,
+              None, None, None, PWS, ws, None) == SPEC_EWORKSPACE
+    assert sa(P4K, P4K, 1, PWS, 4 * sums, P4K, 2, 3, 1000, 4, 9, P4K, None, None, None, PWS, ws,
               None) == SPEC_EINVAL
+
+
+def test_shard_gathered_inputs_are_size_checked(lib):
+    """Every gathered input (G record, sums or values slots) comes with its
+    size; one byte short of G slots is rejected before anything is enqueued,
+    and exactly G slots passes the check (the next error is the test's
+    missing stream-side inputs, never a launch)."""
+    G, B, K, V = 4, 2, 3, 1000
+    ws = lib.spec_shard_workspace_bytes(B)
+    sums = lib.spec_shard_sums_bytes(B, V, G)
+    rec_pq = lib.spec_shard_record_bytes(1, B, 2 * K + 1, V, G)
+    rec_g = lib.spec_shard_record_bytes(1, B, K + 1, V, G)
+    rec_t = lib.spec_shard_record_bytes(1, B, 8, V, G)
+    vals = lib.spec_shard_values_bytes(B, K)
+    f = ctypes.c_float
+    # argument lists with every pointer valid and the gathered input's size n,
+    # and the same with a required output (or the logits) missing
+    calls = {
+        "combine_greedy": (lib.spec_shard_combine_greedy, G * rec_g,
+                           lambda n, o: [PWS, n, 1, P4K, B, K, V, G, P4K, P4K, None, None, o, None]),
+        "combine_tree": (lib.spec_shard_combine_tree, G * rec_t,
+                         lambda n, o: [PWS, n, 1, P4K, P4K, None, B, 8, V, G, P4K, P4K, P4K, None,
+                                       None, o, None]),
+        "sweep_exact": (lib.spec_shard_sweep_exact, G * rec_pq,
+                        lambda n, o: [P4K, P4K, 1, PWS, n, P4K, P4K, B, K, V, G, 1, P4K, P4K, None,
+                                      None, o, PWS, sums, PWS, ws, None]),
+        "sweep_power": (lib.spec_shard_sweep_power, G * rec_pq,
+                        lambda n, o: [P4K, P4K, 1, PWS, n, P4K, P4K, B, K, V, G, 1, f(0.5), P4K, P4K,
+                                      None, None, o, PWS, sums, PWS, ws, None]),
+        "sweep_relaxed": (lib.spec_shard_sweep_relaxed, G * rec_g,
+                          lambda n, o: [P4K, 1, PWS, n, P4K, P4K, B, K, V, G, 0, f(0.1), 4, P4K, P4K,
+                                        None, None, o, PWS, sums, PWS, ws, None]),
+        "sample_exact": (lib.spec_shard_sample_exact, G * sums,
+                         lambda n, o: [P4K, P4K, 1, PWS, n, P4K, B, K, V, G, 1, o, None, None, None,
+                                       PWS, ws, None]),
+        "sample_power": (lib.spec_shard_sample_power, G * sums,
+                         lambda n, o: [P4K, P4K, 1, PWS, n, P4K, B, K, V, G, 1, o, None, None, None,
+                                       PWS, ws, None]),
+        "sample_relaxed": (lib.spec_shard_sample_relaxed, G * sums,
+                           lambda n, o: [P4K, 1, PWS, n, P4K, B, K, V, G, 0, o, None, None, None,
+                                         PWS, ws, None]),
+        "stats_relaxed": (lib.spec_shard_stats_relaxed, G * vals,
+                          lambda n, o: [o, 1, P4K, PWS, n, B, K, V, G, 0, PWS, 0, None]),
+    }
+    for name, (fn, need, args) in calls.items():
+        assert need > 0, name
+        # short by one byte, or empty: rejected whatever else is wrong
+        assert fn(*args(need - 1, P4K)) == SPEC_EWORKSPACE, name
+        assert fn(*args(0, None)) == SPEC_EWORKSPACE, name
+        assert fn(*args(need - 1, None)) == SPEC_EWORKSPACE, name
+        # G full slots pass the size check: the call stops at the missing
+        # output instead
+        assert fn(*args(need, None)) == SPEC_EINVAL, name
 
 
 def test_read_ceiling_argument_errors(lib):
@@ -231,17 +285,17 @@ def test_read_ceiling_argument_errors(lib):
 
 def test_shard_power_argument_errors(lib):
     sums, ws = lib.spec_shard_sums_bytes(2, 1000, 4), lib.spec_shard_workspace_bytes(2)
-    base = [P4K, P4K, 1, PWS, P4K, P4K, 2, 3, 1000, 4, 1, ctypes.c_float(0.5), P4K, P4K, None, None,
-            P4K, PWS, sums, PWS, ws, None]
+    base = [P4K, P4K, 1, PWS, 1 << 30, P4K, P4K, 2, 3, 1000, 4, 1, ctypes.c_float(0.5), P4K, P4K,
+            None, None, P4K, PWS, sums, PWS, ws, None]
     for alpha in (-1.0, float("inf"), float("nan")):
         bad = list(base)
-        bad[11] = ctypes.c_float(alpha)
+        bad[12] = ctypes.c_float(alpha)
         assert lib.spec_shard_sweep_power(*bad) == SPEC_EINVAL
     bad = list(base)
-    bad[8] = 1001                     # not a multiple of G
+    bad[9] = 1001                     # not a multiple of G
     assert lib.spec_shard_sweep_power(*bad) == SPEC_EINVAL
-    assert lib.spec_shard_sample_power(P4K, P4K, 1, PWS, P4K, 2, 3, 1000, 4, 4, P4K, None, None,
-                                       None, PWS, ws, None) == SPEC_EINVAL   # shard = G
+    assert lib.spec_shard_sample_power(P4K, P4K, 1, PWS, 1 << 30, P4K, 2, 3, 1000, 4, 4, P4K, None,
+                                       None, None, PWS, ws, None) == SPEC_EINVAL   # shard = G
 
 
 def test_shard_relaxed_argument_errors(lib):
@@ -254,18 +308,20 @@ def test_shard_relaxed_argument_errors(lib):
     assert v(P4K, 1, P4K, 2, 3, 1000, 4, 0, PWS, vb - 256, None) == SPEC_EWORKSPACE
     rb = lib.spec_shard_record_bytes(1, 2, 4, 1000, 4)
     st = lib.spec_shard_stats_relaxed
-    assert st(P4K, 1, P4K, ctypes.c_void_p((1 << 20) + 8), 2, 3, 1000, 4, 0, PWS, rb, None) == SPEC_EWORKSPACE
-    assert st(P4K, 1, P4K, PWS, 2, 3, 1000, 4, 4, PWS, rb, None) == SPEC_EINVAL   # shard = G
-    assert st(P4K, 1, P4K, PWS, 2, 3, 1000, 4, 0, PWS, rb - 256, None) == SPEC_EWORKSPACE
+    assert st(P4K, 1, P4K, ctypes.c_void_p((1 << 20) + 8), 4 * vb, 2, 3, 1000, 4, 0, PWS, rb,
+              None) == SPEC_EWORKSPACE
+    assert st(P4K, 1, P4K, PWS, 4 * vb, 2, 3, 1000, 4, 4, PWS, rb, None) == SPEC_EINVAL   # shard = G
+    assert st(P4K, 1, P4K, PWS, 4 * vb, 2, 3, 1000, 4, 0, PWS, rb - 256, None) == SPEC_EWORKSPACE
     sums, ws = lib.spec_shard_sums_bytes(2, 1000, 4), lib.spec_shard_workspace_bytes(2)
     sw = lib.spec_shard_sweep_relaxed
-    base = [P4K, 1, PWS, P4K, P4K, 2, 3, 1000, 4, 0, ctypes.c_float(0.1), 4, P4K, P4K, None, None,
-            P4K, PWS, sums, PWS, ws, None]
+    base = [P4K, 1, PWS, 4 * rb, P4K, P4K, 2, 3, 1000, 4, 0, ctypes.c_float(0.1), 4, P4K, P4K, None,
+            None, P4K, PWS, sums, PWS, ws, None]
     bad = list(base)
-    bad[10] = ctypes.c_float(float("nan"))
+    bad[11] = ctypes.c_float(float("nan"))
     assert sw(*bad) == SPEC_EINVAL
     bad = list(base)
-    bad[11] = -1
+    bad[12] = -1
     assert sw(*bad) == SPEC_EINVAL
     sa = lib.spec_shard_sample_relaxed
-    assert sa(P4K, 1, PWS, None, 2, 3, 1000, 4, 0, P4K, None, None, None, PWS, ws, None) == SPEC_EINVAL
+    assert sa(P4K, 1, PWS, 4 * sums, None, 2, 3, 1000, 4, 0, P4K, None, None, None, PWS, ws,
+              None) == SPEC_EINVAL
