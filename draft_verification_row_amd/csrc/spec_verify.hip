@@ -65,6 +65,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "spec_verify.h"
 
@@ -1853,7 +1854,16 @@ spec_status shard_launch(K kernel, dim3 grid, dim3 block, const Args& a, hipStre
     return SPEC_OK;
 }
 
-bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
+// A caller written in C may pass any int as the dtype (a C enum is an int);
+// in C++ reading a value outside the enumerators through the enum type is
+// undefined, so the argument's bytes are inspected before it is ever read as
+// spec_dtype.
+static_assert(sizeof(spec_dtype) == sizeof(int), "spec_dtype is passed as an int");
+bool dtype_ok(const spec_dtype& dt) {
+    int v;
+    memcpy(&v, &dt, sizeof v);
+    return v == SPEC_F32 || v == SPEC_BF16;
+}
 
 // The draft sampler's workspace: the layout of one row per request (it uses
 // the chunk-sum region) and a row-count tail that the size query has always
