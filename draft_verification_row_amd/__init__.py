@@ -57,6 +57,7 @@ def load_library():
     lib.spec_verify_relaxed.argtypes = [P, I, P, P, I, I, I, F, I, P, P, P, P, P, P, Z, P]
     lib.spec_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, P, P, P, Z, P]
     lib.spec_verify_power.argtypes = [P, P, I, P, P, I, I, I, F, P, P, P, P, P, P, Z, P]
+    lib.spec_verify_exact_noalloc.argtypes = [P, P, I, P, P, I, I, I, P, P, P, P, P, P]
     lib.spec_sample_workspace_bytes.argtypes = [I, I]
     lib.spec_sample_workspace_bytes.restype = Z
     lib.spec_sample_drafts.argtypes = [P, I, P, I, I, P, P, P, P, Z, P]
@@ -86,7 +87,8 @@ def load_library():
     lib.spec_shard_sweep_relaxed.argtypes = [P, I, P, Z, P, P, I, I, I, I, I, F, I, P, P, P, P, P,
                                              P, Z, P, Z, P]
     lib.spec_shard_sample_relaxed.argtypes = [P, I, P, Z, P, I, I, I, I, I, P, P, P, P, P, Z, P]
-    for fn in ("spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed", "spec_verify_tree",
+    for fn in ("spec_verify_greedy", "spec_verify_exact", "spec_verify_exact_noalloc",
+               "spec_verify_relaxed", "spec_verify_tree",
                "spec_verify_power", "spec_sample_drafts", "spec_shard_stats_greedy",
                "spec_shard_stats_tree", "spec_shard_stats_exact", "spec_shard_combine_greedy",
                "spec_shard_combine_tree", "spec_shard_sweep_exact", "spec_shard_sample_exact",

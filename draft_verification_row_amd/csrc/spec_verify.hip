@@ -63,6 +63,8 @@
 
 #include <limits.h>
 #include <math.h>
+
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -1909,6 +1911,7 @@ const char* spec_status_string(int s) {
         case SPEC_EDTYPE: return "unsupported dtype";
         case SPEC_EWORKSPACE: return "workspace missing, misaligned or too small";
         case SPEC_EHIP: return "HIP launch failed";
+        case SPEC_ESCRATCH: return "call needs more than the static scratch array holds";
         default: return "unknown status";
     }
 }
@@ -2508,3 +2511,56 @@ spec_status spec_shard_sample_relaxed(const void* target_shard, spec_dtype dtype
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------- allocation-free call
+// The exact rule's workspace in a file-scope device array, for callers that
+// cannot allocate.  In host code `scratch` names a host-side stand-in, not
+// the array: its device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` on device d, once looked up
+
+// The current device's address of the scratch array.
+spec_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPEC_EHIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" spec_status spec_verify_exact_noalloc(const void* target_logits, const void* draft_logits,
+                                                 spec_dtype dtype, const int32_t* draft_tokens,
+                                                 const float* uniforms, int B, int K, int V,
+                                                 int32_t* out_tokens, int32_t* out_accept_len,
+                                                 float* out_target_logprob,
+                                                 float* out_behavior_logprob, int32_t* out_status,
+                                                 void* stream) {
+    if (!dtype_ok(dtype)) return SPEC_EDTYPE;
+    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, 2 * K + 1)) return SPEC_EINVAL;
+    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
+        !out_accept_len || !out_status)
+        return SPEC_EINVAL;
+    // the exact call's workspace layout at this dtype, as spec_verify_exact checks it
+    const size_t need = make_layout(B, 2 * K + 1, tpr_of(dtype, V), c2_of(dtype, V)).total;
+    if (need > SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_ESCRATCH;
+    void* ws = nullptr;
+    const spec_status s = scratch_on_current_device(&ws);
+    if (s != SPEC_OK) return s;
+    return spec_verify_exact(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K, V,
+                             out_tokens, out_accept_len, out_target_logprob, out_behavior_logprob,
+                             out_status, ws, SPEC_NOALLOC_SCRATCH_BYTES, stream);
+}

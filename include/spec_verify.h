@@ -81,7 +81,8 @@ typedef enum {
     SPEC_EINVAL = 1,     /* bad size, null required pointer, bad tau/top_k */
     SPEC_EDTYPE = 2,     /* dtype is neither SPEC_F32 nor SPEC_BF16 */
     SPEC_EWORKSPACE = 3, /* workspace null, misaligned or too small */
-    SPEC_EHIP = 4        /* the HIP runtime refused a launch */
+    SPEC_EHIP = 4,       /* the HIP runtime refused a launch */
+    SPEC_ESCRATCH = 5    /* the call needs more than the static scratch array holds */
 } spec_status;
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
@@ -422,6 +423,35 @@ spec_status spec_shard_sample_exact(const void *target_shard, const void *draft_
                                     float *out_target_logprob, float *out_behavior_logprob,
                                     int32_t *out_sample_shard, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/*
+ * ------------------------------------------------------------------------
+ * Exact verification that allocates nothing, for callers that cannot call
+ * hipMalloc: code under HIP graph capture, serving loops and harnesses that
+ * forbid device allocation.  Same rule, arguments and outputs as
+ * spec_verify_exact, without the workspace: the call's per-tile records,
+ * decisions and chunk sums go to a static device array of
+ * SPEC_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends.  A call whose workspace size
+ * (spec_verify_workspace_bytes(B, 2K+1, V)) exceeds it returns SPEC_ESCRATCH
+ * before anything is enqueued; 4 MiB covers, for example, B = 64, K = 8 at
+ * V = 262144 in fp32.  The library makes no allocating call on this path.
+ *
+ * The array is per device and shared by every call on that device, and each
+ * call writes every byte of it that it reads before reading it (nothing
+ * needs clearing, and the previous call's contents never matter).  Calls
+ * that overlap on one device -- on different streams, or from several
+ * threads without ordering -- race on it and corrupt each other's results;
+ * calls ordered on one stream are fine.  The device is the calling thread's
+ * current HIP device, which must be the one the stream belongs to.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+spec_status spec_verify_exact_noalloc(const void *target_logits, const void *draft_logits,
+                                      spec_dtype dtype, const int32_t *draft_tokens,
+                                      const float *uniforms, int B, int K, int V,
+                                      int32_t *out_tokens, int32_t *out_accept_len,
+                                      float *out_target_logprob, float *out_behavior_logprob,
+                                      int32_t *out_status, void *stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,7 @@ import draft_verification_row_amd as sv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 
-SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP = range(5)
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_ESCRATCH = range(6)
 
 
 @pytest.fixture(scope="module")
@@ -36,9 +36,28 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert lib.spec_status_string(code)
+    assert b"scratch" in lib.spec_status_string(5)
     assert b"unknown" in lib.spec_status_string(99)
+
+
+def test_noalloc_argument_errors(lib):
+    """The allocation-free exact call rejects bad arguments, and calls whose
+    workspace would exceed the 4 MiB static scratch array, before anything
+    is enqueued (and before the array's address is looked up)."""
+    f = lib.spec_verify_exact_noalloc
+    p = P4K
+    assert f(p, p, 7, p, p, 2, 3, 1000, p, p, None, None, p, None) == SPEC_EDTYPE
+    assert f(p, None, 1, p, p, 2, 3, 1000, p, p, None, None, p, None) == SPEC_EINVAL
+    assert f(p, p, 1, p, p, 2, 64, 1000, p, p, None, None, p, None) == SPEC_EINVAL
+    assert f(p, p, 1, p, p, 2, 3, 1000, None, p, None, None, p, None) == SPEC_EINVAL
+    limit = 4 << 20
+    q = lib.spec_verify_workspace_bytes
+    assert q(64, 17, 262144) <= limit            # the documented example fits
+    assert q(1024, 11, 262144) > limit
+    assert f(p, p, 0, p, p, 1024, 5, 262144, p, p, None, None, p, None) == SPEC_ESCRATCH
+    assert f(p, p, 1, p, p, 4096, 5, 128256, p, p, None, None, p, None) == SPEC_ESCRATCH
 
 
 def test_workspace_query(lib):
@@ -52,6 +71,8 @@ def test_workspace_query(lib):
 
 
 ws_buf = (ctypes.c_uint8 * 64)()  # host memory: only its address is inspected
+P4K = ctypes.c_void_p(4096)
+PWS = ctypes.c_void_p(1 << 20)
 
 
 def _greedy(lib, **over):
@@ -167,8 +188,6 @@ def test_shard_size_queries(lib):
         assert v % 256 == 0
 
 
-P4K = ctypes.c_void_p(4096)
-PWS = ctypes.c_void_p(1 << 20)
 
 
 def test_shard_argument_errors(lib):
