@@ -155,9 +155,9 @@ def spec_verify_workspace_bytes(B: int, rows_per_request: int, V: int) -> int:
 
 
 def _workspace(device: torch.device, nbytes: int, workspace: Optional[torch.Tensor]):
-    """Caller-provided workspace, or one cached per (device, stream).  The
-    library needs no initialization of it and keeps nothing in it between
-    calls; calls on one stream may share it."""
+    """Caller-provided workspace (zero-filled before its first call), or one
+    cached per (device, stream), allocated zeroed.  Every call leaves the
+    workspace zero-filled again, so calls on one stream may share it."""
     if workspace is not None:
         _check(workspace, "workspace", torch.uint8)
         return workspace

@@ -141,22 +141,29 @@ struct alignas(16) ChunkSums {
 };
 
 struct Layout {
-    size_t seg, dec, sums, xv, total;
+    size_t seg, dec, sums, xv;  // records, decisions, chunk sums, drafted-token logits
+    size_t frec, fsums, ticket;  // single-launch calls: published words and tickets
+    size_t total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // [tile records B*R*tpr][decisions B][chunk sums B*C2][drafted-token logits
-// B*K*2, sized B*R*2]; every region is written before it is read within a
-// call, so the workspace needs no initialization and keeps nothing between
-// calls.
+// B*K*2, sized B*R*2][published tile records B*R*tpr, two words each]
+// [published chunk records B*C2, eleven words each][tickets B].  The workspace is
+// zero when a call starts (zero-filled once by its owner) and every call
+// leaves every byte it wrote zero again, whatever the rule or shape: the
+// single-launch calls read zero as "not published yet".
 inline Layout make_layout(int B, int R, int tpr, int C2) {
     Layout L;
     L.seg = 0;
     L.dec = align_up(L.seg + (size_t)B * R * tpr * 16, 256);
     L.sums = align_up(L.dec + (size_t)B * 64, 256);
     L.xv = align_up(L.sums + (size_t)B * C2 * sizeof(ChunkSums), 256);
-    L.total = align_up(L.xv + (size_t)B * R * 8, 256);
+    L.frec = align_up(L.xv + (size_t)B * R * 8, 256);
+    L.fsums = align_up(L.frec + (size_t)B * R * tpr * 16, 256);
+    L.ticket = align_up(L.fsums + (size_t)B * C2 * (3 + 2 * (kChunk / 1024)) * 8, 256);
+    L.total = align_up(L.ticket + (size_t)B * 4, 256);
     return L;
 }
 
@@ -576,6 +583,11 @@ struct Args {
     float* xv_out;         // this shard's drafted-token logits ([B][K][2])
     size_t sums_slot;      // bytes between the shard slots of chunk sums
     int32_t* out_owner;    // [B] shard holding the terminal draw, or null
+    // single-launch calls: published words and per-request tickets
+    uint64_t* frec;     // [B][R][tpr] tile records, two words each
+    uint64_t* fsums;    // [B][C2] chunk records, eleven words each
+    uint32_t* ticket;   // [B] sweep workgroups done
+    int nstream;        // workgroups of the launch that stream tiles
 };
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -586,6 +598,44 @@ __device__ inline const T* uniform_ptr(const T* p) {
     const uint32_t lo = (uint32_t)uniform((int)(uint32_t)u), hi = (uint32_t)uniform((int)(uint32_t)(u >> 32));
     return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 }
+
+// ------------------------------------------------- published words
+// Single-launch calls pass tile records and chunk sums between workgroups of
+// one launch, on any XCD, through 64-bit words written and read with
+// agent-scope relaxed atomics (coherent across the XCDs' L2 caches without
+// a fence).  A word of zero means "not written yet": every published word is
+// encoded so it is never zero, the reader waits (a bounded spin) until every
+// word it needs is non-zero, and the call's last workgroup for a request
+// zeroes that request's words again.  The workspace region holding them must
+// therefore be zero when a call starts; every call leaves it so.
+__device__ inline uint64_t load_word(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_word(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr uint64_t kTop = 1ull << 63;
+// A non-negative double (or NaN, or +inf) with its sign bit flipped: never
+// zero, since none of them is -0.0.
+__device__ inline uint64_t enc_nonneg(double v) { return (uint64_t)__double_as_longlong(v) ^ kTop; }
+__device__ inline double dec_nonneg(uint64_t w) { return __longlong_as_double((long long)(w ^ kTop)); }
+// Tile record {m, ic, s}: word 0 = valid bit | ic (31 bits, ic in [0, INT_MAX])
+// | the bits of m; word 1 = s encoded as above (s >= 0 or NaN).
+__device__ inline void publish_record(uint64_t* w, const Seg& sg) {
+    store_word(w, kTop | ((uint64_t)((uint32_t)sg.ic & 0x7fffffffu) << 32) | __float_as_uint(sg.m));
+    store_word(w + 1, enc_nonneg(sg.s));
+}
+__device__ inline Seg decode_record(uint64_t w0, uint64_t w1) {
+    Seg sg;
+    sg.m = __uint_as_float((uint32_t)w0);
+    sg.ic = (int)((w0 >> 32) & 0x7fffffffu);
+    sg.s = dec_nonneg(w1);
+    return sg;
+}
+// Bound of every wait for published words (each round trip is about a
+// microsecond, so about a second in all); a wait that runs out reports
+// status 2 for its request instead of hanging the launch.
+constexpr int kSpinLimit = 1 << 20;
 
 // Logit row g of the call (request g / R, row g % R of that request).  The
 // result is wave-uniform, so loads use a scalar base and 32-bit offsets.
@@ -636,8 +686,12 @@ __device__ inline void load_tile(const T* row, int V, int c, u32x4 (&q)[NV]) {
 // SHARD (a vocabulary shard's relaxed-rule statistics): the rank count's
 // threshold l_x comes from the gathered drafted-token logits, since the token
 // may be another shard's column.
-template <typename T, int MODE, bool SUM, bool VECP, bool XV, bool SHARD, int NV>
-__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const Args a) {
+// PUBLISH (the single-launch calls): the tile record goes out as two
+// agent-scope atomic words (publish_record), which workgroups on any XCD of
+// the same launch read coherently; otherwise it is a plain store that the
+// next kernel reads.  blk is the tile's index in the call's streaming grid.
+template <typename T, int MODE, bool SUM, bool VECP, bool XV, bool SHARD, int NV, bool PUBLISH>
+__device__ __forceinline__ void stream_tile(const Args& a, const unsigned blk) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int TILE = kThreads * NV * VEC;
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
@@ -657,8 +711,8 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     // that has arrived, so the memory system sees every load as early as
     // possible (measured: 0.4 us of 16 at the exact rule's B=32, K=5 shape).
     __builtin_amdgcn_s_setprio(3);
-    const int g = uniform((int)(blockIdx.x / (unsigned)a.tpr));
-    const int c = (int)blockIdx.x - g * a.tpr;
+    const int g = uniform((int)(blk / (unsigned)a.tpr));
+    const int c = (int)blk - g * a.tpr;
     int vec, act;
     const T* row = call_row<T, MODE>(a, g, vec, act);
     if (!act) return;  // tree node past num_nodes: never read
@@ -673,8 +727,8 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
     // size 0 (no memory access) outside the recording workgroups and for an
     // out-of-range token.
     constexpr int kinds = uses_draft(MODE) ? 2 : 1;
-    const bool xvw = XV && (int)blockIdx.x < kinds * a.B * a.K;
-    const int xi = uniform((int)blockIdx.x / kinds), xslot = 2 * xi + ((int)blockIdx.x - xi * kinds);
+    const bool xvw = XV && (int)blk < kinds * a.B * a.K;
+    const int xi = uniform((int)blk / kinds), xslot = 2 * xi + ((int)blk - xi * kinds);
     // COUNT: a target row j < K counts the tokens strictly above l_x of its
     // drafted token x; l_x is needed from the second pass over the tile on
     const int cb = COUNT ? g / a.R : 0, cr = COUNT ? g - cb * a.R : 0;
@@ -791,9 +845,17 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
         sg.m = M;
         sg.ic = (ARGMAX || COUNT) ? I : 0;
         sg.s = s;
-        a.segs[blockIdx.x] = sg;
+        if (PUBLISH)
+            publish_record(a.frec + 2 * (size_t)blk, sg);
+        else
+            a.segs[blk] = sg;
         if (xvw && (unsigned)xl < (unsigned)a.V) a.xv_out[xslot] = Elem<T>::from_bits(xraw);
     }
+}
+
+template <typename T, int MODE, bool SUM, bool VECP, bool XV, bool SHARD, int NV>
+__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const Args a) {
+    stream_tile<T, MODE, SUM, VECP, XV, SHARD, NV, false>(a, blockIdx.x);
 }
 
 // ------------------------------------------------------ sampler stream
@@ -918,51 +980,23 @@ struct RowStats {
     double lnS[kMaxRows];
 };
 
-// Folds the tile records of rows [0, nrows) of request b.  Wave w of NW takes
-// rows w, w + NW, ... in batches of four, one tile record per lane; every batch's
-// loads are issued before any is used, and `hook` runs once in every thread
-// after the first batch is issued, before any record is used: the caller's
-// own loads go there, and the barrier that publishes the exp_nonpos table, so
-// that all of them share one memory round trip.  Ends with a barrier.
-template <int MODE, bool SUM, int NW, bool SHARD, typename Hook>
-__device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const double* tab, Hook hook) {
+// Folds the tile records of rows [0, nrows) of request b into RowStats.
+// Wave w of NW takes rows w, w + NW, ... in batches of kFoldBatch, one tile
+// record per lane; load(k0, sg) fills the batch starting at k0 (neutral
+// records for absent rows and lanes), and runs at least once in every wave.
+// Ends with a barrier.
+constexpr int kFoldBatch = 4;
+template <int MODE, bool SUM, int NW, typename Load>
+__device__ void fold_batches(int nrows, RowStats& rs, const double* tab, Load load) {
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
-    constexpr int kBatch = 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // Sharded: lane l takes tile l % tpr of shard l / tpr's slot; a shard's
-    // argmax is a column of its own, offset to a vocabulary index here.
-    size_t off = lane;
-    unsigned goff = 0u;
-    int nrec = a.tpr;
-    if (SHARD) {
-        const int sl = lane / a.tpr;
-        off = (size_t)sl * a.slot_segs + (lane - sl * a.tpr);
-        goff = (unsigned)sl * (unsigned)a.V;
-        nrec = a.G * a.tpr;
-    }
-    bool hooked = false;
-    for (int k0 = 0; k0 == 0 || wave + NW * k0 < nrows; k0 += kBatch) {
-        Seg sg[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int r = wave + NW * (k0 + j);
-            if (r < nrows && lane < nrec) {
-                sg[j] = a.segs[((size_t)b * a.R + r) * a.tpr + off];
-                if (SHARD && ARGMAX && sg[j].ic != INT_MAX) sg[j].ic = (int)((unsigned)sg[j].ic + goff);
-            } else {
-                sg[j].m = -INFINITY;
-                sg[j].ic = ARGMAX ? INT_MAX : 0;
-                sg[j].s = 0.0;
-            }
-        }
-        if (!hooked) {
-            hook();
-            hooked = true;
-        }
+    for (int k0 = 0; k0 == 0 || wave + NW * k0 < nrows; k0 += kFoldBatch) {
+        Seg sg[kFoldBatch];
+        load(k0, sg);
         double Sl = 1.0;  // lane j: normalizer of batch row j
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
+        for (int j = 0; j < kFoldBatch; ++j) {
             const int r = wave + NW * (k0 + j);
             if (r >= nrows) break;
             float M = sg[j].m;
@@ -991,10 +1025,99 @@ __device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const d
         if (SUM) {
             const double lS = log(Sl);  // one log for the whole batch
             const int r = wave + NW * (k0 + lane);
-            if (lane < kBatch && r < nrows) rs.lnS[r] = lS;
+            if (lane < kFoldBatch && r < nrows) rs.lnS[r] = lS;
         }
     }
     __syncthreads();
+}
+
+__device__ inline Seg neutral_record(bool argmax) {
+    Seg sg;
+    sg.m = -INFINITY;
+    sg.ic = argmax ? INT_MAX : 0;
+    sg.s = 0.0;
+    return sg;
+}
+
+// Records written by a previous kernel.  Every batch's loads are issued
+// before any is used, and `hook` runs once in every thread after the first
+// batch is issued, before any record is used: the caller's own loads go
+// there, and the barrier that publishes the exp_nonpos table, so that all of
+// them share one memory round trip.
+template <int MODE, bool SUM, int NW, bool SHARD, typename Hook>
+__device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const double* tab, Hook hook) {
+    constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Sharded: lane l takes tile l % tpr of shard l / tpr's slot; a shard's
+    // argmax is a column of its own, offset to a vocabulary index here.
+    size_t off = lane;
+    unsigned goff = 0u;
+    int nrec = a.tpr;
+    if (SHARD) {
+        const int sl = lane / a.tpr;
+        off = (size_t)sl * a.slot_segs + (lane - sl * a.tpr);
+        goff = (unsigned)sl * (unsigned)a.V;
+        nrec = a.G * a.tpr;
+    }
+    bool hooked = false;
+    fold_batches<MODE, SUM, NW>(nrows, rs, tab, [&](int k0, Seg (&sg)[kFoldBatch]) {
+#pragma unroll
+        for (int j = 0; j < kFoldBatch; ++j) {
+            const int r = wave + NW * (k0 + j);
+            if (r < nrows && lane < nrec) {
+                sg[j] = a.segs[((size_t)b * a.R + r) * a.tpr + off];
+                if (SHARD && ARGMAX && sg[j].ic != INT_MAX) sg[j].ic = (int)((unsigned)sg[j].ic + goff);
+            } else {
+                sg[j] = neutral_record(ARGMAX);
+            }
+        }
+        if (!hooked) {
+            hook();
+            hooked = true;
+        }
+    });
+}
+
+// Records published by the streaming workgroups of the same launch: each
+// batch waits until its records' words are all written.  Returns false in a
+// thread whose wait ran out (kSpinLimit).
+template <int MODE, bool SUM, int NW>
+__device__ bool fold_rows_published(const Args& a, int b, int nrows, RowStats& rs, const double* tab) {
+    constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    bool ok = true;
+    fold_batches<MODE, SUM, NW>(nrows, rs, tab, [&](int k0, Seg (&sg)[kFoldBatch]) {
+        uint64_t w0[kFoldBatch], w1[kFoldBatch];
+        const uint64_t* src[kFoldBatch];
+#pragma unroll
+        for (int j = 0; j < kFoldBatch; ++j) {
+            const int r = wave + NW * (k0 + j);
+            const bool need = r < nrows && lane < a.tpr;
+            src[j] = need ? a.frec + 2 * (((size_t)b * a.R + r) * a.tpr + lane) : nullptr;
+            w0[j] = w1[j] = need ? 0ull : 1ull;
+        }
+        for (int it = 0;; ++it) {
+            bool missing = false;
+#pragma unroll
+            for (int j = 0; j < kFoldBatch; ++j) {
+                if (w0[j] == 0ull || w1[j] == 0ull) {
+                    w0[j] = load_word(src[j]);
+                    w1[j] = load_word(src[j] + 1);
+                    missing |= (w0[j] == 0ull || w1[j] == 0ull);
+                }
+            }
+            if (__ballot(missing) == 0ull) break;
+            if (it == kSpinLimit) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+#pragma unroll
+        for (int j = 0; j < kFoldBatch; ++j)
+            sg[j] = src[j] ? decode_record(w0[j], w1[j]) : neutral_record(ARGMAX);
+    });
+    return ok;
 }
 
 // ------------------------------------------------------ chain decision
@@ -1132,6 +1255,14 @@ __device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
     }
 }
 
+// Zeroes request b's tile records in the workspace once the fold has read
+// them (every thread of the workgroup, after the fold's barrier), leaving the
+// workspace zero for the next call.
+__device__ inline void clear_records(const Args& a, int b) {
+    Seg* r = a.segs + (size_t)b * a.R * a.tpr;
+    for (int i = threadIdx.x; i < a.R * a.tpr; i += blockDim.x) r[i] = Seg{0.f, 0, 0.0};
+}
+
 // -------------------------------------------------------------- decide
 // The greedy rule's decide workgroup folds only K + 1 rows: eight waves take
 // them in one batch for K < 8 and launch faster than sixteen.
@@ -1155,6 +1286,7 @@ __global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
             if (threadIdx.x < 64) chain_load_values<T, MODE, SHARD>(a, b, cv);
             __syncthreads();  // the exp table; every load above is in flight
         });
+        if (!SHARD) clear_records(a, b);
         if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
         __syncthreads();
         write_prefix<MODE>(a, b, cd);
@@ -1186,6 +1318,7 @@ __global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
         fold_rows<kTree, SUM, NW, SHARD>(a, b, N, rs, tab, [] {
             __syncthreads();  // the exp table; every load above is in flight
         });
+        if (!SHARD) clear_records(a, b);
         const int nb = min(max(nraw, 1), N);
         if (threadIdx.x < 64) {
             // wave 0, lane i = node i.  Pointer jumping: `ok` says every node
@@ -1259,6 +1392,57 @@ __global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
     }
 }
 
+// This thread's share of the fp64 sums of chunk c of the terminal row(s) of
+// request b: exp(l - Mt) and exp(d - Md) over its tokens, and over those
+// classified p > q against the threshold cls, with the smallest distance of
+// (l - Mt) - (d - Md) from cls.  Thread tid of kThreads covers the tokens
+// c*kChunk + (k*kThreads + tid)*VEC + [0, VEC) for k < kRun/VEC; a thread
+// past the row's end reads nothing (its loads are masked).
+struct ChunkPartial {
+    double sa, sb, pa, pb, dmin;
+};
+template <typename T>
+__device__ inline ChunkPartial chunk_partial(const Args& a, int b, int n, bool residual, double Mt,
+                                             double Md, double cls, int c, int tid, const double* tab) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NV = kRun / VEC;  // 16-byte vectors per thread per chunk
+    const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
+    const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
+    const __amdgpu_buffer_rsrc_t rt = row_rsrc(trow, a.V);
+    const __amdgpu_buffer_rsrc_t rd = row_rsrc(drow, a.V);
+    const int c0 = c * kChunk;
+    const int c1 = min(c0 + kChunk, a.V);
+    u32x4 qt[NV], qd[NV];
+    ChunkPartial p = {0.0, 0.0, 0.0, 0.0, INFINITY};
+    if (residual) {  // uniform: one loop per case, no per-token branch
+        load_chunk<T, NV>(rt, c0, c1, a.vec_t, tid, qt);
+        load_chunk<T, NV>(rd, c0, c1, a.vec_d, tid, qd);
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                const double xa = (double)Elem<T>::get(qt[k], i) - Mt;
+                const double xb = (double)Elem<T>::get(qd[k], i) - Md;
+                const double ea = exp_nonpos(xa, tab);
+                const double eb = exp_nonpos(xb, tab);
+                p.sa += ea;
+                p.sb += eb;
+                const double dd = (xa - xb) - cls;
+                const double pq = (dd > 0.0) ? 1.0 : 0.0;  // p > q
+                p.pa = fma(ea, pq, p.pa);
+                p.pb = fma(eb, pq, p.pb);
+                p.dmin = fmin(p.dmin, fabs(dd));
+            }
+    } else {
+        load_chunk<T, NV>(rt, c0, c1, a.vec_t, tid, qt);
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) p.sa += exp_nonpos((double)Elem<T>::get(qt[k], i) - Mt, tab);
+    }
+    return p;
+}
+
 // -------------------------------------------------------------------- pass 2
 // Sweep: one workgroup per (request, 4096-token chunk).  Every workgroup of
 // the request folds the tile records and takes the decision itself (same
@@ -1269,8 +1453,6 @@ __global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
 template <typename T, int MODE, bool SHARD>
 __global__ __launch_bounds__(kSweepThreads, kPass2WavesPerSimd) void k_sweep(const Args a) {
     constexpr bool EXACT = (MODE == kExact);
-    constexpr int VEC = Elem<T>::kVec;
-    constexpr int NV = kRun / VEC;  // 16-byte vectors per thread per chunk
     constexpr int NW = kSweepThreads / 64;
 
     // kSweepGroups consecutive chunks per workgroup, one 256-thread group each
@@ -1315,43 +1497,8 @@ __global__ __launch_bounds__(kSweepThreads, kPass2WavesPerSimd) void k_sweep(con
             a.dec[b] = d;
         }
     }
-    const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
-    const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
-    const __amdgpu_buffer_rsrc_t rt = row_rsrc(trow, a.V);
-    const __amdgpu_buffer_rsrc_t rd = row_rsrc(drow, a.V);
-
-    // a group past the row's last chunk reads nothing (its loads return zeros
-    // and are masked) and writes nothing
-    const int c0 = c * kChunk;
-    const int c1 = min(c0 + kChunk, a.V);
-    u32x4 qt[NV], qd[NV];
-    double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0, dmin = INFINITY;
-    if (residual) {  // uniform: one loop per case, no per-token branch
-        load_chunk<T, NV>(rt, c0, c1, a.vec_t, tid, qt);
-        load_chunk<T, NV>(rd, c0, c1, a.vec_d, tid, qd);
-#pragma unroll
-        for (int k = 0; k < NV; ++k)
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                const double xa = (double)Elem<T>::get(qt[k], i) - Mt;
-                const double xb = (double)Elem<T>::get(qd[k], i) - Md;
-                const double ea = exp_nonpos(xa, tab);
-                const double eb = exp_nonpos(xb, tab);
-                sa += ea;
-                sb += eb;
-                const double dd = (xa - xb) - cls;
-                const double pq = (dd > 0.0) ? 1.0 : 0.0;  // p > q
-                pa = fma(ea, pq, pa);
-                pb = fma(eb, pq, pb);
-                dmin = fmin(dmin, fabs(dd));
-            }
-    } else {
-        load_chunk<T, NV>(rt, c0, c1, a.vec_t, tid, qt);
-#pragma unroll
-        for (int k = 0; k < NV; ++k)
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) sa += exp_nonpos((double)Elem<T>::get(qt[k], i) - Mt, tab);
-    }
+    const ChunkPartial cp = chunk_partial<T>(a, b, n, residual, Mt, Md, cls, c, tid, tab);
+    double sa = cp.sa, sb = cp.sb, pa = cp.pa, pb = cp.pb, dmin = cp.dmin;
     sa = wave_sum(sa);
     if (residual) {
         sb = wave_sum(sb);
@@ -1462,6 +1609,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
             cs = *src;
         }
         if (ROWS) {
+            // the chunk records are read: zero them for the next call
+            if (lane < nchunk) a.sums[(size_t)b * a.C2 + lane] = ChunkSums{0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
             // chunk records {sum of exp(l - m), m}: rescale to the row max
             const float mc = lane < nchunk ? (float)cs.sb : -INFINITY;
             const float Mr = wave_max(mc);
@@ -1654,6 +1803,504 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     }
 }
 
+// ------------------------------------------------------------ single launch
+// The exact, relaxed and power rules run as one launch per call, with no
+// kernel boundary between the stream and the terminal draw.  The launch's
+// first nstream workgroups stream tiles (stream_tile, records published).
+// Behind them, one sweep workgroup per (request, 4096-token chunk) -- these
+// are dispatched after every streaming workgroup, so while the last tiles
+// stream, the requests whose tiles are done already fold and sweep -- waits
+// for its request's records, folds them and takes the decision (the same
+// fold and decision in every workgroup of the request), writes the accepted
+// prefix (chunk 0), sums its chunk of the terminal row(s) in fp64 and
+// publishes the sums.  The request's last sweep workgroup to finish (a
+// ticket counts them) waits for all of the request's chunk sums, draws the
+// terminal token (draw_terminal) and zeroes the request's published words
+// and ticket for the next call.
+
+// Sub-chunks: a sweep workgroup publishes its chunk's masses per 1024-token
+// sub-chunk, so the draw rescans 1024 tokens (four per thread) instead of a
+// whole chunk.  Published per chunk: the chunk's exp sums of the target and
+// draft rows (S, Sq), dmin (see ChunkSums), then per sub-chunk the two sums
+// the draw's mass is formed from (target and draft exp sums over the tokens
+// classified p > q for a residual draw, the target exp sum otherwise).
+constexpr int kSub = 1024;
+constexpr int kSubs = kChunk / kSub;
+constexpr int kChunkWords = 3 + 2 * kSubs;
+
+// Drafted-token logits read from the inputs (the token is loaded first, so
+// these loads wait for it; they overlap the wait for the records).
+template <typename T, int MODE>
+__device__ inline void chain_load_inputs(const Args& a, int b, ChainVals& cv) {
+    const int j = threadIdx.x;
+    if (j < a.K) {
+        cv.bad = (unsigned)cv.x >= (unsigned)a.V;
+        if (MODE == kGreedy || cv.bad) return;
+        cv.lx = Elem<T>::at(reinterpret_cast<const T*>(a.T), (size_t)(b * a.rows_t + j) * a.V + cv.x);
+        if (uses_draft(MODE))
+            cv.dx = Elem<T>::at(reinterpret_cast<const T*>(a.D), (size_t)(b * a.K + j) * a.V + cv.x);
+    }
+}
+
+// Weight of one token in the terminal draw: exp(l - Mt) from p, or for the
+// residual relu(p - q) = max(p - q, 0) with p > q decided by the threshold
+// clsx on (l - Mt) - (d - Md).  One expression wherever a weight is formed.
+__device__ inline double draw_weight(bool res, float l, float d, double Mt, double Md, double clsx,
+                                     double iS, double iSq, const double* tab) {
+    const double xa = (double)l - Mt;
+    const double ea = exp_nonpos(xa, tab);
+    if (!res) return ea;
+    const double xb = (double)d - Md;
+    if (!(xa - xb > clsx)) return 0.0;
+    return fmax(fma(ea, iS, -(exp_nonpos(xb, tab) * iSq)), 0.0);
+}
+
+// Zeroes request b's published words and ticket (every thread; after all of
+// the workgroup's reads of them).
+__device__ inline void clear_published(const Args& a, int b) {
+    uint64_t* r = a.frec + (size_t)b * a.R * a.tpr * 2;
+    for (int i = threadIdx.x; i < a.R * a.tpr * 2; i += blockDim.x) store_word(r + i, 0ull);
+    uint64_t* m = a.fsums + (size_t)b * a.C2 * kChunkWords;
+    for (int i = threadIdx.x; i < a.C2 * kChunkWords; i += blockDim.x) store_word(m + i, 0ull);
+    if (threadIdx.x == 0) __hip_atomic_store(a.ticket + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The terminal draw of request b, by the request's last sweep workgroup.
+// Wave 0 waits for the C2 published chunk records (lane = chunk), forms S,
+// Sq, the exact p > q threshold and the sub-chunk masses, recomputes the
+// masses of chunks the streamed threshold may have classified otherwise,
+// scans the chunks and then the sub-chunks of the chunk holding u_K * Z.
+// The workgroup rescans that sub-chunk, four consecutive tokens per thread,
+// with a block scan, and writes the terminal token and its log-probs.
+template <typename T, int MODE>
+__device__ void draw_terminal(const Args& a, const int b, const ChainDecision& cd, const RowStats& rs,
+                              const double* tab) {
+    constexpr bool EXACT = (MODE == kExact);
+    constexpr int NT = kThreads, NWV = NT / 64, RUN = kSub / NT;
+    static_assert(RUN == 4, "four tokens per thread (one load4 per row)");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
+    const int n = cd.n;
+    const bool residual = EXACT && n < a.K;
+    const double Mt = rs.M[n];
+    const double Md = residual ? (double)rs.M[a.rows_t + n] : 0.0;
+    const double cls = residual ? rs.lnS[n] - rs.lnS[a.rows_t + n] : 0.0;
+    const double rn = cd.r[n < a.K ? n : 0];
+    const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
+    const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
+    const __amdgpu_buffer_rsrc_t rt = row_rsrc(trow, a.V);
+    const __amdgpu_buffer_rsrc_t rd = row_rsrc(drow, a.V);
+
+    __shared__ int s_sub, s_res, s_ok;
+    __shared__ double s_base, s_target, s_iS, s_iSq, s_lnS, s_lnZ, s_l1r, s_cls;
+    __shared__ double s_wtot[NWV];
+    __shared__ int s_pick[NWV][3];
+    __shared__ double s_W[64][kSubs];
+    __shared__ unsigned long long s_sus;
+
+    // wave 0, lane l: chunk l's target exp sum (the fallback's p mass per
+    // sub-chunk is kept in s_W when needed) and the draw's normalizers
+    double S0 = 1.0, Z0 = 1.0;
+    double S = 1.0;
+    double pm[kSubs];  // wave 0, lane l: chunk l's p mass per sub-chunk (non-residual) or unused
+    // Wave 0: the draw's total from the sub-chunk masses W[] (lane = chunk),
+    // a scan over chunks, then over the sub-chunks of the chunk holding
+    // u_K * Z.
+    auto pick = [&](const double (&W)[kSubs], const double (&P)[kSubs]) {
+        double wc = 0.0;
+#pragma unroll
+        for (int k = 0; k < kSubs; ++k) wc += W[k];
+        const double Zr = residual ? wave_sum(wc) : 0.0;
+        const bool res = residual && (Zr > 0.0);
+        double Wk[kSubs];
+#pragma unroll
+        for (int k = 0; k < kSubs; ++k) Wk[k] = (residual && !res) ? P[k] : W[k];  // no residual mass: draw from p
+        double cw = 0.0;
+#pragma unroll
+        for (int k = 0; k < kSubs; ++k) cw += Wk[k];
+        const double Z = res ? Zr : S;
+        const double target = (double)a.u[b * (a.K + 1) + a.K] * Z;
+        const double incl = wave_incl_scan(cw);
+        double excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = 0.0;  // [excl, incl) of consecutive chunks tile [0, Z)
+        const bool has = lane < a.C2 && cw > 0.0;
+        const unsigned long long mine = __ballot(has && excl <= target && target < incl);
+        const unsigned long long hasm = __ballot(has);
+        // the unique chunk whose interval holds target; if rounding pushed
+        // target past the last boundary, the last chunk with mass
+        const int cstar = mine ? __builtin_ctzll(mine) : (hasm ? 63 - __builtin_clzll(hasm) : 0);
+        // within it, the sub-chunk whose interval holds target, or its last
+        // sub-chunk with mass (lane cstar decides, in sub-chunk order)
+        int sub = 0;
+        double base = excl;
+        if (lane == cstar) {
+            double run = excl;
+            int last = -1, hit = -1;
+            double hbase = excl, lbase = excl;
+#pragma unroll
+            for (int k = 0; k < kSubs; ++k) {
+                if (Wk[k] > 0.0) {
+                    if (hit < 0 && target < run + Wk[k]) {
+                        hit = k;
+                        hbase = run;
+                    }
+                    last = k;
+                    lbase = run;
+                }
+                run += Wk[k];
+            }
+            sub = hit >= 0 ? hit : (last >= 0 ? last : 0);
+            base = hit >= 0 ? hbase : lbase;
+        }
+        sub = __builtin_amdgcn_readlane(sub, cstar);
+        base = readlane_d(base, cstar);
+        S0 = S;
+        Z0 = Z;
+        if (lane == 0) {
+            s_sub = cstar * kSubs + sub;
+            s_base = base;
+            s_target = target;
+            s_res = res;
+        }
+    };
+    if (wave == 0) {
+        bool ok = true;
+        uint64_t w[kChunkWords];
+#pragma unroll
+        for (int i = 0; i < kChunkWords; ++i) w[i] = lane < a.C2 ? 0ull : kTop;  // absent chunks: zero sums
+        if (lane < a.C2) {
+            const uint64_t* src = a.fsums + ((size_t)b * a.C2 + lane) * kChunkWords;
+            for (int it = 0;; ++it) {
+                bool missing = false;
+#pragma unroll
+                for (int i = 0; i < kChunkWords; ++i) {
+                    if (w[i] == 0ull) {
+                        w[i] = load_word(src + i);
+                        missing |= w[i] == 0ull;
+                    }
+                }
+                if (!missing) break;
+                if (it == kSpinLimit) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        const bool all_ok = __ballot(!ok) == 0ull;
+        const double sa = dec_nonneg(w[0]), sb = dec_nonneg(w[1]);
+        const double dmin = lane < a.C2 ? dec_nonneg(w[2]) : INFINITY;
+        S = wave_sum(sa);
+        const double Sq = residual ? wave_sum(sb) : 1.0;
+        const double iS = 1.0 / S, iSq = 1.0 / Sq;
+        double W[kSubs];
+#pragma unroll
+        for (int k = 0; k < kSubs; ++k) {
+            const double A = dec_nonneg(w[3 + 2 * k]), Bq = dec_nonneg(w[4 + 2 * k]);
+            // residual mass of the sub-chunk (clamped: rounding can leave a
+            // rounding-size negative), or its p mass
+            W[k] = residual ? fmax(A * iS - Bq * iSq, 0.0) : A;
+            pm[k] = residual ? 0.0 : A;
+        }
+        // The sweep classified tokens p > q against the streamed normalizers;
+        // the exact threshold comes from the fp64 sums.  A token the two
+        // thresholds classify differently lies between them, so only chunks
+        // holding a token that close (plus a rounding allowance) need their
+        // masses recomputed.
+        double clsx = cls;
+        unsigned long long sus = 0ull;
+        if (residual) {
+            clsx = log(S) - log(Sq);
+            const double gap = fabs(clsx - cls) + 1e-12;
+            sus = __ballot(lane < a.C2 && dmin <= gap);
+        }
+        if (lane == 0) {
+            s_ok = all_ok;
+            s_cls = clsx;
+            s_sus = all_ok ? sus : 0ull;
+            s_iS = iS;
+            s_iSq = iSq;
+        }
+        if (all_ok) {
+            if (sus || residual) {
+                // the residual's fallback (no mass) draws from p: keep the
+                // p masses too
+#pragma unroll
+                for (int k = 0; k < kSubs; ++k) s_W[lane][k] = W[k];
+            }
+            if (!sus) pick(W, pm);
+        }
+    }
+    __syncthreads();
+    if (!s_ok) {  // a chunk's sums never arrived: report, leave the words as they are
+        if (t == 0) a.out_status[b] = 2;
+        return;
+    }
+    const double clsx = s_cls, iS = s_iS, iSq = s_iSq;
+    if (s_sus) {  // workgroup-uniform and rare: recompute those chunks' sub-chunk masses
+        for (unsigned long long m = s_sus; m; m &= m - 1) {
+            const int c = __builtin_ctzll(m);
+            for (int k = 0; k < kSubs; ++k) {
+                const int e = c * kChunk + k * kSub + t * RUN;
+                float lt[RUN], ld[RUN];
+                Elem<T>::load4(rt, e, a.V, a.vec_t, lt);
+                Elem<T>::load4(rd, e, a.V, a.vec_d, ld);
+                double sum = 0.0;
+#pragma unroll
+                for (int i = 0; i < RUN; ++i) sum += draw_weight(true, lt[i], ld[i], Mt, Md, clsx, iS, iSq, tab);
+                sum = wave_sum(sum);
+                if (lane == 0) s_wtot[wave] = sum;
+                __syncthreads();
+                if (t == 0) {
+                    double z = 0.0;
+                    for (int ww = 0; ww < NWV; ++ww) z += s_wtot[ww];
+                    s_W[c][k] = z;
+                }
+                __syncthreads();
+            }
+        }
+        if (wave == 0) {
+            double W[kSubs];
+#pragma unroll
+            for (int k = 0; k < kSubs; ++k) W[k] = s_W[lane][k];
+            pick(W, pm);
+        }
+        __syncthreads();
+    }
+
+    const int sub = s_sub;
+    const bool res = s_res;
+    const double target = s_target;
+    const int e0 = sub * kSub + t * RUN;
+    float lt[RUN], ld[RUN];
+    Elem<T>::load4(rt, e0, a.V, a.vec_t, lt);
+    Elem<T>::load4(rd, e0, a.V, residual ? a.vec_d : a.vec_t, ld);
+    // the logs of the outputs, while the loads are in flight (the next
+    // barrier publishes them)
+    if (t == 0) {
+        s_lnS = log(S0);
+        s_lnZ = log(Z0);
+        s_l1r = res ? log1p(-rn) : 0.0;
+    }
+    double w[RUN];
+    double tsum = 0.0;
+    unsigned pos = 0u, fin = 0u;  // bit i: token i has mass / a finite logit
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+        w[i] = draw_weight(res, lt[i], ld[i], Mt, Md, clsx, iS, iSq, tab);
+        tsum += w[i];
+        pos |= (w[i] > 0.0) ? (1u << i) : 0u;
+        fin |= (lt[i] > -INFINITY) ? (1u << i) : 0u;
+    }
+    // block scan in thread order; the exclusive prefix of a thread is the
+    // previous thread's inclusive prefix, bit for bit
+    const double wincl = wave_incl_scan(tsum);
+    if (lane == 63) s_wtot[wave] = wincl;
+    __syncthreads();
+    double off = 0.0;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww)
+        if (ww < wave) off += s_wtot[ww];
+    const double tincl = wincl + off;
+    double texcl = __shfl_up(tincl, 1);
+    if (lane == 0) texcl = off;
+    // first crossing of the running sum past target in this thread's tokens
+    double cum = s_base + texcl;
+    int cand = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+        if (w[i] > 0.0 && cand == INT_MAX) {
+            cum += w[i];
+            if (cum > target) cand = e0 + i;
+        }
+    }
+    const int lastpos = pos ? e0 + 31 - __builtin_clz(pos) : -1;
+    const int anypos = fin ? e0 + 31 - __builtin_clz(fin) : -1;
+    const int wc = wave_min_i(cand), wl = wave_max_i(lastpos), wa = wave_max_i(anypos);
+    if (lane == 0) {
+        s_pick[wave][0] = wc;
+        s_pick[wave][1] = wl;
+        s_pick[wave][2] = wa;
+    }
+    __syncthreads();
+    int yc = INT_MAX, yl = -1, ya = -1;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) {
+        yc = min(yc, s_pick[ww][0]);
+        yl = max(yl, s_pick[ww][1]);
+        ya = max(ya, s_pick[ww][2]);
+    }
+    // The crossing token; if rounding left none, the last token with mass in
+    // the sub-chunk; if it had none, its last finite token.  Always a valid
+    // index.
+    int y = (yc != INT_MAX) ? yc : (yl >= 0 ? yl : ya);
+    if (y < 0 || y >= a.V) y = 0;
+    const int rel = y - sub * kSub;
+    const bool insub = rel >= 0 && rel < kSub;
+    if (t == (insub ? rel / RUN : 0)) {
+        float ly = lt[0], dy = ld[0];
+        double wy = w[0];
+        if (insub) {
+#pragma unroll
+            for (int i = 1; i < RUN; ++i)
+                if (e0 + i == y) {
+                    ly = lt[i];
+                    dy = ld[i];
+                    wy = w[i];
+                }
+        } else {
+            ly = Elem<T>::at(trow, (size_t)y);
+            dy = res ? Elem<T>::at(drow, (size_t)y) : 0.f;
+            wy = draw_weight(res, ly, dy, Mt, Md, clsx, iS, iSq, tab);
+        }
+        (void)dy;
+        const int L = a.L;
+        a.out_tok[(size_t)b * L + n] = y;
+        const double tlp = ((double)ly - Mt) - s_lnS;
+        // behaviour log-prob: residual draw, power-rule fallback after a
+        // rejection (1 - a_n) p_n(y), or a plain draw from p
+        const double blp = res ? s_l1r + log(wy) - s_lnZ
+                               : ((MODE == kPower && n < a.K) ? log1p(-rn) + tlp : tlp);
+        if (a.out_tlp) a.out_tlp[(size_t)b * L + n] = (float)tlp;
+        if (a.out_blp) a.out_blp[(size_t)b * L + n] = (float)blp;
+    }
+    __syncthreads();  // every read of the request's published words is done
+    clear_published(a, b);
+}
+
+// One sweep workgroup: request idx / C2, chunk idx % C2.
+template <typename T, int MODE>
+__device__ void sweep_role(const Args& a, const int idx) {
+    constexpr bool EXACT = (MODE == kExact);
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NV = kRun / VEC;  // 16-byte vectors per thread
+    const int b = idx / a.C2, c = idx - b * a.C2;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+    __shared__ double tab[kExpTab];
+    __shared__ RowStats rs;
+    __shared__ ChainDecision cd;
+    __shared__ double red[kWaves][3 + 2 * NV];
+    __shared__ int s_ok, s_last;
+    fill_exp_table(tab);
+    if (tid == 0) s_ok = 1;
+    ChainVals cv;
+    if (tid < 64) {
+        chain_load_tokens<MODE>(a, b, cv);
+        chain_load_inputs<T, MODE>(a, b, cv);
+    }
+    __syncthreads();  // the exp table and s_ok
+    if (!fold_rows_published<MODE, true, kWaves>(a, b, a.R, rs, tab)) s_ok = 0;
+    __syncthreads();
+    if (!s_ok) {  // a record never arrived: report, leave the words as they are
+        if (tid == 0) a.out_status[b] = 2;
+        return;
+    }
+    if (tid < 64) chain_decide<MODE>(a, rs, cv, cd);
+    __syncthreads();
+    const int n = cd.n;
+    const bool residual = EXACT && n < a.K;
+    const double Mt = rs.M[n], Md = residual ? (double)rs.M[a.rows_t + n] : 0.0;
+    // p > q  <=>  (l - Mt) - (d - Md) > lnSt - lnSd, with the streamed normalizers
+    const double cls = residual ? rs.lnS[n] - rs.lnS[a.rows_t + n] : 0.0;
+    if (c == 0) write_prefix<MODE>(a, b, cd);
+
+    // this thread's vectors k cover tokens c*kChunk + (k*kThreads + tid)*VEC +
+    // [0, VEC): vector k lies in sub-chunk ((k*kThreads + tid)*VEC) / kSub
+    const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
+    const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
+    const int c0 = c * kChunk, c1 = min(c0 + kChunk, a.V);
+    u32x4 qt[NV], qd[NV];
+    double sa = 0.0, sb = 0.0, dmin = INFINITY;
+    double A[NV], Bq[NV];  // per vector: the sums its sub-chunk's mass is formed from
+    if (residual) {
+        load_chunk<T, NV>(row_rsrc(trow, a.V), c0, c1, a.vec_t, tid, qt);
+        load_chunk<T, NV>(row_rsrc(drow, a.V), c0, c1, a.vec_d, tid, qd);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            A[k] = Bq[k] = 0.0;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                const double xa = (double)Elem<T>::get(qt[k], i) - Mt;
+                const double xb = (double)Elem<T>::get(qd[k], i) - Md;
+                const double ea = exp_nonpos(xa, tab);
+                const double eb = exp_nonpos(xb, tab);
+                sa += ea;
+                sb += eb;
+                const double dd = (xa - xb) - cls;
+                const double pq = (dd > 0.0) ? 1.0 : 0.0;  // p > q
+                A[k] = fma(ea, pq, A[k]);
+                Bq[k] = fma(eb, pq, Bq[k]);
+                dmin = fmin(dmin, fabs(dd));
+            }
+        }
+    } else {
+        load_chunk<T, NV>(row_rsrc(trow, a.V), c0, c1, a.vec_t, tid, qt);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            A[k] = Bq[k] = 0.0;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) A[k] += exp_nonpos((double)Elem<T>::get(qt[k], i) - Mt, tab);
+            sa += A[k];
+        }
+    }
+    sa = wave_sum(sa);
+    if (residual) {
+        sb = wave_sum(sb);
+        dmin = wave_min_d(dmin);
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        A[k] = wave_sum(A[k]);
+        if (residual) Bq[k] = wave_sum(Bq[k]);
+    }
+    if (lane == 0) {
+        red[wave][0] = sa;
+        red[wave][1] = sb;
+        red[wave][2] = dmin;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            red[wave][3 + 2 * k] = A[k];
+            red[wave][4 + 2 * k] = Bq[k];
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double v[kChunkWords];
+        v[0] = v[1] = 0.0;
+        v[2] = INFINITY;
+        for (int i = 3; i < kChunkWords; ++i) v[i] = 0.0;
+        for (int w = 0; w < kWaves; ++w) {
+            v[0] += red[w][0];
+            v[1] += red[w][1];
+            v[2] = fmin(v[2], red[w][2]);
+        }
+        // sub-chunk sums in a fixed order: vector k, then wave
+        for (int k = 0; k < NV; ++k)
+            for (int w = 0; w < kWaves; ++w) {
+                const int sc = ((k * kThreads + w * 64) * VEC) / kSub;
+                v[3 + 2 * sc] += red[w][3 + 2 * k];
+                v[4 + 2 * sc] += red[w][4 + 2 * k];
+            }
+        uint64_t* dst = a.fsums + ((size_t)b * a.C2 + c) * kChunkWords;
+        for (int i = 0; i < kChunkWords; ++i) store_word(dst + i, enc_nonneg(v[i]));
+        // the request's last sweep workgroup draws; the others are done
+        const uint32_t done = __hip_atomic_fetch_add(a.ticket + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = done == (uint32_t)(a.C2 - 1);
+    }
+    __syncthreads();
+    if (s_last) draw_terminal<T, MODE>(a, b, cd, rs, tab);
+}
+
+// The single launch of an exact, relaxed or power call.
+template <typename T, int MODE, bool VECP>
+__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_single(const Args a) {
+    const unsigned blk = blockIdx.x;
+    if (blk < (unsigned)a.nstream) {
+        stream_tile<T, MODE, true, VECP, false, false, kTileVecs, true>(a, blk);
+        return;
+    }
+    sweep_role<T, MODE>(a, (int)(blk - (unsigned)a.nstream));
+}
+
 // ------------------------------------------------------------------- host
 inline int esize(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
 inline int tile_elems(spec_dtype dt) { return kTileBytes / esize(dt); }
@@ -1767,6 +2414,46 @@ spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
+}
+
+// The single launch of an exact, relaxed or power call (k_single): the
+// streaming workgroups, then one sweep workgroup per (request, chunk).  With
+// the profiling hook set, the launch carries the start and stop events: the
+// whole call is this one kernel.
+template <int MODE>
+spec_status launch_single(Args a, spec_dtype dt, hipStream_t st) {
+    a.tpr = tpr_of(dt, a.V);
+    a.Vtot = a.V;
+    const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
+    a.frec = reinterpret_cast<uint64_t*>(a.ws + lay.frec);
+    a.fsums = reinterpret_cast<uint64_t*>(a.ws + lay.fsums);
+    a.ticket = reinterpret_cast<uint32_t*>(a.ws + lay.ticket);
+    a.nstream = a.B * a.R * a.tpr;
+    const dim3 grid((unsigned)a.nstream + (unsigned)a.B * (unsigned)a.C2), block(kThreads);
+    hipEvent_t ev[3];
+    take_prof(ev);
+    const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
+    if (dt == SPEC_BF16) {
+        if (vecp)
+            hipExtLaunchKernelGGL((k_single<uint16_t, MODE, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        else
+            hipExtLaunchKernelGGL((k_single<uint16_t, MODE, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
+    } else {
+        if (vecp)
+            hipExtLaunchKernelGGL((k_single<float, MODE, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        else
+            hipExtLaunchKernelGGL((k_single<float, MODE, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
+    }
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+// The single launch's grid (streaming tiles plus one sweep workgroup per
+// chunk) stays below 2^32 threads.
+inline bool single_grid_ok(spec_dtype dt, int B, int R, int V) {
+    const long long wg = (long long)B * R * tpr_of(dt, V) + (long long)B * c2_of(dt, V);
+    return wg * kThreads < (1ll << 32);
 }
 
 // ------------------------------------------------------ vocabulary shards
@@ -1958,7 +2645,8 @@ spec_status spec_verify_exact(const void* target_logits, const void* draft_logit
                               int32_t* out_status, void* workspace, size_t workspace_bytes,
                               void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, 2 * K + 1)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, 2 * K + 1) || !single_grid_ok(dtype, B, 2 * K + 1, V))
+        return SPEC_EINVAL;
     if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
         !out_accept_len || !out_status)
         return SPEC_EINVAL;
@@ -1985,7 +2673,7 @@ spec_status spec_verify_exact(const void* target_logits, const void* draft_logit
     a.L = K + 1;
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return launch<kExact, true>(a, dtype, st);
+    return launch_single<kExact>(a, dtype, st);
 }
 
 spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
@@ -1995,7 +2683,8 @@ spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
                                 float* out_behavior_logprob, int32_t* out_status, void* workspace,
                                 size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, K + 1)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, K + 1) || !single_grid_ok(dtype, B, K + 1, V))
+        return SPEC_EINVAL;
     if (tau != tau || top_k < 0) return SPEC_EINVAL;
     if (!target_logits || !draft_tokens || !uniforms || !out_tokens || !out_accept_len ||
         !out_status)
@@ -2023,7 +2712,7 @@ spec_status spec_verify_relaxed(const void* target_logits, spec_dtype dtype,
     a.L = K + 1;
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return launch<kRelaxed, true>(a, dtype, st);
+    return launch_single<kRelaxed>(a, dtype, st);
 }
 
 spec_status spec_verify_power(const void* target_logits, const void* draft_logits,
@@ -2033,7 +2722,8 @@ spec_status spec_verify_power(const void* target_logits, const void* draft_logit
                               float* out_behavior_logprob, int32_t* out_status, void* workspace,
                               size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, 2 * K + 1)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || !sizes_ok(dtype, B, K, V, 2 * K + 1) || !single_grid_ok(dtype, B, 2 * K + 1, V))
+        return SPEC_EINVAL;
     if (!(alpha >= 0.f) || alpha == INFINITY) return SPEC_EINVAL;
     if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
         !out_accept_len || !out_status)
@@ -2061,7 +2751,7 @@ spec_status spec_verify_power(const void* target_logits, const void* draft_logit
     a.out_status = out_status;
     a.L = K + 1;
     a.ws = static_cast<unsigned char*>(workspace);
-    return launch<kPower, true>(a, dtype, static_cast<hipStream_t>(stream));
+    return launch_single<kPower>(a, dtype, static_cast<hipStream_t>(stream));
 }
 
 size_t spec_sample_workspace_bytes(int rows, int V) {

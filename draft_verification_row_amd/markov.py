@@ -45,11 +45,13 @@ def _tables(target_table, draft_table):
 
 
 def _workspaces(P, B, K):
-    """Workspaces of the round's two library calls (no initialization needed)."""
+    """Workspaces of the round's two library calls."""
     V = P.shape[0]
     u8 = dict(dtype=torch.uint8, device=P.device)
-    return (torch.empty(spec_sample_workspace_bytes(B, V), **u8),
-            torch.empty(spec_verify_workspace_bytes(B, 2 * K + 1, V), **u8))
+    # zero-filled: the library reads published words as "not written" while
+    # they are zero and leaves every byte zero after each call
+    return (torch.zeros(spec_sample_workspace_bytes(B, V), **u8),
+            torch.zeros(spec_verify_workspace_bytes(B, 2 * K + 1, V), **u8))
 
 
 def _round(P, Q, cur, udt_r, uv_r, ws, rows, emitted_r, accept_r):

@@ -42,7 +42,12 @@
  *                               malformed (a consulted draft token outside
  *                               [0,V), or a tree parent outside [-1, i)):
  *                               the offending draft counts as rejected and
- *                               the offending tree node as unmatched.
+ *                               the offending tree node as unmatched.  2
+ *                               (exact, relaxed and power rules) when a wait
+ *                               for data from another workgroup of the same
+ *                               launch ran out (about a second); the
+ *                               request's other outputs are then undefined.
+ *                               It does not occur on a working device.
  *
  * Randomness is supplied by the caller (spec-decode README, "Use it": the
  * generator takes an rng), as uniforms[b][K+1] in [0,1): uniforms[b][j]
@@ -53,12 +58,18 @@
  *   Each call needs a device workspace of at least
  *   spec_verify_workspace_bytes(B, rows_per_request, V) bytes, 256-byte
  *   aligned, for per-tile statistics and per-chunk sums passed between the
- *   call's kernels.  It needs no initialization and carries nothing from one
- *   call to the next, so one workspace serves calls of any shape in turn on
- *   the same stream.  Calls that run concurrently (different streams) need
- *   different workspaces.  The library allocates nothing and keeps no state
- *   besides the one-shot, per-thread profiling hook
- *   (spec_verify_profile_next_call).
+ *   call's workgroups.  It must be zero-filled before its first call (for
+ *   example allocated zeroed); every call leaves every byte of it zero
+ *   again, so one workspace serves calls of any rule and shape in turn on
+ *   the same stream with no further initialization.  (The exact, relaxed
+ *   and power calls run as one launch whose workgroups pass data through the
+ *   workspace while the launch runs, and read a zero word as "not written
+ *   yet".)  Calls that run concurrently (different streams) need different
+ *   workspaces.  A call that reports status 2 for a request (see
+ *   out_status) may leave its workspace dirty: zero-fill it before reusing
+ *   it.  The library allocates nothing and keeps no state besides the
+ *   one-shot, per-thread profiling hook (spec_verify_profile_next_call) and
+ *   the static array of spec_verify_exact_noalloc.
  *
  * Streams and errors
  *   stream is a hipStream_t (NULL = the default stream).  Calls enqueue
@@ -248,7 +259,7 @@ spec_status spec_verify_power(const void *target_logits, const void *draft_logit
  *   out_tokens   [rows] int32
  *   out_logprob  [rows] float, or NULL (not written)
  *   out_status   [rows] int32, always 0
- * rows <= SPEC_MAX_B; the workspace (256-byte aligned, no initialization) must
+ * rows <= SPEC_MAX_B; the workspace (256-byte aligned, zero-filled as above) must
  * hold spec_sample_workspace_bytes(rows, V) bytes.
  */
 size_t spec_sample_workspace_bytes(int rows, int V);

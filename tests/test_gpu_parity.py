@@ -309,11 +309,11 @@ def test_bitwise_determinism():
 
 
 def test_workspace_reuse_across_shapes():
-    """The workspace needs no initialization and keeps nothing between calls:
-    one buffer, filled with random bytes first, serves calls of several
-    shapes in turn."""
+    """One zero-filled workspace serves calls of several rules and shapes in
+    turn, and every call leaves it zero-filled again (the single-launch rules
+    read zero as "not yet published")."""
     nb = sv.spec_verify_workspace_bytes(64, 17, 151936)
-    ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     for (B, K, V) in [(4, 3, 5000), (32, 5, 20000), (2, 8, 3000), (32, 5, 20000)]:
         ci = synth.chain_inputs(B, K, V, "bf16", seed=B * 7 + K, useed=V)
         T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
@@ -323,6 +323,7 @@ def test_workspace_reuse_across_shapes():
         compare_chain(r, oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
                       what=f"reuse exact {B},{K},{V}")
         compare_chain(g, oracle.greedy(ci.target, ci.tokens, "bf16"), what=f"reuse greedy {B}")
+        assert int(ws.count_nonzero()) == 0, f"workspace left dirty after B={B} K={K} V={V}"
 
 
 # --------------------------------------------------------- statistical pin
