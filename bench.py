@@ -12,13 +12,17 @@ logits are streamed from HBM, not from that cache.  The K timed calls are
 captured into one HIP graph and replayed once between two events (launches
 then cost no host time); the same loop run eagerly is reported alongside.
 
-The streaming kernel's duration is measured with HIP start/stop events that
-its dispatch timestamps itself (spec_verify_profile_next_call) over K further
-calls; its algorithmic bytes (every logit read once) divided by that duration
-give the roofline figure.  The same kernel is also timed launched back to back
-with nothing between its launches (kernel_alone_*), which shows what starting
-it after the previous call's last kernel costs.  The fp64 CPU oracle is timed
-on a bounded sample of the same workload on the host's cores.
+The exact call is one kernel launch (k_single).  Its duration is measured
+with HIP start/stop events that its dispatch timestamps itself
+(spec_verify_profile_next_call) over K further calls; the call's algorithmic
+bytes (every logit read once, plus tokens, uniforms and outputs) divided by
+that duration give the roofline figure.  The streaming kernel alone (k_stream,
+no sweep or draw) is also timed back to back, as the floor under the
+launch's streaming phase.  With the CPU leg on (the default), the outputs of
+every timed workload are checked against the fp64 oracle on the same inputs
+(mismatches, near-tie flags per decision, largest log-prob difference, mean
+accepted length), and the oracle is timed on a bounded sample of the
+benchmark batch on the host's cores.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counters
@@ -41,12 +45,12 @@ HBM_PEAK_GBS = 8000.0
 POWER_ALPHA = 0.5  # exponent of the power-rule measurement
 KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_verify.hip")
 
-# HBM traffic of one exact-mode streaming-kernel dispatch on this workload,
+# HBM traffic of one exact call's kernel dispatch (k_single) on this workload,
 # from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch,
 # averaged over dispatches), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
-# Reported only while the source of the streaming kernel (the file up to its
-# end) is the one the counters were taken on.
+# Reported only while the kernel source file is the one the counters were
+# taken on.
 TRAFFIC = {"source_sha256": "5dfa910647df06454bf3d0f6119dc019a5de2f229c97cfc57911dc455055d2aa",
            "fetch_kib": 44145.4, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
@@ -238,6 +242,7 @@ def time_case(case, steps, warmup, hip, use_graph):
     torch.cuda.synchronize()
     res["eager_ms_per_step"] = hip.elapsed_ms(a, b) / steps
     eager_out = case.snapshot()
+    res["outputs"] = eager_out
     # graph replay of exactly `steps` calls
     if use_graph:
         g = torch.cuda.CUDAGraph()
@@ -260,7 +265,8 @@ def time_case(case, steps, warmup, hip, use_graph):
         res["graph_ms_per_step"] = sorted(runs)[len(runs) // 2]
         res["graph_ms_per_step_runs"] = runs
         # the timed replays must reproduce the eager results bit for bit
-        for o1, o2 in zip(eager_out, case.snapshot()):
+        res["outputs"] = case.snapshot()
+        for o1, o2 in zip(eager_out, res["outputs"]):
             for k in o1:
                 if not torch.equal(o1[k], o2[k]):
                     raise RuntimeError(f"graph replay output {k} differs from the eager call")
@@ -386,22 +392,93 @@ def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, 
         rate = oracle_call_rate(mode, ci)
         out["cpu_oracle_rounds_per_s"] = rate
         out["cpu_oracle_gbs_equivalent"] = rate * nbytes / 1e9
+        out["oracle_check"] = oracle_leg(mode, ci, r["outputs"])
     return out
 
 
-def oracle_call_rate(mode, ci):
+def oracle_call(mode, ci):
+    """The fp64 oracle's call on the inputs a workload times (CPU oracle leg)."""
     import oracle
     if mode == "tree":
-        fn = lambda: oracle.tree(ci.target, ci.node_tok, ci.parents, "bf16",  # noqa: E731
-                                 num_nodes=ci.num_nodes)
-    elif mode == "greedy":
-        fn = lambda: oracle.greedy(ci.target, ci.tokens, "bf16")  # noqa: E731
-    elif mode == "relaxed":
-        fn = lambda: oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", ci.tau,  # noqa: E731
-                                    ci.top_k)
-    else:
-        fn = lambda: oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")  # noqa: E731
-    return oracle_rate(fn, 2.0, 50)
+        return lambda: oracle.tree(ci.target, ci.node_tok, ci.parents, "bf16",  # noqa: E731
+                                   num_nodes=ci.num_nodes)
+    if mode == "greedy":
+        return lambda: oracle.greedy(ci.target, ci.tokens, "bf16")  # noqa: E731
+    if mode == "relaxed":
+        return lambda: oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", ci.tau,  # noqa: E731
+                                      ci.top_k)
+    if mode == "power":
+        return lambda: oracle.power(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16",  # noqa: E731
+                                    POWER_ALPHA)
+    if mode == "sample":
+        return lambda: oracle.sample(ci.draft, ci.uniforms[:, :ci.K].copy(), "bf16")  # noqa: E731
+    return lambda: oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16")  # noqa: E731
+
+
+def oracle_call_rate(mode, ci):
+    return oracle_rate(oracle_call(mode, ci), 2.0, 50)
+
+
+def check_outputs(mode, outputs, orc):
+    """Compares the outputs of the timed calls (every input set holds the same
+    inputs) with the oracle's: a request mismatches when its accepted count,
+    status or emitted tokens differ outside a flagged near-tie (from a flagged
+    position on only the prefix must agree), or its log-probs differ by more
+    than 1e-4.  Returns the counts, the largest log-prob difference and the
+    mean accepted length on both sides."""
+    import numpy as np
+    mism, worst, lens = 0, 0.0, []
+    if mode == "sample":
+        ok = orc.flag == 0
+        for o in outputs:
+            tok, lq = o["tok"].cpu().numpy(), o["lq"].cpu().numpy()
+            st = o["st"].cpu().numpy()
+            bad = ((tok != orc.tokens) & ok) | (st != 0)
+            d = np.abs(lq - orc.logq)[ok]
+            dmax = float(d.max()) if d.size else 0.0
+            worst = max(worst, dmax)
+            mism += int(bad.sum()) + int((d >= 1e-4).sum())
+        rows = orc.flag.size
+        return {"calls_checked": len(outputs), "rows_per_call": rows, "mismatched_rows": mism,
+                "flagged_rows_per_call": int(orc.flag.sum()),
+                "flagged_per_draw": float(orc.flag.sum()) / rows, "max_abs_dlogprob": worst}
+    for o in outputs:
+        tok, ln, st = (o[k].cpu().numpy() for k in ("tok", "ln", "st"))
+        lps = [(o[k].cpu().numpy(), ref) for k, ref in (("tlp", orc.target_logprob),
+                                                       ("blp", orc.behavior_logprob)) if k in o]
+        if mode == "tree":
+            path = o["path"].cpu().numpy()
+        lens.append(ln.astype(np.float64))
+        for b in range(tok.shape[0]):
+            f, n = int(orc.flag[b]), int(orc.accept_len[b])
+            if f >= 0:
+                good = ln[b] >= f and n >= f and (tok[b, :f] == orc.tokens[b, :f]).all()
+                span = f
+            else:
+                good = (ln[b] == n and st[b] == orc.status[b] and
+                        (tok[b, :n + 1] == orc.tokens[b, :n + 1]).all() and (tok[b, n + 1:] == -1).all())
+                if mode == "tree":
+                    good = good and (path[b] == orc.path[b]).all()
+                span = n + 1
+            for got, ref in lps:
+                if span > 0:
+                    d = float(np.abs(got[b, :span] - ref[b, :span]).max())
+                    worst = max(worst, d)
+                    good = good and d < 1e-4
+            mism += 0 if good else 1
+    B = orc.accept_len.size
+    dec = int(orc.decisions.sum())
+    flagged = int((orc.flag >= 0).sum())
+    return {"calls_checked": len(outputs), "requests_per_call": B, "mismatched_requests": mism,
+            "decisions_per_call": dec, "flagged_per_call": flagged,
+            "flagged_per_decision": flagged / max(dec, 1), "max_abs_dlogprob": worst,
+            "mean_accept_len": float(np.mean(lens)),
+            "mean_accept_len_oracle": float(orc.accept_len.mean())}
+
+
+def oracle_leg(mode, ci, outputs):
+    """One oracle call on the timed inputs and the check of the timed outputs."""
+    return check_outputs(mode, outputs, oracle_call(mode, ci)())
 
 
 def sharded_block(lib, ci, G, steps, warmup, hip, torch, dev):
@@ -592,27 +669,17 @@ def markov_block(torch, dev, rounds, with_cpu, use_graph=True):
     return res
 
 
-# The streaming kernel can only depend on source above its end; the section
-# that follows it in the file starts with this line.
-KERNEL_END_MARKER = "// ------------------------------------------------------ sampler stream"
-
-
 def kernel_source_sha256():
-    """SHA-256 of the kernel source up to the end of the streaming kernel
-    (everything it can depend on), or None if the layout has changed."""
+    """SHA-256 of the kernel source file (the counters below belong to it)."""
     import hashlib
-    with open(KERNEL_SRC, encoding="utf-8") as f:
-        src = f.read()
-    i = src.find(KERNEL_END_MARKER)
-    if i < 0 or "void k_stream(" not in src[:i]:
-        return None
-    return hashlib.sha256(src[:i].encode()).hexdigest()
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def traffic_bytes():
-    """HBM bytes per streaming-kernel dispatch from the recorded counters, or
-    None when none are recorded for the current kernel source."""
-    if not TRAFFIC or kernel_source_sha256() is None or TRAFFIC["source_sha256"] != kernel_source_sha256():
+    """HBM bytes per dispatch of the exact call's kernel from the recorded
+    counters, or None when none are recorded for the current kernel source."""
+    if not TRAFFIC or TRAFFIC["source_sha256"] != kernel_source_sha256():
         return None
     return int(TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] * 1024 +
                TRAFFIC["write_kib"] * TRAFFIC["write_scale"] * 1024)
@@ -761,9 +828,10 @@ def main():
     ms = r_ex["graph_ms_per_step"] if use_graph else r_ex["eager_ms_per_step"]
     value = 1000.0 / ms
     k_ms = r_ex["kernel_ms_mean"]
-    # the streaming kernel reads every logit once: its algorithmic bytes
+    # the exact call is one kernel launch: its algorithmic bytes are the call's
+    # (every logit read once, the tokens and uniforms, the outputs)
     stream_bytes = ci.target.nbytes + ci.draft.nbytes
-    achieved = stream_bytes / (k_ms * 1e-3) / 1e9
+    achieved = bytes_exact / (k_ms * 1e-3) / 1e9
     g_ms = r_gr["graph_ms_per_step"] if use_graph else r_gr["eager_ms_per_step"]
     s_ms = r_sa["graph_ms_per_step"] if use_graph else r_sa["eager_ms_per_step"]
     p_ms = r_pw["graph_ms_per_step"] if use_graph else r_pw["eager_ms_per_step"]
@@ -788,17 +856,19 @@ def main():
         "hbm_frac_call": bytes_exact / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(),
-                     "kernel": "k_stream<bf16, exact> (reads every logit once)",
+                     "kernel": "k_single<bf16, exact>: the whole call in one launch (streams every "
+                               "logit once, decides, draws the terminal token)",
                      "kernel_us_mean": k_ms * 1e3, "kernel_us_min": r_ex["kernel_ms_min"] * 1e3,
-                     "algorithmic_bytes_per_launch": stream_bytes,
+                     "algorithmic_bytes_per_launch": bytes_exact,
+                     "logit_bytes_per_launch": stream_bytes,
                      "rest_of_call_us_mean": r_ex["rest_ms_mean"] * 1e3,
                      "frac_of_read_ceiling": achieved / ceiling["gbs"],
-                     "kernel_alone_us_mean": alone_ms * 1e3,
-                     "kernel_alone_frac": stream_bytes / (alone_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "kernel_alone_note": "the same kernel launched back to back, nothing between "
-                                          "its launches; achieved and frac above are inside the "
-                                          "call, after the previous call's sampling kernel",
-                     "call_gbs_on_kernel_time": bytes_exact / ((k_ms + r_ex["rest_ms_mean"]) * 1e-3) / 1e9},
+                     "stream_alone_us_mean": alone_ms * 1e3,
+                     "stream_alone_frac": stream_bytes / (alone_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "stream_alone_note": "k_stream alone (the same 16 KiB tile streaming with no "
+                                          "sweep or draw, as the one-shard statistics step "
+                                          "launches it), back to back: the floor under the "
+                                          "single launch's streaming phase"},
         "read_ceiling": ceiling,
         "graph_ms_per_step_runs": r_ex.get("graph_ms_per_step_runs"),
         "eager": {"rounds_per_s": 1000.0 / r_ex["eager_ms_per_step"],
@@ -832,6 +902,18 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
+        progress("oracle checks of the timed outputs start")
+        checks = {"exact_b32_k5": oracle_leg("exact", ci, r_ex["outputs"]),
+                  "greedy_b32_k5": oracle_leg("greedy", ci, r_gr["outputs"]),
+                  "power_b32_k5": oracle_leg("power", ci, r_pw["outputs"]),
+                  "draft_sampler_b32_k5_draft_rows": oracle_leg("sample", ci, r_sa["outputs"])}
+        for k, v in (others or {}).items():
+            if isinstance(v, dict) and "oracle_check" in v:
+                checks[k] = v["oracle_check"]
+        out["timed_outputs_vs_oracle"] = checks
+        bad = {k: v.get("mismatched_requests", v.get("mismatched_rows")) for k, v in checks.items()}
+        if any(bad.values()):
+            print(f"bench: timed outputs differ from the oracle: {bad}", file=sys.stderr, flush=True)
         progress("CPU baseline starts")
         out["cpu_baseline"] = cpu_baseline(ci, args.cpu_seconds)
     print(json.dumps(out), flush=True)
