@@ -61,6 +61,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <limits.h>
 #include <math.h>
 
@@ -142,7 +143,7 @@ struct alignas(16) ChunkSums {
 
 struct Layout {
     size_t seg, dec, sums, xv;  // records, decisions, chunk sums, drafted-token logits
-    size_t frec, fsums, ticket;  // single-launch calls: published words and tickets
+    size_t frec, fsums;  // single-launch calls: published words
     size_t total;
 };
 
@@ -150,7 +151,7 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // [tile records B*R*tpr][decisions B][chunk sums B*C2][drafted-token logits
 // B*K*2, sized B*R*2][published tile records B*R*tpr, two words each]
-// [published chunk records B*C2, eleven words each][tickets B].  The workspace is
+// [published chunk records B*C2, eleven words each].  The workspace is
 // zero when a call starts (zero-filled once by its owner) and every call
 // leaves every byte it wrote zero again, whatever the rule or shape: the
 // single-launch calls read zero as "not published yet".
@@ -162,8 +163,7 @@ inline Layout make_layout(int B, int R, int tpr, int C2) {
     L.xv = align_up(L.sums + (size_t)B * C2 * sizeof(ChunkSums), 256);
     L.frec = align_up(L.xv + (size_t)B * R * 8, 256);
     L.fsums = align_up(L.frec + (size_t)B * R * tpr * 16, 256);
-    L.ticket = align_up(L.fsums + (size_t)B * C2 * (3 + 2 * (kChunk / 1024)) * 8, 256);
-    L.total = align_up(L.ticket + (size_t)B * 4, 256);
+    L.total = align_up(L.fsums + (size_t)B * C2 * (3 + 2 * (kChunk / 1024)) * 8, 256);
     return L;
 }
 
@@ -371,32 +371,40 @@ __device__ inline void load_run(__amdgpu_buffer_rsrc_t r, int e0, int V, bool ve
 }
 
 // ------------------------------------------------------------ fp64 exp(x<=0)
-// Reduction x = k ln2/256 + r with k = rint(x * 256/ln2) and |r| <= ln2/512,
-// a degree-4 Taylor polynomial (truncation error r^5/120 < 4e-17 relative)
-// and 2^(k/256) = 2^(k>>8) * tab[k & 255], the power of two applied by
-// v_ldexp.  r uses the double nearest ln2/256 in one fma: its error,
-// |k| * 2^-61, stays below 3e-15 relative for x >= -30 and below 2e-13 at the
+// Reduction x = k ln2/512 + r with k = rint(x * 512/ln2) and |r| <= ln2/1024,
+// a degree-3 Taylor polynomial (truncation error r^4/24 < 9e-15 relative)
+// and 2^(k/512) = 2^(k>>9) * tab[k & 511], the power of two applied by
+// v_ldexp.  k is rounded by adding 1.5 * 2^52 in the fma that scales x (the
+// integer then sits in the low bits of the sum; one subtraction recovers it
+// as a double).  r uses the double nearest ln2/512 in one fma: its error,
+// |k| * 2^-63, stays below 3e-15 relative for x >= -30 and below 1e-13 at the
 // clamp.  x is first clamped to -1000 (which also maps -inf to -1000), where
 // v_ldexp underflows to exactly 0.  Branch-free; every op is full rate.
-constexpr int kExpTab = 256;
-constexpr double kInvLn2x256 = 369.3299304675746;       // 256 / ln 2
-constexpr double kLn2o256 = 0.0027076061740622863;      // ln 2 / 256
+constexpr int kExpTab = 512;
+constexpr double kInvLn2x512 = 0x1.71547652b82fep+9;  // 512 / ln 2
+constexpr double kLn2o512 = 0x1.62e42fefa39efp-10;    // ln 2 / 512
+constexpr double kRoundMagic = 0x1.8p52;              // 1.5 * 2^52
 
 __device__ inline double exp_nonpos(double x, const double* tab) {
     const double xc = fmax(x, -1000.0);
-    const double kd = __builtin_rint(xc * kInvLn2x256);
-    const int k = (int)kd;
-    const double r = fma(-kd, kLn2o256, xc);
-    double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
-    p = fma(p, r, 0.5);
+    const double t = fma(xc, kInvLn2x512, kRoundMagic);  // 1.5 * 2^52 + k, |k| < 2^20
+    const int k = (int)(uint32_t)__double_as_longlong(t);
+    const double kd = t - kRoundMagic;
+    const double r = fma(-kd, kLn2o512, xc);
+    double p = fma(r, 1.0 / 6.0, 0.5);
     p = fma(p, r, 1.0);
     p = fma(p, r, 1.0);
-    return ldexp(tab[k & (kExpTab - 1)] * p, k >> 8);
+    return ldexp(tab[k & (kExpTab - 1)] * p, k >> 9);
 }
 
-// tab[j] = 2^(j/256); needs kExpTab threads
+// 2^(j/512), each the double nearest the exact value
+__constant__ const double kExp2Tab[kExpTab] = {
+#include "exp2_table.inc"
+};
+
+// the workgroup's copy of kExp2Tab in LDS (the fp64 exp reads it per token)
 __device__ inline void fill_exp_table(double* tab) {
-    if (threadIdx.x < kExpTab) tab[threadIdx.x] = exp2((double)threadIdx.x / kExpTab);
+    for (int j = threadIdx.x; j < kExpTab; j += blockDim.x) tab[j] = kExp2Tab[j];
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -583,10 +591,9 @@ struct Args {
     float* xv_out;         // this shard's drafted-token logits ([B][K][2])
     size_t sums_slot;      // bytes between the shard slots of chunk sums
     int32_t* out_owner;    // [B] shard holding the terminal draw, or null
-    // single-launch calls: published words and per-request tickets
+    // single-launch calls: published words
     uint64_t* frec;     // [B][R][tpr] tile records, two words each
     uint64_t* fsums;    // [B][C2] chunk records, eleven words each
-    uint32_t* ticket;   // [B] sweep workgroups done
     int nstream;        // workgroups of the launch that stream tiles
 };
 
@@ -1089,23 +1096,28 @@ __device__ bool fold_rows_published(const Args& a, int b, int nrows, RowStats& r
     fold_batches<MODE, SUM, NW>(nrows, rs, tab, [&](int k0, Seg (&sg)[kFoldBatch]) {
         uint64_t w0[kFoldBatch], w1[kFoldBatch];
         const uint64_t* src[kFoldBatch];
+        bool need[kFoldBatch];
 #pragma unroll
         for (int j = 0; j < kFoldBatch; ++j) {
             const int r = wave + NW * (k0 + j);
-            const bool need = r < nrows && lane < a.tpr;
-            src[j] = need ? a.frec + 2 * (((size_t)b * a.R + r) * a.tpr + lane) : nullptr;
-            w0[j] = w1[j] = need ? 0ull : 1ull;
+            need[j] = r < nrows && lane < a.tpr;
+            // a batch row past the last reads the last row's record and ignores it
+            src[j] = a.frec + 2 * (((size_t)b * a.R + min(r, nrows - 1)) * a.tpr + lane);
+            w0[j] = w1[j] = 0ull;
         }
         for (int it = 0;; ++it) {
-            bool missing = false;
+            // lanes past the row's tiles read nothing; the others read every
+            // word each round, so the loads of a round are in flight together
+            if (lane < a.tpr) {
 #pragma unroll
-            for (int j = 0; j < kFoldBatch; ++j) {
-                if (w0[j] == 0ull || w1[j] == 0ull) {
+                for (int j = 0; j < kFoldBatch; ++j) {
                     w0[j] = load_word(src[j]);
                     w1[j] = load_word(src[j] + 1);
-                    missing |= (w0[j] == 0ull || w1[j] == 0ull);
                 }
             }
+            bool missing = false;
+#pragma unroll
+            for (int j = 0; j < kFoldBatch; ++j) missing |= need[j] && (w0[j] == 0ull || w1[j] == 0ull);
             if (__ballot(missing) == 0ull) break;
             if (it == kSpinLimit) {
                 ok = false;
@@ -1115,7 +1127,7 @@ __device__ bool fold_rows_published(const Args& a, int b, int nrows, RowStats& r
         }
 #pragma unroll
         for (int j = 0; j < kFoldBatch; ++j)
-            sg[j] = src[j] ? decode_record(w0[j], w1[j]) : neutral_record(ARGMAX);
+            sg[j] = need[j] ? decode_record(w0[j], w1[j]) : neutral_record(ARGMAX);
     });
     return ok;
 }
@@ -1807,16 +1819,15 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
 // The exact, relaxed and power rules run as one launch per call, with no
 // kernel boundary between the stream and the terminal draw.  The launch's
 // first nstream workgroups stream tiles (stream_tile, records published).
-// Behind them, one sweep workgroup per (request, 4096-token chunk) -- these
-// are dispatched after every streaming workgroup, so while the last tiles
-// stream, the requests whose tiles are done already fold and sweep -- waits
-// for its request's records, folds them and takes the decision (the same
-// fold and decision in every workgroup of the request), writes the accepted
+// Behind them, one sweep workgroup per (request, 4096-token chunk) waits for
+// its request's records, folds them and takes the decision (the same fold
+// and decision in every workgroup of the request), writes the accepted
 // prefix (chunk 0), sums its chunk of the terminal row(s) in fp64 and
-// publishes the sums.  The request's last sweep workgroup to finish (a
-// ticket counts them) waits for all of the request's chunk sums, draws the
-// terminal token (draw_terminal) and zeroes the request's published words
-// and ticket for the next call.
+// publishes the sums.  The workgroup of the request's last chunk then waits
+// for all of the request's chunk sums, draws the terminal token
+// (draw_terminal) and zeroes the request's published words for the next
+// call: every other workgroup of the request has read the records before it
+// published its sums.
 
 // Sub-chunks: a sweep workgroup publishes its chunk's masses per 1024-token
 // sub-chunk, so the draw rescans 1024 tokens (four per thread) instead of a
@@ -1855,17 +1866,16 @@ __device__ inline double draw_weight(bool res, float l, float d, double Mt, doub
     return fmax(fma(ea, iS, -(exp_nonpos(xb, tab) * iSq)), 0.0);
 }
 
-// Zeroes request b's published words and ticket (every thread; after all of
+// Zeroes request b's published words (every thread; after all of
 // the workgroup's reads of them).
 __device__ inline void clear_published(const Args& a, int b) {
     uint64_t* r = a.frec + (size_t)b * a.R * a.tpr * 2;
     for (int i = threadIdx.x; i < a.R * a.tpr * 2; i += blockDim.x) store_word(r + i, 0ull);
     uint64_t* m = a.fsums + (size_t)b * a.C2 * kChunkWords;
     for (int i = threadIdx.x; i < a.C2 * kChunkWords; i += blockDim.x) store_word(m + i, 0ull);
-    if (threadIdx.x == 0) __hip_atomic_store(a.ticket + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The terminal draw of request b, by the request's last sweep workgroup.
+// The terminal draw of request b, by the sweep workgroup of its last chunk.
 // Wave 0 waits for the C2 published chunk records (lane = chunk), forms S,
 // Sq, the exact p > q threshold and the sub-chunk masses, recomputes the
 // masses of chunks the streamed threshold may have classified otherwise,
@@ -1966,25 +1976,36 @@ __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& c
         bool ok = true;
         uint64_t w[kChunkWords];
 #pragma unroll
-        for (int i = 0; i < kChunkWords; ++i) w[i] = lane < a.C2 ? 0ull : kTop;  // absent chunks: zero sums
-        if (lane < a.C2) {
-            const uint64_t* src = a.fsums + ((size_t)b * a.C2 + lane) * kChunkWords;
-            for (int it = 0;; ++it) {
-                bool missing = false;
+        for (int i = 0; i < kChunkWords; ++i) w[i] = kTop;  // lanes past the last chunk: zero sums
+        const bool have = lane < a.C2;
+        const uint64_t* src = a.fsums + ((size_t)b * a.C2 + (have ? lane : 0)) * kChunkWords;
+        // the other chunks' workgroups may still be summing: first wait for
+        // every chunk's first word (one load per chunk a round), then read
+        // all words (every word each round, the round's loads in flight
+        // together) until none is missing
+        for (int it = 0, all = 0;; ++it) {
+            bool missing = false;
+            if (have) {
+                if (all) {
 #pragma unroll
-                for (int i = 0; i < kChunkWords; ++i) {
-                    if (w[i] == 0ull) {
-                        w[i] = load_word(src + i);
-                        missing |= w[i] == 0ull;
-                    }
+                    for (int i = 0; i < kChunkWords; ++i) w[i] = load_word(src + i);
+#pragma unroll
+                    for (int i = 0; i < kChunkWords; ++i) missing |= w[i] == 0ull;
+                } else {
+                    missing = load_word(src) == 0ull;
                 }
-                if (!missing) break;
-                if (it == kSpinLimit) {
-                    ok = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
             }
+            const bool none = __ballot(missing) == 0ull;
+            if (none && all) break;
+            if (none) {
+                all = 1;
+                continue;
+            }
+            if (it == kSpinLimit) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
         }
         const bool all_ok = __ballot(!ok) == 0ull;
         const double sa = dec_nonneg(w[0]), sb = dec_nonneg(w[1]);
@@ -2179,7 +2200,7 @@ __device__ void sweep_role(const Args& a, const int idx) {
     __shared__ RowStats rs;
     __shared__ ChainDecision cd;
     __shared__ double red[kWaves][3 + 2 * NV];
-    __shared__ int s_ok, s_last;
+    __shared__ int s_ok;
     fill_exp_table(tab);
     if (tid == 0) s_ok = 1;
     ChainVals cv;
@@ -2187,8 +2208,20 @@ __device__ void sweep_role(const Args& a, const int idx) {
         chain_load_tokens<MODE>(a, b, cv);
         chain_load_inputs<T, MODE>(a, b, cv);
     }
-    __syncthreads();  // the exp table and s_ok
-    if (!fold_rows_published<MODE, true, kWaves>(a, b, a.R, rs, tab)) s_ok = 0;
+    // One lane waits for the request's last tile record (the last of its
+    // tiles to be taken) before the waves read all of them.
+    if (tid == 0) {
+        const uint64_t* hint = a.frec + 2 * (((size_t)b * a.R + a.R - 1) * a.tpr + a.tpr - 1);
+        for (int it = 0; load_word(hint) == 0ull; ++it) {
+            if (it == kSpinLimit) {
+                s_ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+    __syncthreads();  // the exp table, s_ok
+    if (s_ok && !fold_rows_published<MODE, true, kWaves>(a, b, a.R, rs, tab)) s_ok = 0;
     __syncthreads();
     if (!s_ok) {  // a record never arrived: report, leave the words as they are
         if (tid == 0) a.out_status[b] = 2;
@@ -2282,27 +2315,53 @@ __device__ void sweep_role(const Args& a, const int idx) {
             }
         uint64_t* dst = a.fsums + ((size_t)b * a.C2 + c) * kChunkWords;
         for (int i = 0; i < kChunkWords; ++i) store_word(dst + i, enc_nonneg(v[i]));
-        // the request's last sweep workgroup draws; the others are done
-        const uint32_t done = __hip_atomic_fetch_add(a.ticket + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = done == (uint32_t)(a.C2 - 1);
     }
-    __syncthreads();
-    if (s_last) draw_terminal<T, MODE>(a, b, cd, rs, tab);
+    // the workgroup of the request's last chunk (the last of its sweep
+    // workgroups to start) draws; the others are done
+    if (c == a.C2 - 1) draw_terminal<T, MODE>(a, b, cd, rs, tab);
 }
 
-// The single launch of an exact, relaxed or power call.
+// The single launch of an exact, relaxed or power call.  Its first nstream
+// workgroups stream: workgroup p takes tiles p, p + nstream, ..., so the
+// tiles complete about in index order, request by request, with about
+// nstream tiles in flight (enough to keep HBM busy; few enough that the
+// other workgroups' loads do not queue behind many microseconds of them).
+// The sweep workgroups follow, request by request; they start while the
+// stream runs, and each waits only for its own request's records (and the
+// drawing workgroup, the last of its request to start, for the sums of the
+// others).
 template <typename T, int MODE, bool VECP>
 __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_single(const Args a) {
-    const unsigned blk = blockIdx.x;
-    if (blk < (unsigned)a.nstream) {
-        stream_tile<T, MODE, true, VECP, false, false, kTileVecs, true>(a, blk);
+    const unsigned P = (unsigned)a.nstream, ntiles = (unsigned)(a.B * a.R * a.tpr);
+    if (blockIdx.x < P) {
+        for (unsigned t = blockIdx.x; t < ntiles; t += P)
+            stream_tile<T, MODE, true, VECP, false, false, kTileVecs, true>(a, t);
         return;
     }
-    sweep_role<T, MODE>(a, (int)(blk - (unsigned)a.nstream));
+    sweep_role<T, MODE>(a, (int)(blockIdx.x - P));
 }
 
 // ------------------------------------------------------------------- host
 inline int esize(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
+
+// Streaming workgroups of a single launch: kStreamPerCu per compute unit of
+// the current device (the count is looked up once per device; 256 if the
+// lookup fails).
+constexpr int kStreamPerCu = 8;
+constexpr int kMaxCuCache = 64;
+std::atomic<int> g_cus[kMaxCuCache];
+inline int stream_workgroups() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    if (dev >= 0 && dev < kMaxCuCache) cus = g_cus[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        if (dev >= 0 && dev < kMaxCuCache) g_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    return kStreamPerCu * cus;
+}
 inline int tile_elems(spec_dtype dt) { return kTileBytes / esize(dt); }
 inline int tpr_of(spec_dtype dt, int V) { return (V + tile_elems(dt) - 1) / tile_elems(dt); }
 constexpr int kSmallTileElems = kThreads * kSmallTileVecs * 8;  // bf16 elements of an 8 KiB tile
@@ -2427,8 +2486,7 @@ spec_status launch_single(Args a, spec_dtype dt, hipStream_t st) {
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
     a.frec = reinterpret_cast<uint64_t*>(a.ws + lay.frec);
     a.fsums = reinterpret_cast<uint64_t*>(a.ws + lay.fsums);
-    a.ticket = reinterpret_cast<uint32_t*>(a.ws + lay.ticket);
-    a.nstream = a.B * a.R * a.tpr;
+    a.nstream = min(a.B * a.R * a.tpr, stream_workgroups());
     const dim3 grid((unsigned)a.nstream + (unsigned)a.B * (unsigned)a.C2), block(kThreads);
     hipEvent_t ev[3];
     take_prof(ev);
