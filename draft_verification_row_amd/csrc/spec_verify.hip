@@ -397,6 +397,30 @@ __device__ inline double exp_nonpos(double x, const double* tab) {
     return ldexp(tab[k & (kExpTab - 1)] * p, k >> 9);
 }
 
+// exp_nonpos of N values at once: the reductions and polynomials first, then
+// all N table reads, then the scalings, so the reads are in flight together
+// instead of one LDS round trip per value.  Bit-identical to exp_nonpos.
+template <int N>
+__device__ inline void exp_nonpos_n(const double (&x)[N], double (&e)[N], const double* tab) {
+    double p[N], tv[N];
+    int k[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const double xc = fmax(x[i], -1000.0);
+        const double t = fma(xc, kInvLn2x512, kRoundMagic);
+        k[i] = (int)(uint32_t)__double_as_longlong(t);
+        const double kd = t - kRoundMagic;
+        const double r = fma(-kd, kLn2o512, xc);
+        double q = fma(r, 1.0 / 6.0, 0.5);
+        q = fma(q, r, 1.0);
+        p[i] = fma(q, r, 1.0);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) tv[i] = tab[k[i] & (kExpTab - 1)];
+#pragma unroll
+    for (int i = 0; i < N; ++i) e[i] = ldexp(tv[i] * p[i], k[i] >> 9);
+}
+
 // 2^(j/512), each the double nearest the exact value
 __constant__ const double kExp2Tab[kExpTab] = {
 #include "exp2_table.inc"
@@ -868,11 +892,13 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
 // ------------------------------------------------------ sampler stream
 // The draft sampler draws from every row it streams, so the fp64 chunk sums
 // its inverse CDF needs are taken in the one pass: one workgroup per 16 KiB
-// tile finds the tile max M, then sums exp(l - M) in fp64 (the Cody-Waite exp
+// tile finds the tile max M, then sums exp(l - M) in fp64 (the table exp
 // above) over each 4096-token chunk of the tile.  Each chunk's record is
-// {sum, M}; the sampling kernel rescales them to the row max.
+// {sum, M}; the sampling kernel rescales them to the row max.  One fp64 exp
+// per token makes the pass VALU-bound, so it keeps eight waves per SIMD and
+// takes the exps four at a time, their table reads in flight together.
 template <typename T, bool VECP>
-__global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_stream_rows(const Args a) {
+__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream_rows(const Args a) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int TILE = kThreads * kTileVecs * VEC;
     constexpr int CPT = TILE / kChunk;  // chunks per tile: 2 (bf16) or 1 (fp32)
@@ -917,7 +943,14 @@ __global__ __launch_bounds__(kThreads, kPass2WavesPerSimd) void k_stream_rows(co
             float v[VEC];
             Elem<T>::unpack(q[k], v);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[k / (kTileVecs / CPT)] += exp_nonpos((double)v[i] - (double)M, tab);
+            for (int i0 = 0; i0 < VEC; i0 += 4) {
+                double x[4], e[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = (double)v[i0 + i] - (double)M;
+                exp_nonpos_n<4>(x, e, tab);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[k / (kTileVecs / CPT)] += e[i];
+            }
         }
     }
 #pragma unroll
@@ -2344,13 +2377,13 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_single(const 
 // ------------------------------------------------------------------- host
 inline int esize(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
 
-// Streaming workgroups of a single launch: kStreamPerCu per compute unit of
-// the current device (the count is looked up once per device; 256 if the
-// lookup fails).
+// Compute units of the current device, looked up once per device (256 if the
+// lookup fails); a single launch streams with kStreamPerCu workgroups per
+// compute unit.
 constexpr int kStreamPerCu = 8;
 constexpr int kMaxCuCache = 64;
 std::atomic<int> g_cus[kMaxCuCache];
-inline int stream_workgroups() {
+inline int compute_units() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = -1;
     if (dev >= 0 && dev < kMaxCuCache) cus = g_cus[dev].load(std::memory_order_relaxed);
@@ -2360,8 +2393,9 @@ inline int stream_workgroups() {
             cus = 256;
         if (dev >= 0 && dev < kMaxCuCache) g_cus[dev].store(cus, std::memory_order_relaxed);
     }
-    return kStreamPerCu * cus;
+    return cus;
 }
+inline int stream_workgroups() { return kStreamPerCu * compute_units(); }
 inline int tile_elems(spec_dtype dt) { return kTileBytes / esize(dt); }
 inline int tpr_of(spec_dtype dt, int V) { return (V + tile_elems(dt) - 1) / tile_elems(dt); }
 constexpr int kSmallTileElems = kThreads * kSmallTileVecs * 8;  // bf16 elements of an 8 KiB tile
