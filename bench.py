@@ -51,8 +51,8 @@ KERNEL_SRC = os.path.join(ROOT, "draft_verification_row_amd", "csrc", "spec_veri
 # plain 1 GiB device copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Reported only while the kernel source file is the one the counters were
 # taken on.
-TRAFFIC = {"source_sha256": "5dfa910647df06454bf3d0f6119dc019a5de2f229c97cfc57911dc455055d2aa",
-           "fetch_kib": 44145.4, "write_kib": 186.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"source_sha256": "ffa4c0dbccfe24b934aa4fd864704c1aa312f6368f5e72ed27f58b98aa7cb827",
+           "fetch_kib": 51228.1, "write_kib": 884.5, "fetch_scale": 2.0, "write_scale": 1.0}
 
 MALL_BYTES = 256 * 1024 * 1024
 RUNS = 3  # timed replays of the captured steps; the median is reported
