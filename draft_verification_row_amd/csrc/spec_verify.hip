@@ -14,50 +14,38 @@
 //   * greedy tree verification of an EAGLE-style draft tree (nanospec
 //     README, intro and benchmark section).
 //
-// How it is computed here (no kernel design comes from the pages): two or
-// three kernels per call on the caller's stream.  Vocabulary-sharded calls
-// run the same kernels one step at a time (spec_shard_*).
+// How it is computed here (no kernel design comes from the pages).  Every
+// logit is read once, by streaming tiles: one workgroup of 256 threads
+// reduces a 16 KB tile (8 KB for the greedy rule without log-probs) of one
+// row to its max (with the lowest index among equal maxima for the greedy
+// rules, and the rank count #{t : l_t > l_x} for the relaxed rule) and, where
+// a normalizer is needed, the sum of exp(l - tile max): v_exp_f32 per logit,
+// fp32 over a thread's terms, fp64 beyond.  Decisions and terminal draws are
+// taken on the device in fp64, with a table-driven fp64 exp.
 //
-//   k_stream  one workgroup per (logit row, 16 KB tile; 8 KB for the greedy
-//             rule without log-probs).  Each thread issues its 16-byte loads
-//             at once; the workgroup reduces the tile max (with the lowest
-//             index among equal maxima for the greedy rules, and the rank
-//             count #{t : l_t > l_x} for the relaxed rule) and, where a
-//             normalizer is needed, the sum of exp(l - tile max): v_exp_f32
-//             per logit, fp32 over a thread's terms, fp64 beyond.  One
-//             16-byte record per tile goes to the workspace.  This kernel
-//             reads every logit once and carries all of the call's HBM
-//             traffic.
+//   exact, relaxed, power: one launch (k_single).  Its first workgroups
+//             stream the tiles in a grid-stride loop and publish each tile's
+//             record; one sweep workgroup per (request, 4096-token chunk)
+//             waits for its request's records, folds them, decides, sums its
+//             chunk of the terminal row(s) in fp64 and publishes the sums;
+//             the request's last-chunk workgroup draws the terminal token.
 //
-//   k_decide  (greedy, tree) one workgroup per request.  A wave folds the
-//             tile records of a row, one record per lane: max and argmax by
-//             cross-lane steps, the tile sums rescaled to the row max in
-//             fp64.  Wave 0 then runs the acceptance tests (one lane per
-//             draft or tree node) and writes the outputs.
+//   greedy, tree: k_stream (one workgroup per tile, one record each), then
+//             k_decide (one workgroup per request: fold the records, run the
+//             tests one lane per draft or tree node, write the outputs).
 //
-//   k_sweep   (exact, relaxed) one workgroup per (request, 4096-token
-//             chunk).  Every workgroup of a request folds the records and
-//             takes the decision itself (same data, same order, same result);
-//             chunk 0 writes the accepted prefix.  Each workgroup then sums its
-//             chunk of the row(s) the terminal token is drawn from, in fp64
-//             with an explicit Cody-Waite exp: exp(l - Mt) and exp(d - Md),
-//             over the chunk and over its tokens with p > q.
+//   draft sampler: one launch (k_sample_rows): the tiles publish fp64 chunk
+//             sums, and one workgroup per row draws.
 //
-//   k_sample  (exact, relaxed) one workgroup per request.  Wave 0 turns the
-//             chunk sums into chunk masses of relu(p - q) (or of p), scans
-//             them and finds the chunk holding u_K * Z; the workgroup rescans
-//             that chunk with a block scan and writes the terminal token and
-//             its log-probs.
+//   vocabulary shards (spec_shard_*): k_stream per shard, then after the
+//             caller's exchanges k_decide, or k_sweep and k_sample.
 //
-//   The draft sampler (one draw per row) streams with k_stream_rows, which
-//   leaves the fp64 chunk sums in the one pass, then runs k_sample.
-//
-// Every reduction runs in a fixed order, so results are bitwise
-// reproducible.  No atomics are used: data passes between workgroups only
-// across kernel boundaries, which make the previous kernel's writes visible
-// to the next one on every XCD (their L2 caches are not coherent with each
-// other, and a fence inside a kernel would write back and invalidate a whole
-// L2).
+// Within a launch, workgroups hand data to each other through words in the
+// workspace written and read with relaxed agent-scope atomics, which are
+// coherent across the XCDs' L2 caches without a fence.  A published word is
+// never zero, so zero means "not yet"; a waiting workgroup only waits on
+// workgroups that start before it, and each wait is bounded.  Every
+// reduction runs in a fixed order, so results are bitwise reproducible.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -104,7 +92,7 @@ static_assert(kMaxTiles <= 64, "a row's tile records must fit one wave");
 constexpr int kMaxC2 = (SPEC_MAX_V + kChunk - 1) / kChunk;
 static_assert(kMaxC2 <= 64, "a row's pass-2 chunks must fit one wave");
 
-enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3, kPower = 4, kSample = 5 };
+enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3, kPower = 4 };
 
 // Rules that stream the draft rows and test p/q.
 constexpr bool uses_draft(int mode) { return mode == kExact || mode == kPower; }
@@ -894,11 +882,14 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream(const 
 // its inverse CDF needs are taken in the one pass: one workgroup per 16 KiB
 // tile finds the tile max M, then sums exp(l - M) in fp64 (the table exp
 // above) over each 4096-token chunk of the tile.  Each chunk's record is
-// {sum, M}; the sampling kernel rescales them to the row max.  One fp64 exp
+// {sum, M}, published for the row's drawing workgroup, which rescales them to
+// the row max.  One fp64 exp
 // per token makes the pass VALU-bound, so it keeps eight waves per SIMD and
 // takes the exps four at a time, their table reads in flight together.
+constexpr int kRowWords = 2;  // published words per chunk of a sampled row
+
 template <typename T, bool VECP>
-__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream_rows(const Args a) {
+__device__ __forceinline__ void rows_tile(const Args& a, const unsigned blk) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int TILE = kThreads * kTileVecs * VEC;
     constexpr int CPT = TILE / kChunk;  // chunks per tile: 2 (bf16) or 1 (fp32)
@@ -910,8 +901,8 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream_rows(c
     __shared__ double s_s[kWaves][CPT];
     fill_exp_table(tab);
 
-    const int g = uniform((int)(blockIdx.x / (unsigned)a.tpr));
-    const int c = (int)blockIdx.x - g * a.tpr;
+    const int g = uniform((int)(blk / (unsigned)a.tpr));
+    const int c = (int)blk - g * a.tpr;
     int vec, act;
     const T* row = call_row<T, kRelaxed>(a, g, vec, act);
     u32x4 q[kTileVecs];
@@ -962,13 +953,10 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_stream_rows(c
     if ((int)threadIdx.x < CPT) {
         const int h = threadIdx.x, ch = c * CPT + h;
         if (ch < a.C2) {
-            ChunkSums cs;
-            cs.sa = ((s_s[0][h] + s_s[1][h]) + s_s[2][h]) + s_s[3][h];
-            cs.sb = (double)M;
-            cs.pa = cs.pb = 0.0;
-            cs.dmin = INFINITY;
-            cs.pad = 0.0;
-            a.sums[(size_t)g * a.C2 + ch] = cs;
+            // published as two never-zero words: the sum (>= +0) and the tile max
+            uint64_t* w = a.fsums + ((size_t)g * a.C2 + ch) * kRowWords;
+            store_word(w, enc_nonneg(((s_s[0][h] + s_s[1][h]) + s_s[2][h]) + s_s[3][h]));
+            store_word(w + 1, kTop | (uint64_t)__float_as_uint(M));
         }
     }
 }
@@ -1596,16 +1584,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
     __shared__ int s_pick[kSampleWaves][3];
     fill_exp_table(tab);
 
-    // The draft sampler (kSample) has no decision: it draws from its only row,
-    // whose max and chunk masses it takes from the chunk records.
-    constexpr bool ROWS = (MODE == kSample);
-    __shared__ double s_Mt;
-    Decision dc = {};
-    if (!ROWS) dc = a.dec[b];
+    const Decision dc = a.dec[b];
     const int n = dc.n;
     const bool residual = EXACT && dc.residual;
     const double Md = dc.Md, cls = dc.cls;
-    if (ROWS) __syncthreads();  // the exp table, used by wave 0 below
     // Chunk masses of a residual draw whose classification must be redone
     // (see below), the exact threshold, and the chunks concerned.
     __shared__ double s_W[64];
@@ -1652,15 +1634,6 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
                       (size_t)b * a.C2 + (lane - sl * a.C2);
             }
             cs = *src;
-        }
-        if (ROWS) {
-            // the chunk records are read: zero them for the next call
-            if (lane < nchunk) a.sums[(size_t)b * a.C2 + lane] = ChunkSums{0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-            // chunk records {sum of exp(l - m), m}: rescale to the row max
-            const float mc = lane < nchunk ? (float)cs.sb : -INFINITY;
-            const float Mr = wave_max(mc);
-            cs.sa = mc > -INFINITY ? cs.sa * exp_nonpos((double)mc - (double)Mr, tab) : 0.0;
-            if (lane == 0) s_Mt = (double)Mr;
         }
         S = wave_sum(cs.sa);
         const double Sq = residual ? wave_sum(cs.sb) : 1.0;
@@ -1725,8 +1698,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
         __syncthreads();
     }
 
-    const double Mt = ROWS ? s_Mt : dc.Mt;
-    if (ROWS && t == 0) a.out_status[b] = 0;
+    const double Mt = dc.Mt;
     int cstar = s_cstar;
     if (SHARD) {
         const int owner = cstar / a.C2;
@@ -2374,6 +2346,181 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_single(const 
     sweep_role<T, MODE>(a, (int)(blockIdx.x - P));
 }
 
+// The draw of sampled row g, by the row's drawing workgroup of the sampler's
+// single launch.  Wave 0 waits for the row's chunk words (lane = chunk),
+// rescales each chunk sum to the row max (one fp64 exp per lane), scans the
+// chunks and picks the one holding u * Z; it clears the words it read.  The
+// workgroup rescans that chunk, sixteen consecutive tokens per thread, with a
+// block scan whose exclusive prefixes are the previous thread's inclusive
+// ones bit for bit, and writes the first crossing and its log-prob.
+template <typename T>
+__device__ void draw_row(const Args& a, const int g) {
+    constexpr int RUN = kChunk / kThreads;  // 16 tokens per thread
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
+    __shared__ double tab[kExpTab];
+    __shared__ int s_cstar, s_ok;
+    __shared__ double s_base, s_target, s_M, s_lnZ;
+    __shared__ double s_wtot[kWaves];
+    __shared__ int s_pick[kWaves][3];
+    fill_exp_table(tab);
+    if (t == 0) s_ok = 1;
+    __syncthreads();  // the exp table
+    if (wave == 0) {
+        const bool have = lane < a.C2;
+        uint64_t* src = a.fsums + ((size_t)g * a.C2 + (have ? lane : 0)) * kRowWords;
+        uint64_t w0 = 0ull, w1 = 0ull;
+        bool ok = true;
+        for (int it = 0;; ++it) {
+            if (have) {  // both words each round, in flight together
+                w0 = load_word(src);
+                w1 = load_word(src + 1);
+            }
+            if (__ballot(have && (w0 == 0ull || w1 == 0ull)) == 0ull) break;
+            if (it == kSpinLimit) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+        }
+        if (ok) {
+            if (have) {  // read: zero them for the next call
+                store_word(src, 0ull);
+                store_word(src + 1, 0ull);
+            }
+            const float mc = have ? __uint_as_float((uint32_t)w1) : -INFINITY;
+            const float Mr = wave_max(mc);
+            // chunk record {sum of exp(l - m), m}: rescaled to the row max
+            const double W = mc > -INFINITY ? dec_nonneg(w0) * exp_nonpos((double)mc - (double)Mr, tab) : 0.0;
+            const double Z = wave_sum(W);
+            const double target = (double)a.u[g] * Z;
+            const double incl = wave_incl_scan(W);
+            double excl = __shfl_up(incl, 1);
+            if (lane == 0) excl = 0.0;  // [excl, incl) of consecutive chunks tile [0, Z)
+            const bool hasm = have && W > 0.0;
+            const unsigned long long mine = __ballot(hasm && excl <= target && target < incl);
+            const unsigned long long any = __ballot(hasm);
+            // the unique chunk whose interval holds target; if rounding pushed
+            // target past the last boundary, the last chunk with mass
+            const int cstar = mine ? __builtin_ctzll(mine) : (any ? 63 - __builtin_clzll(any) : 0);
+            const double base = readlane_d(excl, cstar);
+            if (lane == 0) {
+                s_cstar = cstar;
+                s_base = base;
+                s_target = target;
+                s_M = (double)Mr;
+                s_lnZ = log(Z);
+            }
+        } else if (lane == 0) {
+            s_ok = 0;
+        }
+    }
+    __syncthreads();
+    if (!s_ok) {  // a chunk's words never arrived: report, leave them as they are
+        if (t == 0) a.out_status[g] = 2;
+        return;
+    }
+    const int cstar = s_cstar;
+    const double M = s_M, target = s_target;
+    const T* row = reinterpret_cast<const T*>(a.T) + (size_t)g * a.V;
+    const __amdgpu_buffer_rsrc_t rr = row_rsrc(row, a.V);
+    const int e0 = cstar * kChunk + t * RUN;
+    // weights exp(l - M) of the thread's tokens, four at a time; its sum and
+    // which tokens have mass or a finite logit
+    double tsum = 0.0;
+    unsigned pos = 0u, fin = 0u;
+#pragma unroll 1
+    for (int j = 0; j < RUN; j += 4) {
+        float v[4];
+        Elem<T>::load4(rr, e0 + j, a.V, a.vec_t, v);
+        double x[4], w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (double)v[i] - M;
+        exp_nonpos_n<4>(x, w, tab);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tsum += w[i];
+            pos |= (w[i] > 0.0) ? (1u << (j + i)) : 0u;
+            fin |= (v[i] > -INFINITY) ? (1u << (j + i)) : 0u;
+        }
+    }
+    const double wincl = wave_incl_scan(tsum);
+    if (lane == 63) s_wtot[wave] = wincl;
+    __syncthreads();
+    double off = 0.0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww)
+        if (ww < wave) off += s_wtot[ww];
+    const double tincl = wincl + off;
+    double texcl = __shfl_up(tincl, 1);
+    if (lane == 0) texcl = off;
+    // first crossing of the running sum past target in this thread's tokens
+    // (read again, now from cache, and their weights formed again, bit for
+    // bit).  Threads whose interval ends at or before target have none; a
+    // thread past it crosses at its first token with mass, which covers a
+    // rounding that leaves the crossing just past the interval holding target.
+    int cand = INT_MAX;
+    if (target < s_base + tincl) {
+        double cum = s_base + texcl;
+#pragma unroll 1
+        for (int j = 0; j < RUN && cand == INT_MAX; j += 4) {
+            float v[4];
+            Elem<T>::load4(rr, e0 + j, a.V, a.vec_t, v);
+            double x[4], w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (double)v[i] - M;
+            exp_nonpos_n<4>(x, w, tab);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (w[i] > 0.0 && cand == INT_MAX) {
+                    cum += w[i];
+                    if (cum > target) cand = e0 + j + i;
+                }
+            }
+        }
+    }
+    const int lastpos = pos ? e0 + 31 - __builtin_clz(pos) : -1;
+    const int anypos = fin ? e0 + 31 - __builtin_clz(fin) : -1;
+    const int wc = wave_min_i(cand), wl = wave_max_i(lastpos), wa = wave_max_i(anypos);
+    if (lane == 0) {
+        s_pick[wave][0] = wc;
+        s_pick[wave][1] = wl;
+        s_pick[wave][2] = wa;
+    }
+    __syncthreads();
+    int yc = INT_MAX, yl = -1, ya = -1;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+        yc = min(yc, s_pick[ww][0]);
+        yl = max(yl, s_pick[ww][1]);
+        ya = max(ya, s_pick[ww][2]);
+    }
+    // The crossing token; if rounding left none, the last token with mass in
+    // the chunk; if the chunk had none, its last finite token.  Always a valid
+    // index.
+    int y = (yc != INT_MAX) ? yc : (yl >= 0 ? yl : ya);
+    if (y < 0 || y >= a.V) y = 0;
+    if (t == 0) {
+        const float ly = Elem<T>::at(row, (size_t)y);
+        a.out_tok[g] = y;
+        if (a.out_tlp) a.out_tlp[g] = (float)(((double)ly - M) - s_lnZ);
+        a.out_status[g] = 0;
+    }
+}
+
+// The draft sampler as one launch: rows x tpr streaming workgroups (one tile
+// each, chunk records published), then one drawing workgroup per row.
+// Workgroups start in index order, so a drawing workgroup waits only on
+// streaming workgroups, which never wait.
+template <typename T, bool VECP>
+__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_sample_rows(const Args a) {
+    const unsigned ns = (unsigned)a.B * (unsigned)a.tpr;
+    if (blockIdx.x < ns) {
+        rows_tile<T, VECP>(a, blockIdx.x);
+        return;
+    }
+    draw_row<T>(a, (int)(blockIdx.x - ns));
+}
+
 // ------------------------------------------------------------------- host
 inline int esize(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
 
@@ -2880,26 +3027,23 @@ spec_status spec_sample_drafts(const void* logits, spec_dtype dtype, const float
     a.ws = static_cast<unsigned char*>(workspace);
     a.tpr = tpr_of(dtype, V);
     a.Vtot = V;
-    a.sums = reinterpret_cast<ChunkSums*>(a.ws + make_layout(rows, 1, a.tpr, a.C2).sums);
-    // one pass that leaves fp64 chunk sums, then the draw
+    a.fsums = reinterpret_cast<uint64_t*>(a.ws + make_layout(rows, 1, a.tpr, a.C2).fsums);
+    // one launch: the tiles publish fp64 chunk sums, each row's drawing
+    // workgroup picks them up and draws
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipEvent_t ev[3];
     take_prof(ev);
-    const dim3 grid((unsigned)rows * (unsigned)a.tpr), block(kThreads);
+    const dim3 grid((unsigned)rows * (unsigned)a.tpr + (unsigned)rows), block(kThreads);
     if (dtype == SPEC_BF16) {
         if (a.vec_t)
-            hipExtLaunchKernelGGL((k_stream_rows<uint16_t, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+            hipExtLaunchKernelGGL((k_sample_rows<uint16_t, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
         else
-            hipExtLaunchKernelGGL((k_stream_rows<uint16_t, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
-        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-        hipLaunchKernelGGL((k_sample<uint16_t, kSample, false>), dim3(rows), dim3(kSampleThreads), 0, st, a);
+            hipExtLaunchKernelGGL((k_sample_rows<uint16_t, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
     } else {
         if (a.vec_t)
-            hipExtLaunchKernelGGL((k_stream_rows<float, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+            hipExtLaunchKernelGGL((k_sample_rows<float, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
         else
-            hipExtLaunchKernelGGL((k_stream_rows<float, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
-        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-        hipLaunchKernelGGL((k_sample<float, kSample, false>), dim3(rows), dim3(kSampleThreads), 0, st, a);
+            hipExtLaunchKernelGGL((k_sample_rows<float, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
