@@ -55,6 +55,13 @@ TRAFFIC = {"source_sha256": "96ae15cafd4c20e3d5866ae5ab5e117822732c438479d791016
            "fetch_kib": 51226.9, "write_kib": 884.5, "fetch_scale": 2.0, "write_scale": 1.0}
 
 MALL_BYTES = 256 * 1024 * 1024
+# What the profiling hook's start/stop events bracket in each entry point.
+KERNEL_TIMED = {"exact": "k_single: the whole call (one launch)",
+                "power": "k_single: the whole call (one launch)",
+                "relaxed": "k_single: the whole call (one launch)",
+                "greedy": "k_greedy: the whole call (one launch)",
+                "sample": "k_sample_rows: the whole call (one launch)",
+                "tree": "k_stream: the streaming kernel (k_decide follows)"}
 RUNS = 3  # timed replays of the captured steps; the median is reported
 METRIC = "verify rounds/s + achieved HBM GB/s (% of peak), B=32 K=5 V=128256 bf16"
 
@@ -367,8 +374,10 @@ def oracle_rate(fn, seconds, max_calls):
 
 def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, torch, dev,
                    cpu=False):
-    """Call rate and streaming-kernel rate of one more workload; with cpu, the
-    oracle's rate on the same inputs beside it (a bounded sample)."""
+    """Call rate, and the rate of the launch the library's profiling hook
+    brackets (the whole call for the single-launch rules, the streaming kernel
+    for the tree), of one more workload; with cpu, the oracle's rate on the
+    same inputs beside it (a bounded sample)."""
     sets = math.ceil(2 * MALL_BYTES / nbytes)
     case = Case(lib, mode, ci, sets, torch, dev)
     r = time_case(case, steps, warmup, hip, use_graph)
@@ -377,6 +386,7 @@ def other_workload(lib, mode, ci, nbytes, label, steps, warmup, hip, use_graph, 
     ms = r["graph_ms_per_step"] if use_graph else r["eager_ms_per_step"]
     logit_bytes = ci.target.nbytes + (ci.draft.nbytes if mode == "exact" else 0)
     out = {"workload": label, "entry_point": f"spec_verify_{mode}",
+           "kernel": KERNEL_TIMED[mode],
            "rounds_per_s": 1000.0 / ms, "us_per_call": ms * 1e3,
            "hbm_gbs_call": nbytes / (ms * 1e-3) / 1e9,
            "hbm_frac_call": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -874,6 +884,7 @@ def main():
         "eager": {"rounds_per_s": 1000.0 / r_ex["eager_ms_per_step"],
                   "ms_per_step": r_ex["eager_ms_per_step"]},
         "greedy_b32_k5": {
+            "kernel": KERNEL_TIMED["greedy"],
             "rounds_per_s": 1000.0 / g_ms, "ms_per_step": g_ms,
             "hbm_gbs_call": bytes_greedy / (g_ms * 1e-3) / 1e9,
             "kernel_us_mean": r_gr["kernel_ms_mean"] * 1e3,

@@ -30,9 +30,13 @@
 //             chunk of the terminal row(s) in fp64 and publishes the sums;
 //             the request's last-chunk workgroup draws the terminal token.
 //
-//   greedy, tree: k_stream (one workgroup per tile, one record each), then
-//             k_decide (one workgroup per request: fold the records, run the
-//             tests one lane per draft or tree node, write the outputs).
+//   greedy: one launch (k_greedy): one workgroup per tile publishes the
+//             tile's record, then one deciding workgroup per request folds
+//             the records, tests the drafts and writes the outputs.
+//
+//   tree: k_stream (one workgroup per tile, one record each), then k_decide
+//             (one workgroup per request: fold the records, run the tests one
+//             lane per tree node, write the outputs).
 //
 //   draft sampler: one launch (k_sample_rows): the tiles publish fp64 chunk
 //             sums, and one workgroup per row draws.
@@ -651,6 +655,14 @@ __device__ inline Seg decode_record(uint64_t w0, uint64_t w1) {
     sg.s = dec_nonneg(w1);
     return sg;
 }
+// The record of a tile with nothing in it (the fold's identity).
+__device__ inline Seg neutral_record(bool argmax) {
+    Seg sg;
+    sg.m = -INFINITY;
+    sg.ic = argmax ? INT_MAX : 0;
+    sg.s = 0.0;
+    return sg;
+}
 // Bound of every wait for published words (each round trip is about a
 // microsecond, so about a second in all); a wait that runs out reports
 // status 2 for its request instead of hanging the launch.
@@ -1059,14 +1071,6 @@ __device__ void fold_batches(int nrows, RowStats& rs, const double* tab, Load lo
     __syncthreads();
 }
 
-__device__ inline Seg neutral_record(bool argmax) {
-    Seg sg;
-    sg.m = -INFINITY;
-    sg.ic = argmax ? INT_MAX : 0;
-    sg.s = 0.0;
-    return sg;
-}
-
 // Records written by a previous kernel.  Every batch's loads are issued
 // before any is used, and `hook` runs once in every thread after the first
 // batch is issued, before any record is used: the caller's own loads go
@@ -1301,6 +1305,22 @@ __device__ inline void clear_records(const Args& a, int b) {
 // them in one batch for K < 8 and launch faster than sixteen.
 constexpr int decide_threads(int mode) { return mode == kGreedy ? 512 : kDecideThreads; }
 
+// Greedy: wave 0 takes the decision from the folded rows; the workgroup
+// writes the accepted prefix, and position n gets the argmax of target row n
+// (the correction after a mismatch, or the bonus token).
+__device__ void greedy_finish(const Args& a, int b, const RowStats& rs, const ChainVals& cv) {
+    __shared__ ChainDecision cd;
+    if (threadIdx.x < 64) chain_decide<kGreedy>(a, rs, cv, cd);
+    __syncthreads();
+    write_prefix<kGreedy>(a, b, cd);
+    if (threadIdx.x == 0) {
+        const int n = cd.n;
+        a.out_tok[(size_t)b * a.L + n] = rs.g[n];
+        if (a.out_tlp) a.out_tlp[(size_t)b * a.L + n] = (float)(-rs.lnS[n]);
+        if (a.out_blp) a.out_blp[(size_t)b * a.L + n] = 0.f;
+    }
+}
+
 // Greedy and tree: one workgroup (decide_threads) per request folds the tile
 // records (one row per wave), takes the decision and writes the outputs.
 template <typename T, int MODE, bool SUM, bool SHARD>
@@ -1312,7 +1332,6 @@ __global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
     __shared__ RowStats rs;
     if (SUM) fill_exp_table(tab);
     if constexpr (MODE == kGreedy) {
-        __shared__ ChainDecision cd;
         ChainVals cv;
         if (threadIdx.x < 64) chain_load_tokens<MODE>(a, b, cv);
         fold_rows<MODE, SUM, NW, SHARD>(a, b, a.R, rs, tab, [&]() {
@@ -1320,15 +1339,7 @@ __global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
             __syncthreads();  // the exp table; every load above is in flight
         });
         if (!SHARD) clear_records(a, b);
-        if (threadIdx.x < 64) chain_decide<MODE>(a, rs, cv, cd);
-        __syncthreads();
-        write_prefix<MODE>(a, b, cd);
-        if (threadIdx.x == 0) {
-            const int n = cd.n;
-            a.out_tok[(size_t)b * a.L + n] = rs.g[n];
-            if (a.out_tlp) a.out_tlp[(size_t)b * a.L + n] = (float)(-rs.lnS[n]);
-            if (a.out_blp) a.out_blp[(size_t)b * a.L + n] = 0.f;
-        }
+        greedy_finish(a, b, rs, cv);
         return;
     } else {
         // tree: a node is accepted iff its token is its parent's argmax and
@@ -2346,6 +2357,62 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_single(const 
     sweep_role<T, MODE>(a, (int)(blockIdx.x - P));
 }
 
+// The deciding workgroup of request b in the greedy rule's single launch:
+// one lane waits for the request's last tile record, the waves fold all of
+// its rows' records (waiting for any still missing), and the workgroup zeroes
+// them, decides and writes the outputs.
+template <typename T, bool SUM>
+__device__ void greedy_role(const Args& a, const int b) {
+    const int tid = threadIdx.x;
+    __shared__ double tab[kExpTab];
+    __shared__ RowStats rs;
+    __shared__ int s_ok;
+    if (SUM) fill_exp_table(tab);
+    if (tid == 0) s_ok = 1;
+    ChainVals cv;
+    if (tid < 64) {
+        chain_load_tokens<kGreedy>(a, b, cv);
+        chain_load_values<T, kGreedy, false>(a, b, cv);
+    }
+    if (tid == 0) {
+        const uint64_t* hint = a.frec + 2 * (((size_t)b * a.R + a.R - 1) * a.tpr + a.tpr - 1);
+        for (int it = 0; load_word(hint) == 0ull; ++it) {
+            if (it == kSpinLimit) {
+                s_ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+    __syncthreads();  // the exp table, s_ok
+    if (s_ok && !fold_rows_published<kGreedy, SUM, kWaves>(a, b, a.R, rs, tab)) s_ok = 0;
+    __syncthreads();
+    if (!s_ok) {  // a record never arrived: report, leave the words as they are
+        if (tid == 0) a.out_status[b] = 2;
+        return;
+    }
+    // every record of the request is read: zero them for the next call
+    uint64_t* w = a.frec + 2 * (size_t)b * a.R * a.tpr;
+    for (int i = tid; i < 2 * a.R * a.tpr; i += kThreads) store_word(w + i, 0ull);
+    greedy_finish(a, b, rs, cv);
+}
+
+// The greedy rule as one launch: nstream workgroups stream the tiles in a
+// grid-stride loop and publish their records, then one deciding workgroup
+// per request.  Workgroups start in index order, so a deciding workgroup
+// waits only on streaming workgroups, which never wait.  NV: 16-byte loads
+// per thread (8 KiB tiles for bf16 rows without log-probs).
+template <typename T, bool SUM, bool VECP, int NV>
+__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_greedy(const Args a) {
+    const unsigned P = (unsigned)a.nstream, ntiles = (unsigned)(a.B * a.R * a.tpr);
+    if (blockIdx.x < P) {
+        for (unsigned t = blockIdx.x; t < ntiles; t += P)
+            stream_tile<T, kGreedy, SUM, VECP, false, false, NV, true>(a, t);
+        return;
+    }
+    greedy_role<T, SUM>(a, (int)(blockIdx.x - P));
+}
+
 // The draw of sampled row g, by the row's drawing workgroup of the sampler's
 // single launch.  Wave 0 waits for the row's chunk words (lane = chunk),
 // rescales each chunk sum to the row max (one fp64 exp per lane), scans the
@@ -2546,12 +2613,6 @@ inline int stream_workgroups() { return kStreamPerCu * compute_units(); }
 inline int tile_elems(spec_dtype dt) { return kTileBytes / esize(dt); }
 inline int tpr_of(spec_dtype dt, int V) { return (V + tile_elems(dt) - 1) / tile_elems(dt); }
 constexpr int kSmallTileElems = kThreads * kSmallTileVecs * 8;  // bf16 elements of an 8 KiB tile
-// Whether a call's stream reads 8 KiB tiles: the greedy rule without
-// log-probs on bf16 rows, where the doubled grid still fits in 2^32 threads.
-inline bool small_tiles(spec_dtype dt, int V, long long rows, bool greedy_no_logprobs) {
-    if (!greedy_no_logprobs || dt != SPEC_BF16) return false;
-    return rows * ((V + kSmallTileElems - 1) / kSmallTileElems) * kThreads < (1ll << 32);
-}
 // Tiles per row of the stream (8 KiB tiles have as many as an fp32 row's 16
 // KiB tiles, so the workspace query, sized for fp32, covers them).
 inline int stream_tpr(spec_dtype dt, int V, bool small) {
@@ -2605,52 +2666,23 @@ inline void take_prof(hipEvent_t (&ev)[3]) {
     }
 }
 
-// Streaming kernel, then the per-request kernels: decide (greedy, tree), or
-// sweep and sample (exact, relaxed).  With the profiling hook set, the
-// streaming kernel is launched with start/stop events that the dispatch
-// itself timestamps, so their interval is the kernel's own duration.
-template <int MODE, bool SUM>
-spec_status launch(Args a, spec_dtype dt, hipStream_t st) {
-    constexpr bool SMALL_OK = !SUM && MODE == kGreedy;
-    const bool small = small_tiles(dt, a.V, (long long)a.B * a.R, SMALL_OK);
-    a.tpr = stream_tpr(dt, a.V, small);
+// The tree rule: the streaming kernel, then one deciding workgroup per
+// request (k_decide).  With the profiling hook set, the streaming kernel is
+// launched with start/stop events that the dispatch itself timestamps, so
+// their interval is the kernel's own duration.
+template <bool SUM>
+spec_status launch_tree(Args a, spec_dtype dt, hipStream_t st) {
+    a.tpr = tpr_of(dt, a.V);
     a.Vtot = a.V;
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
     a.segs = reinterpret_cast<Seg*>(a.ws + lay.seg);
-    a.dec = reinterpret_cast<Decision*>(a.ws + lay.dec);
-    a.sums = reinterpret_cast<ChunkSums*>(a.ws + lay.sums);
-    a.xv_out = reinterpret_cast<float*>(a.ws + lay.xv);
-    a.xv_in = a.xv_out;
     hipEvent_t ev[3];
     take_prof(ev);
-    // the rules that test drafted-token values record them in the stream
-    constexpr bool XV = (MODE == kExact || MODE == kPower || MODE == kRelaxed);
-    spec_status ls;
-    if constexpr (SMALL_OK) {
-        ls = small ? launch_stream<MODE, SUM, XV, false, kSmallTileVecs>(a, dt, st, ev[0], ev[1])
-                   : launch_stream<MODE, SUM, XV>(a, dt, st, ev[0], ev[1]);
-    } else {
-        ls = launch_stream<MODE, SUM, XV>(a, dt, st, ev[0], ev[1]);
-    }
-    if (ls != SPEC_OK) return SPEC_EHIP;
-    if constexpr (MODE == kGreedy || MODE == kTree) {
-        if (dt == SPEC_BF16)
-            hipLaunchKernelGGL((k_decide<uint16_t, MODE, SUM, false>), dim3(a.B), dim3(decide_threads(MODE)), 0, st, a);
-        else
-            hipLaunchKernelGGL((k_decide<float, MODE, SUM, false>), dim3(a.B), dim3(decide_threads(MODE)), 0, st, a);
-    } else {
-        const dim3 grid2((unsigned)a.B * (unsigned)((a.C2 + kSweepGroups - 1) / kSweepGroups));
-        const dim3 block2(kSweepThreads);
-        if (dt == SPEC_BF16) {
-            hipLaunchKernelGGL((k_sweep<uint16_t, MODE, false>), grid2, block2, 0, st, a);
-            if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-            hipLaunchKernelGGL((k_sample<uint16_t, MODE, false>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
-        } else {
-            hipLaunchKernelGGL((k_sweep<float, MODE, false>), grid2, block2, 0, st, a);
-            if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-            hipLaunchKernelGGL((k_sample<float, MODE, false>), dim3(a.B), dim3(kSampleThreads), 0, st, a);
-        }
-    }
+    if (launch_stream<kTree, SUM, false>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
+    if (dt == SPEC_BF16)
+        hipLaunchKernelGGL((k_decide<uint16_t, kTree, SUM, false>), dim3(a.B), dim3(decide_threads(kTree)), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_decide<float, kTree, SUM, false>), dim3(a.B), dim3(decide_threads(kTree)), 0, st, a);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
@@ -2683,6 +2715,51 @@ spec_status launch_single(Args a, spec_dtype dt, hipStream_t st) {
         else
             hipExtLaunchKernelGGL((k_single<float, MODE, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
     }
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+// Whether the greedy rule's single launch streams 8 KiB tiles: bf16 rows
+// without log-probs, when 16 KiB tiles would number fewer than the streaming
+// workgroups the chip holds at once (measured: 8 KiB tiles are faster at
+// B=8, K=5, V=128256 and slower at B=32).
+inline bool greedy_small_tiles(spec_dtype dt, int V, long long rows, bool logprobs) {
+    return !logprobs && dt == SPEC_BF16 && rows * tpr_of(dt, V) < stream_workgroups();
+}
+// Streaming workgroups of the greedy launch: one per tile (measured faster
+// than a grid-stride loop at these sizes), up to a cap that keeps the grid
+// far below 2^32 threads; above it they loop.
+constexpr int kMaxStreamGroups = 1 << 20;
+
+template <typename T, bool SUM, int NV>
+void launch_greedy_kernel(const Args& a, bool vecp, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    if (vecp)
+        hipExtLaunchKernelGGL((k_greedy<T, SUM, true, NV>), grid, dim3(kThreads), 0, st, e0, e1, 0, a);
+    else
+        hipExtLaunchKernelGGL((k_greedy<T, SUM, false, NV>), grid, dim3(kThreads), 0, st, e0, e1, 0, a);
+}
+
+// The greedy rule's single launch (k_greedy): the streaming workgroups, then
+// one deciding workgroup per request.  With the profiling hook set, the
+// launch carries the start and stop events.
+template <bool SUM>
+spec_status launch_greedy(Args a, spec_dtype dt, hipStream_t st) {
+    const bool small = greedy_small_tiles(dt, a.V, (long long)a.B * a.R, SUM);
+    a.tpr = stream_tpr(dt, a.V, small);
+    a.Vtot = a.V;
+    const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
+    a.frec = reinterpret_cast<uint64_t*>(a.ws + lay.frec);
+    a.nstream = (int)min((long long)a.B * a.R * a.tpr, (long long)kMaxStreamGroups);
+    const dim3 grid((unsigned)a.nstream + (unsigned)a.B);
+    hipEvent_t ev[3];
+    take_prof(ev);
+    if (dt != SPEC_BF16)
+        launch_greedy_kernel<float, SUM, kTileVecs>(a, a.vec_t, grid, st, ev[0], ev[1]);
+    else if (!SUM && small)  // 8 KiB tiles (never with log-probs)
+        launch_greedy_kernel<uint16_t, false, kSmallTileVecs>(a, a.vec_t, grid, st, ev[0], ev[1]);
+    else
+        launch_greedy_kernel<uint16_t, SUM, kTileVecs>(a, a.vec_t, grid, st, ev[0], ev[1]);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
@@ -2853,7 +2930,7 @@ spec_status spec_verify_greedy(const void* target_logits, spec_dtype dtype,
     if (!target_logits || !draft_tokens || !out_tokens || !out_accept_len || !out_status)
         return SPEC_EINVAL;
     const spec_status ws = check_ws(workspace, workspace_bytes, B, K + 1, V, dtype,
-                                    small_tiles(dtype, V, (long long)B * (K + 1), !out_target_logprob));
+                                    greedy_small_tiles(dtype, V, (long long)B * (K + 1), out_target_logprob));
     if (ws != SPEC_OK) return ws;
     Args a = {};
     a.T = target_logits;
@@ -2873,8 +2950,8 @@ spec_status spec_verify_greedy(const void* target_logits, spec_dtype dtype,
     a.L = K + 1;
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (out_target_logprob) return launch<kGreedy, true>(a, dtype, st);
-    return launch<kGreedy, false>(a, dtype, st);
+    if (out_target_logprob) return launch_greedy<true>(a, dtype, st);
+    return launch_greedy<false>(a, dtype, st);
 }
 
 spec_status spec_verify_exact(const void* target_logits, const void* draft_logits,
@@ -3085,8 +3162,8 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
     a.L = N;
     a.ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (out_target_logprob) return launch<kTree, true>(a, dtype, st);
-    return launch<kTree, false>(a, dtype, st);
+    if (out_target_logprob) return launch_tree<true>(a, dtype, st);
+    return launch_tree<false>(a, dtype, st);
 }
 
 size_t spec_read_ceiling_out_words(size_t bytes) {

@@ -43,10 +43,11 @@
  *                               [0,V), or a tree parent outside [-1, i)):
  *                               the offending draft counts as rejected and
  *                               the offending tree node as unmatched.  2
- *                               (exact, relaxed and power rules) when a wait
- *                               for data from another workgroup of the same
- *                               launch ran out (about a second); the
- *                               request's other outputs are then undefined.
+ *                               (greedy, exact, relaxed and power rules)
+ *                               when a wait for data from another
+ *                               workgroup of the same launch ran out (about
+ *                               a second); the request's other outputs are
+ *                               then undefined.
  *                               It does not occur on a working device.
  *
  * Randomness is supplied by the caller (spec-decode README, "Use it": the
@@ -61,10 +62,10 @@
  *   call's workgroups.  It must be zero-filled before its first call (for
  *   example allocated zeroed); every call leaves every byte of it zero
  *   again, so one workspace serves calls of any rule and shape in turn on
- *   the same stream with no further initialization.  (The exact, relaxed
- *   and power calls run as one launch whose workgroups pass data through the
- *   workspace while the launch runs, and read a zero word as "not written
- *   yet".)  Calls that run concurrently (different streams) need different
+ *   the same stream with no further initialization.  (The greedy, exact,
+ *   relaxed and power calls and the draft sampler run as one launch whose
+ *   workgroups pass data through the workspace while the launch runs, and
+ *   read a zero word as "not written yet".)  Calls that run concurrently (different streams) need different
  *   workspaces.  A call that reports status 2 for a request (see
  *   out_status) may leave its workspace dirty: zero-fill it before reusing
  *   it.  The library allocates nothing and keeps no state besides the
@@ -122,8 +123,9 @@ const char *spec_status_string(int status);
 /*
  * Host-only profiling hook (for benchmarks).  The arguments are hipEvent_t
  * handles created by the caller (with timing enabled), or NULL.  The next
- * spec_verify_* call made from the calling thread launches its streaming
- * kernel (the one that reads every logit once) with before_stream and
+ * spec_verify_* or spec_sample_drafts call made from the calling thread
+ * launches its streaming kernel (the one that reads every logit once: for
+ * the calls made as one launch, that launch) with before_stream and
  * after_stream as the dispatch's own start and stop events, so that
  * hipEventElapsedTime(before_stream, after_stream) is that kernel's
  * duration, and records after_call on its stream after the call's last
@@ -258,7 +260,11 @@ spec_status spec_verify_power(const void *target_logits, const void *draft_logit
  *   uniforms     [rows] float in [0,1)
  *   out_tokens   [rows] int32
  *   out_logprob  [rows] float, or NULL (not written)
- *   out_status   [rows] int32, always 0
+ *   out_status   [rows] int32: 0, or 2 when the row's drawing workgroup's
+ *                wait for the chunk sums of the same launch ran out (about a
+ *                second; the row's other outputs are then undefined, and the
+ *                workspace may be left dirty).  It does not occur on a
+ *                working device.
  * rows <= SPEC_MAX_B; the workspace (256-byte aligned, zero-filled as above) must
  * hold spec_sample_workspace_bytes(rows, V) bytes.
  */
