@@ -413,14 +413,36 @@ __device__ inline void exp_nonpos_n(const double (&x)[N], double (&e)[N], const 
     for (int i = 0; i < N; ++i) e[i] = ldexp(tv[i] * p[i], k[i] >> 9);
 }
 
-// 2^(j/512), each the double nearest the exact value
-__constant__ const double kExp2Tab[kExpTab] = {
-#include "exp2_table.inc"
-};
+// 1/k! as a double (k! is exact in binary64 for k <= 18)
+constexpr double inv_factorial(int k) {
+    double f = 1.0;
+    for (int i = 2; i <= k; ++i) f *= i;
+    return 1.0 / f;
+}
+constexpr double kLn2o16 = 0x1.62e42fefa39efp-5;  // ln 2 / 16
+constexpr int kTabDegree = 15;
 
-// the workgroup's copy of kExp2Tab in LDS (the fp64 exp reads it per token)
+// The workgroup's table of 2^(j/512), j < 512, in LDS (the fp64 exp reads it
+// per token), computed in place instead of loaded (a copy from memory cost a
+// memory round trip at the start of every workgroup, all of them reading the
+// same lines at once).  2^(j/512) = 2^(h/16) * 2^(l/512) with j = 32h + l:
+// the first 48 threads take the 16 + 32 factors e^y, y = h ln2/16 or
+// l ln2/512, by their Taylor series to degree 15 in Horner form (truncation
+// below 1e-17 for y < ln 2), then every entry is one product.  Each entry is
+// within 1.9 ulp of the exact value.  Called by every thread of the
+// workgroup (it has a barrier); the caller's barrier publishes the table.
 __device__ inline void fill_exp_table(double* tab) {
-    for (int j = threadIdx.x; j < kExpTab; j += blockDim.x) tab[j] = kExp2Tab[j];
+    __shared__ double fac[48];
+    const int t = threadIdx.x;
+    if (t < 48) {
+        const double y = t < 16 ? (double)t * kLn2o16 : (double)(t - 16) * kLn2o512;
+        double p = inv_factorial(kTabDegree);
+#pragma unroll
+        for (int k = kTabDegree - 1; k >= 0; --k) p = fma(p, y, inv_factorial(k));
+        fac[t] = p;
+    }
+    __syncthreads();
+    for (int j = t; j < kExpTab; j += blockDim.x) tab[j] = fac[j >> 5] * fac[16 + (j & 31)];
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -911,7 +933,6 @@ __device__ __forceinline__ void rows_tile(const Args& a, const unsigned blk) {
     __shared__ double tab[kExpTab];
     __shared__ float s_m[kWaves];
     __shared__ double s_s[kWaves][CPT];
-    fill_exp_table(tab);
 
     const int g = uniform((int)(blk / (unsigned)a.tpr));
     const int c = (int)blk - g * a.tpr;
@@ -919,6 +940,7 @@ __device__ __forceinline__ void rows_tile(const Args& a, const unsigned blk) {
     const T* row = call_row<T, kRelaxed>(a, g, vec, act);
     u32x4 q[kTileVecs];
     load_tile<T, true, VECP, kTileVecs>(row, a.V, c, q);
+    fill_exp_table(tab);  // while the tile's loads are in flight
     const int t0 = c * TILE + (int)threadIdx.x * VEC;
     if (c == a.tpr - 1 && a.V % TILE != 0) {
 #pragma unroll
@@ -2217,26 +2239,30 @@ __device__ void sweep_role(const Args& a, const int idx) {
     __shared__ ChainDecision cd;
     __shared__ double red[kWaves][3 + 2 * NV];
     __shared__ int s_ok;
-    fill_exp_table(tab);
-    if (tid == 0) s_ok = 1;
+    // The request's last tile record (the last of its tiles to be taken) and
+    // the drafted tokens are loaded while the exp table is computed; one lane
+    // waits for that record before the waves read all of the request's
+    // records.  The drafted tokens' logits, whose addresses depend on the
+    // tokens, are loaded right before the records, in the same round trip.
+    const uint64_t* hint = a.frec + 2 * (((size_t)b * a.R + a.R - 1) * a.tpr + a.tpr - 1);
+    uint64_t h = 0ull;
+    if (tid == 0) h = load_word(hint);
     ChainVals cv;
-    if (tid < 64) {
-        chain_load_tokens<MODE>(a, b, cv);
-        chain_load_inputs<T, MODE>(a, b, cv);
-    }
-    // One lane waits for the request's last tile record (the last of its
-    // tiles to be taken) before the waves read all of them.
+    if (tid < 64) chain_load_tokens<MODE>(a, b, cv);
+    fill_exp_table(tab);
     if (tid == 0) {
-        const uint64_t* hint = a.frec + 2 * (((size_t)b * a.R + a.R - 1) * a.tpr + a.tpr - 1);
-        for (int it = 0; load_word(hint) == 0ull; ++it) {
+        s_ok = 1;
+        for (int it = 0; h == 0ull; ++it) {
             if (it == kSpinLimit) {
                 s_ok = 0;
                 break;
             }
             __builtin_amdgcn_s_sleep(8);
+            h = load_word(hint);
         }
     }
     __syncthreads();  // the exp table, s_ok
+    if (tid < 64) chain_load_inputs<T, MODE>(a, b, cv);
     if (s_ok && !fold_rows_published<MODE, true, kWaves>(a, b, a.R, rs, tab)) s_ok = 0;
     __syncthreads();
     if (!s_ok) {  // a record never arrived: report, leave the words as they are
@@ -2367,21 +2393,26 @@ __device__ void greedy_role(const Args& a, const int b) {
     __shared__ double tab[kExpTab];
     __shared__ RowStats rs;
     __shared__ int s_ok;
-    if (SUM) fill_exp_table(tab);
-    if (tid == 0) s_ok = 1;
+    // as in the sweep role: the last tile's record and the drafted tokens are
+    // loaded while the exp table is computed
+    const uint64_t* hint = a.frec + 2 * (((size_t)b * a.R + a.R - 1) * a.tpr + a.tpr - 1);
+    uint64_t h = 0ull;
+    if (tid == 0) h = load_word(hint);
     ChainVals cv;
     if (tid < 64) {
         chain_load_tokens<kGreedy>(a, b, cv);
         chain_load_values<T, kGreedy, false>(a, b, cv);
     }
+    if (SUM) fill_exp_table(tab);
     if (tid == 0) {
-        const uint64_t* hint = a.frec + 2 * (((size_t)b * a.R + a.R - 1) * a.tpr + a.tpr - 1);
-        for (int it = 0; load_word(hint) == 0ull; ++it) {
+        s_ok = 1;
+        for (int it = 0; h == 0ull; ++it) {
             if (it == kSpinLimit) {
                 s_ok = 0;
                 break;
             }
             __builtin_amdgcn_s_sleep(8);
+            h = load_word(hint);
         }
     }
     __syncthreads();  // the exp table, s_ok
