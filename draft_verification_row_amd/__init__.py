@@ -19,7 +19,7 @@ import torch
 __all__ = ["spec_verify_greedy", "spec_verify_exact", "spec_verify_relaxed", "spec_verify_tree",
            "spec_verify_power", "spec_sample_drafts", "spec_verify_workspace_bytes", "spec_sample_workspace_bytes",
            "VerifyResult", "TreeResult", "SampleResult", "SpecVerifyError",
-           "library_path", "load_library", "SPEC_MAX_K", "SPEC_MAX_NODES"]
+           "library_path", "load_library", "spec_set_spin_limit", "SPEC_MAX_K", "SPEC_MAX_NODES"]
 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
@@ -87,6 +87,8 @@ def load_library():
     lib.spec_shard_sweep_relaxed.argtypes = [P, I, P, Z, P, P, I, I, I, I, I, F, I, P, P, P, P, P,
                                              P, Z, P, Z, P]
     lib.spec_shard_sample_relaxed.argtypes = [P, I, P, Z, P, I, I, I, I, I, P, P, P, P, P, Z, P]
+    lib.spec_set_spin_limit.argtypes = [I]
+    lib.spec_set_spin_limit.restype = None
     for fn in ("spec_verify_greedy", "spec_verify_exact", "spec_verify_exact_noalloc",
                "spec_verify_relaxed", "spec_verify_tree",
                "spec_verify_power", "spec_sample_drafts", "spec_shard_stats_greedy",
@@ -148,6 +150,12 @@ def _stream_ptr(device: torch.device):
 
 
 _workspaces = {}
+
+
+def spec_set_spin_limit(limit: int) -> None:
+    """Testing aid: the bound of the single-launch calls' waits (0: give up at
+    the first poll that finds nothing; negative: the default)."""
+    load_library().spec_set_spin_limit(int(limit))
 
 
 def spec_verify_workspace_bytes(B: int, rows_per_request: int, V: int) -> int:

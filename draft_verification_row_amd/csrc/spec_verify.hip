@@ -633,6 +633,7 @@ struct Args {
     uint64_t* frec;     // [B][R][tpr] tile records, two words each
     uint64_t* fsums;    // [B][C2] chunk records, eleven words each
     int nstream;        // workgroups of the launch that stream tiles
+    int spin_limit;     // polling rounds of a wait before it gives up (status 2)
 };
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -685,9 +686,10 @@ __device__ inline Seg neutral_record(bool argmax) {
     sg.s = 0.0;
     return sg;
 }
-// Bound of every wait for published words (each round trip is about a
-// microsecond, so about a second in all); a wait that runs out reports
-// status 2 for its request instead of hanging the launch.
+// Default bound of every wait for published words, in polling rounds (each
+// round trip is about a microsecond, so about a second in all); a wait that
+// runs out reports status 2 for its request instead of hanging the launch.
+// Launches carry the bound in Args::spin_limit (spec_set_spin_limit).
 constexpr int kSpinLimit = 1 << 20;
 
 // Logit row g of the call (request g / R, row g % R of that request).  The
@@ -1134,7 +1136,7 @@ __device__ void fold_rows(const Args& a, int b, int nrows, RowStats& rs, const d
 
 // Records published by the streaming workgroups of the same launch: each
 // batch waits until its records' words are all written.  Returns false in a
-// thread whose wait ran out (kSpinLimit).
+// thread whose wait ran out (Args::spin_limit).
 template <int MODE, bool SUM, int NW>
 __device__ bool fold_rows_published(const Args& a, int b, int nrows, RowStats& rs, const double* tab) {
     constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
@@ -1166,7 +1168,7 @@ __device__ bool fold_rows_published(const Args& a, int b, int nrows, RowStats& r
 #pragma unroll
             for (int j = 0; j < kFoldBatch; ++j) missing |= need[j] && (w0[j] == 0ull || w1[j] == 0ull);
             if (__ballot(missing) == 0ull) break;
-            if (it == kSpinLimit) {
+            if (it >= a.spin_limit) {
                 ok = false;
                 break;
             }
@@ -1288,9 +1290,10 @@ __device__ void chain_decide(const Args& a, const RowStats& rs, const ChainVals&
 }
 
 // Writes positions j < n (accepted drafts) and n < j < L (padding) of the
-// chain outputs, plus accept_len and status.  Position n is the caller's.
+// chain outputs, plus accept_len and (with status) status.  Position n is the
+// caller's.
 template <int MODE>
-__device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
+__device__ void write_prefix(const Args& a, int b, const ChainDecision& cd, bool status = true) {
     const int n = cd.n, L = a.L;
     int32_t* otok = a.out_tok + (size_t)b * L;
     float* otlp = a.out_tlp ? a.out_tlp + (size_t)b * L : nullptr;
@@ -1310,7 +1313,7 @@ __device__ void write_prefix(const Args& a, int b, const ChainDecision& cd) {
     }
     if (threadIdx.x == 0) {
         a.out_len[b] = n;
-        a.out_status[b] = cd.bad_n;
+        if (status) a.out_status[b] = cd.bad_n;
     }
 }
 
@@ -2039,7 +2042,7 @@ __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& c
                 all = 1;
                 continue;
             }
-            if (it == kSpinLimit) {
+            if (it >= a.spin_limit) {
                 ok = false;
                 break;
             }
@@ -2221,6 +2224,7 @@ __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& c
                                : ((MODE == kPower && n < a.K) ? log1p(-rn) + tlp : tlp);
         if (a.out_tlp) a.out_tlp[(size_t)b * L + n] = (float)tlp;
         if (a.out_blp) a.out_blp[(size_t)b * L + n] = (float)blp;
+        a.out_status[b] = cd.bad_n;
     }
     __syncthreads();  // every read of the request's published words is done
     clear_published(a, b);
@@ -2253,7 +2257,7 @@ __device__ void sweep_role(const Args& a, const int idx) {
     if (tid == 0) {
         s_ok = 1;
         for (int it = 0; h == 0ull; ++it) {
-            if (it == kSpinLimit) {
+            if (it >= a.spin_limit) {
                 s_ok = 0;
                 break;
             }
@@ -2276,7 +2280,9 @@ __device__ void sweep_role(const Args& a, const int idx) {
     const double Mt = rs.M[n], Md = residual ? (double)rs.M[a.rows_t + n] : 0.0;
     // p > q  <=>  (l - Mt) - (d - Md) > lnSt - lnSd, with the streamed normalizers
     const double cls = residual ? rs.lnS[n] - rs.lnS[a.rows_t + n] : 0.0;
-    if (c == 0) write_prefix<MODE>(a, b, cd);
+    // the request's status is the drawing workgroup's: it succeeds only if
+    // every sweep workgroup of the request did (it waits for all their sums)
+    if (c == 0) write_prefix<MODE>(a, b, cd, false);
 
     // this thread's vectors k cover tokens c*kChunk + (k*kThreads + tid)*VEC +
     // [0, VEC): vector k lies in sub-chunk ((k*kThreads + tid)*VEC) / kSub
@@ -2407,7 +2413,7 @@ __device__ void greedy_role(const Args& a, const int b) {
     if (tid == 0) {
         s_ok = 1;
         for (int it = 0; h == 0ull; ++it) {
-            if (it == kSpinLimit) {
+            if (it >= a.spin_limit) {
                 s_ok = 0;
                 break;
             }
@@ -2474,7 +2480,7 @@ __device__ void draw_row(const Args& a, const int g) {
                 w1 = load_word(src + 1);
             }
             if (__ballot(have && (w0 == 0ull || w1 == 0ull)) == 0ull) break;
-            if (it == kSpinLimit) {
+            if (it >= a.spin_limit) {
                 ok = false;
                 break;
             }
@@ -2661,6 +2667,9 @@ spec_status check_ws(void* ws, size_t bytes, int B, int R, int V, spec_dtype dt,
     return bytes >= L.total ? SPEC_OK : SPEC_EWORKSPACE;
 }
 
+// Bound of the single launches' waits (spec_set_spin_limit).
+std::atomic<int> g_spin_limit{kSpinLimit};
+
 // One-shot profiling hook: events for the kernels of the next call made from
 // this thread.
 thread_local hipEvent_t g_prof[3] = {nullptr, nullptr, nullptr};
@@ -2730,6 +2739,7 @@ spec_status launch_single(Args a, spec_dtype dt, hipStream_t st) {
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
     a.frec = reinterpret_cast<uint64_t*>(a.ws + lay.frec);
     a.fsums = reinterpret_cast<uint64_t*>(a.ws + lay.fsums);
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     a.nstream = min(a.B * a.R * a.tpr, stream_workgroups());
     const dim3 grid((unsigned)a.nstream + (unsigned)a.B * (unsigned)a.C2), block(kThreads);
     hipEvent_t ev[3];
@@ -2781,6 +2791,7 @@ spec_status launch_greedy(Args a, spec_dtype dt, hipStream_t st) {
     a.Vtot = a.V;
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
     a.frec = reinterpret_cast<uint64_t*>(a.ws + lay.frec);
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     a.nstream = (int)min((long long)a.B * a.R * a.tpr, (long long)kMaxStreamGroups);
     const dim3 grid((unsigned)a.nstream + (unsigned)a.B);
     hipEvent_t ev[3];
@@ -2936,6 +2947,10 @@ void spec_verify_profile_next_call(void* before_stream, void* after_stream, void
     g_prof[0] = static_cast<hipEvent_t>(before_stream);
     g_prof[1] = static_cast<hipEvent_t>(after_stream);
     g_prof[2] = static_cast<hipEvent_t>(after_call);
+}
+
+void spec_set_spin_limit(int limit) {
+    g_spin_limit.store(limit < 0 ? kSpinLimit : limit, std::memory_order_relaxed);
 }
 
 const char* spec_status_string(int s) {
@@ -3136,6 +3151,7 @@ spec_status spec_sample_drafts(const void* logits, spec_dtype dtype, const float
     a.tpr = tpr_of(dtype, V);
     a.Vtot = V;
     a.fsums = reinterpret_cast<uint64_t*>(a.ws + make_layout(rows, 1, a.tpr, a.C2).fsums);
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     // one launch: the tiles publish fp64 chunk sums, each row's drawing
     // workgroup picks them up and draws
     hipStream_t st = static_cast<hipStream_t>(stream);

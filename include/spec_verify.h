@@ -135,6 +135,18 @@ const char *spec_status_string(int status);
 void spec_verify_profile_next_call(void *before_stream, void *after_stream, void *after_call);
 
 /*
+ * Host-only testing aid for callers that check the timeout path: the bound,
+ * in polling rounds, of every wait a single-launch call (greedy, exact,
+ * relaxed, power, draft sampler) makes for data from another workgroup of
+ * the same launch.  Calls launched afterwards, from any thread, carry it.
+ * With 0, a wait that does not find its data on the first poll gives up at
+ * once: the request reports status 2 (its other outputs undefined, the
+ * workspace possibly left dirty), and every kernel still ends.  A negative
+ * limit restores the default (2^20 rounds, about a second).
+ */
+void spec_set_spin_limit(int limit);
+
+/*
  * Host-only benchmarking aid: the practical read ceiling.  spec_read_ceiling
  * reads `bytes` bytes (a multiple of 16, from a 16-byte aligned device
  * pointer) with the streaming kernel's access pattern and no arithmetic: one
