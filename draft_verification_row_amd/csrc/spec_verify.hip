@@ -135,7 +135,7 @@ struct alignas(16) ChunkSums {
 
 struct Layout {
     size_t seg, dec, sums, xv;  // records, decisions, chunk sums, drafted-token logits
-    size_t frec, fsums;  // single-launch calls: published words
+    size_t frec, fsums, frow;  // single-launch calls: published words
     size_t total;
 };
 
@@ -143,7 +143,8 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // [tile records B*R*tpr][decisions B][chunk sums B*C2][drafted-token logits
 // B*K*2, sized B*R*2][published tile records B*R*tpr, two words each]
-// [published chunk records B*C2, eleven words each].  The workspace is
+// [published chunk records B*C2, eleven words each][published row records
+// B*R, two words each].  The workspace is
 // zero when a call starts (zero-filled once by its owner) and every call
 // leaves every byte it wrote zero again, whatever the rule or shape: the
 // single-launch calls read zero as "not published yet".
@@ -155,7 +156,8 @@ inline Layout make_layout(int B, int R, int tpr, int C2) {
     L.xv = align_up(L.sums + (size_t)B * C2 * sizeof(ChunkSums), 256);
     L.frec = align_up(L.xv + (size_t)B * R * 8, 256);
     L.fsums = align_up(L.frec + (size_t)B * R * tpr * 16, 256);
-    L.total = align_up(L.fsums + (size_t)B * C2 * (3 + 2 * (kChunk / 1024)) * 8, 256);
+    L.frow = align_up(L.fsums + (size_t)B * C2 * (3 + 2 * (kChunk / 1024)) * 8, 256);
+    L.total = align_up(L.frow + (size_t)B * R * 16, 256);
     return L;
 }
 
@@ -632,6 +634,7 @@ struct Args {
     // single-launch calls: published words
     uint64_t* frec;     // [B][R][tpr] tile records, two words each
     uint64_t* fsums;    // [B][C2] chunk records, eleven words each
+    uint64_t* frow;     // [B][R] folded row records, two words each
     int nstream;        // workgroups of the launch that stream tiles
     int spin_limit;     // polling rounds of a wait before it gives up (status 2)
 };
@@ -1907,11 +1910,12 @@ __device__ inline double draw_weight(bool res, float l, float d, double Mt, doub
     return fmax(fma(ea, iS, -(exp_nonpos(xb, tab) * iSq)), 0.0);
 }
 
-// Zeroes request b's published words (every thread; after all of
-// the workgroup's reads of them).
+// Zeroes request b's published row and chunk records (every thread; after
+// all of the request's reads of them).  Its tile records were zeroed by the
+// workgroups that folded them.
 __device__ inline void clear_published(const Args& a, int b) {
-    uint64_t* r = a.frec + (size_t)b * a.R * a.tpr * 2;
-    for (int i = threadIdx.x; i < a.R * a.tpr * 2; i += blockDim.x) store_word(r + i, 0ull);
+    uint64_t* r = a.frow + (size_t)b * a.R * 2;
+    for (int i = threadIdx.x; i < a.R * 2; i += blockDim.x) store_word(r + i, 0ull);
     uint64_t* m = a.fsums + (size_t)b * a.C2 * kChunkWords;
     for (int i = threadIdx.x; i < a.C2 * kChunkWords; i += blockDim.x) store_word(m + i, 0ull);
 }
@@ -2230,6 +2234,103 @@ __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& c
     clear_published(a, b);
 }
 
+// Row r of request b, by one wave: waits for the row's published tile
+// records (lane = tile), folds them as fold_batches does (max, rank count,
+// fp64 sum rescaled to the row max), publishes the row's record
+// {M, count, S} and zeroes the tile records.  Returns false (in every lane)
+// if the wait ran out.
+template <int MODE>
+__device__ bool fold_publish_row(const Args& a, int b, int r, const double* tab) {
+    constexpr bool COUNT = (MODE == kRelaxed);
+    const int lane = threadIdx.x & 63;
+    const bool have = lane < a.tpr;
+    uint64_t* src = a.frec + 2 * (((size_t)b * a.R + r) * a.tpr + (have ? lane : 0));
+    uint64_t w0 = 0ull, w1 = 0ull;
+    for (int it = 0;; ++it) {
+        if (have) {  // both words each round, in flight together
+            w0 = load_word(src);
+            w1 = load_word(src + 1);
+        }
+        if (__ballot(have && (w0 == 0ull || w1 == 0ull)) == 0ull) break;
+        if (it >= a.spin_limit) return false;
+        __builtin_amdgcn_s_sleep(4);
+    }
+    const Seg sg = have ? decode_record(w0, w1) : neutral_record(false);
+    const float M = wave_max(sg.m);
+    const int ic = COUNT ? wave_sum_i(sg.ic) : 0;
+    // tile sum * 2^(fl(m*L) - M*L), exact reference difference in fp64
+    double t = 0.0;
+    if (sg.m > -INFINITY) {
+        const float mL = sg.m * kLog2e;
+        t = sg.s * exp_nonpos(((double)mL - (double)M * (double)kLog2e) * kLn2, tab);
+    }
+    const double S = wave_sum(t);
+    if (have) {  // read: zero them for the next call
+        store_word(src, 0ull);
+        store_word(src + 1, 0ull);
+    }
+    if (lane == 0) {
+        Seg row;
+        row.m = M;
+        row.ic = ic;
+        row.s = S;
+        publish_record(a.frow + 2 * ((size_t)b * a.R + r), row);
+    }
+    return true;
+}
+
+// The R row records of request b into rs (lane = row, in waves 0 and 1;
+// R <= 2 * 64): one lane waits for the last row's record, then the lanes
+// read all of them, waiting for any still missing.  lnS = log S per row, in
+// parallel.  Returns false in a thread whose wait ran out.  Ends with a
+// barrier.
+template <int MODE>
+__device__ bool read_row_records(const Args& a, int b, RowStats& rs) {
+    constexpr bool COUNT = (MODE == kRelaxed);
+    const int tid = threadIdx.x;
+    __shared__ int s_hint;
+    bool ok = true;
+    if (tid == 0) {
+        s_hint = 1;
+        const uint64_t* hint = a.frow + 2 * ((size_t)b * a.R + a.R - 1);
+        for (int it = 0; load_word(hint) == 0ull; ++it) {
+            if (it >= a.spin_limit) {
+                s_hint = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+    __syncthreads();
+    if (!s_hint) ok = false;
+    if (ok && tid < 128) {
+        const bool have = tid < a.R;
+        const uint64_t* src = a.frow + 2 * ((size_t)b * a.R + (have ? tid : 0));
+        uint64_t w0 = 0ull, w1 = 0ull;
+        for (int it = 0;; ++it) {
+            if (have) {
+                w0 = load_word(src);
+                w1 = load_word(src + 1);
+            }
+            if (__ballot(have && (w0 == 0ull || w1 == 0ull)) == 0ull) break;
+            if (it >= a.spin_limit) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (ok && have) {
+            const Seg sg = decode_record(w0, w1);
+            rs.M[tid] = sg.m;
+            rs.g[tid] = 0;
+            rs.c[tid] = COUNT ? sg.ic : 0;
+            rs.lnS[tid] = log(sg.s);
+        }
+    }
+    __syncthreads();
+    return ok;
+}
+
 // One sweep workgroup: request idx / C2, chunk idx % C2.
 template <typename T, int MODE>
 __device__ void sweep_role(const Args& a, const int idx) {
@@ -2243,31 +2344,23 @@ __device__ void sweep_role(const Args& a, const int idx) {
     __shared__ ChainDecision cd;
     __shared__ double red[kWaves][3 + 2 * NV];
     __shared__ int s_ok;
-    // The request's last tile record (the last of its tiles to be taken) and
-    // the drafted tokens are loaded while the exp table is computed; one lane
-    // waits for that record before the waves read all of the request's
-    // records.  The drafted tokens' logits, whose addresses depend on the
-    // tokens, are loaded right before the records, in the same round trip.
-    const uint64_t* hint = a.frec + 2 * (((size_t)b * a.R + a.R - 1) * a.tpr + a.tpr - 1);
-    uint64_t h = 0ull;
-    if (tid == 0) h = load_word(hint);
+    // Each row of the request is folded once: the request's sweep workgroup
+    // c takes rows c, c + C2, ... (only the first R workgroups have one) and
+    // publishes the row's record; then every sweep workgroup of the request
+    // reads the R row records.  A workgroup waits only on streaming
+    // workgroups and on its own request's first R sweep workgroups, which
+    // start before any later one.  The drafted tokens are loaded while the
+    // exp table is computed, their logits (addresses depending on them)
+    // while the row records are awaited.
     ChainVals cv;
     if (tid < 64) chain_load_tokens<MODE>(a, b, cv);
+    if (tid == 0) s_ok = 1;
     fill_exp_table(tab);
-    if (tid == 0) {
-        s_ok = 1;
-        for (int it = 0; h == 0ull; ++it) {
-            if (it >= a.spin_limit) {
-                s_ok = 0;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(8);
-            h = load_word(hint);
-        }
-    }
     __syncthreads();  // the exp table, s_ok
+    for (int r = c; r < a.R; r += a.C2)
+        if (wave == 0 && !fold_publish_row<MODE>(a, b, r, tab) && lane == 0) s_ok = 0;
     if (tid < 64) chain_load_inputs<T, MODE>(a, b, cv);
-    if (s_ok && !fold_rows_published<MODE, true, kWaves>(a, b, a.R, rs, tab)) s_ok = 0;
+    if (!read_row_records<MODE>(a, b, rs)) s_ok = 0;
     __syncthreads();
     if (!s_ok) {  // a record never arrived: report, leave the words as they are
         if (tid == 0) a.out_status[b] = 2;
@@ -2739,6 +2832,7 @@ spec_status launch_single(Args a, spec_dtype dt, hipStream_t st) {
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
     a.frec = reinterpret_cast<uint64_t*>(a.ws + lay.frec);
     a.fsums = reinterpret_cast<uint64_t*>(a.ws + lay.fsums);
+    a.frow = reinterpret_cast<uint64_t*>(a.ws + lay.frow);
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     a.nstream = min(a.B * a.R * a.tpr, stream_workgroups());
     const dim3 grid((unsigned)a.nstream + (unsigned)a.B * (unsigned)a.C2), block(kThreads);
