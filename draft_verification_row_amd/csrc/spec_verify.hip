@@ -25,18 +25,21 @@
 //
 //   exact, relaxed, power: one launch (k_single).  Its first workgroups
 //             stream the tiles in a grid-stride loop and publish each tile's
-//             record; one sweep workgroup per (request, 4096-token chunk)
-//             waits for its request's records, folds them, decides, sums its
-//             chunk of the terminal row(s) in fp64 and publishes the sums;
-//             the request's last-chunk workgroup draws the terminal token.
+//             record; one sweep workgroup per (request, 4096-token chunk):
+//             the first R of a request each fold one row's records and
+//             publish the row's record, then every one reads the row
+//             records, decides, sums its chunk of the terminal row(s) in
+//             fp64 and publishes the sums; the request's last-chunk
+//             workgroup draws the terminal token.
 //
 //   greedy: one launch (k_greedy): one workgroup per tile publishes the
 //             tile's record, then one deciding workgroup per request folds
 //             the records, tests the drafts and writes the outputs.
 //
-//   tree: k_stream (one workgroup per tile, one record each), then k_decide
-//             (one workgroup per request: fold the records, run the tests one
-//             lane per tree node, write the outputs).
+//   tree: one launch (k_tree): one workgroup per tile publishes the tile's
+//             record, folding workgroups publish one record per row, and one
+//             deciding workgroup per request reads the node rows' records,
+//             runs the tests one lane per tree node and writes the outputs.
 //
 //   draft sampler: one launch (k_sample_rows): the tiles publish fp64 chunk
 //             sums, and one workgroup per row draws.
@@ -760,7 +763,7 @@ __device__ __forceinline__ void stream_tile(const Args& a, const unsigned blk) {
     constexpr bool NT = true;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = uniform((int)(threadIdx.x >> 6));  // scalar: per-wave LDS addresses stay in SGPRs
     __shared__ float s_m[kWaves];
     __shared__ int s_j[kWaves];
     __shared__ double s_s[kWaves];
@@ -1349,6 +1352,91 @@ __device__ void greedy_finish(const Args& a, int b, const RowStats& rs, const Ch
     }
 }
 
+// Tree: wave 0 (lane i = node i) finds the deepest accepted node from the
+// rows' argmax (rs.g) by pointer jumping and walks its path; the workgroup
+// writes the outputs (NT threads).  p and t: node threadIdx.x's parent and
+// token (threads 1 <= i < N), loaded before the fold; nraw the node count.
+// Rows past the node count are never consulted (a parent index is below its
+// child's).
+template <int NT>
+__device__ void tree_finish(const Args& a, int b, const RowStats& rs, int nraw, int p, int t) {
+    __shared__ int t_par[SPEC_MAX_NODES];
+    __shared__ int t_tok[SPEC_MAX_NODES];
+    __shared__ int t_path[SPEC_MAX_NODES];
+    __shared__ int t_d, t_e, t_bad;
+    const int N = a.rows_t;
+    const int nb = min(max(nraw, 1), N);
+    if (threadIdx.x < 64) {
+        // wave 0, lane i = node i.  Pointer jumping: `ok` says every node
+        // from i up to (not including) `anc` matches, `dep` counts those
+        // edges; each round doubles the span, so six rounds reach the root
+        // from any depth below 64.  A node that does not match (or is
+        // malformed, or lies beyond the tree) stops its chain with ok =
+        // false, which its descendants inherit.
+        const int i = threadIdx.x;
+        bool bad = false, match = false;
+        int par = -1;
+        if (i >= 1 && i < nb) {
+            bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.Vtot);
+            par = bad ? -1 : p;
+            match = !bad && (t == rs.g[p]);
+        }
+        t_par[i] = par;
+        t_tok[i] = t;
+        const unsigned long long bm = __ballot(bad);
+        bool ok = (i == 0) || match;
+        int anc = match ? par : -1;
+        int dep = (i == 0) ? 0 : 1;
+#pragma unroll
+        for (int round = 0; round < 6; ++round) {
+            const int src = anc >= 0 ? anc : i;
+            const int ok_a = __shfl(ok ? 1 : 0, src);
+            const int dep_a = __shfl(dep, src);
+            const int anc_a = __shfl(anc, src);
+            if (anc >= 0) {
+                ok = ok && ok_a;
+                dep += dep_a;
+                anc = anc_a;
+            }
+        }
+        // deepest accepted node, ties to the lowest index (the root is
+        // always accepted at depth 0)
+        const int key = ok ? (dep << 6) | (63 - i) : -1;
+        const int kmax = wave_max_i(key);
+        const int e = 63 - (kmax & 63), d = kmax >> 6;
+        int v = e;
+        for (int k = d - 1; k >= 0; --k) {
+            if (i == 0) t_path[k] = v;
+            v = __builtin_amdgcn_readlane(par, v);
+        }
+        if (i == 0) {
+            t_bad = bm != 0ull;
+            t_d = d;
+            t_e = e;
+        }
+    }
+    __syncthreads();
+    const int d = t_d, e = t_e;
+    for (int k = threadIdx.x; k < N; k += NT) {
+        int32_t* otok = a.out_tok + (size_t)b * N;
+        if (k < d) {
+            const int v = t_path[k];
+            a.out_path[(size_t)b * N + k] = v;
+            otok[k] = t_tok[v];
+            if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (float)(-rs.lnS[t_par[v]]);
+        } else {
+            a.out_path[(size_t)b * N + k] = -1;
+            otok[k] = (k == d) ? rs.g[e] : -1;
+            if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (k == d) ? (float)(-rs.lnS[e]) : 0.f;
+        }
+        if (a.out_blp) a.out_blp[(size_t)b * N + k] = 0.f;
+    }
+    if (threadIdx.x == 0) {
+        a.out_len[b] = d;
+        a.out_status[b] = t_bad;
+    }
+}
+
 // Greedy and tree: one workgroup (decide_threads) per request folds the tile
 // records (one row per wave), takes the decision and writes the outputs.
 template <typename T, int MODE, bool SUM, bool SHARD>
@@ -1372,10 +1460,6 @@ __global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
     } else {
         // tree: a node is accepted iff its token is its parent's argmax and
         // its parent is accepted; parents precede children
-        __shared__ int t_par[SPEC_MAX_NODES];
-        __shared__ int t_tok[SPEC_MAX_NODES];
-        __shared__ int t_path[SPEC_MAX_NODES];
-        __shared__ int t_d, t_e, t_bad;
         const int N = a.rows_t;
         // the node count, parents and tokens are loaded together, before the
         // fold, which takes every row of the request: records of rows past
@@ -1391,76 +1475,7 @@ __global__ __launch_bounds__(decide_threads(MODE)) void k_decide(const Args a) {
             __syncthreads();  // the exp table; every load above is in flight
         });
         if (!SHARD) clear_records(a, b);
-        const int nb = min(max(nraw, 1), N);
-        if (threadIdx.x < 64) {
-            // wave 0, lane i = node i.  Pointer jumping: `ok` says every node
-            // from i up to (not including) `anc` matches, `dep` counts those
-            // edges; each round doubles the span, so six rounds reach the root
-            // from any depth below 64.  A node that does not match (or is
-            // malformed, or lies beyond the tree) stops its chain with ok =
-            // false, which its descendants inherit.
-            const int i = threadIdx.x;
-            bool bad = false, match = false;
-            int par = -1;
-            if (i >= 1 && i < nb) {
-                bad = !(p >= 0 && p < i && (unsigned)t < (unsigned)a.Vtot);
-                par = bad ? -1 : p;
-                match = !bad && (t == rs.g[p]);
-            }
-            t_par[i] = par;
-            t_tok[i] = t;
-            const unsigned long long bm = __ballot(bad);
-            bool ok = (i == 0) || match;
-            int anc = match ? par : -1;
-            int dep = (i == 0) ? 0 : 1;
-#pragma unroll
-            for (int round = 0; round < 6; ++round) {
-                const int src = anc >= 0 ? anc : i;
-                const int ok_a = __shfl(ok ? 1 : 0, src);
-                const int dep_a = __shfl(dep, src);
-                const int anc_a = __shfl(anc, src);
-                if (anc >= 0) {
-                    ok = ok && ok_a;
-                    dep += dep_a;
-                    anc = anc_a;
-                }
-            }
-            // deepest accepted node, ties to the lowest index (the root is
-            // always accepted at depth 0)
-            const int key = ok ? (dep << 6) | (63 - i) : -1;
-            const int kmax = wave_max_i(key);
-            const int e = 63 - (kmax & 63), d = kmax >> 6;
-            int v = e;
-            for (int k = d - 1; k >= 0; --k) {
-                if (i == 0) t_path[k] = v;
-                v = __builtin_amdgcn_readlane(par, v);
-            }
-            if (i == 0) {
-                t_bad = bm != 0ull;
-                t_d = d;
-                t_e = e;
-            }
-        }
-        __syncthreads();
-        const int d = t_d, e = t_e;
-        for (int k = threadIdx.x; k < N; k += NT) {
-            int32_t* otok = a.out_tok + (size_t)b * N;
-            if (k < d) {
-                const int v = t_path[k];
-                a.out_path[(size_t)b * N + k] = v;
-                otok[k] = t_tok[v];
-                if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (float)(-rs.lnS[t_par[v]]);
-            } else {
-                a.out_path[(size_t)b * N + k] = -1;
-                otok[k] = (k == d) ? rs.g[e] : -1;
-                if (a.out_tlp) a.out_tlp[(size_t)b * N + k] = (k == d) ? (float)(-rs.lnS[e]) : 0.f;
-            }
-            if (a.out_blp) a.out_blp[(size_t)b * N + k] = 0.f;
-        }
-        if (threadIdx.x == 0) {
-            a.out_len[b] = d;
-            a.out_status[b] = t_bad;
-        }
+        tree_finish<NT>(a, b, rs, nraw, p, t);
     }
 }
 
@@ -2235,12 +2250,14 @@ __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& c
 }
 
 // Row r of request b, by one wave: waits for the row's published tile
-// records (lane = tile), folds them as fold_batches does (max, rank count,
-// fp64 sum rescaled to the row max), publishes the row's record
-// {M, count, S} and zeroes the tile records.  Returns false (in every lane)
-// if the wait ran out.
-template <int MODE>
+// records (lane = tile), folds them as fold_batches does (max with the
+// lowest index of the max for the greedy rules or the rank count for the
+// relaxed rule, and with SUM the fp64 sum rescaled to the row max),
+// publishes the row's record {M, argmax or count, S} and zeroes the tile
+// records.  Returns false (in every lane) if the wait ran out.
+template <int MODE, bool SUM = true>
 __device__ bool fold_publish_row(const Args& a, int b, int r, const double* tab) {
+    constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
     const int lane = threadIdx.x & 63;
     const bool have = lane < a.tpr;
@@ -2255,16 +2272,25 @@ __device__ bool fold_publish_row(const Args& a, int b, int r, const double* tab)
         if (it >= a.spin_limit) return false;
         __builtin_amdgcn_s_sleep(4);
     }
-    const Seg sg = have ? decode_record(w0, w1) : neutral_record(false);
-    const float M = wave_max(sg.m);
-    const int ic = COUNT ? wave_sum_i(sg.ic) : 0;
-    // tile sum * 2^(fl(m*L) - M*L), exact reference difference in fp64
-    double t = 0.0;
-    if (sg.m > -INFINITY) {
-        const float mL = sg.m * kLog2e;
-        t = sg.s * exp_nonpos(((double)mL - (double)M * (double)kLog2e) * kLn2, tab);
+    const Seg sg = have ? decode_record(w0, w1) : neutral_record(ARGMAX);
+    float M = sg.m;
+    int ic = sg.ic;
+    if (ARGMAX)
+        wave_argmax(M, ic);
+    else
+        M = wave_max(M);
+    if (COUNT) ic = wave_sum_i(ic);
+    if (!ARGMAX && !COUNT) ic = 0;
+    double S = 0.0;
+    if (SUM) {
+        // tile sum * 2^(fl(m*L) - M*L), exact reference difference in fp64
+        double t = 0.0;
+        if (sg.m > -INFINITY) {
+            const float mL = sg.m * kLog2e;
+            t = sg.s * exp_nonpos(((double)mL - (double)M * (double)kLog2e) * kLn2, tab);
+        }
+        S = wave_sum(t);
     }
-    const double S = wave_sum(t);
     if (have) {  // read: zero them for the next call
         store_word(src, 0ull);
         store_word(src + 1, 0ull);
@@ -2279,20 +2305,21 @@ __device__ bool fold_publish_row(const Args& a, int b, int r, const double* tab)
     return true;
 }
 
-// The R row records of request b into rs (lane = row, in waves 0 and 1;
-// R <= 2 * 64): one lane waits for the last row's record, then the lanes
-// read all of them, waiting for any still missing.  lnS = log S per row, in
-// parallel.  Returns false in a thread whose wait ran out.  Ends with a
-// barrier.
-template <int MODE>
-__device__ bool read_row_records(const Args& a, int b, RowStats& rs) {
+// Row records 0..nrows-1 of request b into rs (lane = row, in waves 0 and
+// 1; nrows <= 2 * 64): one lane waits for the last row's record, then the
+// lanes read all of them, waiting for any still missing.  With SUM, lnS =
+// log S per row, in parallel.  Returns false in a thread whose wait ran out.
+// Ends with a barrier.
+template <int MODE, bool SUM = true>
+__device__ bool read_row_records(const Args& a, int b, RowStats& rs, int nrows) {
+    constexpr bool ARGMAX = (MODE == kGreedy || MODE == kTree);
     constexpr bool COUNT = (MODE == kRelaxed);
     const int tid = threadIdx.x;
     __shared__ int s_hint;
     bool ok = true;
     if (tid == 0) {
         s_hint = 1;
-        const uint64_t* hint = a.frow + 2 * ((size_t)b * a.R + a.R - 1);
+        const uint64_t* hint = a.frow + 2 * ((size_t)b * a.R + nrows - 1);
         for (int it = 0; load_word(hint) == 0ull; ++it) {
             if (it >= a.spin_limit) {
                 s_hint = 0;
@@ -2304,7 +2331,7 @@ __device__ bool read_row_records(const Args& a, int b, RowStats& rs) {
     __syncthreads();
     if (!s_hint) ok = false;
     if (ok && tid < 128) {
-        const bool have = tid < a.R;
+        const bool have = tid < nrows;
         const uint64_t* src = a.frow + 2 * ((size_t)b * a.R + (have ? tid : 0));
         uint64_t w0 = 0ull, w1 = 0ull;
         for (int it = 0;; ++it) {
@@ -2322,9 +2349,9 @@ __device__ bool read_row_records(const Args& a, int b, RowStats& rs) {
         if (ok && have) {
             const Seg sg = decode_record(w0, w1);
             rs.M[tid] = sg.m;
-            rs.g[tid] = 0;
+            rs.g[tid] = ARGMAX ? sg.ic : 0;
             rs.c[tid] = COUNT ? sg.ic : 0;
-            rs.lnS[tid] = log(sg.s);
+            rs.lnS[tid] = SUM ? log(sg.s) : 0.0;
         }
     }
     __syncthreads();
@@ -2360,7 +2387,7 @@ __device__ void sweep_role(const Args& a, const int idx) {
     for (int r = c; r < a.R; r += a.C2)
         if (wave == 0 && !fold_publish_row<MODE>(a, b, r, tab) && lane == 0) s_ok = 0;
     if (tid < 64) chain_load_inputs<T, MODE>(a, b, cv);
-    if (!read_row_records<MODE>(a, b, rs)) s_ok = 0;
+    if (!read_row_records<MODE>(a, b, rs, a.R)) s_ok = 0;
     __syncthreads();
     if (!s_ok) {  // a record never arrived: report, leave the words as they are
         if (tid == 0) a.out_status[b] = 2;
@@ -2541,6 +2568,75 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_greedy(const 
         return;
     }
     greedy_role<T, SUM>(a, (int)(blockIdx.x - P));
+}
+
+// Folding workgroups of the tree rule's single launch: workgroup f of
+// request b folds rows kWaves*f + w (wave w), those below the request's node
+// count (the stream reads no other row), and publishes their row records.
+__device__ inline int tree_node_count(const Args& a, int b) {
+    return min(max(a.num_nodes ? a.num_nodes[b] : a.rows_t, 1), a.rows_t);
+}
+
+template <bool SUM>
+__device__ void tree_fold_role(const Args& a, const int idx) {
+    const int fpr = (a.R + kWaves - 1) / kWaves;  // folding workgroups per request
+    const int b = idx / fpr, f = idx - b * fpr;
+    __shared__ double tab[kExpTab];
+    if (SUM) {
+        fill_exp_table(tab);
+        __syncthreads();
+    }
+    const int r = f * kWaves + (int)(threadIdx.x >> 6);
+    if (r < tree_node_count(a, b)) fold_publish_row<kTree, SUM>(a, b, r, tab);
+}
+
+// The deciding workgroup of request b in the tree rule's single launch: the
+// node count, parents and tokens are loaded first, then the row records of
+// the nodes (lane = node), which it zeroes; then the tree decision.
+template <bool SUM>
+__device__ void tree_decide_role(const Args& a, const int b) {
+    const int tid = threadIdx.x, N = a.rows_t;
+    __shared__ RowStats rs;
+    __shared__ int s_ok;
+    const int nraw = a.num_nodes ? a.num_nodes[b] : N;
+    int p = -1, t = -1;
+    if (tid >= 1 && tid < N) {
+        p = a.parents[b * N + tid];
+        t = a.tok[b * N + tid];
+    }
+    if (tid == 0) s_ok = 1;
+    const int nb = min(max(nraw, 1), N);
+    if (!read_row_records<kTree, SUM>(a, b, rs, nb)) s_ok = 0;
+    __syncthreads();
+    if (!s_ok) {  // a row record never arrived: report, leave the words as they are
+        if (tid == 0) a.out_status[b] = 2;
+        return;
+    }
+    uint64_t* w = a.frow + 2 * (size_t)b * a.R;
+    for (int i = tid; i < 2 * nb; i += kThreads) store_word(w + i, 0ull);
+    tree_finish<kThreads>(a, b, rs, nraw, p, t);
+}
+
+// The tree rule as one launch: one workgroup per tile streams it and
+// publishes its record (nstream = the tile count), then the folding
+// workgroups (kWaves rows each), then one deciding workgroup per request.  Workgroups start in index order: a
+// folding workgroup waits only on streaming ones, which never wait, and a
+// deciding workgroup only on folding ones.
+template <typename T, bool SUM, bool VECP>
+__global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_tree(const Args a) {
+    const unsigned P = (unsigned)a.nstream;
+    const unsigned nfold = (unsigned)a.B * (unsigned)((a.R + kWaves - 1) / kWaves);
+    if (blockIdx.x < P) {
+        // one tile per workgroup (a loop over tiles keeps more registers
+        // live and spills)
+        stream_tile<T, kTree, SUM, VECP, false, false, kTileVecs, true>(a, blockIdx.x);
+        return;
+    }
+    if (blockIdx.x < P + nfold) {
+        tree_fold_role<SUM>(a, (int)(blockIdx.x - P));
+        return;
+    }
+    tree_decide_role<SUM>(a, (int)(blockIdx.x - P - nfold));
 }
 
 // The draw of sampled row g, by the row's drawing workgroup of the sampler's
@@ -2740,6 +2836,11 @@ inline int compute_units() {
     return cus;
 }
 inline int stream_workgroups() { return kStreamPerCu * compute_units(); }
+// Streaming workgroups of the greedy and tree launches: one per tile
+// (measured faster than a grid-stride loop for the greedy rule at these
+// sizes), up to a cap that keeps the grid far below 2^32 threads; above it
+// they loop.
+constexpr int kMaxStreamGroups = 1 << 20;
 inline int tile_elems(spec_dtype dt) { return kTileBytes / esize(dt); }
 inline int tpr_of(spec_dtype dt, int V) { return (V + tile_elems(dt) - 1) / tile_elems(dt); }
 constexpr int kSmallTileElems = kThreads * kSmallTileVecs * 8;  // bf16 elements of an 8 KiB tile
@@ -2799,23 +2900,34 @@ inline void take_prof(hipEvent_t (&ev)[3]) {
     }
 }
 
-// The tree rule: the streaming kernel, then one deciding workgroup per
-// request (k_decide).  With the profiling hook set, the streaming kernel is
-// launched with start/stop events that the dispatch itself timestamps, so
-// their interval is the kernel's own duration.
+// The tree rule's single launch (k_tree): one streaming workgroup per tile,
+// the folding workgroups, one deciding workgroup per request (tree_grid_ok
+// bounds the grid).  With the profiling hook set, the launch carries the start and
+// stop events.
 template <bool SUM>
 spec_status launch_tree(Args a, spec_dtype dt, hipStream_t st) {
     a.tpr = tpr_of(dt, a.V);
     a.Vtot = a.V;
     const Layout lay = make_layout(a.B, a.R, a.tpr, a.C2);
-    a.segs = reinterpret_cast<Seg*>(a.ws + lay.seg);
+    a.frec = reinterpret_cast<uint64_t*>(a.ws + lay.frec);
+    a.frow = reinterpret_cast<uint64_t*>(a.ws + lay.frow);
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    a.nstream = a.B * a.R * a.tpr;
+    const unsigned nfold = (unsigned)a.B * (unsigned)((a.R + kWaves - 1) / kWaves);
+    const dim3 grid((unsigned)a.nstream + nfold + (unsigned)a.B), block(kThreads);
     hipEvent_t ev[3];
     take_prof(ev);
-    if (launch_stream<kTree, SUM, false>(a, dt, st, ev[0], ev[1]) != SPEC_OK) return SPEC_EHIP;
-    if (dt == SPEC_BF16)
-        hipLaunchKernelGGL((k_decide<uint16_t, kTree, SUM, false>), dim3(a.B), dim3(decide_threads(kTree)), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_decide<float, kTree, SUM, false>), dim3(a.B), dim3(decide_threads(kTree)), 0, st, a);
+    if (dt == SPEC_BF16) {
+        if (a.vec_t)
+            hipExtLaunchKernelGGL((k_tree<uint16_t, SUM, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        else
+            hipExtLaunchKernelGGL((k_tree<uint16_t, SUM, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
+    } else {
+        if (a.vec_t)
+            hipExtLaunchKernelGGL((k_tree<float, SUM, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        else
+            hipExtLaunchKernelGGL((k_tree<float, SUM, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
+    }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
@@ -2862,10 +2974,6 @@ spec_status launch_single(Args a, spec_dtype dt, hipStream_t st) {
 inline bool greedy_small_tiles(spec_dtype dt, int V, long long rows, bool logprobs) {
     return !logprobs && dt == SPEC_BF16 && rows * tpr_of(dt, V) < stream_workgroups();
 }
-// Streaming workgroups of the greedy launch: one per tile (measured faster
-// than a grid-stride loop at these sizes), up to a cap that keeps the grid
-// far below 2^32 threads; above it they loop.
-constexpr int kMaxStreamGroups = 1 << 20;
 
 template <typename T, bool SUM, int NV>
 void launch_greedy_kernel(const Args& a, bool vecp, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
@@ -2899,6 +3007,13 @@ spec_status launch_greedy(Args a, spec_dtype dt, hipStream_t st) {
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
+}
+
+// The tree launch's grid (one workgroup per tile, the folding workgroups,
+// one deciding workgroup per request) stays below 2^32 threads.
+inline bool tree_grid_ok(spec_dtype dt, int B, int N, int V) {
+    const long long wg = (long long)B * N * tpr_of(dt, V) + (long long)B * ((N + kWaves - 1) / kWaves) + B;
+    return wg * kThreads < (1ll << 32);
 }
 
 // The single launch's grid (streaming tiles plus one sweep workgroup per
@@ -3276,7 +3391,8 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dtype,
                              int32_t* out_status, void* workspace, size_t workspace_bytes,
                              void* stream) {
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (N < 1 || N > SPEC_MAX_NODES || !sizes_ok(dtype, B, 1, V, N)) return SPEC_EINVAL;
+    if (N < 1 || N > SPEC_MAX_NODES || !sizes_ok(dtype, B, 1, V, N) || !tree_grid_ok(dtype, B, N, V))
+        return SPEC_EINVAL;
     if (!target_logits || !node_tokens || !parents || !out_path_nodes || !out_tokens ||
         !out_accept_len || !out_status)
         return SPEC_EINVAL;

@@ -324,6 +324,16 @@ def test_workspace_reuse_across_shapes():
                       what=f"reuse exact {B},{K},{V}")
         compare_chain(g, oracle.greedy(ci.target, ci.tokens, "bf16"), what=f"reuse greedy {B}")
         assert int(ws.count_nonzero()) == 0, f"workspace left dirty after B={B} K={K} V={V}"
+    # the tree rule's single launch on the same workspace, partial node counts
+    ti = synth.tree_inputs(B=6, V=3001, seed=76)
+    ti.num_nodes = np.array([61, 1, 2, 30, 60, 17], np.int32)
+    for logprobs in (False, True):
+        r = sv.spec_verify_tree(dev_logits(ti.target, "bf16"), dev(ti.node_tok), dev(ti.parents),
+                                dev(ti.num_nodes), logprobs=logprobs, workspace=ws)
+        torch.cuda.synchronize()
+        compare_tree(r, oracle.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes),
+                     logprobs=logprobs, what=f"reuse tree logprobs={logprobs}")
+        assert int(ws.count_nonzero()) == 0, f"workspace left dirty after the tree (logprobs={logprobs})"
 
 
 # --------------------------------------------------------- statistical pin
