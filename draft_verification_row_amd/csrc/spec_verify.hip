@@ -2384,8 +2384,10 @@ __device__ void sweep_role(const Args& a, const int idx) {
     if (tid == 0) s_ok = 1;
     fill_exp_table(tab);
     __syncthreads();  // the exp table, s_ok
-    for (int r = c; r < a.R; r += a.C2)
-        if (wave == 0 && !fold_publish_row<MODE>(a, b, r, tab) && lane == 0) s_ok = 0;
+    // (wave w takes the workgroup's rows w, w + kWaves, ...: with fewer
+    // chunks than rows, a workgroup's rows are folded in parallel)
+    for (int r = c + a.C2 * wave; r < a.R; r += a.C2 * kWaves)
+        if (!fold_publish_row<MODE>(a, b, r, tab) && lane == 0) s_ok = 0;
     if (tid < 64) chain_load_inputs<T, MODE>(a, b, cv);
     if (!read_row_records<MODE>(a, b, rs, a.R)) s_ok = 0;
     __syncthreads();
