@@ -18,7 +18,7 @@ import torch
 import draft_verification_row_amd as sv
 import oracle
 import synth
-from parity import compare_chain, dev, dev_logits
+from parity import compare_chain, compare_tree, dev, dev_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,17 @@ def zero_spin_limit():
     sv.spec_set_spin_limit(0)
     try:
         yield
+    finally:
+        sv.spec_set_spin_limit(-1)
+
+
+@pytest.fixture(params=[0, 4])
+def small_spin_limit(request):
+    """0: every wait that is not already satisfied gives up; 4: a few polling
+    rounds, so that some requests complete and some do not."""
+    sv.spec_set_spin_limit(request.param)
+    try:
+        yield request.param
     finally:
         sv.spec_set_spin_limit(-1)
 
@@ -64,9 +75,9 @@ def _chain_cases(ci):
     ]
 
 
-def test_chain_rules_time_out_cleanly(zero_spin_limit):
-    """B=32, K=5, V=128256 bf16: every status in {0, 1, 2}; the requests that
-    did not time out equal the oracle's."""
+def test_chain_rules_time_out_cleanly(small_spin_limit):
+    """B=32, K=5, V=128256 bf16 at a small bound: every status in {0, 1, 2};
+    the requests that did not time out equal the oracle's."""
     ci = synth.exact_b32_k5()
     B, V = ci.B, ci.V
     timed_out = {}
@@ -82,7 +93,7 @@ def test_chain_rules_time_out_cleanly(zero_spin_limit):
             compare_chain(_keep(r, keep), _keep_oracle(orc(), keep), logprobs=lp,
                           what=f"{name}, zero spin limit")
         del ws
-    print("requests timed out per rule:", timed_out, flush=True)
+    print(f"spin limit {small_spin_limit}: requests timed out per rule:", timed_out, flush=True)
 
 
 def test_sampler_times_out_cleanly(zero_spin_limit):
@@ -99,6 +110,28 @@ def test_sampler_times_out_cleanly(zero_spin_limit):
     o = oracle.sample(rows, u, "bf16")
     keep = (st == 0) & (o.flag < 0)
     assert (r.tokens.cpu().numpy()[keep] == o.tokens[keep]).all()
+
+
+def test_tree_times_out_cleanly(zero_spin_limit):
+    """The tree rule (B=8, 61 nodes, V=128256): status in {0, 1, 2}; requests
+    that did not time out equal the oracle's."""
+    ti = synth.tree_b8_n61()
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(ti.B, ti.N, ti.V), dtype=torch.uint8, device="cuda")
+    r = sv.spec_verify_tree(dev_logits(ti.target, "bf16"), dev(ti.node_tok), dev(ti.parents),
+                            dev(ti.num_nodes), workspace=ws)
+    torch.cuda.synchronize()
+    st = r.status.cpu().numpy()
+    assert set(np.unique(st).tolist()) <= {0, 1, 2}, st
+    keep = st != 2
+    o = oracle.tree(ti.target, ti.node_tok, ti.parents, "bf16", num_nodes=ti.num_nodes)
+    k = torch.from_numpy(keep).cuda()
+    sub = SimpleNamespace(path_nodes=r.path_nodes[k], tokens=r.tokens[k], accept_len=r.accept_len[k],
+                          status=r.status[k], target_logprob=r.target_logprob[k],
+                          behavior_logprob=r.behavior_logprob[k])
+    osub = SimpleNamespace(path=o.path[keep], tokens=o.tokens[keep], accept_len=o.accept_len[keep],
+                           status=o.status[keep], target_logprob=o.target_logprob[keep])
+    compare_tree(sub, osub, what="tree, zero spin limit")
+    print("tree requests timed out:", int((~keep).sum()), flush=True)
 
 
 def test_default_limit_restored_after_timeouts():
