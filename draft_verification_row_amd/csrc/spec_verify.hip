@@ -137,27 +137,21 @@ struct alignas(16) ChunkSums {
 };
 
 struct Layout {
-    size_t seg, dec, sums, xv;  // records, decisions, chunk sums, drafted-token logits
-    size_t frec, fsums, frow;  // single-launch calls: published words
+    size_t frec, fsums, frow;  // published tile, chunk and row records
     size_t total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// [tile records B*R*tpr][decisions B][chunk sums B*C2][drafted-token logits
-// B*K*2, sized B*R*2][published tile records B*R*tpr, two words each]
-// [published chunk records B*C2, eleven words each][published row records
-// B*R, two words each].  The workspace is
-// zero when a call starts (zero-filled once by its owner) and every call
-// leaves every byte it wrote zero again, whatever the rule or shape: the
-// single-launch calls read zero as "not published yet".
+// The workspace of an unsharded call: [published tile records B*R*tpr, two
+// words each][published chunk records B*C2, eleven words each][published
+// row records B*R, two words each].  It is zero when a call starts
+// (zero-filled once by its owner) and every call leaves every byte it wrote
+// zero again, whatever the rule or shape: the single-launch calls read zero
+// as "not published yet".
 inline Layout make_layout(int B, int R, int tpr, int C2) {
     Layout L;
-    L.seg = 0;
-    L.dec = align_up(L.seg + (size_t)B * R * tpr * 16, 256);
-    L.sums = align_up(L.dec + (size_t)B * 64, 256);
-    L.xv = align_up(L.sums + (size_t)B * C2 * sizeof(ChunkSums), 256);
-    L.frec = align_up(L.xv + (size_t)B * R * 8, 256);
+    L.frec = 0;
     L.fsums = align_up(L.frec + (size_t)B * R * tpr * 16, 256);
     L.frow = align_up(L.fsums + (size_t)B * C2 * (3 + 2 * (kChunk / 1024)) * 8, 256);
     L.total = align_up(L.frow + (size_t)B * R * 16, 256);
@@ -3127,7 +3121,7 @@ bool dtype_ok(const spec_dtype& dt) {
 // the chunk-sum region) and a row-count tail that the size query has always
 // included.
 size_t sample_layout_bytes(int rows, int V, spec_dtype dt) {
-    return make_layout(rows, 1, tpr_of(dt, V), c2_of(dt, V)).total + align_up((size_t)rows * 4, 256);
+    return make_layout(rows, 1, tpr_of(dt, V), c2_of(dt, V)).total;
 }
 
 bool sizes_ok(spec_dtype dt, int B, int K, int V, long rows_per_req) {
@@ -3802,6 +3796,16 @@ spec_status scratch_on_current_device(void** out) {
     return SPEC_OK;
 }
 
+// Zeroes n bytes (a multiple of 16) at p with vector stores: the single-launch
+// protocol reads a zero word as "not published yet", and a call that timed out
+// may have left words behind.  A kernel rather than hipMemsetAsync, so that the
+// call can be captured into a HIP graph.
+__global__ __launch_bounds__(kThreads) void k_zero(uint4* p, size_t n16) {
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += (size_t)gridDim.x * kThreads)
+        p[i] = z;
+}
+
 }  // namespace
 
 extern "C" spec_status spec_verify_exact_noalloc(const void* target_logits, const void* draft_logits,
@@ -3822,6 +3826,14 @@ extern "C" spec_status spec_verify_exact_noalloc(const void* target_logits, cons
     void* ws = nullptr;
     const spec_status s = scratch_on_current_device(&ws);
     if (s != SPEC_OK) return s;
+    // need is a multiple of 256 (make_layout aligns every region)
+    const size_t n16 = need / 16;
+    if (n16 > 0) {
+        const size_t want = (n16 + kThreads - 1) / kThreads;
+        const unsigned blocks = (unsigned)(want < 1024 ? want : 1024);
+        hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, (uint4*)ws, n16);
+        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    }
     return spec_verify_exact(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K, V,
                              out_tokens, out_accept_len, out_target_logprob, out_behavior_logprob,
                              out_status, ws, SPEC_NOALLOC_SCRATCH_BYTES, stream);

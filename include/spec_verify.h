@@ -458,21 +458,24 @@ spec_status spec_shard_sample_exact(const void *target_shard, const void *draft_
  * Exact verification that allocates nothing, for callers that cannot call
  * hipMalloc: code under HIP graph capture, serving loops and harnesses that
  * forbid device allocation.  Same rule, arguments and outputs as
- * spec_verify_exact, without the workspace: the call's per-tile records,
- * decisions and chunk sums go to a static device array of
- * SPEC_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
- * on until the process ends.  A call whose workspace size
- * (spec_verify_workspace_bytes(B, 2K+1, V)) exceeds it returns SPEC_ESCRATCH
- * before anything is enqueued; 4 MiB covers, for example, B = 64, K = 8 at
- * V = 262144 in fp32.  The library makes no allocating call on this path.
+ * spec_verify_exact, without the workspace: the records the call's
+ * workgroups publish to each other (tile, row and chunk records) go to a
+ * static device array of SPEC_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends.  A call whose workspace
+ * size (spec_verify_workspace_bytes(B, 2K+1, V)) exceeds it returns
+ * SPEC_ESCRATCH before anything is enqueued; 4 MiB covers, for example,
+ * B = 128, K = 8 at V = 262144 in fp32.  The library makes no allocating
+ * call on this path.
  *
- * The array is per device and shared by every call on that device, and each
- * call writes every byte of it that it reads before reading it (nothing
- * needs clearing, and the previous call's contents never matter).  Calls
- * that overlap on one device -- on different streams, or from several
- * threads without ordering -- race on it and corrupt each other's results;
- * calls ordered on one stream are fine.  The device is the calling thread's
- * current HIP device, which must be the one the stream belongs to.
+ * The array is per device and shared by every call on that device.  Each
+ * call first zeroes the part it uses, with a fill kernel on the same stream
+ * (not hipMemsetAsync, so the call may be captured into a HIP graph): the
+ * previous call's contents never matter, even when that call timed out
+ * (status 2).  Calls that overlap on one device -- on different streams, or
+ * from several threads without ordering -- race on it and corrupt each
+ * other's results; calls ordered on one stream are fine.  The device is the
+ * calling thread's current HIP device, which must be the one the stream
+ * belongs to.
  */
 #define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
 spec_status spec_verify_exact_noalloc(const void *target_logits, const void *draft_logits,

@@ -3,7 +3,8 @@ workspace entry point it is a variant of (spec_verify_exact), through the C
 ABI: two calls in a row on the same device, the second with a smaller input,
 each bit-identical to spec_verify_exact on the same inputs and within the
 parity rule of the fp64 oracle.  The second call reuses the static scratch
-array the first one filled, so stale contents must not matter."""
+array the first one filled, so stale contents must not matter; nor may the
+words a call that timed out (status 2) left behind."""
 import ctypes
 
 import numpy as np
@@ -58,6 +59,30 @@ def test_noalloc_matches_workspace_call_twice_then_smaller(dtype):
     torch.cuda.synchronize()
     compare_chain(got, oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, dtype),
                   logprobs=False, what="no-alloc exact without log-probs")
+
+
+def test_noalloc_after_a_timed_out_call():
+    """A call at a zero wait bound may leave published words in the shared
+    array; the next call at the default bound zeroes what it uses first and
+    must equal spec_verify_exact and the oracle."""
+    lib = sv.load_library()
+    ci = synth.exact_b32_k5()
+    T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
+    x, u = dev(ci.tokens), dev(ci.uniforms)
+    sv.spec_set_spin_limit(0)
+    try:
+        first = _noalloc(lib, T, D, x, u)
+        torch.cuda.synchronize()
+    finally:
+        sv.spec_set_spin_limit(-1)
+    print("requests timed out at a zero bound:", int((first.status == 2).sum()), flush=True)
+    got = _noalloc(lib, T, D, x, u)
+    want = sv.spec_verify_exact(T, D, x, u)
+    torch.cuda.synchronize()
+    for a, b, name in zip(got, want, want._fields):
+        assert torch.equal(a, b), f"{name} differs from spec_verify_exact after a timed-out call"
+    compare_chain(got, oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
+                  what="no-alloc exact after a timed-out call")
 
 
 def test_noalloc_rejects_calls_beyond_the_scratch_array():
