@@ -144,7 +144,8 @@ struct Layout {
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // The workspace of an unsharded call: [published tile records B*R*tpr, two
-// words each][published chunk records B*C2, eleven words each][published
+// words each][published chunk records: B*2*C2 sweep records of seven words
+// or B*C2 of eleven, or the draft sampler's two words per chunk][published
 // row records B*R, two words each].  It is zero when a call starts
 // (zero-filled once by its owner) and every call leaves every byte it wrote
 // zero again, whatever the rule or shape: the single-launch calls read zero
@@ -153,7 +154,7 @@ inline Layout make_layout(int B, int R, int tpr, int C2) {
     Layout L;
     L.frec = 0;
     L.fsums = align_up(L.frec + (size_t)B * R * tpr * 16, 256);
-    L.frow = align_up(L.fsums + (size_t)B * C2 * (3 + 2 * (kChunk / 1024)) * 8, 256);
+    L.frow = align_up(L.fsums + (size_t)B * C2 * (kChunk / 2048) * (3 + 2 * (2048 / 1024)) * 8, 256);
     L.total = align_up(L.frow + (size_t)B * R * 16, 256);
     return L;
 }
@@ -604,6 +605,7 @@ struct Args {
     int R;       // rows streamed per request
     int tpr;     // streaming tiles per row
     int C2;      // pass-2 chunks per row
+    int C2s;        // single launch: 2048-token sweep chunks per request
     int vec_t, vec_d;
     float tau;
     float alpha;  // power rule exponent
@@ -630,7 +632,7 @@ struct Args {
     int32_t* out_owner;    // [B] shard holding the terminal draw, or null
     // single-launch calls: published words
     uint64_t* frec;     // [B][R][tpr] tile records, two words each
-    uint64_t* fsums;    // [B][C2] chunk records, eleven words each
+    uint64_t* fsums;    // [B][sweep workgroups] sweep records (sweep_words words each)
     uint64_t* frow;     // [B][R] folded row records, two words each
     int nstream;        // workgroups of the launch that stream tiles
     int spin_limit;     // polling rounds of a wait before it gives up (status 2)
@@ -1890,7 +1892,20 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
 // classified p > q for a residual draw, the target exp sum otherwise).
 constexpr int kSub = 1024;
 constexpr int kSubs = kChunk / kSub;
-constexpr int kChunkWords = 3 + 2 * kSubs;
+
+// A sweep workgroup sums PER * kSweepChunk tokens (PER = 1 or 2: half of a
+// draw chunk or all of it) and publishes one record: S, Sq, dmin and its
+// sub-chunks' two sums (3 + 2 * PER * kSweepSubs words: seven or eleven).
+// The drawer's lane l combines the kSweepSplit / PER records of draw chunk l.
+// Half-chunk sweeps give twice the workgroups, each with half the fp64 work,
+// which shortens the slowest one while the chip holds them all at once.
+constexpr int kSweepChunk = 2048;
+constexpr int kSweepSplit = kChunk / kSweepChunk;
+constexpr int kSweepSubs = kSweepChunk / kSub;
+constexpr int sweep_words(int per) { return 3 + 2 * per * kSweepSubs; }
+static_assert(kSweepSplit * kSweepChunk == kChunk && kSweepSubs * kSub == kSweepChunk, "whole sub-chunks");
+static_assert(kSweepChunk == 2048 && sweep_words(1) == 7 && sweep_words(2) == 11,
+              "make_layout sizes the sweep records");
 
 // Drafted-token logits read from the inputs (the token is loaded first, so
 // these loads wait for it; they overlap the wait for the records).
@@ -1922,11 +1937,11 @@ __device__ inline double draw_weight(bool res, float l, float d, double Mt, doub
 // Zeroes request b's published row and chunk records (every thread; after
 // all of the request's reads of them).  Its tile records were zeroed by the
 // workgroups that folded them.
-__device__ inline void clear_published(const Args& a, int b) {
+__device__ inline void clear_published(const Args& a, int b, int sums_words) {
     uint64_t* r = a.frow + (size_t)b * a.R * 2;
     for (int i = threadIdx.x; i < a.R * 2; i += blockDim.x) store_word(r + i, 0ull);
-    uint64_t* m = a.fsums + (size_t)b * a.C2 * kChunkWords;
-    for (int i = threadIdx.x; i < a.C2 * kChunkWords; i += blockDim.x) store_word(m + i, 0ull);
+    uint64_t* m = a.fsums + (size_t)b * sums_words;
+    for (int i = threadIdx.x; i < sums_words; i += blockDim.x) store_word(m + i, 0ull);
 }
 
 // The terminal draw of request b, by the sweep workgroup of its last chunk.
@@ -1936,12 +1951,16 @@ __device__ inline void clear_published(const Args& a, int b) {
 // scans the chunks and then the sub-chunks of the chunk holding u_K * Z.
 // The workgroup rescans that sub-chunk, four consecutive tokens per thread,
 // with a block scan, and writes the terminal token and its log-probs.
-template <typename T, int MODE>
+template <typename T, int MODE, int PER>
 __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& cd, const RowStats& rs,
                               const double* tab) {
     constexpr bool EXACT = (MODE == kExact);
     constexpr int NT = kThreads, NWV = NT / 64, RUN = kSub / NT;
     static_assert(RUN == 4, "four tokens per thread (one load4 per row)");
+    constexpr int RPL = kSweepSplit / PER;     // sweep records per draw chunk (lane)
+    constexpr int WPR = sweep_words(PER);      // words per record
+    constexpr int SPR = PER * kSweepSubs;      // sub-chunks per record
+    const int nrec = (a.C2s + PER - 1) / PER;  // the request's sweep records
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
     const int n = cd.n;
     const bool residual = EXACT && n < a.K;
@@ -2028,25 +2047,42 @@ __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& c
     };
     if (wave == 0) {
         bool ok = true;
-        uint64_t w[kChunkWords];
+        // lane l: the records RPL*l + j of draw chunk l that exist
+        uint64_t w[RPL][WPR];
+        bool have[RPL];
+        const uint64_t* src[RPL];
 #pragma unroll
-        for (int i = 0; i < kChunkWords; ++i) w[i] = kTop;  // lanes past the last chunk: zero sums
-        const bool have = lane < a.C2;
-        const uint64_t* src = a.fsums + ((size_t)b * a.C2 + (have ? lane : 0)) * kChunkWords;
+        for (int j = 0; j < RPL; ++j) {
+            const int cs = RPL * lane + j;
+            have[j] = lane < a.C2 && cs < nrec;
+            src[j] = a.fsums + ((size_t)b * nrec + (have[j] ? cs : 0)) * WPR;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i) w[j][i] = kTop;  // absent: zero sums
+        }
         // the other chunks' workgroups may still be summing: first wait for
-        // every chunk's first word (one load per chunk a round), then read
+        // every record's first word (one load per record a round), then read
         // all words (every word each round, the round's loads in flight
         // together) until none is missing
         for (int it = 0, all = 0;; ++it) {
             bool missing = false;
-            if (have) {
+#pragma unroll
+            for (int j = 0; j < RPL; ++j) {
+                if (!have[j]) continue;
                 if (all) {
 #pragma unroll
-                    for (int i = 0; i < kChunkWords; ++i) w[i] = load_word(src + i);
-#pragma unroll
-                    for (int i = 0; i < kChunkWords; ++i) missing |= w[i] == 0ull;
+                    for (int i = 0; i < WPR; ++i) w[j][i] = load_word(src[j] + i);
                 } else {
-                    missing = load_word(src) == 0ull;
+                    w[j][0] = load_word(src[j]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < RPL; ++j) {
+                if (!have[j]) continue;
+                if (all) {
+#pragma unroll
+                    for (int i = 0; i < WPR; ++i) missing |= w[j][i] == 0ull;
+                } else {
+                    missing |= w[j][0] == 0ull;
                 }
             }
             const bool none = __ballot(missing) == 0ull;
@@ -2062,15 +2098,21 @@ __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& c
             __builtin_amdgcn_s_sleep(4);
         }
         const bool all_ok = __ballot(!ok) == 0ull;
-        const double sa = dec_nonneg(w[0]), sb = dec_nonneg(w[1]);
-        const double dmin = lane < a.C2 ? dec_nonneg(w[2]) : INFINITY;
+        double sa = 0.0, sb = 0.0, dmin = INFINITY;
+#pragma unroll
+        for (int j = 0; j < RPL; ++j) {
+            sa += dec_nonneg(w[j][0]);
+            sb += dec_nonneg(w[j][1]);
+            if (have[j]) dmin = fmin(dmin, dec_nonneg(w[j][2]));
+        }
         S = wave_sum(sa);
         const double Sq = residual ? wave_sum(sb) : 1.0;
         const double iS = 1.0 / S, iSq = 1.0 / Sq;
         double W[kSubs];
 #pragma unroll
         for (int k = 0; k < kSubs; ++k) {
-            const double A = dec_nonneg(w[3 + 2 * k]), Bq = dec_nonneg(w[4 + 2 * k]);
+            const int j = k / SPR, kk = k - j * SPR;
+            const double A = dec_nonneg(w[j][3 + 2 * kk]), Bq = dec_nonneg(w[j][4 + 2 * kk]);
             // residual mass of the sub-chunk (clamped: rounding can leave a
             // rounding-size negative), or its p mass
             W[k] = residual ? fmax(A * iS - Bq * iSq, 0.0) : A;
@@ -2240,7 +2282,7 @@ __device__ void draw_terminal(const Args& a, const int b, const ChainDecision& c
         a.out_status[b] = cd.bad_n;
     }
     __syncthreads();  // every read of the request's published words is done
-    clear_published(a, b);
+    clear_published(a, b, nrec * WPR);
 }
 
 // Row r of request b, by one wave: waits for the row's published tile
@@ -2352,13 +2394,16 @@ __device__ bool read_row_records(const Args& a, int b, RowStats& rs, int nrows) 
     return ok;
 }
 
-// One sweep workgroup: request idx / C2, chunk idx % C2.
-template <typename T, int MODE>
+// One sweep workgroup: request idx / C2w, tokens [PER * kSweepChunk * c,
+// PER * kSweepChunk * (c + 1)) with c = idx % C2w; publishes one record.
+template <typename T, int MODE, int PER>
 __device__ void sweep_role(const Args& a, const int idx) {
     constexpr bool EXACT = (MODE == kExact);
     constexpr int VEC = Elem<T>::kVec;
-    constexpr int NV = kRun / VEC;  // 16-byte vectors per thread
-    const int b = idx / a.C2, c = idx - b * a.C2;
+    constexpr int NV = PER * kSweepChunk / kThreads / VEC;  // 16-byte vectors per thread
+    static_assert(NV * VEC * kThreads == PER * kSweepChunk && PER <= kSweepSplit, "whole vectors per thread");
+    const int C2w = (a.C2s + PER - 1) / PER;  // sweep workgroups per request
+    const int b = idx / C2w, c = idx - b * C2w;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
     __shared__ double tab[kExpTab];
     __shared__ RowStats rs;
@@ -2366,7 +2411,7 @@ __device__ void sweep_role(const Args& a, const int idx) {
     __shared__ double red[kWaves][3 + 2 * NV];
     __shared__ int s_ok;
     // Each row of the request is folded once: the request's sweep workgroup
-    // c takes rows c, c + C2, ... (only the first R workgroups have one) and
+    // c takes rows c, c + C2w, ... (only the first R workgroups have one) and
     // publishes the row's record; then every sweep workgroup of the request
     // reads the R row records.  A workgroup waits only on streaming
     // workgroups and on its own request's first R sweep workgroups, which
@@ -2380,7 +2425,7 @@ __device__ void sweep_role(const Args& a, const int idx) {
     __syncthreads();  // the exp table, s_ok
     // (wave w takes the workgroup's rows w, w + kWaves, ...: with fewer
     // chunks than rows, a workgroup's rows are folded in parallel)
-    for (int r = c + a.C2 * wave; r < a.R; r += a.C2 * kWaves)
+    for (int r = c + C2w * wave; r < a.R; r += C2w * kWaves)
         if (!fold_publish_row<MODE>(a, b, r, tab) && lane == 0) s_ok = 0;
     if (tid < 64) chain_load_inputs<T, MODE>(a, b, cv);
     if (!read_row_records<MODE>(a, b, rs, a.R)) s_ok = 0;
@@ -2400,11 +2445,12 @@ __device__ void sweep_role(const Args& a, const int idx) {
     // every sweep workgroup of the request did (it waits for all their sums)
     if (c == 0) write_prefix<MODE>(a, b, cd, false);
 
-    // this thread's vectors k cover tokens c*kChunk + (k*kThreads + tid)*VEC +
-    // [0, VEC): vector k lies in sub-chunk ((k*kThreads + tid)*VEC) / kSub
+    // this thread's vectors k cover tokens c0 + (k*kThreads + tid)*VEC +
+    // [0, VEC): vector k lies in sub-chunk ((k*kThreads + tid)*VEC) / kSub of
+    // the workgroup's tokens, i.e. in record sub-chunk / kSweepSubs
     const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
     const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
-    const int c0 = c * kChunk, c1 = min(c0 + kChunk, a.V);
+    const int c0 = c * PER * kSweepChunk, c1 = min(c0 + PER * kSweepChunk, a.V);
     u32x4 qt[NV], qd[NV];
     double sa = 0.0, sb = 0.0, dmin = INFINITY;
     double A[NV], Bq[NV];  // per vector: the sums its sub-chunk's mass is formed from
@@ -2461,10 +2507,11 @@ __device__ void sweep_role(const Args& a, const int idx) {
     }
     __syncthreads();
     if (tid == 0) {
-        double v[kChunkWords];
+        constexpr int WPR = sweep_words(PER);
+        double v[WPR];
         v[0] = v[1] = 0.0;
         v[2] = INFINITY;
-        for (int i = 3; i < kChunkWords; ++i) v[i] = 0.0;
+        for (int i = 3; i < WPR; ++i) v[i] = 0.0;
         for (int w = 0; w < kWaves; ++w) {
             v[0] += red[w][0];
             v[1] += red[w][1];
@@ -2477,12 +2524,12 @@ __device__ void sweep_role(const Args& a, const int idx) {
                 v[3 + 2 * sc] += red[w][3 + 2 * k];
                 v[4 + 2 * sc] += red[w][4 + 2 * k];
             }
-        uint64_t* dst = a.fsums + ((size_t)b * a.C2 + c) * kChunkWords;
-        for (int i = 0; i < kChunkWords; ++i) store_word(dst + i, enc_nonneg(v[i]));
+        uint64_t* dst = a.fsums + ((size_t)b * C2w + c) * WPR;
+        for (int i = 0; i < WPR; ++i) store_word(dst + i, enc_nonneg(v[i]));
     }
     // the workgroup of the request's last chunk (the last of its sweep
     // workgroups to start) draws; the others are done
-    if (c == a.C2 - 1) draw_terminal<T, MODE>(a, b, cd, rs, tab);
+    if (c == C2w - 1) draw_terminal<T, MODE, PER>(a, b, cd, rs, tab);
 }
 
 // The single launch of an exact, relaxed or power call.  Its first nstream
@@ -2493,8 +2540,8 @@ __device__ void sweep_role(const Args& a, const int idx) {
 // The sweep workgroups follow, request by request; they start while the
 // stream runs, and each waits only for its own request's records (and the
 // drawing workgroup, the last of its request to start, for the sums of the
-// others).
-template <typename T, int MODE, bool VECP>
+// others).  PER: 2048-token records per sweep workgroup.
+template <typename T, int MODE, bool VECP, int PER>
 __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_single(const Args a) {
     const unsigned P = (unsigned)a.nstream, ntiles = (unsigned)(a.B * a.R * a.tpr);
     if (blockIdx.x < P) {
@@ -2502,7 +2549,7 @@ __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_single(const 
             stream_tile<T, MODE, true, VECP, false, false, kTileVecs, true>(a, t);
         return;
     }
-    sweep_role<T, MODE>(a, (int)(blockIdx.x - P));
+    sweep_role<T, MODE, PER>(a, (int)(blockIdx.x - P));
 }
 
 // The deciding workgroup of request b in the greedy rule's single launch:
@@ -2943,20 +2990,29 @@ spec_status launch_single(Args a, spec_dtype dt, hipStream_t st) {
     a.frow = reinterpret_cast<uint64_t*>(a.ws + lay.frow);
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     a.nstream = min(a.B * a.R * a.tpr, stream_workgroups());
-    const dim3 grid((unsigned)a.nstream + (unsigned)a.B * (unsigned)a.C2), block(kThreads);
+    const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
+    // Aligned bf16 rows take one sweep workgroup per 2048-token record when
+    // the chip holds them all at once beside the streamers' slots (measured
+    // faster at B=32, V=128256); otherwise, and on the other paths, one per
+    // two records (twice the workgroups was slower at B=64, V=151936).
+    a.C2s = (a.V + kSweepChunk - 1) / kSweepChunk;
+    const bool per1 = dt == SPEC_BF16 && vecp && (long long)a.B * a.C2s <= stream_workgroups();
+    const int C2w = per1 ? a.C2s : (a.C2s + kSweepSplit - 1) / kSweepSplit;
+    const dim3 grid((unsigned)a.nstream + (unsigned)a.B * (unsigned)C2w), block(kThreads);
     hipEvent_t ev[3];
     take_prof(ev);
-    const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
     if (dt == SPEC_BF16) {
-        if (vecp)
-            hipExtLaunchKernelGGL((k_single<uint16_t, MODE, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        if (per1)
+            hipExtLaunchKernelGGL((k_single<uint16_t, MODE, true, 1>), grid, block, 0, st, ev[0], ev[1], 0, a);
+        else if (vecp)
+            hipExtLaunchKernelGGL((k_single<uint16_t, MODE, true, 2>), grid, block, 0, st, ev[0], ev[1], 0, a);
         else
-            hipExtLaunchKernelGGL((k_single<uint16_t, MODE, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
+            hipExtLaunchKernelGGL((k_single<uint16_t, MODE, false, 2>), grid, block, 0, st, ev[0], ev[1], 0, a);
     } else {
         if (vecp)
-            hipExtLaunchKernelGGL((k_single<float, MODE, true>), grid, block, 0, st, ev[0], ev[1], 0, a);
+            hipExtLaunchKernelGGL((k_single<float, MODE, true, 2>), grid, block, 0, st, ev[0], ev[1], 0, a);
         else
-            hipExtLaunchKernelGGL((k_single<float, MODE, false>), grid, block, 0, st, ev[0], ev[1], 0, a);
+            hipExtLaunchKernelGGL((k_single<float, MODE, false, 2>), grid, block, 0, st, ev[0], ev[1], 0, a);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return SPEC_EHIP;
