@@ -2394,8 +2394,12 @@ __device__ bool read_row_records(const Args& a, int b, RowStats& rs, int nrows) 
     return ok;
 }
 
-// One sweep workgroup: request idx / C2w, tokens [PER * kSweepChunk * c,
-// PER * kSweepChunk * (c + 1)) with c = idx % C2w; publishes one record.
+// One sweep workgroup: request b, tokens [PER * kSweepChunk * c,
+// PER * kSweepChunk * (c + 1)); publishes one record.  The first F =
+// min(R, C2w) workgroups of every request fold its rows: they come first in
+// index order, request by request (idx < B * F), so they start while the
+// stream runs and fold each row as its tiles arrive; the request's other
+// workgroups follow, request by request, and find the row records there.
 template <typename T, int MODE, int PER>
 __device__ void sweep_role(const Args& a, const int idx) {
     constexpr bool EXACT = (MODE == kExact);
@@ -2403,7 +2407,16 @@ __device__ void sweep_role(const Args& a, const int idx) {
     constexpr int NV = PER * kSweepChunk / kThreads / VEC;  // 16-byte vectors per thread
     static_assert(NV * VEC * kThreads == PER * kSweepChunk && PER <= kSweepSplit, "whole vectors per thread");
     const int C2w = (a.C2s + PER - 1) / PER;  // sweep workgroups per request
-    const int b = idx / C2w, c = idx - b * C2w;
+    const int F = min(a.R, C2w);              // folding workgroups per request
+    int b, c;
+    if (idx < a.B * F) {
+        b = idx / F;
+        c = idx - b * F;
+    } else {
+        const int j = idx - a.B * F, nf = C2w - F;
+        b = j / nf;
+        c = F + (j - b * nf);
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
     __shared__ double tab[kExpTab];
     __shared__ RowStats rs;
@@ -2414,8 +2427,10 @@ __device__ void sweep_role(const Args& a, const int idx) {
     // c takes rows c, c + C2w, ... (only the first R workgroups have one) and
     // publishes the row's record; then every sweep workgroup of the request
     // reads the R row records.  A workgroup waits only on streaming
-    // workgroups and on its own request's first R sweep workgroups, which
-    // start before any later one.  The drafted tokens are loaded while the
+    // workgroups, on its request's folding workgroups (which publish their
+    // rows before they wait for anything but tiles, and start before every
+    // non-folding workgroup), and the drawer on the request's other sweep
+    // workgroups, which start before it.  The drafted tokens are loaded while the
     // exp table is computed, their logits (addresses depending on them)
     // while the row records are awaited.
     ChainVals cv;
