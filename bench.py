@@ -61,7 +61,7 @@ KERNEL_TIMED = {"exact": "k_single: the whole call (one launch)",
                 "relaxed": "k_single: the whole call (one launch)",
                 "greedy": "k_greedy: the whole call (one launch)",
                 "sample": "k_sample_rows: the whole call (one launch)",
-                "tree": "k_stream: the streaming kernel (k_decide follows)"}
+                "tree": "k_tree: the whole call (one launch)"}
 RUNS = 3  # timed replays of the captured steps; the median is reported
 METRIC = "verify rounds/s + achieved HBM GB/s (% of peak), B=32 K=5 V=128256 bf16"
 

@@ -25,12 +25,13 @@
 //
 //   exact, relaxed, power: one launch (k_single).  Its first workgroups
 //             stream the tiles in a grid-stride loop and publish each tile's
-//             record; one sweep workgroup per (request, 4096-token chunk):
-//             the first R of a request each fold one row's records and
-//             publish the row's record, then every one reads the row
-//             records, decides, sums its chunk of the terminal row(s) in
-//             fp64 and publishes the sums; the request's last-chunk
-//             workgroup draws the terminal token.
+//             record; one sweep workgroup per (request, 2048- or 4096-token
+//             chunk): the first R of a request (first in index order,
+//             before every request's other sweep workgroups) each fold one
+//             row's records and publish the row's record, then every one
+//             reads the row records, decides, sums its chunk of the
+//             terminal row(s) in fp64 and publishes the sums; the request's
+//             last sweep workgroup draws the terminal token.
 //
 //   greedy: one launch (k_greedy): one workgroup per tile publishes the
 //             tile's record, then one deciding workgroup per request folds
@@ -1874,12 +1875,13 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
 // The exact, relaxed and power rules run as one launch per call, with no
 // kernel boundary between the stream and the terminal draw.  The launch's
 // first nstream workgroups stream tiles (stream_tile, records published).
-// Behind them, one sweep workgroup per (request, 4096-token chunk) waits for
-// its request's records, folds them and takes the decision (the same fold
-// and decision in every workgroup of the request), writes the accepted
-// prefix (chunk 0), sums its chunk of the terminal row(s) in fp64 and
-// publishes the sums.  The workgroup of the request's last chunk then waits
-// for all of the request's chunk sums, draws the terminal token
+// Behind them, one sweep workgroup per (request, 2048- or 4096-token chunk)
+// waits for its request's row records (folded once per row by the request's
+// first sweep workgroups) and takes the decision (the same decision in every
+// workgroup of the request), writes the accepted prefix (chunk 0), sums its
+// chunk of the terminal row(s) in fp64 and publishes the sums.  The
+// request's last sweep workgroup then waits for all of the request's chunk
+// sums, draws the terminal token
 // (draw_terminal) and zeroes the request's published words for the next
 // call: every other workgroup of the request has read the records before it
 // published its sums.
