@@ -244,6 +244,27 @@ def test_exact_greedy_relaxed_ragged_shapes(B, K, V, dtype):
     compare_chain(_relaxed(ci), orl, what=f"relaxed {B},{K},{V}")
 
 
+@pytest.mark.parametrize("B,K,V", [(32, 3, 131072), (33, 3, 131072), (32, 2, 129025), (33, 2, 129025)])
+def test_sweep_chunking_boundary(B, K, V):
+    """The exact, power and relaxed launches sum the terminal rows in 2048-token
+    sweep chunks while B * ceil(V / 2048) <= 2048 (the chip's resident
+    workgroups beside the streamers) and in 4096-token chunks above: B = 32
+    and 33 sit on either side of it, and V = 129025 leaves a one-token last
+    chunk."""
+    print(f"sweep boundary B={B} K={K} V={V}", flush=True)
+    ci = synth.chain_inputs(B, K, V, "bf16", seed=3100 + B, useed=3200 + V % 97)
+    compare_chain(_exact(ci), oracle.exact(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16"),
+                  what=f"exact {B},{K},{V}")
+    T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
+    r = sv.spec_verify_power(T, D, dev(ci.tokens), dev(ci.uniforms), 0.5)
+    torch.cuda.synchronize()
+    compare_chain(r, oracle.power(ci.target, ci.draft, ci.tokens, ci.uniforms, "bf16", 0.5),
+                  what=f"power {B},{K},{V}")
+    ci.tau, ci.top_k = 0.1, 4
+    compare_chain(_relaxed(ci), oracle.relaxed(ci.target, ci.tokens, ci.uniforms, "bf16", 0.1, 4),
+                  what=f"relaxed {B},{K},{V}")
+
+
 def test_misaligned_rows_take_element_path():
     """A view starting one element into an allocation is not 16-byte aligned."""
     ci = synth.chain_inputs(3, 4, 4096, "bf16", seed=81, useed=82)
