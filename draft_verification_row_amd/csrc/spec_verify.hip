@@ -100,6 +100,25 @@ static_assert(kMaxTiles <= 64, "a row's tile records must fit one wave");
 constexpr int kMaxC2 = (SPEC_MAX_V + kChunk - 1) / kChunk;
 static_assert(kMaxC2 <= 64, "a row's pass-2 chunks must fit one wave");
 
+// Sub-chunks: a sweep workgroup publishes its chunk's masses per 1024-token
+// sub-chunk, so the draw rescans 1024 tokens (four per thread) instead of a
+// whole chunk.
+constexpr int kSub = 1024;
+constexpr int kSubs = kChunk / kSub;
+
+// A sweep workgroup of the single launch sums PER * kSweepChunk tokens
+// (PER = 1 or 2: half of a draw chunk or all of it) and publishes one
+// record: S, Sq, dmin and its sub-chunks' two sums (sweep_words(PER) words:
+// seven or eleven).  The drawer's lane l combines the kSweepSplit / PER
+// records of draw chunk l.  Half-chunk sweeps give twice the workgroups, each
+// with half the fp64 work, which shortens the slowest one while the chip
+// holds them all at once.
+constexpr int kSweepChunk = 2048;
+constexpr int kSweepSplit = kChunk / kSweepChunk;
+constexpr int kSweepSubs = kSweepChunk / kSub;
+constexpr int sweep_words(int per) { return 3 + 2 * per * kSweepSubs; }
+static_assert(kSweepSplit * kSweepChunk == kChunk && kSweepSubs * kSub == kSweepChunk, "whole sub-chunks");
+
 enum Mode { kGreedy = 0, kExact = 1, kRelaxed = 2, kTree = 3, kPower = 4 };
 
 // Rules that stream the draft rows and test p/q.
@@ -155,7 +174,10 @@ inline Layout make_layout(int B, int R, int tpr, int C2) {
     Layout L;
     L.frec = 0;
     L.fsums = align_up(L.frec + (size_t)B * R * tpr * 16, 256);
-    L.frow = align_up(L.fsums + (size_t)B * C2 * (kChunk / 2048) * (3 + 2 * (2048 / 1024)) * 8, 256);
+    // the most any call publishes there: B * C2 * kSweepSplit sweep records of
+    // sweep_words(1) words (at least B * C2 records of sweep_words(2), and the
+    // draft sampler's two words per chunk)
+    L.frow = align_up(L.fsums + (size_t)B * C2 * kSweepSplit * sweep_words(1) * 8, 256);
     L.total = align_up(L.frow + (size_t)B * R * 16, 256);
     return L;
 }
@@ -1886,28 +1908,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const Args a) {
 // call: every other workgroup of the request has read the records before it
 // published its sums.
 
-// Sub-chunks: a sweep workgroup publishes its chunk's masses per 1024-token
-// sub-chunk, so the draw rescans 1024 tokens (four per thread) instead of a
-// whole chunk.  Published per chunk: the chunk's exp sums of the target and
-// draft rows (S, Sq), dmin (see ChunkSums), then per sub-chunk the two sums
-// the draw's mass is formed from (target and draft exp sums over the tokens
+// A sweep record holds the chunk's exp sums of the target and draft rows (S,
+// Sq), dmin (see ChunkSums), then per 1024-token sub-chunk the two sums the
+// draw's mass is formed from (target and draft exp sums over the tokens
 // classified p > q for a residual draw, the target exp sum otherwise).
-constexpr int kSub = 1024;
-constexpr int kSubs = kChunk / kSub;
-
-// A sweep workgroup sums PER * kSweepChunk tokens (PER = 1 or 2: half of a
-// draw chunk or all of it) and publishes one record: S, Sq, dmin and its
-// sub-chunks' two sums (3 + 2 * PER * kSweepSubs words: seven or eleven).
-// The drawer's lane l combines the kSweepSplit / PER records of draw chunk l.
-// Half-chunk sweeps give twice the workgroups, each with half the fp64 work,
-// which shortens the slowest one while the chip holds them all at once.
-constexpr int kSweepChunk = 2048;
-constexpr int kSweepSplit = kChunk / kSweepChunk;
-constexpr int kSweepSubs = kSweepChunk / kSub;
-constexpr int sweep_words(int per) { return 3 + 2 * per * kSweepSubs; }
-static_assert(kSweepSplit * kSweepChunk == kChunk && kSweepSubs * kSub == kSweepChunk, "whole sub-chunks");
-static_assert(kSweepChunk == 2048 && sweep_words(1) == 7 && sweep_words(2) == 11,
-              "make_layout sizes the sweep records");
 
 // Drafted-token logits read from the inputs (the token is loaded first, so
 // these loads wait for it; they overlap the wait for the records).
