@@ -2885,6 +2885,7 @@ inline int esize(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
 // lookup fails); a single launch streams with kStreamPerCu workgroups per
 // compute unit.
 constexpr int kStreamPerCu = 8;
+constexpr int kStreamPerCuBig = 6;  // single launches whose sweep workgroups outnumber the streamers
 constexpr int kMaxCuCache = 64;
 std::atomic<int> g_cus[kMaxCuCache];
 inline int compute_units() {
@@ -3010,14 +3011,19 @@ spec_status launch_single(Args a, spec_dtype dt, hipStream_t st) {
     a.fsums = reinterpret_cast<uint64_t*>(a.ws + lay.fsums);
     a.frow = reinterpret_cast<uint64_t*>(a.ws + lay.frow);
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-    a.nstream = min(a.B * a.R * a.tpr, stream_workgroups());
     const bool vecp = a.vec_t && (!uses_draft(MODE) || a.vec_d);
     // Aligned bf16 rows take one sweep workgroup per 2048-token record when
     // the chip holds them all at once beside the streamers' slots (measured
     // faster at B=32, V=128256); otherwise, and on the other paths, one per
-    // two records (twice the workgroups was slower at B=64, V=151936).
+    // two records (twice the workgroups was slower at B=64, V=151936).  When
+    // they would not all fit, 6 streaming workgroups per compute unit leave
+    // two slots per unit to sweep workgroups during the stream (measured at
+    // B=64, K=8, V=151936: exact 75.3 -> 74.3 us, relaxed 44.3 -> 43.8; at
+    // B=32, V=128256 it made no difference to exact and slowed power).
     a.C2s = (a.V + kSweepChunk - 1) / kSweepChunk;
-    const bool per1 = dt == SPEC_BF16 && vecp && (long long)a.B * a.C2s <= stream_workgroups();
+    const bool big = (long long)a.B * a.C2s > stream_workgroups();
+    a.nstream = min(a.B * a.R * a.tpr, big ? kStreamPerCuBig * compute_units() : stream_workgroups());
+    const bool per1 = dt == SPEC_BF16 && vecp && !big;
     const int C2w = per1 ? a.C2s : (a.C2s + kSweepSplit - 1) / kSweepSplit;
     const dim3 grid((unsigned)a.nstream + (unsigned)a.B * (unsigned)C2w), block(kThreads);
     hipEvent_t ev[3];
