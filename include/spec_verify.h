@@ -43,8 +43,7 @@
  *                               [0,V), or a tree parent outside [-1, i)):
  *                               the offending draft counts as rejected and
  *                               the offending tree node as unmatched.  2
- *                               (greedy, exact, relaxed and power rules)
- *                               when a wait for data from another
+ *                               (every rule) when a wait for data from another
  *                               workgroup of the same launch ran out (about
  *                               a second); the request's other outputs are
  *                               then undefined.
@@ -58,15 +57,15 @@
  * Workspace
  *   Each call needs a device workspace of at least
  *   spec_verify_workspace_bytes(B, rows_per_request, V) bytes, 256-byte
- *   aligned, for per-tile statistics and per-chunk sums passed between the
- *   call's workgroups.  It must be zero-filled before its first call (for
+ *   aligned, for the per-tile, per-row and per-chunk records passed between
+ *   the call's workgroups.  It must be zero-filled before its first call (for
  *   example allocated zeroed); every call leaves every byte of it zero
  *   again, so one workspace serves calls of any rule and shape in turn on
- *   the same stream with no further initialization.  (The greedy, exact,
- *   relaxed and power calls and the draft sampler run as one launch whose
- *   workgroups pass data through the workspace while the launch runs, and
- *   read a zero word as "not written yet".)  Calls that run concurrently (different streams) need different
- *   workspaces.  A call that reports status 2 for a request (see
+ *   the same stream with no further initialization.  (Every rule's call and
+ *   the draft sampler run as one launch whose workgroups pass data through
+ *   the workspace while the launch runs, and read a zero word as "not
+ *   written yet".)  Calls that run concurrently (different streams) need
+ *   different workspaces.  A call that reports status 2 for a request (see
  *   out_status) may leave its workspace dirty: zero-fill it before reusing
  *   it.  The library allocates nothing and keeps no state besides the
  *   one-shot, per-thread profiling hook (spec_verify_profile_next_call) and
@@ -137,8 +136,8 @@ void spec_verify_profile_next_call(void *before_stream, void *after_stream, void
 /*
  * Host-only testing aid for callers that check the timeout path: the bound,
  * in polling rounds, of every wait a single-launch call (greedy, exact,
- * relaxed, power, draft sampler) makes for data from another workgroup of
- * the same launch.  Calls launched afterwards, from any thread, carry it.
+ * relaxed, power, tree, draft sampler) makes for data from another
+ * workgroup of the same launch.  Calls launched afterwards, from any thread, carry it.
  * With 0, a wait that does not find its data on the first poll gives up at
  * once: the request reports status 2 (its other outputs undefined, the
  * workspace possibly left dirty), and every kernel still ends.  A negative
