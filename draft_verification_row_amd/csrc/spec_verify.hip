@@ -1950,8 +1950,9 @@ __device__ inline void clear_published(const Args& a, int b, int sums_words) {
     for (int i = threadIdx.x; i < sums_words; i += blockDim.x) store_word(m + i, 0ull);
 }
 
-// The terminal draw of request b, by the sweep workgroup of its last chunk.
-// Wave 0 waits for the C2 published chunk records (lane = chunk), forms S,
+// The terminal draw of request b, by its last sweep workgroup.  Wave 0 waits
+// for the request's published sweep records (lane l = draw chunk l of 4096
+// tokens: one record, or two of 2048 tokens), forms S,
 // Sq, the exact p > q threshold and the sub-chunk masses, recomputes the
 // masses of chunks the streamed threshold may have classified otherwise,
 // scans the chunks and then the sub-chunks of the chunk holding u_K * Z.
@@ -2468,7 +2469,7 @@ __device__ void sweep_role(const Args& a, const int idx) {
 
     // this thread's vectors k cover tokens c0 + (k*kThreads + tid)*VEC +
     // [0, VEC): vector k lies in sub-chunk ((k*kThreads + tid)*VEC) / kSub of
-    // the workgroup's tokens, i.e. in record sub-chunk / kSweepSubs
+    // the workgroup's record
     const T* trow = reinterpret_cast<const T*>(a.T) + (size_t)(b * a.rows_t + n) * a.V;
     const T* drow = residual ? reinterpret_cast<const T*>(a.D) + (size_t)(b * a.K + n) * a.V : trow;
     const int c0 = c * PER * kSweepChunk, c1 = min(c0 + PER * kSweepChunk, a.V);
@@ -2548,8 +2549,8 @@ __device__ void sweep_role(const Args& a, const int idx) {
         uint64_t* dst = a.fsums + ((size_t)b * C2w + c) * WPR;
         for (int i = 0; i < WPR; ++i) store_word(dst + i, enc_nonneg(v[i]));
     }
-    // the workgroup of the request's last chunk (the last of its sweep
-    // workgroups to start) draws; the others are done
+    // the request's last sweep workgroup (the last of them to start) draws;
+    // the others are done
     if (c == C2w - 1) draw_terminal<T, MODE, PER>(a, b, cd, rs, tab);
 }
 
@@ -2558,10 +2559,11 @@ __device__ void sweep_role(const Args& a, const int idx) {
 // tiles complete about in index order, request by request, with about
 // nstream tiles in flight (enough to keep HBM busy; few enough that the
 // other workgroups' loads do not queue behind many microseconds of them).
-// The sweep workgroups follow, request by request; they start while the
-// stream runs, and each waits only for its own request's records (and the
-// drawing workgroup, the last of its request to start, for the sums of the
-// others).  PER: 2048-token records per sweep workgroup.
+// The sweep workgroups follow: every request's folding workgroups first,
+// then the others, request by request; they start while the stream runs, and
+// each waits only for its own request's records (and the drawing workgroup,
+// the last of its request to start, for the sums of the others).  PER:
+// 2048-token chunks per sweep workgroup.
 template <typename T, int MODE, bool VECP, int PER>
 __global__ __launch_bounds__(kThreads, kStreamWavesPerSimd) void k_single(const Args a) {
     const unsigned P = (unsigned)a.nstream, ntiles = (unsigned)(a.B * a.R * a.tpr);
