@@ -54,7 +54,7 @@ def test_noalloc_argument_errors(lib):
     assert f(p, p, 1, p, p, 2, 3, 1000, None, p, None, None, p, None) == SPEC_EINVAL
     limit = 4 << 20
     q = lib.spec_verify_workspace_bytes
-    assert q(64, 17, 262144) <= limit            # the documented example fits
+    assert q(128, 17, 262144) <= limit           # the documented example fits
     assert q(1024, 11, 262144) > limit
     assert f(p, p, 0, p, p, 1024, 5, 262144, p, p, None, None, p, None) == SPEC_ESCRATCH
     assert f(p, p, 1, p, p, 4096, 5, 128256, p, p, None, None, p, None) == SPEC_ESCRATCH
