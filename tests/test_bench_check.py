@@ -72,3 +72,15 @@ def test_sampler_rows():
     i = np.unravel_index(int(np.flatnonzero(o.flag.ravel() == 0)[0]), o.flag.shape)
     out["tok"][i] = (out["tok"][i] + 1) % ci.V
     assert bench.check_outputs("sample", [out], o)["mismatched_rows"] == 1
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and a message,
+    before touching any device."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=root, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
+    assert not r.stdout.strip().startswith("{")  # no benchmark line
