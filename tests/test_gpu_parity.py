@@ -443,6 +443,41 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_concurrent_calls_on_two_streams():
+    """Calls on two streams (default priority) with their own workspaces run
+    concurrently: an exact call on one, an exact and a greedy call on the
+    other, five rounds without a synchronization between the streams; every
+    result equals the oracle's."""
+    a = synth.chain_inputs(32, 5, 128256, "bf16", seed=131, useed=132)
+    b = synth.chain_inputs(24, 4, 100003, "bf16", seed=133, useed=134)
+    Ta, Da, xa, ua = dev_logits(a.target, "bf16"), dev_logits(a.draft, "bf16"), dev(a.tokens), dev(a.uniforms)
+    Tb, Db, xb, ub = dev_logits(b.target, "bf16"), dev_logits(b.draft, "bf16"), dev(b.tokens), dev(b.uniforms)
+    ws_a = torch.zeros(sv.spec_verify_workspace_bytes(32, 11, 128256), dtype=torch.uint8, device="cuda")
+    ws_b = torch.zeros(sv.spec_verify_workspace_bytes(24, 9, 100003), dtype=torch.uint8, device="cuda")
+    ws_g = torch.zeros(sv.spec_verify_workspace_bytes(24, 5, 100003), dtype=torch.uint8, device="cuda")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    res = []
+    for rnd in range(5):
+        print(f"concurrent round {rnd}", flush=True)
+        with torch.cuda.stream(sa):
+            ra = sv.spec_verify_exact(Ta, Da, xa, ua, workspace=ws_a)
+        with torch.cuda.stream(sb):
+            rb = sv.spec_verify_exact(Tb, Db, xb, ub, workspace=ws_b)
+            rg = sv.spec_verify_greedy(Tb, xb, workspace=ws_g)
+        res.append((ra, rb, rg))
+    torch.cuda.synchronize()
+    oa = oracle.exact(a.target, a.draft, a.tokens, a.uniforms, "bf16")
+    ob = oracle.exact(b.target, b.draft, b.tokens, b.uniforms, "bf16")
+    og = oracle.greedy(b.target, b.tokens, "bf16")
+    for rnd, (ra, rb, rg) in enumerate(res):
+        compare_chain(ra, oa, what=f"stream a, round {rnd}")
+        compare_chain(rb, ob, what=f"stream b exact, round {rnd}")
+        compare_chain(rg, og, what=f"stream b greedy, round {rnd}")
+    for ws in (ws_a, ws_b, ws_g):
+        assert int(ws.count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_largest_vocabulary(dtype):
     """V = 262144: in fp32 a row has 64 tile records and 64 pass-2 chunks, so
