@@ -85,6 +85,33 @@ def test_noalloc_after_a_timed_out_call():
                   what="no-alloc exact after a timed-out call")
 
 
+def test_noalloc_captured_in_a_graph():
+    """The allocation-free call captured into a HIP graph: each replay, with
+    eager allocation-free calls on other inputs in between (which leave their
+    own words in the shared static array), equals the eager result."""
+    lib = sv.load_library()
+    ci = synth.exact_b32_k5()
+    T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
+    x, u = dev(ci.tokens), dev(ci.uniforms)
+    eager = [t.clone() for t in _noalloc(lib, T, D, x, u)]
+    other = synth.chain_inputs(8, 3, 50000, "bf16", seed=991, useed=992)
+    To, Do = dev_logits(other.target, "bf16"), dev_logits(other.draft, "bf16")
+    xo, uo = dev(other.tokens), dev(other.uniforms)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        captured = _noalloc(lib, T, D, x, u)
+    for rep in range(3):
+        print(f"no-alloc graph replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b, name in zip(eager, captured, sv.VerifyResult._fields):
+            assert torch.equal(a, b), f"{name} differs on replay {rep}"
+        _noalloc(lib, To, Do, xo, uo)  # eager work on the same static array
+        torch.cuda.synchronize()
+
+
 def test_noalloc_rejects_calls_beyond_the_scratch_array():
     lib = sv.load_library()
     T = torch.zeros((1, 6, 16), dtype=torch.bfloat16, device="cuda")
