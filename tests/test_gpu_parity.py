@@ -404,9 +404,9 @@ def test_read_ceiling_kernel_runs_on_odd_sizes():
 
 
 def test_graph_capture_replays_match_eager():
-    """Calls captured in a HIP graph: every replay equals the eager result bit
-    for bit, with other eager calls (reusing the same workspace) between the
-    replays."""
+    """Calls captured in a HIP graph (every rule and the draft sampler): every
+    replay equals the eager result bit for bit, with other eager calls
+    (reusing the same workspace) between the replays."""
     ci = synth.chain_inputs(16, 5, 50000, "bf16", seed=111, useed=112)
     T, D = dev_logits(ci.target, "bf16"), dev_logits(ci.draft, "bf16")
     x, u = dev(ci.tokens), dev(ci.uniforms)
@@ -415,11 +415,17 @@ def test_graph_capture_replays_match_eager():
                      device="cuda")
     ws_s = torch.zeros(sv.spec_sample_workspace_bytes(B * K, V), dtype=torch.uint8, device="cuda")
     ud = u[:, :K].contiguous()
+    ti = synth.tree_inputs(B=4, V=50000, seed=115)
+    Tt, tok_t, par_t, nn_t = dev_logits(ti.target, "bf16"), dev(ti.node_tok), dev(ti.parents), dev(ti.num_nodes)
+    ws_t = torch.zeros(sv.spec_verify_workspace_bytes(ti.B, ti.N, ti.V), dtype=torch.uint8, device="cuda")
 
     def calls():
         return (sv.spec_verify_exact(T, D, x, u, workspace=ws),
                 sv.spec_verify_greedy(T, x, workspace=ws),
                 sv.spec_verify_greedy(T, x, logprobs=False, workspace=ws),  # 8 KiB tiles
+                sv.spec_verify_relaxed(T, x, u, 0.1, 4, workspace=ws),
+                sv.spec_verify_power(T, D, x, u, 0.5, workspace=ws),
+                sv.spec_verify_tree(Tt, tok_t, par_t, nn_t, workspace=ws_t),
                 sv.spec_sample_drafts(D, ud, workspace=ws_s))
 
     eager = [[t.clone() for t in r if t is not None] for r in calls()]
