@@ -50,6 +50,12 @@ def _tree_cases(n, seed):
 
 CHAIN = _chain_cases(40, 4242)
 TREE = _tree_cases(16, 4343)
+# 2048-token sweep chunks (aligned bf16 rows): V at and around their
+# boundaries, a multiple of 8 so the rows take the 16-byte path
+CHAIN += [dict(i=100 + j, B=B, K=K, V=V, dtype="bf16", scale=sc, noise=nz, tau=0.1, top_k=3, alpha=0.5)
+          for j, (B, K, V, sc, nz) in enumerate([(3, 4, 2040, 3.0, 0.5), (5, 2, 2048, 0.3, 2.0),
+                                                 (4, 6, 2056, 12.0, 0.1), (2, 3, 6136, 3.0, 2.0),
+                                                 (6, 5, 6144, 3.0, 0.5), (3, 8, 6152, 0.3, 0.5)])]
 
 
 def _sync(r):
